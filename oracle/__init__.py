@@ -1,0 +1,268 @@
+"""CPU oracle for the RHT + lattice + bit-strip + Rice codec -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this package.  The product path (``kv_quantization_tile_amd``) never imports it, and it never imports
+the product.  The C source ``hq_oracle.c`` is compiled with gcc, ``-O2 -ffp-contract=off``, no
+fast-math, so that every binary32 operation is rounded exactly once in the order written.
+
+The method follows the HyperQuant technical summaries (gist.science/ko/paper/2606.23406 and
+gist.science/ja/paper/2606.23406), "Methodology: the HyperQuant pipeline", components 1-4.
+
+Parity: the tests pin each function to something outside this package (a dense Hadamard matrix,
+brute-force nearest-point search, closed forms, the rocRAND Philox source, statistical invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hq_oracle.c")
+_LIB = os.path.join(_HERE, "libhq_oracle.so")
+
+LAT_Z, LAT_D4, LAT_E8 = 0, 1, 2
+LATTICES = {"z": LAT_Z, "d4": LAT_D4, "e8": LAT_E8}
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NONFINITE, ERR_CAPACITY, ERR_CORRUPT, ERR_RATE = (
+    0, -1, -2, -3, -4, -5, -6)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/libhq_oracle.so`` with gcc."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        u64, u32, i32, f32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float
+        L.hqo_philox4x32_10.argtypes = [P, P, P]
+        L.hqo_signs.argtypes = [u64, P]
+        L.hqo_fwht128.argtypes = [P]
+        L.hqo_sumsq128.argtypes = [P]
+        L.hqo_sumsq128.restype = f32
+        L.hqo_scale_bits.argtypes = [f32]
+        L.hqo_scale_bits.restype = ctypes.c_uint16
+        L.hqo_nearest_octet.argtypes = [i32, P, P]
+        L.hqo_nearest_batch.argtypes = [i32, P, u64, P]
+        L.hqo_dither_octet.argtypes = [u64, u64, i32, i32, P]
+        L.hqo_strip_octet.argtypes = [i32, P, P, P]
+        L.hqo_unstrip_octet.argtypes = [i32, P, i32, P]
+        L.hqo_tile_fixed_bits.argtypes = [i32, i32]
+        L.hqo_tile_fixed_bits.restype = u32
+        L.hqo_quantize.argtypes = [P, i32, u64, i32, i32, u64, f32, P, P]
+        L.hqo_dequantize.argtypes = [P, P, u64, i32, i32, u64, f32, P]
+        L.hqo_sample_tile.argtypes = [u64, u64, u64]
+        L.hqo_sample_tile.restype = u64
+        L.hqo_rate.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, P]
+        L.hqo_rice_roundtrip.argtypes = [P, u64, i32, P, P, P, u64, P]
+        L.hqo_encode_layout.argtypes = [u64, i32, i32, P, P, P]
+        L.hqo_encode.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, u64, P, P]
+        L.hqo_decode.argtypes = [P, u64, u64, P, i32]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return 0
+    if x.dtype == np.uint16:  # bfloat16 bit patterns
+        return 1
+    raise TypeError("oracle input must be float32 or uint16 (bfloat16 bits)")
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: oracle status {code}")
+        self.code = code
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise OracleError(rc, what)
+
+
+# ---- primitives ---------------------------------------------------------------------------------
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().hqo_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def signs(seed: int) -> np.ndarray:
+    d = np.zeros(128, dtype=np.float32)
+    lib().hqo_signs(seed, _p(d))
+    return d
+
+
+def fwht128(x) -> np.ndarray:
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    assert y.shape == (128,)
+    lib().hqo_fwht128(_p(y))
+    return y
+
+
+def sumsq128(y) -> float:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    return float(lib().hqo_sumsq128(_p(y)))
+
+
+def scale_bits(S: float) -> int:
+    return int(lib().hqo_scale_bits(ctypes.c_float(S)))
+
+
+def nearest(lattice: int, v) -> np.ndarray:
+    """Nearest-point integer codes for an array of octets, shape (..., 8)."""
+    v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1, 8)
+    out = np.zeros(v.shape, dtype=np.int32)
+    _check(lib().hqo_nearest_batch(lattice, _p(v), v.shape[0], _p(out)), "nearest")
+    return out
+
+
+def dither_octet(seed: int, tile: int, octet: int, lattice: int) -> np.ndarray:
+    u = np.zeros(8, dtype=np.float32)
+    lib().hqo_dither_octet(seed, tile, octet, lattice, _p(u))
+    return u
+
+
+def strip_octet(lattice: int, code):
+    c = np.ascontiguousarray(code, dtype=np.int32)
+    sym = np.zeros(8, dtype=np.uint32)
+    cos = ctypes.c_int(0)
+    _check(lib().hqo_strip_octet(lattice, _p(c), _p(sym), ctypes.byref(cos)), "strip")
+    return sym, cos.value
+
+
+def unstrip_octet(lattice: int, sym, coset: int) -> np.ndarray:
+    s = np.ascontiguousarray(sym, dtype=np.uint32)
+    out = np.zeros(8, dtype=np.int32)
+    _check(lib().hqo_unstrip_octet(lattice, _p(s), coset, _p(out)), "unstrip")
+    return out
+
+
+def tile_fixed_bits(lattice: int, k: int) -> int:
+    return int(lib().hqo_tile_fixed_bits(lattice, k))
+
+
+def sample_tile(i: int, T: int, N: int) -> int:
+    return int(lib().hqo_sample_tile(i, T, N))
+
+
+def rice_roundtrip(vals, k: int):
+    v = np.ascontiguousarray(vals, dtype=np.uint32)
+    n = v.size
+    out = np.zeros(n, dtype=np.uint32)
+    fixed = np.zeros((k * n + 7) // 8 + 8, dtype=np.uint8)
+    ubits = int(sum(int(a) >> k for a in v) + n)
+    unary = np.zeros((ubits + 7) // 8 + 8, dtype=np.uint8)
+    ulen = ctypes.c_uint64(0)
+    _check(lib().hqo_rice_roundtrip(_p(v), n, k, _p(out), _p(fixed), _p(unary), ubits + 64,
+                                    ctypes.byref(ulen)), "rice")
+    return out, ulen.value
+
+
+# ---- the codec ----------------------------------------------------------------------------------
+
+def quantize(x: np.ndarray, lattice: int, step: float, seed: int = 0, dither: bool = False):
+    """Per-value integer codes (int32) and per-tile bf16 scale bits (uint16) at a fixed step."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    n = x.size
+    codes = np.zeros(n, dtype=np.int32)
+    scales = np.zeros(max(n // 128, 1), dtype=np.uint16)
+    _check(lib().hqo_quantize(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
+                              ctypes.c_float(step), _p(codes), _p(scales)), "quantize")
+    return codes, scales[: n // 128]
+
+
+def dequantize(codes, scales, lattice: int, step: float, seed: int = 0, dither: bool = False):
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    out = np.zeros(codes.size, dtype=np.float32)
+    _check(lib().hqo_dequantize(_p(codes), _p(scales), codes.size, lattice, int(bool(dither)), seed,
+                                ctypes.c_float(step), _p(out)), "dequantize")
+    return out
+
+
+def rate(x, lattice: int, target_bps: float, seed: int = 0, dither: bool = False, step: float = 0.0,
+         rice_k: int = -1):
+    """Rate control only: returns (step as float32, step bit pattern, k)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    sb = ctypes.c_uint32(0)
+    k = ctypes.c_int(0)
+    _check(lib().hqo_rate(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
+                          ctypes.c_float(target_bps), ctypes.c_float(step), rice_k,
+                          ctypes.byref(sb), ctypes.byref(k)), "rate")
+    step_f = np.array([sb.value], dtype=np.uint32).view(np.float32)[0]
+    return float(step_f), sb.value, k.value
+
+
+def layout(n: int, lattice: int, k: int):
+    fo, uo, F = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint32(0)
+    lib().hqo_encode_layout(n, lattice, k, ctypes.byref(fo), ctypes.byref(uo), ctypes.byref(F))
+    return fo.value, uo.value, F.value
+
+
+def encode(x, lattice: int, target_bps: float = 4.0, seed: int = 0, dither: bool = False,
+           step: float = 0.0, rice_k: int = -1, capacity: int | None = None):
+    """Full encoder.  Returns (stream bytes as uint8 array, info dict)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    n = x.size
+    if capacity is None:
+        capacity = 4096 + n * 4
+    info = np.zeros(4, dtype=np.uint64)
+    nbytes = ctypes.c_uint64(0)
+    while True:
+        out = np.zeros(capacity, dtype=np.uint8)
+        rc = lib().hqo_encode(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
+                              ctypes.c_float(target_bps), ctypes.c_float(step), rice_k, _p(out),
+                              capacity, ctypes.byref(nbytes), _p(info))
+        if rc == ERR_CAPACITY and nbytes.value > capacity:
+            capacity = int(nbytes.value)
+            continue
+        _check(rc, "encode")
+        break
+    step_f = np.array([info[0]], dtype=np.uint64).astype(np.uint32).view(np.float32)[0]
+    d = {"step": float(step_f), "step_bits": int(info[0]), "k": int(info[1]),
+         "payload_bits": int(info[2]), "unary_bits": int(info[3]), "bytes": int(nbytes.value),
+         "payload_bps": float(info[2]) / n if n else 0.0,
+         "total_bps": 8.0 * float(nbytes.value) / n if n else 0.0}
+    return out[: nbytes.value].copy(), d
+
+
+def decode(stream, n: int, out_dtype: str = "f32"):
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    if out_dtype == "f32":
+        out = np.zeros(n, dtype=np.float32)
+        code = 0
+    else:
+        out = np.zeros(n, dtype=np.uint16)
+        code = 1
+    _check(lib().hqo_decode(_p(s), s.size, n, _p(out), code), "decode")
+    return out
+
+
+def decode_status(stream, n: int) -> int:
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(max(n, 1), dtype=np.float32)
+    return int(lib().hqo_decode(_p(s), s.size, n, _p(out), 0))

@@ -1,0 +1,79 @@
+"""Pins of the oracle's Rice coder and bitstream (HyperQuant summary, gist.science/ko/paper/2606.23406,
+Methodology component 3: remaining symbols are Rice-coded; the coding is lossless).
+
+Exhaustive Rice round trips on a small domain, the code-length formula, whole-stream round trips
+(decode(encode(x)) equals the direct dequantisation of the quantiser's codes), and corrupt-stream
+rejection.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+
+def test_rice_exhaustive_roundtrip_and_length(orc):
+    vals = np.arange(4096, dtype=np.uint32)
+    for k in range(16):
+        out, ulen = orc.rice_roundtrip(vals, k)
+        assert np.array_equal(out, vals)
+        assert ulen == int(np.sum(vals >> k)) + vals.size     # unary part: q zeros + a one
+
+
+@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("dither", [False, True])
+def test_stream_roundtrip_equals_dequantisation(orc, lattice, dither):
+    L = orc.LATTICES[lattice]
+    x = synth.tiny(seed=3, tiles=130)          # two full chunks + a ragged one
+    s, info = orc.encode(x, L, 3.0, seed=7, dither=dither)
+    y = orc.decode(s, x.size)
+    codes, scales = orc.quantize(x, L, info["step"], seed=7, dither=dither)
+    ref = orc.dequantize(codes, scales, L, info["step"], seed=7, dither=dither)
+    assert np.array_equal(y, ref)
+    # bf16 output is the round-to-nearest-even of the fp32 output
+    yb = orc.decode(s, x.size, out_dtype="bf16")
+    assert np.array_equal(yb, synth.bf16_bits(ref))
+    # stream size bookkeeping
+    assert info["bytes"] == s.size
+    fo, uo, F = orc.layout(x.size, L, info["k"])
+    assert info["payload_bits"] == 130 * (F - 16) + info["unary_bits"]
+
+
+def test_bf16_input_and_empty(orc):
+    w = synth.weight(rows=16, cols=512)
+    s, info = orc.encode(w, orc.LAT_E8, 4.0)
+    y = orc.decode(s, w.size)
+    codes, scales = orc.quantize(w, orc.LAT_E8, info["step"])
+    assert np.array_equal(y, orc.dequantize(codes, scales, orc.LAT_E8, info["step"]))
+    e = np.zeros(0, dtype=np.float32)
+    s0, info0 = orc.encode(e, orc.LAT_E8, 4.0)
+    assert s0.size == info0["bytes"] and orc.decode(s0, 0).size == 0
+
+
+def test_fixed_step_and_k(orc):
+    x = synth.tiny(seed=4)
+    s, info = orc.encode(x, orc.LAT_E8, 0.0, step=0.3, rice_k=5)
+    assert info["k"] == 5 and abs(info["step"] - 0.3) < 1e-7
+    codes, scales = orc.quantize(x, orc.LAT_E8, info["step"])
+    assert np.array_equal(orc.decode(s, x.size), orc.dequantize(codes, scales, orc.LAT_E8, info["step"]))
+
+
+def test_corrupt_streams_rejected(orc):
+    x = synth.tiny(seed=5)
+    s, info = orc.encode(x, orc.LAT_E8, 4.0)
+    assert orc.decode_status(s, x.size) == orc.OK
+    bad = s.copy(); bad[0] ^= 1
+    assert orc.decode_status(bad, x.size) == orc.ERR_CORRUPT           # magic
+    assert orc.decode_status(s, x.size + 128) == orc.ERR_CORRUPT       # wrong n
+    assert orc.decode_status(s[:-8], x.size) == orc.ERR_CORRUPT        # truncated
+    bad = s.copy(); bad[128 + 4] ^= 0xFF                                # chunk index end entry
+    assert orc.decode_status(bad, x.size) == orc.ERR_CORRUPT
+    bad = s.copy(); bad[-8:] = 0                                         # lose terminators
+    assert orc.decode_status(bad, x.size) == orc.ERR_CORRUPT
+
+
+def test_nonfinite_input(orc):
+    x = synth.tiny(seed=6).copy()
+    x[3, 7] = np.inf
+    with pytest.raises(orc.OracleError) as e:
+        orc.encode(x, orc.LAT_E8, 4.0, step=0.3, rice_k=2)
+    assert e.value.code == orc.ERR_NONFINITE
