@@ -1,0 +1,141 @@
+/*
+ * hq.h -- C ABI of the MI355X (gfx950) RHT + lattice + bit-strip + Rice codec.
+ *
+ * The method is the per-tile pipeline of the HyperQuant technical summary
+ * (gist.science/ko/paper/2606.23406; Japanese version gist.science/ja/paper/2606.23406), section
+ * "Methodology: the HyperQuant pipeline":
+ *   component 1  per-tile randomized Hadamard transform RHT_128(x) = H_128 D x (D: random +-1),
+ *   component 2  nearest-point quantisation onto E8 (or D4, or scalar Z) in an integer embedding,
+ *                scaled so the rotated tile matches the lattice,
+ *   component 3  stripping of the bits that lattice membership fixes, then Rice coding, with the
+ *                realised rate within ~0.01 bits per value of the target,
+ *   component 4  for KV caches: a per-layer +-1 rotation (folded into D through the seed) and a
+ *                subtractive dither U ~ Uniform(V(lattice)) added before and removed after.
+ *
+ * Conventions of every entry point:
+ *  - Pointers named x, out, stream, workspace are DEVICE pointers (HIP global memory of the current
+ *    device); `params`, `info`, `out_bytes` are HOST pointers.  `stream` arguments of type
+ *    hq_stream_t are hipStream_t values (0 = the null stream).
+ *  - The caller owns every buffer.  The library allocates no device memory and keeps no state
+ *    between calls apart from immutable constants; one workspace serves one call in flight.
+ *  - Tensors are flat arrays of n values, n a multiple of 128; tile t is values [128 t, 128 t + 128).
+ *  - Every call returns HQ_OK (0) or a negative hq_status code; no exception crosses the ABI.
+ *  - Errors found on the device (non-finite input, too small an output buffer, corrupt stream) are
+ *    recorded in the workspace; blocking calls return them, hq_status() reads them otherwise.
+ *
+ * Bitstream (format version 1, little-endian; the pages give no format, this is the codec's own):
+ *   header, 128 bytes: u32 magic 'HQ01' | u16 version | u8 lattice | u8 flags (bit0 dither) |
+ *     u16 tile (128) | u8 rice k | u8 log2 tiles per chunk (6) | u32 step (binary32 bits) |
+ *     u64 seed | u64 n | u64 tiles | u32 chunks | u32 F (fixed bits per tile) | u64 fixed_off |
+ *     u64 unary_off | u64 unary_words | u64 unary_bits | u64 payload_bits | u64 total_bytes | 32 B 0
+ *   chunk index at byte 128: chunks+1 u32 offsets, in 64-bit words, into the unary plane
+ *   fixed plane at fixed_off = align256(128 + 4 (chunks+1)); chunk c = tiles 64c..64c+63, 8F bytes;
+ *     tile record at bit t F (bit i of a plane = bit i%8 of byte i/8): bf16 tile scale (16) |
+ *     E8 only: coset bit of octet o at bit o (16) | octet 0..15, slot 0..7: Rice remainder, width
+ *     k (full slots) or max(k-1,0) (the parity-fixed slot: 7 of E8, 3 and 7 of D4), LSB first
+ *   unary plane at unary_off = align256(fixed_off + 8 F chunks): chunk c's segment starts at word
+ *     index[c]; each symbol in (tile, octet, slot) order contributes (symbol >> width) zero bits
+ *     and a one; segments are zero-padded to 64 bits.
+ *   Symbols per octet (8 consecutive coordinates): E8: z in 2E8, p = z0 & 1, u = (z-p)/2,
+ *     slots zz(u0..u6), zz((u7 - (u0+..+u6 & 1))/2); D4 (two blocks): zz(x0..x2),
+ *     zz((x3 - (x0+x1+x2 & 1))/2); Z: zz(z0..z7); zz(a) = (a << 1) ^ (a >> 31).
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *hq_stream_t; /* a hipStream_t */
+
+typedef enum {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARG = -1, /* null pointer, bad enum, n % 128 != 0, n > 2^35, step outside 2^+-12 */
+  HQ_ERR_UNSUPPORTED = -2, /* tile size other than 128; or a unary plane of 2^32 words or more      */
+  HQ_ERR_NONFINITE = -3,   /* a tile whose transformed energy is NaN or Inf                         */
+  HQ_ERR_CAPACITY = -4,    /* output buffer too small; *out_bytes holds the size needed            */
+  HQ_ERR_CORRUPT = -5,     /* stream fails validation (header, index, segment, terminator count)   */
+  HQ_ERR_RATE = -6,        /* target rate outside [1.125 (E8) or 1.0 (D4, Z), 12] bits per value    */
+  HQ_ERR_HIP = -7,         /* a HIP runtime call failed                                             */
+  HQ_ERR_TIMEOUT = -8      /* the encoder's cross-workgroup wait exceeded its bound (never expected) */
+} hq_status_code;
+
+typedef enum { HQ_Z = 0, HQ_D4 = 1, HQ_E8 = 2 } hq_lattice;
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+
+typedef struct {
+  uint32_t tile;       /* values per tile; 128 is the only size (component 1: "tiles, e.g. 128")   */
+  int32_t lattice;     /* hq_lattice                                                                */
+  float target_bps;    /* payload bits per value (coset + Rice bits / n); used when step == 0       */
+  uint64_t seed;       /* Philox key of the sign diagonal D and of the dither                        */
+  uint32_t dither;     /* 0 = off, 1 = subtractive dither (component 4)                              */
+  float step;          /* 0 = choose by rate control; > 0 = fixed lattice step (KV append, tests)    */
+  int32_t rice_k;      /* -1 = automatic; 0..15 = fixed Rice parameter                              */
+} hq_params;
+
+typedef struct {
+  float step;           /* lattice step used                                                         */
+  int32_t rice_k;       /* Rice parameter used                                                       */
+  uint64_t bytes;       /* stream size                                                              */
+  uint64_t payload_bits;/* coset + remainder + unary bits                                            */
+  double payload_bps;   /* payload_bits / n: the rate that rate control targets                     */
+  double side_bps;      /* (tile scales + header + index + padding) bits / n                          */
+  double total_bps;     /* 8 bytes / n                                                              */
+} hq_info;
+
+/* Library and format version: returns (major << 16) | format_version. */
+uint32_t hq_version(void);
+
+/* Human-readable text of a status code (static storage). */
+const char *hq_strerror(int code);
+
+/* Bytes of device workspace that hq_encode / hq_rate / hq_decode / hq_codes need for n values
+ * (host only; no device call).  The workspace needs no initialisation. */
+int hq_workspace_size(uint64_t n, const hq_params *params, size_t *bytes);
+
+/* Stream size for n values at a fixed step and Rice k, without the unary plane (host only):
+ * the header, index and fixed plane.  The unary plane adds (symbol >> width) + 1 bits per value,
+ * which depends on the data; hq_encode reports the exact size needed when a buffer is too small. */
+int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t *bytes);
+
+/* Rate control alone (component 3's rate targeting): chooses the lattice step and Rice parameter
+ * for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles meets
+ * params->target_bps.  Blocking.  info->payload_bps is the sample estimate. */
+int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, hq_info *info,
+            void *workspace, size_t workspace_bytes, hq_stream_t stream);
+
+/* Encode x (n values, dtype hq_dtype) into `out` (device, out_capacity bytes).
+ * With out_bytes != NULL the call blocks, stores the stream size in *out_bytes (also when the
+ * result is HQ_ERR_CAPACITY: the size needed) and fills *info (may be NULL).  With out_bytes == NULL
+ * the call only enqueues work on `stream`; the size is in the stream header (total_bytes) and
+ * device-side errors are returned later by hq_status(workspace).  Rate control runs unless
+ * params->step > 0. */
+int hq_encode(const void *x, int32_t dtype, uint64_t n, const hq_params *params, void *out,
+              uint64_t out_capacity, uint64_t *out_bytes, hq_info *info, void *workspace,
+              size_t workspace_bytes, hq_stream_t stream);
+
+/* Decode a stream of `stream_bytes` bytes into out (n values of out_dtype; bf16 is round to nearest
+ * even of the fp32 reconstruction).  Asynchronous: header and per-chunk validation happen on the
+ * device; call hq_status(workspace) to learn of HQ_ERR_CORRUPT.  On a corrupt stream the output
+ * contents are unspecified, but no access leaves the given buffers. */
+int hq_decode(const void *stream_data, uint64_t stream_bytes, void *out, int32_t out_dtype,
+              uint64_t n, void *workspace, size_t workspace_bytes, hq_stream_t stream);
+
+/* Waits for `stream` and returns the first device-side error recorded in `workspace` since the last
+ * hq_encode / hq_decode / hq_rate that used it (HQ_OK when none). */
+int hq_status(void *workspace, hq_stream_t stream);
+
+/* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
+ * E8 codes are twice the lattice point, D4 and Z codes are the point) and per-tile bf16 scale bits
+ * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */
+int hq_codes(const void *x, int32_t dtype, uint64_t n, const hq_params *params, int32_t *codes,
+             uint16_t *scales, void *workspace, size_t workspace_bytes, hq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HQ_H_ */

@@ -1,0 +1,244 @@
+"""Python binding of the gfx950 RHT + lattice + bit-strip + Rice codec (``libhq.so``).
+
+Argument marshalling only: every step of the method runs in the HIP kernels behind the C ABI
+declared in ``include/hq.h``.  PyTorch provides device memory and the stream.  There is no CPU
+fallback: if the library is missing the calls raise.
+
+Entry points mirror the C ABI: ``hq_encode``, ``hq_decode``, ``hq_rate``, ``hq_codes``,
+``hq_status``, ``hq_workspace_size``, ``hq_stream_fixed_bytes``, ``hq_version``, ``hq_strerror``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhq.so")
+
+HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_NONFINITE = 0, -1, -2, -3
+HQ_ERR_CAPACITY, HQ_ERR_CORRUPT, HQ_ERR_RATE, HQ_ERR_HIP, HQ_ERR_TIMEOUT = -4, -5, -6, -7, -8
+HQ_Z, HQ_D4, HQ_E8 = 0, 1, 2
+HQ_F32, HQ_BF16 = 0, 1
+LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8}
+
+EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
+           "hq_encode", "hq_decode", "hq_status", "hq_codes")
+
+
+class HqParams(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_uint32), ("lattice", ctypes.c_int32), ("target_bps", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("dither", ctypes.c_uint32), ("step", ctypes.c_float),
+                ("rice_k", ctypes.c_int32)]
+
+
+class HqInfo(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_float), ("rice_k", ctypes.c_int32), ("bytes", ctypes.c_uint64),
+                ("payload_bits", ctypes.c_uint64), ("payload_bps", ctypes.c_double),
+                ("side_bps", ctypes.c_double), ("total_bps", ctypes.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class HqError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load ``libhq.so`` (built in-tree by ``kv_quantization_tile_amd/build.py``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with kv_quantization_tile_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, u64, i32, sz = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_size_t
+        L.hq_version.restype = ctypes.c_uint32
+        L.hq_strerror.argtypes = [ctypes.c_int]
+        L.hq_strerror.restype = ctypes.c_char_p
+        L.hq_workspace_size.argtypes = [u64, P, ctypes.POINTER(sz)]
+        L.hq_stream_fixed_bytes.argtypes = [u64, i32, i32, ctypes.POINTER(u64)]
+        L.hq_rate.argtypes = [P, i32, u64, P, P, P, sz, P]
+        L.hq_encode.argtypes = [P, i32, u64, P, P, u64, P, P, P, sz, P]
+        L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
+        L.hq_status.argtypes = [P, P]
+        L.hq_codes.argtypes = [P, i32, u64, P, P, P, P, sz, P]
+        for name in EXPORTS:
+            getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().hq_strerror(code).decode()
+
+
+def hq_version() -> int:
+    return int(lib().hq_version())
+
+
+def _check(rc: int, what: str):
+    if rc != HQ_OK:
+        raise HqError(rc, what)
+
+
+def make_params(lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, tile=128) -> HqParams:
+    lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
+    return HqParams(tile=tile, lattice=lat, target_bps=float(target_bps), seed=int(seed),
+                    dither=1 if dither else 0, step=float(step), rice_k=int(rice_k))
+
+
+def hq_workspace_size(n: int, params: HqParams | None = None) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().hq_workspace_size(n, ctypes.byref(params) if params else None, ctypes.byref(out)),
+           "hq_workspace_size")
+    return out.value
+
+
+def hq_stream_fixed_bytes(n: int, lattice, rice_k: int) -> int:
+    out = ctypes.c_uint64(0)
+    lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
+    _check(lib().hq_stream_fixed_bytes(n, lat, rice_k, ctypes.byref(out)), "hq_stream_fixed_bytes")
+    return out.value
+
+
+# ---- torch-side helpers (device memory and streams only) ------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return HQ_F32
+    if t.dtype == torch.bfloat16:
+        return HQ_BF16
+    raise TypeError("input must be float32 or bfloat16")
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace(n: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(hq_workspace_size(n), dtype=torch.uint8, device=device)
+
+
+def capacity_estimate(n: int, lattice, target_bps: float, rice_k: int = -1, step: float = 0.0) -> int:
+    """A starting output size: the fixed plane at a generous Rice k plus 4 unary bits per value."""
+    if rice_k >= 0:
+        k = rice_k
+    elif step > 0:
+        k = 15
+    else:
+        k = min(15, int(target_bps) + 3)
+    return hq_stream_fixed_bytes(n, lattice, k) + n // 2 + 4096
+
+
+def hq_encode(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, out=None,
+              ws=None, stream=None, blocking=True):
+    """Encode a contiguous CUDA tensor (fp32 or bf16, numel % 128 == 0).
+
+    Returns (stream bytes as a uint8 CUDA tensor, info dict).  With blocking=False the call only
+    enqueues work and returns (out, None); the size is then in the stream header."""
+    torch = _torch()
+    assert x.is_cuda and x.is_contiguous()
+    n = x.numel()
+    p = make_params(lattice, target_bps, seed, dither, step, rice_k)
+    if ws is None:
+        ws = workspace(n, x.device)
+    if out is None:
+        out = torch.empty(capacity_estimate(n, p.lattice, target_bps, rice_k, step), dtype=torch.uint8,
+                          device=x.device)
+    sh = _stream_handle(stream)
+    if not blocking:
+        _check(lib().hq_encode(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
+                               ctypes.c_void_p(out.data_ptr()), out.numel(), None, None,
+                               ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh), "hq_encode")
+        return out, None
+    info = HqInfo()
+    nbytes = ctypes.c_uint64(0)
+    while True:
+        rc = lib().hq_encode(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
+                             ctypes.c_void_p(out.data_ptr()), out.numel(), ctypes.byref(nbytes),
+                             ctypes.byref(info), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh)
+        if rc == HQ_ERR_CAPACITY and nbytes.value > out.numel():
+            out = torch.empty(nbytes.value, dtype=torch.uint8, device=x.device)
+            continue
+        _check(rc, "hq_encode")
+        break
+    return out[: nbytes.value], info.as_dict()
+
+
+def hq_decode(stream_bytes, n: int, out_dtype=None, out=None, ws=None, stream=None, check=True):
+    """Decode a uint8 CUDA tensor holding a stream into n values (bf16 by default)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=stream_bytes.device)
+    if ws is None:
+        ws = workspace(0, stream_bytes.device)
+    sh = _stream_handle(stream)
+    _check(lib().hq_decode(ctypes.c_void_p(stream_bytes.data_ptr()), stream_bytes.numel(),
+                           ctypes.c_void_p(out.data_ptr()), _dtype_code(out), n,
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh), "hq_decode")
+    if check:
+        _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_decode")
+    return out
+
+
+def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None):
+    assert x.is_cuda and x.is_contiguous()
+    n = x.numel()
+    p = make_params(lattice, target_bps, seed, dither, step, rice_k)
+    if ws is None:
+        ws = workspace(n, x.device)
+    info = HqInfo()
+    _check(lib().hq_rate(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p), ctypes.byref(info),
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_handle(stream)), "hq_rate")
+    return info.as_dict()
+
+
+def hq_codes(x, step: float, lattice="e8", seed=0, dither=False, ws=None, stream=None):
+    """Integer lattice codes (int32, per value) and bf16 tile-scale bits (int16 view, per tile)."""
+    torch = _torch()
+    assert x.is_cuda and x.is_contiguous()
+    n = x.numel()
+    p = make_params(lattice, 4.0, seed, dither, step, -1)
+    if ws is None:
+        ws = workspace(0, x.device)
+    codes = torch.empty(n, dtype=torch.int32, device=x.device)
+    scales = torch.empty(max(n // 128, 1), dtype=torch.int16, device=x.device)
+    sh = _stream_handle(stream)
+    _check(lib().hq_codes(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
+                          ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh), "hq_codes")
+    _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_codes")
+    return codes, scales[: n // 128]
+
+
+def hq_status(ws, stream=None) -> int:
+    return int(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), _stream_handle(stream)))
+
+
+def header_fields(stream_bytes_host) -> dict:
+    """Parse the 128-byte stream header (host bytes) into a dict."""
+    import struct
+    b = bytes(stream_bytes_host[:128])
+    magic, ver, lat, flags, tile, k, clog, step_bits = struct.unpack_from("<IHBBHBBI", b, 0)
+    seed, n, T = struct.unpack_from("<QQQ", b, 16)
+    chunks, F = struct.unpack_from("<II", b, 40)
+    fixed_off, unary_off, words, ubits, payload, total = struct.unpack_from("<QQQQQQ", b, 48)
+    return dict(magic=magic, version=ver, lattice=lat, dither=flags & 1, tile=tile, k=k, chunk_log2=clog,
+                step_bits=step_bits, seed=seed, n=n, tiles=T, chunks=chunks, F=F, fixed_off=fixed_off,
+                unary_off=unary_off, unary_words=words, unary_bits=ubits, payload_bits=payload,
+                total_bytes=total)

@@ -1,0 +1,269 @@
+// hq_api.hip -- C ABI of the codec (declarations and contracts in include/hq.h).
+//
+// Host side only: argument validation, the order of kernel launches on the caller's stream and
+// the read-back of results.  Every step of the method runs in the kernels of hq_kernels.hip.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/hq.h"
+#include "hq_internal.h"
+
+using namespace hq;
+
+namespace {
+
+constexpr uint32_t kFormatVersion = 1;
+constexpr uint32_t kStepMin = (127u - 12u) << 23, kStepMax = (127u + 12u) << 23;
+
+uint32_t f32_bits(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  return b;
+}
+
+uint64_t align256h(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+int octet_rem_bits_h(int lattice, int k) {
+  const int kh = k > 0 ? k - 1 : 0;
+  return lattice == HQ_E8 ? 7 * k + kh : lattice == HQ_D4 ? 6 * k + 2 * kh : 8 * k;
+}
+uint32_t tile_fixed_bits_h(int lattice, int k) {
+  return (uint32_t)((lattice == HQ_E8 ? 32 : 16) + 16 * octet_rem_bits_h(lattice, k));
+}
+
+uint64_t chunks_of(uint64_t n) { return (n / 128 + 63) / 64; }
+
+int check_params(const hq_params* p, uint64_t n) {
+  if (!p) return HQ_ERR_INVALID_ARG;
+  if (p->tile != 128) return HQ_ERR_UNSUPPORTED;
+  if (p->lattice < HQ_Z || p->lattice > HQ_E8) return HQ_ERR_INVALID_ARG;
+  if (n % 128) return HQ_ERR_INVALID_ARG;
+  if (n > (1ull << 35)) return HQ_ERR_INVALID_ARG;  // the encoder's look-back packs 28-bit padding sums
+  if (p->dither > 1) return HQ_ERR_INVALID_ARG;
+  if (p->rice_k < -1 || p->rice_k > 15) return HQ_ERR_INVALID_ARG;
+  if (!(p->step >= 0.0f)) return HQ_ERR_INVALID_ARG;  // also rejects NaN
+  if (p->step > 0.0f) {
+    const uint32_t b = f32_bits(p->step);
+    if (b < kStepMin || b > kStepMax) return HQ_ERR_INVALID_ARG;
+  } else {
+    const float lo = p->lattice == HQ_E8 ? 1.125f : 1.0f;
+    if (!(p->target_bps >= lo) || !(p->target_bps <= 12.0f)) return HQ_ERR_RATE;
+  }
+  return HQ_OK;
+}
+
+int status_from_flags(uint32_t f) {
+  if (f & kErrCorrupt) return HQ_ERR_CORRUPT;
+  if (f & kErrNonfinite) return HQ_ERR_NONFINITE;
+  if (f & kErrCapacity) return HQ_ERR_CAPACITY;
+  if (f & kErrRange) return HQ_ERR_UNSUPPORTED;
+  if (f & kErrTimeout) return HQ_ERR_TIMEOUT;
+  return HQ_OK;
+}
+
+size_t workspace_bytes_for(uint64_t n) { return kWsHeader + align256h(8ull * (chunks_of(n) + 1)); }
+
+EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, void* out, uint64_t cap,
+                     void* ws, hq_stream_t s) {
+  EncodeArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.n = n;
+  a.tiles = n / 128;
+  a.chunks = (uint32_t)chunks_of(n);
+  a.lattice = p->lattice;
+  a.dither = (int)p->dither;
+  a.seed = p->seed;
+  a.target = p->target_bps;
+  a.rice_k = p->rice_k;
+  a.fixed_step_bits = p->step > 0.0f ? f32_bits(p->step) : 0u;
+  a.out = static_cast<uint8_t*>(out);
+  a.cap = cap;
+  a.ws = static_cast<Workspace*>(ws);
+  a.stream = static_cast<hipStream_t>(s);
+  return a;
+}
+
+// Initial centre of the rate search: the Gaussian high-rate guess log2(step) = 2.05 - target,
+// as a binary32 bit pattern.
+int64_t initial_centre(float target) {
+  return (int64_t)(127u << 23) + (int64_t)floor((2.05 - (double)target) * 8388608.0 + 0.5);
+}
+
+// init + rate passes (when needed); leaves step and k in the workspace.
+int run_rate_control(const EncodeArgs& a) {
+  const uint64_t T = a.tiles;
+  const uint32_t N = (uint32_t)(T < kRcSampleTiles ? T : kRcSampleTiles);
+  hipError_t e;
+  if (a.fixed_step_bits) {
+    e = launch_init(a, (int64_t)a.fixed_step_bits);
+    if (e != hipSuccess) return HQ_ERR_HIP;
+    if (a.rice_k < 0 && N > 0) {
+      e = launch_rate_pass(a, 1, 0, N);
+      if (e != hipSuccess) return HQ_ERR_HIP;
+    }
+    return HQ_OK;
+  }
+  e = launch_init(a, initial_centre(a.target));
+  if (e != hipSuccess) return HQ_ERR_HIP;
+  if (N == 0) return HQ_OK;
+  e = launch_rate_pass(a, kRcCand, 21, N);
+  if (e != hipSuccess) return HQ_ERR_HIP;
+  e = launch_rate_pass(a, kRcCand, 17, N);
+  if (e != hipSuccess) return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+struct Results {
+  uint32_t status, step_bits;
+  int32_t k;
+  uint64_t total_bytes, payload_bits;
+};
+
+int read_results(void* ws, hipStream_t s, Results* r) {
+  Workspace h;
+  if (hipMemcpyAsync(&h, ws, sizeof(Workspace), hipMemcpyDeviceToHost, s) != hipSuccess) return HQ_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return HQ_ERR_HIP;
+  r->status = h.status;
+  r->step_bits = h.res_step_bits;
+  r->k = h.res_k;
+  r->total_bytes = h.res_total_bytes;
+  r->payload_bits = h.res_payload_bits;
+  return HQ_OK;
+}
+
+void fill_info(hq_info* info, uint64_t n, uint32_t step_bits, int k, uint64_t bytes, uint64_t payload_bits) {
+  if (!info) return;
+  float st;
+  memcpy(&st, &step_bits, 4);
+  info->step = st;
+  info->rice_k = k;
+  info->bytes = bytes;
+  info->payload_bits = payload_bits;
+  const double nd = n ? (double)n : 1.0;
+  info->payload_bps = (double)payload_bits / nd;
+  info->total_bps = 8.0 * (double)bytes / nd;
+  info->side_bps = info->total_bps - info->payload_bps;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t hq_version(void) { return (1u << 16) | kFormatVersion; }
+
+const char* hq_strerror(int code) {
+  switch (code) {
+    case HQ_OK: return "ok";
+    case HQ_ERR_INVALID_ARG: return "invalid argument";
+    case HQ_ERR_UNSUPPORTED: return "unsupported (tile size or lattice)";
+    case HQ_ERR_NONFINITE: return "non-finite input tile";
+    case HQ_ERR_CAPACITY: return "output buffer too small";
+    case HQ_ERR_CORRUPT: return "corrupt stream";
+    case HQ_ERR_RATE: return "target rate out of range";
+    case HQ_ERR_HIP: return "HIP runtime error";
+    case HQ_ERR_TIMEOUT: return "cross-workgroup wait exceeded its bound";
+  }
+  return "unknown status";
+}
+
+int hq_workspace_size(uint64_t n, const hq_params* params, size_t* bytes) {
+  (void)params;
+  if (!bytes || n % 128) return HQ_ERR_INVALID_ARG;
+  *bytes = workspace_bytes_for(n);
+  return HQ_OK;
+}
+
+int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t* bytes) {
+  if (!bytes || n % 128 || lattice < HQ_Z || lattice > HQ_E8 || rice_k < 0 || rice_k > 15) return HQ_ERR_INVALID_ARG;
+  const uint64_t chunks = chunks_of(n);
+  const uint64_t fixed_off = align256h(128 + 4 * (chunks + 1));
+  *bytes = align256h(fixed_off + chunks * 8ull * tile_fixed_bits_h(lattice, rice_k));
+  return HQ_OK;
+}
+
+int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, hq_info* info, void* workspace,
+            size_t workspace_bytes, hq_stream_t stream) {
+  int rc = check_params(params, n);
+  if (rc) return rc;
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < workspace_bytes_for(n) || (n && !x)) return HQ_ERR_INVALID_ARG;
+  EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
+  rc = run_rate_control(a);
+  if (rc) return rc;
+  Workspace h;
+  if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
+      hipStreamSynchronize(a.stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  if (h.status) return status_from_flags(h.status);
+  if (info) {
+    memset(info, 0, sizeof(*info));
+    float st;
+    memcpy(&st, &h.step_bits, 4);
+    info->step = st;
+    info->rice_k = h.rice_k;
+    info->payload_bps = params->step > 0.0f ? 0.0 : (double)params->target_bps;
+  }
+  return HQ_OK;
+}
+
+int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params, void* out, uint64_t out_capacity,
+              uint64_t* out_bytes, hq_info* info, void* workspace, size_t workspace_bytes, hq_stream_t stream) {
+  int rc = check_params(params, n);
+  if (rc) return rc;
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < workspace_bytes_for(n) || (n && !x) || !out) return HQ_ERR_INVALID_ARG;
+  if (((uintptr_t)out & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
+  EncodeArgs a = make_args(x, dtype, n, params, out, out_capacity, workspace, stream);
+  rc = run_rate_control(a);
+  if (rc) return rc;
+  if (launch_encode(a) != hipSuccess) return HQ_ERR_HIP;
+  if (!out_bytes) return HQ_OK;
+  Results r;
+  rc = read_results(workspace, a.stream, &r);
+  if (rc) return rc;
+  *out_bytes = r.total_bytes;
+  fill_info(info, n, r.step_bits, r.k, r.total_bytes, r.payload_bits);
+  return status_from_flags(r.status);
+}
+
+int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t out_dtype, uint64_t n,
+              void* workspace, size_t workspace_bytes, hq_stream_t stream) {
+  if (n % 128 || (n / 128 + 63) / 64 >= 0xFFFFFFFFull) return HQ_ERR_INVALID_ARG;
+  if (out_dtype != HQ_F32 && out_dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
+  if (!stream_data || !workspace || workspace_bytes < kWsHeader || (n && !out)) return HQ_ERR_INVALID_ARG;
+  if (((uintptr_t)stream_data & 15u) || ((uintptr_t)out & 15u) || ((uintptr_t)workspace & 255u))
+    return HQ_ERR_INVALID_ARG;
+  if (launch_decode(static_cast<const uint8_t*>(stream_data), stream_bytes, out, out_dtype, n,
+                    static_cast<Workspace*>(workspace), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_status(void* workspace, hq_stream_t stream) {
+  if (!workspace) return HQ_ERR_INVALID_ARG;
+  uint32_t f = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&f, reinterpret_cast<char*>(workspace) + offsetof(Workspace, status), 4,
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return HQ_ERR_HIP;
+  return status_from_flags(f);
+}
+
+int hq_codes(const void* x, int32_t dtype, uint64_t n, const hq_params* params, int32_t* codes, uint16_t* scales,
+             void* workspace, size_t workspace_bytes, hq_stream_t stream) {
+  if (!params || !(params->step > 0.0f)) return HQ_ERR_INVALID_ARG;
+  int rc = check_params(params, n);
+  if (rc) return rc;
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < workspace_bytes_for(0) || (n && (!x || !codes || !scales)))
+    return HQ_ERR_INVALID_ARG;
+  EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
+  a.chunks = 0;  // no look-back flags are needed
+  if (launch_init(a, (int64_t)a.fixed_step_bits) != hipSuccess) return HQ_ERR_HIP;
+  if (launch_codes(a, codes, scales) != hipSuccess) return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+}  // extern "C"

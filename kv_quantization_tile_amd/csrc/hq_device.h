@@ -1,0 +1,386 @@
+// hq_device.h -- device building blocks of the gfx950 codec kernels.
+//
+// Thread layout used by every kernel: a workgroup has 256 lanes in 4 wavefronts of 64.  Lane
+// (wave w, lane l) owns octet o = l % 16 (coordinates 8o..8o+7) of tile 4 w + l / 16 of the
+// workgroup's current group of 16 tiles.  A tile therefore lives in 16 consecutive lanes, 8 values
+// per lane: three Hadamard stages run inside the lane and four across lanes (lane xor 1, 2, 4, 8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+constexpr int kTile = 128;
+constexpr int kChunkTiles = 64;
+constexpr int kBlock = 256;
+constexpr int kHeaderBytes = 128;
+constexpr uint32_t kMagic = 0x31305148u;  // 'H' 'Q' '0' '1'
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kStepBitsMin = (127u - 12u) << 23;
+constexpr uint32_t kStepBitsMax = (127u + 12u) << 23;
+
+enum { kLatZ = 0, kLatD4 = 1, kLatE8 = 2 };
+
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): the counter-based generator behind the sign
+// diagonal D and the dither.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = c.x * 0xD2511F53u, hi0 = __umulhi(c.x, 0xD2511F53u);
+    const uint32_t lo1 = c.z * 0xCD9E8D57u, hi1 = __umulhi(c.z, 0xCD9E8D57u);
+    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Sign word of octet o: bit i (0..7) set means D_{8o+i} = -1.  D comes from one Philox call with
+// counter 0 and key = seed; the 128 sign bits are the output words, least significant bit first.
+__device__ __forceinline__ uint32_t octet_sign_bits(uint64_t seed, int o) {
+  const U4 w = philox4x32_10(U4{0u, 0u, 0u, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t word = (o >> 2) == 0 ? w.x : (o >> 2) == 1 ? w.y : (o >> 2) == 2 ? w.z : w.w;
+  return (word >> ((o & 3) * 8)) & 0xFFu;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Unnormalised Walsh-Hadamard transform of the 128 values held by 16 lanes (8 per lane), stage j
+// pairing index i with i + 2^j in the order j = 0..6; the low element becomes a + b, the high
+// a - b.  Stages 0-2 are in registers, 3-6 exchange with lane xor 1, 2, 4, 8.
+__device__ __forceinline__ void fwht_lane(float a[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float lo = a[i], hi = a[i + h];
+      a[i] = lo + hi;
+      a[i + h] = lo - hi;
+    }
+  }
+}
+
+__device__ __forceinline__ void fwht_cross(float a[8], int lane16) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool high = (lane16 & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __shfl_xor(a[i], m, 64);
+      a[i] = high ? (p - a[i]) : (a[i] + p);
+    }
+  }
+}
+
+// Sum of squares of the tile as a balanced pairwise tree in index order: squares, pairs inside
+// the lane, then lane xor 1, 2, 4, 8 (each add is commutative, so both lanes get equal sums).
+__device__ __forceinline__ float tile_sumsq(const float a[8]) {
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = a[i] * a[i];
+  float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) t = t + __shfl_xor(t, m, 64);
+  return t;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Tile scale s = bfloat16 nearest to sqrt(S / 128), ties to even, decided exactly: start from the
+// rounded square root, then compare S against 128 m^2 for the two neighbouring rounding midpoints
+// m (9 significant bits, so m^2 and 128 m^2 are exact in binary32).  S is brought into
+// [2^-60, 2^60] by an exact power-of-two factor first so that no square under- or overflows.
+__device__ __forceinline__ uint32_t tile_scale_bits(float S) {
+  if (!(S > 0.0f)) return 0u;
+  float Ss = S;
+  int adj = 0;
+  if (S < 0x1p-60f) {
+    Ss = S * 0x1p100f;
+    adj = 50;
+  } else if (S > 0x1p60f) {
+    Ss = S * 0x1p-100f;
+    adj = -50;
+  }
+  const float r = __fsqrt_rn(Ss * 0.0078125f);
+  uint32_t c = f32_to_bf16_rne(r);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const float cv = bf16_bits_to_f32(c);
+    const float mhi = (cv + bf16_bits_to_f32(c + 1u)) * 0.5f;
+    const float mlo = (cv + bf16_bits_to_f32(c - 1u)) * 0.5f;
+    const float thi = 128.0f * (mhi * mhi);
+    const float tlo = 128.0f * (mlo * mlo);
+    if (Ss > thi || (Ss == thi && (c & 1u)))
+      c += 1u;
+    else if (Ss < tlo || (Ss == tlo && (c & 1u)))
+      c -= 1u;
+  }
+  return (uint32_t)((int32_t)c - adj * 128);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Nearest lattice points (Conway-Sloane rules).  Ties: rint is round-half-even; the coordinate
+// moved by a parity fix is the largest |v - rint v| (lowest index among equals), moved toward v
+// (up when v is an integer).  E8 codes are z = 2 c in 2*E8.
+__device__ __forceinline__ void d4_nearest(const float* v, int32_t* x) {
+  float a[4];
+  uint32_t neg = 0;
+  int32_t par = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float r = rintf(v[i]);
+    const float e = v[i] - r;
+    a[i] = fabsf(e);
+    neg |= (__float_as_uint(e) >> 31) << i;
+    x[i] = (int32_t)r;
+    par += x[i];
+  }
+  int k = 0;
+  float amax = a[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (a[i] > amax) {
+      amax = a[i];
+      k = i;
+    }
+  if (par & 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i == k) x[i] += ((neg >> i) & 1u) ? -1 : 1;
+  }
+}
+
+// E8 = D8 u (D8 + 1/2).  With r = rint v, e = v - r, a = |e|, s = sign of e (+ for e >= 0):
+// candidate A (D8) = r, + s at argmax a if sum r is odd; candidate B (D8 + 1/2) = r + s/2, with the
+// coordinate of argmin a turned the other way if sum(B - 1/2) is odd.  |v-A|^2 - |v-B|^2 equals
+// sum a - 2 + pA (1 - 2 a_max) - pB 2 a_min, so A is kept iff
+// ((a0+a1)+(a2+a3))+((a4+a5)+(a6+a7)) [+ (1 - 2 a_max)]  <=  2 [+ 2 a_min]   (binary32, this order).
+__device__ __forceinline__ void e8_nearest(const float* v, int32_t* z) {
+  float a[8];
+  int32_t r[8];
+  uint32_t neg = 0;
+  int32_t par = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ri = rintf(v[i]);
+    const float e = v[i] - ri;
+    a[i] = fabsf(e);
+    neg |= (__float_as_uint(e) >> 31) << i;
+    r[i] = (int32_t)ri;
+    par += r[i];
+  }
+  const int pa = par & 1;
+  const int pb = (pa + __popc(neg)) & 1;
+  int ka = 0, kb = 0;
+  float amax = a[0], amin = a[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    if (a[i] > amax) {
+      amax = a[i];
+      ka = i;
+    }
+    if (a[i] < amin) {
+      amin = a[i];
+      kb = i;
+    }
+  }
+  const float d = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  const float lhs = pa ? d + (1.0f - 2.0f * amax) : d;
+  const float rhs = pb ? 2.0f + 2.0f * amin : 2.0f;
+  const bool keep_a = lhs <= rhs;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int32_t s = ((neg >> i) & 1u) ? -1 : 1;
+    const int32_t za = 2 * r[i] + ((pa && i == ka) ? 2 * s : 0);
+    const int32_t zb = 2 * r[i] + ((pb && i == kb) ? -s : s);
+    z[i] = keep_a ? za : zb;
+  }
+}
+
+template <int LAT>
+__device__ __forceinline__ void nearest_octet(const float* v, int32_t* code) {
+  if (LAT == kLatE8) {
+    e8_nearest(v, code);
+  } else if (LAT == kLatD4) {
+    d4_nearest(v, code);
+    d4_nearest(v + 4, code + 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = (int32_t)rintf(v[i]);
+  }
+}
+
+template <int LAT>
+__device__ __forceinline__ float code_coord(int32_t c) {
+  return LAT == kLatE8 ? (float)c * 0.5f : (float)c;
+}
+
+// Subtractive dither of octet o of tile t: one Philox call, counter (o, t lo, t hi, 1); the eight
+// 16-bit halves h (low half first) give b = h / 32768 in [0, 2), and U = b - Q(b) is uniform on the
+// Voronoi cell (to 16-bit resolution).  Exact in binary32.
+template <int LAT>
+__device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, float* u) {
+  const U4 w = philox4x32_10(U4{(uint32_t)o, (uint32_t)t, (uint32_t)(t >> 32), 1u}, (uint32_t)seed,
+                             (uint32_t)(seed >> 32));
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  float b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
+    b[i] = (float)h * (1.0f / 32768.0f);
+  }
+  int32_t q[8];
+  nearest_octet<LAT>(b, q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = b[i] - code_coord<LAT>(q[i]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Bit-stripping and zigzag (see the format description in hq.h).
+__device__ __forceinline__ uint32_t zigzag(int32_t a) { return ((uint32_t)a << 1) ^ (uint32_t)(a >> 31); }
+__device__ __forceinline__ int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u); }
+
+template <int LAT>
+__device__ __forceinline__ bool slot_halved(int s) {
+  return LAT == kLatE8 ? (s == 7) : LAT == kLatD4 ? ((s & 3) == 3) : false;
+}
+template <int LAT>
+__device__ __forceinline__ int slot_width(int s, int k) {
+  return slot_halved<LAT>(s) ? (k > 0 ? k - 1 : 0) : k;
+}
+template <int LAT>
+__device__ __forceinline__ int octet_rem_bits(int k) {
+  const int kh = k > 0 ? k - 1 : 0;
+  return LAT == kLatE8 ? 7 * k + kh : LAT == kLatD4 ? 6 * k + 2 * kh : 8 * k;
+}
+template <int LAT>
+__device__ __forceinline__ int tile_hdr_bits() {
+  return LAT == kLatE8 ? 32 : 16;
+}
+template <int LAT>
+__device__ __forceinline__ uint32_t tile_fixed_bits(int k) {
+  return (uint32_t)(tile_hdr_bits<LAT>() + 16 * octet_rem_bits<LAT>(k));
+}
+
+template <int LAT>
+__device__ __forceinline__ void strip_octet(const int32_t* code, uint32_t* sym, uint32_t* coset) {
+  *coset = 0;
+  if (LAT == kLatE8) {
+    const int32_t p = code[0] & 1;
+    int32_t u[8], r = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = (code[i] - p) >> 1;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) r += u[i];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) sym[i] = zigzag(u[i]);
+    sym[7] = zigzag((u[7] - (r & 1)) >> 1);
+    *coset = (uint32_t)p;
+  } else if (LAT == kLatD4) {
+#pragma unroll
+    for (int b = 0; b < 8; b += 4) {
+      const int32_t r = (code[b] + code[b + 1] + code[b + 2]) & 1;
+      sym[b] = zigzag(code[b]);
+      sym[b + 1] = zigzag(code[b + 1]);
+      sym[b + 2] = zigzag(code[b + 2]);
+      sym[b + 3] = zigzag((code[b + 3] - r) >> 1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sym[i] = zigzag(code[i]);
+  }
+}
+
+template <int LAT>
+__device__ __forceinline__ void unstrip_octet(const uint32_t* sym, uint32_t coset, int32_t* code) {
+  if (LAT == kLatE8) {
+    int32_t u[8], r = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      u[i] = unzigzag(sym[i]);
+      r += u[i];
+    }
+    u[7] = 2 * unzigzag(sym[7]) + (r & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = 2 * u[i] + (int32_t)coset;
+  } else if (LAT == kLatD4) {
+#pragma unroll
+    for (int b = 0; b < 8; b += 4) {
+      code[b] = unzigzag(sym[b]);
+      code[b + 1] = unzigzag(sym[b + 1]);
+      code[b + 2] = unzigzag(sym[b + 2]);
+      const int32_t r = (code[b] + code[b + 1] + code[b + 2]) & 1;
+      code[b + 3] = 2 * unzigzag(sym[b + 3]) + r;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = unzigzag(sym[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Loads of one lane's 8 values of tile t (DT 0: fp32, 1: bf16 bits).
+template <int DT>
+__device__ __forceinline__ void load_octet(const void* x, uint64_t t, int o, float* v) {
+  if (DT == 1) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * o);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(ws[i] << 16);
+      v[2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * o);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Workgroup exclusive prefix sum over 256 lanes (wave scans + LDS of wave totals).
+// `scratch` holds at least 4 words.  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t s = scratch[w];
+    if (w < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+__device__ __forceinline__ uint64_t atomic_load_acq(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_rel(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace hq

@@ -1,0 +1,82 @@
+// hq_internal.h -- workspace layout and kernel launchers shared by hq_kernels.hip and hq_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+// Device-side error flags recorded in Workspace::status.
+enum { kErrNonfinite = 1u, kErrCapacity = 2u, kErrCorrupt = 4u, kErrTimeout = 8u, kErrRange = 16u };
+
+// Rate control (the pages ask for a realised rate within ~0.01 bits per value and give no
+// algorithm; see hq_kernels.hip for the search).
+constexpr uint32_t kRcSampleTiles = 8192;
+constexpr int kRcCand = 8;
+constexpr int kRcKwin = 4;
+
+// Device workspace.  The fixed part is 4 KiB; the encoder's look-back flags (one 64-bit word per
+// chunk, plus one) follow it.  Every field is (re)initialised by the first kernel of a call.
+struct alignas(256) Workspace {
+  uint32_t pad_ticket;
+  uint32_t rc_ticket;    // last-workgroup detection of a rate pass
+  uint32_t status;       // error flags (kErr*)
+  uint32_t step_bits;    // operating point chosen so far (binary32 bits of the step)
+  int32_t rice_k;
+  uint32_t pad0;
+  int64_t rc_centre;     // centre of the next rate pass (step bits)
+  uint64_t rc_sumq[kRcCand][kRcKwin];  // sum of (symbol >> width) per candidate and Rice k
+  // encoder results, written by the chunk that finishes the look-back chain
+  uint64_t res_total_bytes;
+  uint64_t res_payload_bits;
+  uint64_t res_unary_bits;
+  uint64_t res_words;
+  uint32_t res_step_bits;
+  int32_t res_k;
+  // decoder parameters, written by the header check
+  uint32_t dec_valid;
+  uint32_t dec_lattice;
+  uint32_t dec_dither;
+  int32_t dec_k;
+  uint32_t dec_step_bits;
+  uint32_t dec_F;
+  uint32_t dec_chunks;
+  uint32_t pad1;
+  uint64_t dec_seed;
+  uint64_t dec_tiles;
+  uint64_t dec_fixed_off;
+  uint64_t dec_unary_off;
+  uint64_t dec_words;
+};
+static_assert(sizeof(Workspace) <= 4096, "workspace header");
+constexpr size_t kWsHeader = 4096;
+
+inline uint64_t* lookback_flags(void* ws) {
+  return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader);
+}
+
+struct EncodeArgs {
+  const void* x;
+  int dtype;
+  uint64_t n, tiles;
+  uint32_t chunks;
+  int lattice;
+  int dither;
+  uint64_t seed;
+  float target;
+  int rice_k;          // -1 = automatic
+  uint32_t fixed_step_bits;  // 0 = rate control
+  uint8_t* out;
+  uint64_t cap;
+  Workspace* ws;
+  hipStream_t stream;
+};
+
+hipError_t launch_init(const EncodeArgs& a, int64_t centre);
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample);
+hipError_t launch_encode(const EncodeArgs& a);
+hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
+                         Workspace* ws, hipStream_t stream);
+hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales);
+
+}  // namespace hq

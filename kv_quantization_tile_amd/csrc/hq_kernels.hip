@@ -1,0 +1,873 @@
+// hq_kernels.hip -- gfx950 kernels of the RHT + lattice + bit-strip + Rice codec.
+//
+// Method: HyperQuant technical summary (gist.science/ko/paper/2606.23406), "Methodology: the
+// HyperQuant pipeline", components 1-4 (per-tile RHT, lattice quantisation, bit-stripping + Rice
+// coding with rate targeting, KV dither).  The byte format is described in include/hq.h.
+//
+// Kernels of one encode call, all on the caller's stream, with no host round trip in between:
+//   init_kernel     clears the workspace flags and seeds the rate search;
+//   rate_kernel x2  evaluates 8 candidate steps on a sample of tiles, and its last workgroup solves
+//                   for the next centre (pass A: half-octave spacing, pass B: 1/32 octave);
+//   encode_kernel   one workgroup per 64-tile chunk: load, sign, FWHT, scale, lattice, strip, Rice
+//                   lengths, workgroup scan, decoupled look-back over chunks for the unary offsets,
+//                   and coalesced stores of the chunk's fixed record and unary segment.
+// Decode: decode_check (header validation, 1 lane) then decode_kernel (one workgroup per chunk).
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+
+constexpr int kFixedWordsMax = 3904;      // 2 F u32 words per chunk; F <= 1952 bits
+constexpr int kUnaryWinWords = 4096;      // 16 KiB unary staging window = 131072 bits
+constexpr uint32_t kUnaryWinBits = kUnaryWinWords * 32u;
+constexpr uint64_t kFlagAgg = 1ull << 62, kFlagPrefix = 2ull << 62, kValMask = (1ull << 62) - 1;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+__device__ __forceinline__ uint32_t low_mask(int w) { return w >= 32 ? 0xFFFFFFFFu : ((1u << w) - 1u); }
+
+// OR `nbits` (<= 32 - 0, value < 2^nbits, nbits <= 16 here) bits into an LDS bit array.
+__device__ __forceinline__ void lds_put_bits(uint32_t* s, uint32_t pos, uint32_t val, int nbits) {
+  if (nbits == 0 || val == 0) return;
+  const uint32_t word = pos >> 5, sh = pos & 31u;
+  atomicOr(&s[word], val << sh);
+  if (sh + (uint32_t)nbits > 32u) atomicOr(&s[word + 1], val >> (32u - sh));
+}
+
+__device__ __forceinline__ uint32_t lds_get_bits(const uint32_t* s, uint32_t pos, int nbits) {
+  if (nbits == 0) return 0;
+  const uint32_t word = pos >> 5, sh = pos & 31u;
+  uint64_t v = s[word];
+  if (sh + (uint32_t)nbits > 32u) v |= (uint64_t)s[word + 1] << 32;
+  return (uint32_t)(v >> sh) & low_mask(nbits);
+}
+
+// Sample tile of stratum i (jittered stratified sampling, see rate control below).
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x = x * 0x9E3779B1u + 0x7F4A7C15u;
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return x;
+}
+__device__ __forceinline__ uint64_t sample_tile(uint64_t i, uint64_t T, uint64_t N) {
+  const uint64_t lo = (i * T) / N, hi = ((i + 1) * T) / N;
+  return lo + (uint64_t)mix32((uint32_t)i) % (hi - lo);
+}
+
+__host__ __device__ inline int kwin_base(int64_t b) {
+  const int e = (int)((b >> 23) & 0xFF) - 127;
+  int kb = -e - 2;
+  kb = kb < 0 ? 0 : kb;
+  return kb > 12 ? 12 : kb;
+}
+
+__device__ __forceinline__ int64_t clamp_i64(int64_t v, int64_t lo, int64_t hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Front half shared by the rate, encode and codes kernels: sign, FWHT, tile energy and scale.
+// Returns the scale bits; y holds the transformed values (zeroed when the energy is not finite).
+template <int DT>
+__device__ __forceinline__ uint32_t transform_octet(const void* x, uint64_t t, bool valid, int o,
+                                                     uint32_t sgn, float* y, bool* finite) {
+  if (valid) {
+    load_octet<DT>(x, t, o, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = ((sgn >> i) & 1u) ? -y[i] : y[i];
+  fwht_lane(y);
+  fwht_cross(y, o);
+  float S = tile_sumsq(y);
+  *finite = isfinite(S);
+  if (!*finite) {
+    S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+  }
+  return tile_scale_bits(S);
+}
+
+// v = y * m (+ U); m = 1 / (s * step) rounded once each (0 when s = 0); nearest lattice point.
+template <int LAT, bool DITHER>
+__device__ __forceinline__ void quantize_octet(const float* y, float s, float step, const float* u,
+                                               int32_t* code) {
+  const float m = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = y[i] * m;
+    if (DITHER) v[i] = v[i] + u[i];
+  }
+  nearest_octet<LAT>(v, code);
+}
+
+// ---------------------------------------------------------------------------------------------
+__global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int64_t centre,
+                            uint32_t step_bits, int32_t k) {
+  const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid == 0) {
+    ws->rc_ticket = 0;
+    ws->status = 0;
+    ws->step_bits = step_bits;
+    ws->rice_k = k;
+    ws->rc_centre = centre;
+    ws->res_total_bytes = 0;
+    ws->res_payload_bits = 0;
+    ws->res_unary_bits = 0;
+    ws->res_words = 0;
+    ws->res_step_bits = step_bits;
+    ws->res_k = k;
+  }
+  if (gid < (uint64_t)(kRcCand * kRcKwin)) (&ws->rc_sumq[0][0])[gid] = 0;
+  for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Rate control.  The pages fix only the outcome (realised rate within ~0.01 bits per value); the
+// search is this codec's reading:
+//  - sample: N = min(T, 8192) tiles, one per stratum [floor(iT/N), floor((i+1)T/N)), picked by a
+//    32-bit hash of i;
+//  - the search variable is b, the binary32 bit pattern of the step;
+//  - a pass evaluates up to 8 candidates centre + (2j-7) 2^h (clamped to [2^-12, 2^12]); for each,
+//    the Rice k is the argmin (ties: smaller k) over kb..kb+3, kb = clamp(-exponent - 2, 0, 12);
+//  - its last workgroup interpolates linearly (IEEE double) between the two candidates that
+//    bracket the target bit count (first candidate at or below it) or extrapolates from the end
+//    pair, rounds, clamps, and stores the answer as the next centre together with the k of the
+//    candidate nearest to it.  Pass A (h = 21) starts at 2.05 - target octaves; pass B (h = 17)
+//    refines.  With a fixed step and automatic k one pass with the single candidate picks k.
+template <int LAT>
+__device__ void rate_solve(Workspace* ws, const uint64_t* sumq, int nc, int half_log2, int fixed_k, float target,
+                           uint32_t N) {
+  const int64_t centre = ws->rc_centre;
+  int64_t b[kRcCand];
+  double R[kRcCand];
+  int kc[kRcCand];
+  const double Nd = (double)N;
+  for (int j = 0; j < nc; ++j) {
+    b[j] = nc == 1 ? centre
+                   : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
+                               kStepBitsMax);
+    const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b[j]);
+    int best = 0;
+    double rb = 0.0;
+    for (int w = 0; w < kRcKwin; ++w) {
+      const int k = fixed_k >= 0 ? fixed_k : kb + w;
+      const uint64_t sq = sumq[j * kRcKwin + w];
+      const double per_tile = (double)(tile_fixed_bits<LAT>(k) - 16u) + 128.0;
+      const double bits = per_tile * Nd + (double)sq;
+      if (w == 0 || bits < rb) {
+        rb = bits;
+        best = w;
+      }
+    }
+    R[j] = rb;
+    kc[j] = fixed_k >= 0 ? fixed_k : kb + best;
+  }
+  const double Tb = (double)target * (double)((uint64_t)N * kTile);
+  const double nominal = (double)((uint64_t)N * kTile) / 8388608.0;
+  double xv;
+  int64_t lo, hi;
+  int jf = -1;
+  for (int i = 0; i < nc; ++i)
+    if (R[i] <= Tb) {
+      jf = i;
+      break;
+    }
+  if (nc == 1) {
+    xv = (double)b[0];
+    lo = hi = b[0];
+  } else if (jf < 0) {
+    double slope = (R[nc - 2] - R[nc - 1]) / (double)(b[nc - 1] - b[nc - 2]);
+    if (!(slope > 0.0)) slope = nominal;
+    xv = (double)b[nc - 1] + (R[nc - 1] - Tb) / slope;
+    lo = b[nc - 1];
+    hi = b[nc - 1] + ((int64_t)1 << 25);
+  } else if (jf == 0) {
+    double slope = (R[0] - R[1]) / (double)(b[1] - b[0]);
+    if (!(slope > 0.0)) slope = nominal;
+    xv = (double)b[0] - (Tb - R[0]) / slope;
+    lo = b[0] - ((int64_t)1 << 25);
+    hi = b[0];
+  } else {
+    xv = (double)b[jf - 1] + (R[jf - 1] - Tb) * (double)(b[jf] - b[jf - 1]) / (R[jf - 1] - R[jf]);
+    lo = b[jf - 1];
+    hi = b[jf];
+  }
+  int64_t xb = (int64_t)floor(xv + 0.5);
+  xb = clamp_i64(xb, lo, hi);
+  xb = clamp_i64(xb, kStepBitsMin, kStepBitsMax);
+  int best = 0;
+  for (int i = 1; i < nc; ++i) {
+    const int64_t di = b[i] > xb ? b[i] - xb : xb - b[i];
+    const int64_t db = b[best] > xb ? b[best] - xb : xb - b[best];
+    if (di < db) best = i;
+  }
+  ws->rc_centre = xb;
+  ws->step_bits = (uint32_t)xb;
+  ws->rice_k = kc[best];
+  ws->rc_ticket = 0;
+}
+
+template <int LAT, bool DITHER, int DT>
+__global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
+                                                      Workspace* ws, uint64_t seed, int nc, int half_log2,
+                                                      int fixed_k, float target) {
+  __shared__ uint32_t s_red[4][kRcCand * kRcKwin];
+  __shared__ uint64_t s_sumq[kRcCand * kRcKwin];
+  __shared__ uint32_t s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const uint64_t i = (uint64_t)blockIdx.x * 16 + wave * 4 + tw;
+  const bool valid = i < N;
+  const uint64_t t = valid ? sample_tile(i, T, N) : 0;
+  const uint32_t sgn = octet_sign_bits(seed, o);
+  float y[8];
+  bool finite;
+  const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
+  if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+  const float s = bf16_bits_to_f32(sb);
+  float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  const int64_t centre = ws->rc_centre;
+  uint32_t acc[kRcCand][kRcKwin];
+#pragma unroll
+  for (int j = 0; j < kRcCand; ++j)
+#pragma unroll
+    for (int w = 0; w < kRcKwin; ++w) acc[j][w] = 0;
+#pragma unroll
+  for (int j = 0; j < kRcCand; ++j) {
+    if (j < nc) {
+      const int64_t b = nc == 1 ? centre
+                                : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2),
+                                            kStepBitsMin, kStepBitsMax);
+      int32_t code[8];
+      quantize_octet<LAT, DITHER>(y, s, __uint_as_float((uint32_t)b), u, code);
+      uint32_t sym[8], cos;
+      strip_octet<LAT>(code, sym, &cos);
+      const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
+#pragma unroll
+      for (int w = 0; w < kRcKwin; ++w) {
+        const int k = fixed_k >= 0 ? fixed_k : kb + w;
+        uint32_t q = 0;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) q += sym[sl] >> slot_width<LAT>(sl, k);
+        acc[j][w] = valid ? q : 0u;
+      }
+    }
+  }
+  // workgroup reduction, then one 64-bit atomic per counter
+#pragma unroll
+  for (int j = 0; j < kRcCand; ++j)
+#pragma unroll
+    for (int w = 0; w < kRcKwin; ++w) {
+      uint32_t v = acc[j][w];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == 0) s_red[wave][j * kRcKwin + w] = v;
+    }
+  __syncthreads();
+  if (tid < kRcCand * kRcKwin) {
+    const uint64_t tot = (uint64_t)s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+    if (tot) atomicAdd((unsigned long long*)&(&ws->rc_sumq[0][0])[tid], (unsigned long long)tot);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&ws->rc_ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+  __syncthreads();
+  if (s_last) {  // last workgroup: gather the counters (and clear them for the next pass), solve
+    __threadfence();
+    uint64_t* cnt = &ws->rc_sumq[0][0];
+    if (tid < kRcCand * kRcKwin) {
+      s_sumq[tid] = __hip_atomic_load(&cnt[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&cnt[tid], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (tid == 0) rate_solve<LAT>(ws, s_sumq, nc, half_log2, fixed_k, target, N);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Header of the stream (see hq.h), written by the workgroup that completes the last chunk.
+__device__ void write_header(uint8_t* out, uint64_t cap, int lattice, int dither, int k, uint32_t step_bits,
+                             uint64_t seed, uint64_t n, uint64_t T, uint32_t chunks, uint32_t F,
+                             uint64_t fixed_off, uint64_t unary_off, uint64_t words, uint64_t ubits,
+                             uint64_t payload, uint64_t total) {
+  if (cap < (uint64_t)kHeaderBytes) return;
+  uint32_t h[32];
+  h[0] = kMagic;
+  h[1] = kVersion | ((uint32_t)lattice << 16) | ((uint32_t)(dither ? 1 : 0) << 24);
+  h[2] = (uint32_t)kTile | ((uint32_t)k << 16) | (6u << 24);
+  h[3] = step_bits;
+  h[4] = (uint32_t)seed; h[5] = (uint32_t)(seed >> 32);
+  h[6] = (uint32_t)n; h[7] = (uint32_t)(n >> 32);
+  h[8] = (uint32_t)T; h[9] = (uint32_t)(T >> 32);
+  h[10] = chunks;
+  h[11] = F;
+  h[12] = (uint32_t)fixed_off; h[13] = (uint32_t)(fixed_off >> 32);
+  h[14] = (uint32_t)unary_off; h[15] = (uint32_t)(unary_off >> 32);
+  h[16] = (uint32_t)words; h[17] = (uint32_t)(words >> 32);
+  h[18] = (uint32_t)ubits; h[19] = (uint32_t)(ubits >> 32);
+  h[20] = (uint32_t)payload; h[21] = (uint32_t)(payload >> 32);
+  h[22] = (uint32_t)total; h[23] = (uint32_t)(total >> 32);
+  for (int i = 24; i < 32; ++i) h[i] = 0;
+  uint32_t* o32 = reinterpret_cast<uint32_t*>(out);
+  for (int i = 0; i < 32; ++i) o32[i] = h[i];
+}
+
+// Decoupled look-back (Merrill & Garland, "Single-pass parallel prefix scan with decoupled
+// look-back", 2016) over chunks, run by one wavefront: each round reads the flags of 64
+// predecessors at once, sums the aggregates up to the nearest inclusive prefix, and retries the
+// window while a predecessor there has not published.  Chunk c is workgroup c; workgroups start in
+// index order on each XCD (workgroup i runs on XCD i mod 8), so every predecessor of a running
+// chunk is running or done, and it publishes its aggregate without waiting: every wait ends.  The
+// wait is still bounded (kSpinLimit rounds); on expiry the status records kErrTimeout.
+// Each flag word carries its own value (flag in bits 62-63; the 64-bit word count in bits 0-33
+// and the padding-bit count in bits 34-61, summed field-wise), so relaxed agent-scope atomics
+// suffice and no cache write-back or invalidation is needed.
+__device__ uint64_t lookback_wave(uint64_t* flags, uint32_t c, uint64_t agg, uint32_t* status) {
+  const int lane = threadIdx.x & 63;
+  if (c == 0) {
+    if (lane == 0) __hip_atomic_store(&flags[0], kFlagPrefix | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
+  if (lane == 0) __hip_atomic_store(&flags[c], kFlagAgg | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t excl = 0;
+  int64_t base = (int64_t)c - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const int64_t j = base - lane;
+    const uint64_t sv = j >= 0 ? __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : kFlagPrefix;
+    const uint64_t f = sv & ~kValMask;
+    const uint64_t pmask = __ballot(f == kFlagPrefix);
+    const uint64_t zmask = __ballot(f == 0);
+    const int first_p = pmask ? __ffsll((unsigned long long)pmask) - 1 : 64;
+    const uint64_t need = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
+    if (zmask & need) {
+      if (++spins > kSpinLimit) {
+        if (lane == 0) atomicOr(status, (uint32_t)kErrTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    uint64_t v = lane <= first_p ? (sv & kValMask) : 0ull;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    excl += v;
+    if (first_p < 64) break;
+    base -= 64;
+  }
+  if (lane == 0)
+    __hip_atomic_store(&flags[c], kFlagPrefix | (excl + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return excl;
+}
+
+constexpr int kPadShift = 34;
+constexpr uint64_t kWordsMask = (1ull << kPadShift) - 1;
+
+struct EncParams {
+  const void* x;
+  uint64_t n, T;
+  uint32_t chunks;
+  uint64_t seed;
+  uint8_t* out;
+  uint64_t cap;
+  Workspace* ws;
+  uint64_t* flags;
+};
+
+template <int LAT, bool DITHER, int DT>
+__global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
+  __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
+  __shared__ uint4 s_unary4[kUnaryWinWords / 4];
+  __shared__ uint32_t s_scan[8];
+  __shared__ uint64_t s_prefix;
+  uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
+  uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  Workspace* ws = P.ws;
+  const uint32_t c = blockIdx.x;
+  const uint32_t step_bits = ws->step_bits;
+  const int k = ws->rice_k;
+  const float step = __uint_as_float(step_bits);
+  const uint32_t F = tile_fixed_bits<LAT>(k);
+  const int RW = octet_rem_bits<LAT>(k);
+  const int hdr = tile_hdr_bits<LAT>();
+  const uint32_t fixed_words = 2u * F;
+  const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (P.chunks + 1));
+  const uint64_t unary_off = align256(fixed_off + (uint64_t)P.chunks * 8ull * F);
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) s_fixed4[i] = z4;
+  for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
+  __syncthreads();
+
+  // alignment padding of the stream (after the index, after the fixed plane) is zero bytes
+  if (c == 0) {
+    const uint64_t pads[2][2] = {{kHeaderBytes + 4ull * (P.chunks + 1), fixed_off},
+                                 {fixed_off + (uint64_t)P.chunks * 8ull * F, unary_off}};
+    for (int pz = 0; pz < 2; ++pz)
+      for (uint64_t b = pads[pz][0] + 4ull * tid; b < pads[pz][1]; b += 4ull * kBlock)
+        if (b + 4 <= P.cap) *reinterpret_cast<uint32_t*>(P.out + b) = 0u;
+  }
+
+  if (c >= P.chunks) {  // empty tensor: one workgroup writes the header and the index
+    if (P.chunks == 0 && tid == 0) {
+      const uint64_t total = unary_off;
+      write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, 0, F, fixed_off, unary_off, 0, 0,
+                   0, total);
+      if (P.cap >= kHeaderBytes + 4) reinterpret_cast<uint32_t*>(P.out)[kHeaderBytes / 4] = 0;
+      if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+      ws->res_total_bytes = total;
+      ws->res_payload_bits = 0;
+      ws->res_unary_bits = 0;
+      ws->res_words = 0;
+      ws->res_step_bits = step_bits;
+      ws->res_k = k;
+    }
+    return;
+  }
+
+  const uint32_t sgn = octet_sign_bits(P.seed, o);
+  uint32_t sym[4][8];
+  uint32_t L[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t tc = 16u * r + 4u * wave + tw;
+    const uint64_t t = (uint64_t)c * kChunkTiles + tc;
+    const bool valid = t < P.T;
+    float y[8];
+    bool finite;
+    const uint32_t sb = transform_octet<DT>(P.x, t, valid, o, sgn, y, &finite);
+    if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+    float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (DITHER) dither_octet<LAT>(P.seed, t, o, u);
+    int32_t code[8];
+    quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), step, u, code);
+    uint32_t cos;
+    strip_octet<LAT>(code, sym[r], &cos);
+    const uint64_t bal = __ballot(valid && cos != 0u);
+    uint32_t len = 8;
+    if (valid) {
+      const uint32_t rec = tc * F;
+      if (o == 0) {
+        lds_put_bits(s_fixed, rec, sb, 16);
+        if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (16 * tw)) & 0xFFFFu, 16);
+      }
+      uint32_t pos = rec + hdr + (uint32_t)o * RW;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int w = slot_width<LAT>(sl, k);
+        lds_put_bits(s_fixed, pos, sym[r][sl] & low_mask(w), w);
+        pos += w;
+        len += sym[r][sl] >> w;
+      }
+    }
+    L[r] = valid ? len : 0u;
+  }
+
+  // unary offsets inside the chunk: octet index 256 r + tid is the symbol order
+  uint32_t off[4], B = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(L[r], s_scan, &tot);
+    off[r] = B + ex;
+    B += tot;
+  }
+  const uint64_t W = (B + 63u) / 64u;
+  if (wave == 0) {
+    const uint64_t agg = W | ((64ull * W - B) << kPadShift);
+    const uint64_t ex = lookback_wave(P.flags, c, agg, &ws->status);
+    if (lane == 0) s_prefix = ex;
+  }
+  __syncthreads();
+  const uint64_t prefix = s_prefix & kWordsMask;
+  const uint64_t prefix_pad = s_prefix >> kPadShift;
+
+  // fixed record of the chunk
+  {
+    const uint64_t fbase = fixed_off + (uint64_t)c * 8ull * F;
+    if (fbase + 8ull * F <= P.cap) {
+      uint4* dst = reinterpret_cast<uint4*>(P.out + fbase);
+      for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) dst[i] = s_fixed4[i];
+    } else if (tid == 0) {
+      atomicOr(&ws->status, (uint32_t)kErrCapacity);
+    }
+  }
+  if (tid == 0) {
+    if (prefix + W > 0xFFFFFFFFull) atomicOr(&ws->status, (uint32_t)kErrRange);  // u32 chunk index
+    if (kHeaderBytes + 4ull * c + 4 <= P.cap)
+      reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[c] = (uint32_t)prefix;
+    else
+      atomicOr(&ws->status, (uint32_t)kErrCapacity);
+  }
+
+  // unary segment, staged through LDS in windows of kUnaryWinBits
+  const uint64_t ubase = unary_off + 8ull * prefix;
+  const bool fits = ubase + 8ull * W <= P.cap;
+  const uint32_t seg_words = (uint32_t)(2u * W);
+  for (uint32_t wb = 0; wb < B; wb += kUnaryWinBits) {
+    if (wb) {
+      __syncthreads();
+      for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (L[r] == 0) continue;
+      uint32_t p = off[r];
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        p += sym[r][sl] >> slot_width<LAT>(sl, k);
+        const uint32_t rel = p - wb;
+        if (p >= wb && rel < kUnaryWinBits) atomicOr(&s_unary[rel >> 5], 1u << (rel & 31u));
+        p += 1;
+      }
+    }
+    __syncthreads();
+    const uint32_t w0 = wb >> 5;
+    const uint32_t nw = min((uint32_t)kUnaryWinWords, seg_words - w0);
+    if (fits) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(P.out + ubase) + w0;
+      for (uint32_t i = tid; i < nw; i += kBlock) dst[i] = s_unary[i];
+    }
+  }
+  if (!fits && tid == 0) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+
+  if (c == P.chunks - 1 && tid == 0) {
+    const uint64_t words = prefix + W;
+    const uint64_t total = unary_off + 8ull * words;
+    const uint64_t ubits = 64ull * words - (prefix_pad + (64ull * W - B));
+    const uint64_t payload = P.T * (uint64_t)(F - 16u) + ubits;
+    write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, P.chunks, F, fixed_off, unary_off,
+                 words, ubits, payload, total);
+    if (kHeaderBytes + 4ull * P.chunks + 4 <= P.cap)
+      reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[P.chunks] = (uint32_t)words;
+    if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+    ws->res_total_bytes = total;
+    ws->res_payload_bits = payload;
+    ws->res_unary_bits = ubits;
+    ws->res_words = words;
+    ws->res_step_bits = step_bits;
+    ws->res_k = k;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Diagnostic codes kernel: front half at a fixed step, integer codes and scale bits out.
+template <int LAT, bool DITHER, int DT>
+__global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ x, uint64_t T, uint64_t seed,
+                                                       uint32_t step_bits, int32_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales, Workspace* ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const uint64_t t = (uint64_t)blockIdx.x * 16 + wave * 4 + tw;
+  const bool valid = t < T;
+  const uint32_t sgn = octet_sign_bits(seed, o);
+  float y[8];
+  bool finite;
+  const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
+  if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+  float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  int32_t code[8];
+  quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), __uint_as_float(step_bits), u, code);
+  if (valid) {
+    int4* dst = reinterpret_cast<int4*>(codes + t * kTile + 8 * o);
+    dst[0] = make_int4(code[0], code[1], code[2], code[3]);
+    dst[1] = make_int4(code[4], code[5], code[6], code[7]);
+    if (o == 0) scales[t] = (uint16_t)sb;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decoder.
+__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  ws->status = 0;
+  ws->dec_valid = 0;
+  bool ok = in_bytes >= (uint64_t)kHeaderBytes;
+  uint32_t h[32];
+  if (ok) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(in);
+    for (int i = 0; i < 32; ++i) h[i] = p[i];
+  } else {
+    for (int i = 0; i < 32; ++i) h[i] = 0;
+  }
+  const uint64_t hn = ((uint64_t)h[7] << 32) | h[6];
+  const uint64_t T = n / kTile;
+  const uint32_t chunks = (uint32_t)((T + kChunkTiles - 1) / kChunkTiles);
+  const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
+  ok = ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatE8 && flags <= 1 &&
+       (h[2] & 0xFFFFu) == (uint32_t)kTile && k <= 15 && (h[2] >> 24) == 6u && h[3] >= kStepBitsMin &&
+       h[3] <= kStepBitsMax && hn == n && (n % kTile) == 0;
+  uint32_t F = 0;
+  if (ok) {
+    const int kh = k > 0 ? k - 1 : 0;
+    const int rem = lattice == kLatE8 ? 7 * k + kh : lattice == kLatD4 ? 6 * k + 2 * kh : 8 * k;
+    F = (uint32_t)((lattice == kLatE8 ? 32 : 16) + 16 * rem);
+  }
+  const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (chunks + 1));
+  const uint64_t unary_off = align256(fixed_off + (uint64_t)chunks * 8ull * F);
+  const uint64_t words = ((uint64_t)h[17] << 32) | h[16];
+  const uint64_t total = ((uint64_t)h[23] << 32) | h[22];
+  ok = ok && (((uint64_t)h[9] << 32) | h[8]) == T && h[10] == chunks && h[11] == F &&
+       (((uint64_t)h[13] << 32) | h[12]) == fixed_off && (((uint64_t)h[15] << 32) | h[14]) == unary_off &&
+       total <= in_bytes && words <= (1ull << 32) && unary_off + 8ull * words == total;
+  if (ok) {
+    const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
+    ok = idx[0] == 0u && (uint64_t)idx[chunks] == words;
+  }
+  if (!ok) {
+    ws->status = kErrCorrupt;
+    return;
+  }
+  ws->dec_lattice = (uint32_t)lattice;
+  ws->dec_dither = (uint32_t)flags;
+  ws->dec_k = k;
+  ws->dec_step_bits = h[3];
+  ws->dec_F = F;
+  ws->dec_chunks = chunks;
+  ws->dec_seed = ((uint64_t)h[5] << 32) | h[4];
+  ws->dec_tiles = T;
+  ws->dec_fixed_off = fixed_off;
+  ws->dec_unary_off = unary_off;
+  ws->dec_words = words;
+  ws->dec_valid = 1;
+}
+
+constexpr int kMaxSymsPerChunk = kChunkTiles * kTile;
+
+template <int LAT, int DT_OUT>
+__device__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, uint32_t c,
+                             uint32_t tiles_c, const uint32_t* s_pos, const uint32_t* s_fixed) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const int k = ws->dec_k;
+  const uint32_t F = ws->dec_F;
+  const bool dither = ws->dec_dither != 0;
+  const uint64_t seed = ws->dec_seed;
+  const float step = __uint_as_float(ws->dec_step_bits);
+  const int RW = octet_rem_bits<LAT>(k);
+  const int hdr = tile_hdr_bits<LAT>();
+  const uint32_t sgn = octet_sign_bits(seed, o);
+  bool bad = false;
+#pragma unroll 1
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t tc = 16u * r + 4u * wave + tw;
+    const bool valid = tc < tiles_c;
+    const uint64_t t = (uint64_t)c * kChunkTiles + tc;
+    float yv[8];
+    if (valid) {
+      const uint32_t rec = tc * F;
+      const uint32_t sb = lds_get_bits(s_fixed, rec, 16);
+      const uint32_t coset = LAT == kLatE8 ? lds_get_bits(s_fixed, rec + 16 + o, 1) : 0u;
+      uint32_t pos = rec + hdr + (uint32_t)o * RW;
+      uint32_t sym[8];
+      const uint32_t g0 = (16u * tc + o) * 8u;
+      uint32_t prev = g0 ? s_pos[g0 - 1] + 1u : 0u;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int w = slot_width<LAT>(sl, k);
+        const uint32_t p = s_pos[g0 + sl];
+        const uint32_t q = p - prev;
+        prev = p + 1u;
+        if (q > (0xFFFFFFFFu >> w)) bad = true;
+        sym[sl] = (q << w) | lds_get_bits(s_fixed, pos, w);
+        pos += w;
+      }
+      int32_t code[8];
+      unstrip_octet<LAT>(sym, coset, code);
+      float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (dither) dither_octet<LAT>(seed, t, o, u);
+      const float tsc = bf16_bits_to_f32(sb) * step;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float cc = code_coord<LAT>(code[i]);
+        const float cu = dither ? cc - u[i] : cc;
+        yv[i] = cu * tsc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[i] = 0.0f;
+    }
+    fwht_lane(yv);
+    fwht_cross(yv, o);
+    if (valid) {
+      float xo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = yv[i] * 0.0078125f;
+        xo[i] = ((sgn >> i) & 1u) ? -v : v;
+      }
+      if (DT_OUT == 1) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = f32_to_bf16_rne(xo[2 * i]) | (f32_to_bf16_rne(xo[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * kTile + 8 * o) =
+            make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      } else {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * kTile + 8 * o);
+        dst[0] = make_float4(xo[0], xo[1], xo[2], xo[3]);
+        dst[1] = make_float4(xo[4], xo[5], xo[6], xo[7]);
+      }
+    }
+  }
+  if (bad) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+}
+
+template <int DT_OUT>
+__global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restrict__ in, void* __restrict__ out,
+                                                        Workspace* ws) {
+  __shared__ uint32_t s_pos[kMaxSymsPerChunk];
+  __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
+  __shared__ uint32_t s_scan[8];
+  uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
+  if (!ws->dec_valid) return;
+  const int tid = threadIdx.x;
+  const uint32_t c = blockIdx.x;
+  const uint32_t chunks = ws->dec_chunks;
+  if (c >= chunks) return;
+  const uint64_t T = ws->dec_tiles;
+  const uint32_t tiles_c = (uint32_t)min((uint64_t)kChunkTiles, T - (uint64_t)c * kChunkTiles);
+  const uint32_t nsym = tiles_c * kTile;
+  const uint32_t F = ws->dec_F;
+  const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
+  const uint32_t w0 = idx[c], w1 = idx[c + 1];
+  if (w1 < w0 || (uint64_t)w1 > ws->dec_words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
+    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+    return;
+  }
+  const uint32_t nW = w1 - w0;
+  const uint64_t* seg = reinterpret_cast<const uint64_t*>(in + ws->dec_unary_off) + w0;
+  // terminator positions: popcount per word, workgroup scan, scatter of the set bits
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < nW; base += kBlock) {
+    const uint32_t j = base + tid;
+    const uint64_t word = j < nW ? seg[j] : 0ull;
+    const uint32_t cnt = (uint32_t)__popcll(word);
+    uint32_t tot;
+    uint32_t g = carry + block_excl_scan(cnt, s_scan, &tot);
+    uint64_t bits = word;
+    while (bits) {
+      const uint32_t b = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
+      bits &= bits - 1ull;
+      if (g < nsym) s_pos[g] = j * 64u + b;
+      ++g;
+    }
+    carry += tot;
+  }
+  // stage the fixed record
+  const uint4* src = reinterpret_cast<const uint4*>(in + ws->dec_fixed_off + (uint64_t)c * 8ull * F);
+  for (uint32_t i = tid; i < F / 2; i += kBlock) s_fixed4[i] = src[i];
+  __syncthreads();
+  if (carry != nsym) {
+    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+    return;
+  }
+  switch (ws->dec_lattice) {
+    case kLatE8: decode_chunk<kLatE8, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
+    case kLatD4: decode_chunk<kLatD4, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
+    default: decode_chunk<kLatZ, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers.
+
+#define HQ_DISPATCH(LATV, DITHV, DTV, CALL)                                   \
+  do {                                                                        \
+    if ((LATV) == kLatE8) {                                                   \
+      if (DITHV) { if ((DTV) == 1) CALL(kLatE8, true, 1); else CALL(kLatE8, true, 0); }   \
+      else { if ((DTV) == 1) CALL(kLatE8, false, 1); else CALL(kLatE8, false, 0); }       \
+    } else if ((LATV) == kLatD4) {                                            \
+      if (DITHV) { if ((DTV) == 1) CALL(kLatD4, true, 1); else CALL(kLatD4, true, 0); }   \
+      else { if ((DTV) == 1) CALL(kLatD4, false, 1); else CALL(kLatD4, false, 0); }       \
+    } else {                                                                  \
+      if (DITHV) { if ((DTV) == 1) CALL(kLatZ, true, 1); else CALL(kLatZ, true, 0); }     \
+      else { if ((DTV) == 1) CALL(kLatZ, false, 1); else CALL(kLatZ, false, 0); }         \
+    }                                                                         \
+  } while (0)
+
+hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
+  const uint64_t nflags = (uint64_t)a.chunks + 1;
+  uint64_t blocks = (nflags + kBlock - 1) / kBlock;
+  if (blocks > 1024) blocks = 1024;
+  uint32_t step_bits;
+  int32_t k;
+  if (a.fixed_step_bits) {
+    step_bits = a.fixed_step_bits;
+    k = a.rice_k >= 0 ? a.rice_k : kwin_base(a.fixed_step_bits) + 1;
+  } else {
+    const int64_t c = centre < kStepBitsMin ? kStepBitsMin : (centre > kStepBitsMax ? kStepBitsMax : centre);
+    step_bits = (uint32_t)c;
+    k = a.rice_k >= 0 ? a.rice_k : kwin_base(centre) + 1;
+  }
+  hipLaunchKernelGGL(init_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.ws,
+                     lookback_flags(a.ws), nflags, centre, step_bits, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N) {
+  const uint32_t blocks = (N + 15) / 16;
+  if (blocks == 0) return hipSuccess;
+#define HQ_RATE(L, D, T)                                                                              \
+  hipLaunchKernelGGL((rate_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
+                     a.seed, nc, half_log2, a.rice_k, a.target)
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_RATE);
+#undef HQ_RATE
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs& a) {
+  EncParams P;
+  P.x = a.x;
+  P.n = a.n;
+  P.T = a.tiles;
+  P.chunks = a.chunks;
+  P.seed = a.seed;
+  P.out = a.out;
+  P.cap = a.cap;
+  P.ws = a.ws;
+  P.flags = lookback_flags(a.ws);
+  const uint32_t blocks = a.chunks ? a.chunks : 1u;
+#define HQ_ENC(L, D, T) hipLaunchKernelGGL((encode_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, P)
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_ENC);
+#undef HQ_ENC
+  return hipGetLastError();
+}
+
+hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales) {
+  const uint64_t blocks = (a.tiles + 15) / 16;
+  if (blocks == 0) return hipSuccess;
+#define HQ_CODES(L, D, T)                                                                             \
+  hipLaunchKernelGGL((codes_kernel<L, D, T>), dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, \
+                     a.seed, a.fixed_step_bits, codes, scales, a.ws)
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_CODES);
+#undef HQ_CODES
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
+                         Workspace* ws, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t T = n / kTile;
+  const uint64_t chunks = (T + kChunkTiles - 1) / kChunkTiles;
+  if (chunks == 0) return hipSuccess;
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(decode_kernel<1>, dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws);
+  else
+    hipLaunchKernelGGL(decode_kernel<0>, dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws);
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -66,6 +66,7 @@ def lib():
         L.hqo_tile_fixed_bits.restype = u32
         L.hqo_quantize.argtypes = [P, i32, u64, i32, i32, u64, f32, P, P]
         L.hqo_dequantize.argtypes = [P, P, u64, i32, i32, u64, f32, P]
+        L.hqo_lattice_inputs.argtypes = [P, i32, u64, i32, i32, u64, f32, P]
         L.hqo_sample_tile.argtypes = [u64, u64, u64]
         L.hqo_sample_tile.restype = u64
         L.hqo_rate.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, P]
@@ -193,6 +194,15 @@ def quantize(x: np.ndarray, lattice: int, step: float, seed: int = 0, dither: bo
     _check(lib().hqo_quantize(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
                               ctypes.c_float(step), _p(codes), _p(scales)), "quantize")
     return codes, scales[: n // 128]
+
+
+def lattice_inputs(x, lattice: int, step: float, seed: int = 0, dither: bool = False) -> np.ndarray:
+    """The binary32 values fed to the nearest-point step (y * m, plus U with dither)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    v = np.zeros(x.size, dtype=np.float32)
+    _check(lib().hqo_lattice_inputs(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
+                                    ctypes.c_float(step), _p(v)), "lattice_inputs")
+    return v
 
 
 def dequantize(codes, scales, lattice: int, step: float, seed: int = 0, dither: bool = False):

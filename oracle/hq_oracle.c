@@ -452,6 +452,38 @@ int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, 
   return OK;
 }
 
+/* The binary32 inputs v of the nearest-point step at a fixed step (for locating a code mismatch
+ * relative to the Voronoi boundary in the tests). */
+int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
+                       float step, float *v_out) {
+  if (n % TILE) return ERR_INVALID_ARG;
+  qctx q;
+  qctx_init(&q, lattice, dither, seed);
+  for (uint64_t t = 0; t < n / TILE; ++t) {
+    float y[TILE];
+    load_tile(x, dtype, t, y);
+    for (int i = 0; i < TILE; ++i) y[i] = q.d[i] * y[i];
+    hqo_fwht128(y);
+    float S = hqo_sumsq128(y);
+    if (!isfinite(S)) return ERR_NONFINITE;
+    float s = bf16_to_f32(hqo_scale_bits(S));
+    float m = 0.0f;
+    if (s != 0.0f) {
+      float tsc = s * step;
+      m = 1.0f / tsc;
+    }
+    for (int o = 0; o < 16; ++o) {
+      float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (dither) hqo_dither_octet(seed, t, o, lattice, u);
+      for (int i = 0; i < 8; ++i) {
+        float v = y[8 * o + i] * m;
+        v_out[t * TILE + 8 * o + i] = dither ? v + u[i] : v;
+      }
+    }
+  }
+  return OK;
+}
+
 int hqo_dequantize(const int32_t *codes, const uint16_t *scales, uint64_t n, int lattice,
                    int dither, uint64_t seed, float step, float *out) {
   if (n % TILE) return ERR_INVALID_ARG;

@@ -1,0 +1,103 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point include/hq.h declares, and
+rejects bad arguments on the host before any device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_quantization_tile_amd as hq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hq_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(hq.EXPORTS), names
+    L = hq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert hq.hq_version() == (1 << 16) | 1
+
+
+def test_strerror_codes():
+    for code in range(-8, 1):
+        assert hq.strerror(code) != "unknown status"
+    assert hq.strerror(-99) == "unknown status"
+
+
+def test_sizes_match_oracle_layout(orc):
+    for n in (0, 128, 128 * 65, 128 * 458752):
+        for lat in ("z", "d4", "e8"):
+            for k in (0, 1, 3, 15):
+                fo, uo, F = orc.layout(n, orc.LATTICES[lat], k)
+                assert hq.hq_stream_fixed_bytes(n, lat, k) == uo
+    assert hq.hq_workspace_size(0) == 4096 + 256
+    assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + ((8 * 101 + 255) // 256) * 256
+
+
+def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 21):
+    info = hq.HqInfo()
+    nb = ctypes.c_uint64(0)
+    return hq.lib().hq_encode(ctypes.c_void_p(x), 1, n, ctypes.byref(params), ctypes.c_void_p(out), 1 << 20,
+                              ctypes.byref(nb), ctypes.byref(info), ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tile=64), hq.HQ_ERR_UNSUPPORTED),
+    (dict(lattice=3), hq.HQ_ERR_INVALID_ARG),
+    (dict(rice_k=16), hq.HQ_ERR_INVALID_ARG),
+    (dict(step=-1.0), hq.HQ_ERR_INVALID_ARG),
+    (dict(step=float("nan")), hq.HQ_ERR_INVALID_ARG),
+    (dict(step=1e-6), hq.HQ_ERR_INVALID_ARG),
+    (dict(step=1e6), hq.HQ_ERR_INVALID_ARG),
+    (dict(target_bps=1.0), hq.HQ_ERR_RATE),          # below E8's floor of 1.125
+    (dict(target_bps=13.0), hq.HQ_ERR_RATE),
+    (dict(dither=True, lattice="z", target_bps=0.5), hq.HQ_ERR_RATE),
+])
+def test_encode_rejects_bad_params_on_host(kw, code):
+    base = dict(lattice="e8", target_bps=4.0)
+    base.update(kw)
+    tile = base.pop("tile", 128)
+    p = hq.make_params(**base, tile=tile)
+    assert _encode_rc(p) == code
+
+
+def test_encode_rejects_bad_buffers_on_host():
+    p = hq.make_params("e8", 4.0)
+    assert _encode_rc(p, n=100) == hq.HQ_ERR_INVALID_ARG           # n % 128
+    assert _encode_rc(p, ws_bytes=16) == hq.HQ_ERR_INVALID_ARG       # workspace too small
+    assert _encode_rc(p, ws=0) == hq.HQ_ERR_INVALID_ARG              # null workspace
+    assert _encode_rc(p, x=0) == hq.HQ_ERR_INVALID_ARG               # null input
+    assert _encode_rc(p, out=0) == hq.HQ_ERR_INVALID_ARG             # null output
+    assert _encode_rc(p, out=(1 << 20) + 4) == hq.HQ_ERR_INVALID_ARG  # misaligned output
+
+
+def test_decode_and_codes_reject_bad_args_on_host():
+    L = hq.lib()
+    assert L.hq_decode(ctypes.c_void_p(1 << 20), 4096, ctypes.c_void_p(1 << 20), 1, 100,
+                       ctypes.c_void_p(1 << 21), 8192, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_decode(ctypes.c_void_p(1 << 20), 4096, ctypes.c_void_p(1 << 20), 7, 128,
+                       ctypes.c_void_p(1 << 21), 8192, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_decode(None, 4096, ctypes.c_void_p(1 << 20), 1, 128, ctypes.c_void_p(1 << 21), 8192,
+                       None) == hq.HQ_ERR_INVALID_ARG
+    p = hq.make_params("e8", 4.0)  # step 0: the diagnostic codes call needs a fixed step
+    assert L.hq_codes(ctypes.c_void_p(1 << 20), 1, 128, ctypes.byref(p), ctypes.c_void_p(1 << 20),
+                      ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 8192, None) == hq.HQ_ERR_INVALID_ARG
+    p = hq.make_params("e8", step=0.3)
+    assert L.hq_codes(ctypes.c_void_p(1 << 20), 1, 128, ctypes.byref(p), ctypes.c_void_p(1 << 20),
+                      ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 4096, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_workspace_size(100, None, ctypes.byref(ctypes.c_size_t())) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_status(None, None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_product_package_does_not_import_oracle():
+    src = open(os.path.join(ROOT, "kv_quantization_tile_amd", "__init__.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    for f in os.listdir(os.path.join(ROOT, "kv_quantization_tile_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "kv_quantization_tile_amd", "csrc", f)).read().lower(), f

@@ -1,0 +1,281 @@
+"""GPU parity: the gfx950 codec (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bar (integer, byte and index work is bit-exact):
+* integer lattice codes and tile scales: identical; any mismatch must lie within 1e-5 (lattice
+  units) of a Voronoi boundary and affect at most 1e-6 of the octets;
+* bitstreams: byte-identical, at fixed operating points and after rate control;
+* rate control: the same step bit pattern and Rice parameter;
+* decoded values: identical (fp32 and bf16), which is stricter than the 1e-6 relative bound;
+* payload rate within 0.01 bits per value of the target.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+hq = pytest.importorskip("kv_quantization_tile_amd")
+
+pytestmark = pytest.mark.gpu
+
+LAT = {"z": 0, "d4": 1, "e8": 2}
+
+
+def dev(a: np.ndarray):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+
+
+def host_bytes(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint8)
+
+
+def bf16_host(t) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def assert_same_stream(gpu_bytes: np.ndarray, orc_bytes: np.ndarray, what=""):
+    """Byte equality, reporting the section of the first difference."""
+    if gpu_bytes.size == orc_bytes.size and np.array_equal(gpu_bytes, orc_bytes):
+        return
+    n = min(gpu_bytes.size, orc_bytes.size)
+    diff = np.nonzero(gpu_bytes[:n] != orc_bytes[:n])[0]
+    h = hq.header_fields(orc_bytes)
+    first = int(diff[0]) if diff.size else n
+    sect = ("header" if first < 128 else "index/pad" if first < h["fixed_off"] else
+            "fixed/pad" if first < h["unary_off"] else "unary")
+    raise AssertionError(f"{what}: sizes {gpu_bytes.size} vs {orc_bytes.size}, {diff.size} differing bytes, "
+                         f"first at {first} ({sect}; fixed_off {h['fixed_off']}, unary_off {h['unary_off']})")
+
+
+def boundary_check(orc, x, lattice, step, seed, dither, codes_gpu, codes_orc):
+    """Every mismatching octet must be within 1e-5 of the Voronoi boundary between the two points,
+    and mismatches must be at most 1e-6 of all octets (at least one is allowed on small inputs)."""
+    bad = np.nonzero((codes_gpu.reshape(-1, 8) != codes_orc.reshape(-1, 8)).any(axis=1))[0]
+    if bad.size == 0:
+        return 0
+    v = orc.lattice_inputs(x, LAT[lattice], step, seed, dither).reshape(-1, 8).astype(np.float64)
+    half = 0.5 if lattice == "e8" else 1.0
+    for i in bad:
+        cg = codes_gpu.reshape(-1, 8)[i] * half
+        co = codes_orc.reshape(-1, 8)[i] * half
+        dg, do = ((v[i] - cg) ** 2).sum(), ((v[i] - co) ** 2).sum()
+        dist = abs(dg - do) / (2 * np.linalg.norm(cg - co))
+        assert dist <= 1e-5, (i, dist)
+    assert bad.size <= max(1, int(1e-6 * codes_orc.size / 8)), bad.size
+    return bad.size
+
+
+# ---------------------------------------------------------------------------------------------
+
+def test_tiny_roundtrip_bitexact(orc):
+    say("case: tiny E8 4 bps, rate-controlled")
+    x = synth.tiny()
+    s_orc, info_orc = orc.encode(x, orc.LAT_E8, 4.0)
+    s_gpu, info = hq.hq_encode(dev(x), "e8", 4.0)
+    assert info["step"] == info_orc["step"] and info["rice_k"] == info_orc["k"]
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    y_orc = orc.decode(s_orc, x.size)
+    y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+    assert np.array_equal(y.cpu().numpy(), y_orc)
+    yb = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(yb), orc.decode(s_orc, x.size, out_dtype="bf16"))
+    assert abs(info["payload_bps"] - 4.0) <= 0.01
+    assert info["payload_bits"] == info_orc["payload_bits"] and info["bytes"] == info_orc["bytes"]
+
+
+def _scaled_gaussian_tiles(T, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, 128)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-3, 3, (T, 1))).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("dither", [False, True])
+@pytest.mark.parametrize("T", [1, 65, 130, 1000])
+def test_stream_parity_fixed_point(orc, lattice, dither, T):
+    say(f"case: fixed point {lattice} dither={dither} T={T}")
+    x = _scaled_gaussian_tiles(T, seed=T)
+    for step, k in ((0.3, 2), (1.1, 0), (0.05, 5)):
+        s_orc, _ = orc.encode(x, LAT[lattice], 0.0, seed=9, dither=dither, step=step, rice_k=k)
+        s_gpu, info = hq.hq_encode(dev(x), lattice, 0.0, seed=9, dither=dither, step=step, rice_k=k)
+        assert_same_stream(host_bytes(s_gpu), s_orc, f"step {step} k {k}")
+        y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+        assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+
+
+@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("dither", [False, True])
+def test_codes_parity_weight_slice(orc, lattice, dither):
+    say(f"case: codes {lattice} dither={dither} weight 512x4096")
+    w = synth.weight(rows=512)
+    for step in (0.12, 0.27, 0.6):
+        c_orc, s_orc = orc.quantize(w, LAT[lattice], step, seed=3, dither=dither)
+        c_gpu, s_gpu = hq.hq_codes(dev(w), step, lattice, seed=3, dither=dither)
+        assert np.array_equal(s_gpu.cpu().numpy().view(np.uint16), s_orc)
+        boundary_check(orc, w, lattice, step, 3, dither, c_gpu.cpu().numpy(), c_orc)
+
+
+@pytest.mark.parametrize("case", ["tiny", "weight2048", "kv_dither"])
+def test_rate_control_parity(orc, case):
+    say(f"case: rate control {case}")
+    if case == "tiny":
+        x, lat, tb, seed, dither = synth.tiny(), "e8", 3.0, 0, False
+    elif case == "weight2048":
+        x, lat, tb, seed, dither = synth.weight(rows=2048), "e8", 4.0, 0, False
+    else:
+        x, lat, tb, seed, dither = synth.kv(1, 0, heads=2, tokens=8192), "e8", 2.0, synth.kv_seed(1, 0), True
+    st, sb, k = orc.rate(x, LAT[lat], tb, seed=seed, dither=dither)
+    info = hq.hq_rate(dev(x), lat, tb, seed=seed, dither=dither)
+    got = np.array([info["step"]], dtype=np.float32).view(np.uint32)[0]
+    assert int(got) == sb and info["rice_k"] == k
+
+
+@pytest.mark.parametrize("target", [3.0, 4.0, 5.0])
+def test_weight_full_size(orc, target):
+    """The 14336 x 4096 bf16 MLP weight, E8, no dither: full stream and decode parity."""
+    say(f"case: weight 14336x4096 E8 {target} bps")
+    w = synth.weight()
+    s_orc, info_orc = orc.encode(w, orc.LAT_E8, target)
+    s_gpu, info = hq.hq_encode(dev(w), "e8", target)
+    assert info["step"] == info_orc["step"] and info["rice_k"] == info_orc["k"]
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert abs(info["payload_bps"] - target) <= 0.01
+    y = hq.hq_decode(s_gpu, w.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(y), orc.decode(s_orc, w.size, out_dtype="bf16"))
+
+
+@pytest.mark.parametrize("layer,is_v,target", [(0, 0, 2.0), (31, 1, 3.0)])
+def test_kv_call_full_size(orc, layer, is_v, target):
+    """One (layer, K|V) call of the KV workload: [8][32768][128] bf16, E8 with dither."""
+    say(f"case: kv layer {layer} {'V' if is_v else 'K'} {target} bps")
+    x = synth.kv(layer, is_v)
+    seed = synth.kv_seed(layer, is_v)
+    s_orc, info_orc = orc.encode(x, orc.LAT_E8, target, seed=seed, dither=True)
+    s_gpu, info = hq.hq_encode(dev(x), "e8", target, seed=seed, dither=True)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert abs(info["payload_bps"] - target) <= 0.01
+    y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(y), orc.decode(s_orc, x.size, out_dtype="bf16"))
+
+
+# ---- edge cases and error paths ---------------------------------------------------------------
+
+def test_empty_and_single_tile(orc):
+    say("case: empty and single tile")
+    e = np.zeros(0, dtype=np.float32)
+    s_orc, _ = orc.encode(e, orc.LAT_E8, 4.0)
+    s_gpu, info = hq.hq_encode(torch.zeros(0, device="cuda"), "e8", 4.0)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert hq.hq_decode(s_gpu, 0, out_dtype=torch.float32).numel() == 0
+    x = synth.tiny(tiles=1)
+    s_orc, _ = orc.encode(x, orc.LAT_E8, 4.0)
+    s_gpu, _ = hq.hq_encode(dev(x), "e8", 4.0)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+
+
+def test_zero_tiles_and_tiny_values(orc):
+    say("case: zero and denormal tiles")
+    x = synth.tiny(tiles=70).copy()
+    x[3] = 0.0
+    x[10] = np.float32(1e-30) * x[10]
+    x[11] = np.float32(1e-42)
+    x[20] = np.float32(1e15) * x[20]
+    for lat in ("e8", "d4", "z"):
+        for dither in (False, True):
+            s_orc, _ = orc.encode(x, LAT[lat], 0.0, seed=1, dither=dither, step=0.25, rice_k=3)
+            s_gpu, _ = hq.hq_encode(dev(x), lat, 0.0, seed=1, dither=dither, step=0.25, rice_k=3)
+            assert_same_stream(host_bytes(s_gpu), s_orc, f"{lat} dither={dither}")
+            y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+            assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+
+
+def test_long_unary_segments(orc):
+    """k = 0 at a small step: ~35 unary bits per value, so a chunk's unary segment spans several
+    staging windows of the encoder."""
+    say("case: long unary segments")
+    x = synth.gaussian(128 * 200, seed=4).reshape(200, 128)
+    s_orc, info_orc = orc.encode(x, orc.LAT_Z, 0.0, step=0.05, rice_k=0)
+    assert info_orc["unary_bits"] / x.size > 20
+    s_gpu, _ = hq.hq_encode(dev(x), "z", 0.0, step=0.05, rice_k=0)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+    assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+
+
+def test_nonfinite_reported():
+    say("case: non-finite input")
+    x = synth.tiny().copy()
+    x[5, 3] = np.nan
+    with pytest.raises(hq.HqError) as e:
+        hq.hq_encode(dev(x), "e8", 0.0, step=0.3, rice_k=2)
+    assert e.value.code == hq.HQ_ERR_NONFINITE
+
+
+def test_capacity_reported_and_retry(orc):
+    say("case: capacity")
+    x = synth.tiny(tiles=300)
+    s_orc, _ = orc.encode(x, orc.LAT_E8, 4.0)
+    xd = dev(x)
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    ws = hq.workspace(x.size)
+    import ctypes
+    p = hq.make_params("e8", 4.0)
+    nb = ctypes.c_uint64(0)
+    rc = hq.lib().hq_encode(ctypes.c_void_p(xd.data_ptr()), 0, x.size, ctypes.byref(p),
+                            ctypes.c_void_p(small.data_ptr()), small.numel(), ctypes.byref(nb), None,
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert rc == hq.HQ_ERR_CAPACITY and nb.value == s_orc.size
+    s_gpu, _ = hq.hq_encode(xd, "e8", 4.0, out=small)   # the binding grows the buffer and retries
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+
+
+def test_corrupt_streams_reported(orc):
+    say("case: corrupt streams")
+    x = synth.tiny(tiles=130)
+    s_gpu, _ = hq.hq_encode(dev(x), "e8", 4.0)
+    good = s_gpu.clone()
+    for mutate in ("magic", "n", "index", "terminators"):
+        s = good.clone()
+        n = x.size
+        if mutate == "magic":
+            s[0] ^= 1
+        elif mutate == "n":
+            n = x.size + 128
+        elif mutate == "index":
+            s[128 + 4] = 0xFF
+        else:
+            s[-16:] = 0
+        with pytest.raises(hq.HqError) as e:
+            hq.hq_decode(s, n, out_dtype=torch.float32)
+        assert e.value.code == hq.HQ_ERR_CORRUPT, mutate
+    y = hq.hq_decode(good, x.size, out_dtype=torch.float32)   # and the good one still decodes
+    assert torch.isfinite(y).all()
+
+
+def test_deterministic_repeat():
+    say("case: determinism")
+    w = synth.weight(rows=1024)
+    xd = dev(w)
+    a, _ = hq.hq_encode(xd, "e8", 4.0)
+    b, _ = hq.hq_encode(xd, "e8", 4.0)
+    assert torch.equal(a, b)
+
+
+def test_overflowing_energy_is_nonfinite(orc):
+    """A finite input whose transformed energy overflows binary32 is reported like NaN input."""
+    say("case: energy overflow")
+    x = synth.tiny().copy()
+    x[7] *= np.float32(1e30)
+    with pytest.raises(orc.OracleError) as eo:
+        orc.encode(x, orc.LAT_E8, 0.0, step=0.3, rice_k=2)
+    assert eo.value.code == orc.ERR_NONFINITE
+    with pytest.raises(hq.HqError) as e:
+        hq.hq_encode(dev(x), "e8", 0.0, step=0.3, rice_k=2)
+    assert e.value.code == hq.HQ_ERR_NONFINITE
