@@ -406,7 +406,9 @@ static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float s
 }
 
 /* Inverse of the quantiser for one tile: c = code coordinate; yhat = (c - U) * (s * step);
- * xhat = D (H yhat) * 2^-7 (exact power-of-two factor because H H = 128 I). */
+ * xhat = D (H yhat) * 2^-7 (exact power-of-two factor because H H = 128 I).  Reading: a decoded
+ * value that is exactly zero is +0 (the pages do not speak of signed zeros; the sign of an exact
+ * cancellation depends on the order of the butterflies, not on the data). */
 static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb,
                             float step, float out[TILE]) {
   float s = bf16_to_f32(sb);
@@ -422,7 +424,10 @@ static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE],
     }
   }
   hqo_fwht128(y);
-  for (int i = 0; i < TILE; ++i) out[i] = q->d[i] * (y[i] * 0.0078125f);
+  for (int i = 0; i < TILE; ++i) {
+    float o = q->d[i] * (y[i] * 0.0078125f);
+    out[i] = (o == 0.0f) ? 0.0f : o;
+  }
 }
 
 static void load_tile(const void *x, int dtype, uint64_t t, float out[TILE]) {
