@@ -35,7 +35,26 @@ def parse():
     ap.add_argument("--bps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 256 MiB (known traffic), for scaling "
+                         "the HBM byte counters of a profiler run")
     return ap.parse_args()
+
+
+def copy_calibration(steps: int):
+    """A plain copy of known size: 256 MiB read + 256 MiB written per launch.  A counter run over it
+    gives the factor between the profiler's FETCH_SIZE / WRITE_SIZE readings and true HBM bytes."""
+    import torch
+    nbytes = 256 << 20
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                           "launches": steps}}), flush=True)
 
 
 def workload(cfg: str, bps):
@@ -44,12 +63,38 @@ def workload(cfg: str, bps):
         x = synth.weight()
         tb = 4.0 if bps is None else bps
         return x, dict(workload=f"mlp weight 14336x4096 bf16, E8 {tb:g} bps, no dither",
-                       shape=[14336, 4096], lattice="e8", target_bps=tb, dither=False, seed=0), 0
+                       shape=[14336, 4096], lattice="e8", target_bps=tb, dither=False, seed=0,
+                       profile=f"weight_14336x4096_e8_{tb:g}bps"), 0
     x = synth.kv(0, 0)
     tb = 2.0 if bps is None else bps
     return x, dict(workload=f"kv cache layer 0 K [8][32768][128] bf16, E8 + dither {tb:g} bps",
                    shape=[8, 32768, 128], lattice="e8", target_bps=tb, dither=True,
-                   seed=synth.kv_seed(0, 0)), synth.kv_seed(0, 0)
+                   seed=synth.kv_seed(0, 0), profile=f"kv_8x32768x128_e8_dither_{tb:g}bps"), synth.kv_seed(0, 0)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    pkg = os.path.join(ROOT, "kv_quantization_tile_amd")
+    src = b"".join(open(os.path.join(pkg, f), "rb").read() for f in
+                   ("csrc/hq_kernels.hip", "csrc/hq_device.h", "csrc/hq_internal.h", "build.py"))
+    return hashlib.sha256(src).hexdigest()[:16]
+
+
+def profiled_traffic(profile_stem: str, kernel_prefix: str):
+    """HBM bytes per dispatch of the named kernel, from the committed FETCH_SIZE / WRITE_SIZE summary
+    of this workload (copy-calibrated); None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", profile_stem + "_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    blob = text.split("```json", 1)[-1].split("```", 1)[0]
+    data = json.loads(blob)
+    if data.get("source_sha256_16") != kernel_source_hash():
+        return None
+    for name, rec in data["kernels"].items():
+        if name.startswith("hq::" + kernel_prefix):
+            return int(rec["traffic_bytes"])
+    return None
 
 
 def main():
@@ -58,11 +103,15 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "tiles shard across GPUs without communication, see the design notes", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
     import torch
 
     import kv_quantization_tile_amd as hq
 
     x_host, cfg, seed = workload(args.config, args.bps)
+    profile_stem = cfg.pop("profile")
     n = x_host.size
     dev = torch.device("cuda:0")
     x = torch.from_numpy(x_host.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -77,29 +126,40 @@ def main():
     y = torch.empty(n, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+    # one step = rate control, encode and decode; the encode is issued as an asynchronous hq_rate
+    # followed by hq_encode at the operating point it chose (exactly the kernels of one hq_encode
+    # with rate control), so that events can bracket the encode kernel alone
+    def rate():
+        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
+
+    def encode():
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
+
+    def decode():
         hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
 
     for _ in range(args.warmup):
-        step()
+        rate(); encode(); decode()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+        rate()
         ev[i][1].record(stream)
-        hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
+        encode()
         ev[i][2].record(stream)
+        decode()
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
-    dec_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
-    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]))
+    rate_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    enc_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    dec_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
+    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]))
     st = hq.hq_status(ws)
     st2 = hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
@@ -111,14 +171,16 @@ def main():
     # algorithmic bytes: encode reads the input and writes the stream; decode reads the stream and
     # writes bf16 values
     alg_step = 2 * (input_bytes + total_bytes)
-    # dominant kernel: the decoder (check + decode launches, timed together by the events)
+    # dominant kernel: encode_kernel (timed alone) or decode_kernel (timed with its 1-lane header
+    # check launch, which makes the decode figure slightly conservative)
     dec_alg = total_bytes + input_bytes
     enc_alg = input_bytes + total_bytes
     if dec_ms >= enc_ms:
         dom, dom_ms, dom_bytes = "decode_kernel", dec_ms, dec_alg
     else:
-        dom, dom_ms, dom_bytes = "rate_kernel x2 + encode_kernel", enc_ms, enc_alg
+        dom, dom_ms, dom_bytes = "encode_kernel", enc_ms, enc_alg
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = profiled_traffic(profile_stem, dom)
 
     result = {
         "metric": METRIC,
@@ -139,9 +201,12 @@ def main():
                    "step": float(np.array([hdr["step_bits"]], dtype=np.uint32).view(np.float32)[0]),
                    "rice_k": hdr["k"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                      "alg_bytes_per_launch": dom_bytes, "launch_ms": round(dom_ms, 5)},
-        "extra": {"encode_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5),
+        "extra": {"rate_control_ms": round(rate_ms, 5), "encode_ms": round(enc_ms, 5),
+                  "decode_ms": round(dec_ms, 5),
+                  "encode_kernel_gbs": round(enc_alg / (enc_ms * 1e-3) / 1e9, 1),
+                  "decode_kernel_gbs": round(dec_alg / (dec_ms * 1e-3) / 1e9, 1),
                   "step_alg_bytes": alg_step,
                   "step_hbm_gbs": round(alg_step / (step_ms * 1e-3) / 1e9, 1),
                   "step_hbm_frac": round(alg_step / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -73,7 +73,9 @@ typedef struct {
   float target_bps;    /* payload bits per value (coset + Rice bits / n); used when step == 0       */
   uint64_t seed;       /* Philox key of the sign diagonal D and of the dither                        */
   uint32_t dither;     /* 0 = off, 1 = subtractive dither (component 4)                              */
-  float step;          /* 0 = choose by rate control; > 0 = fixed lattice step (KV append, tests)    */
+  float step;          /* 0 = choose by rate control; > 0 = fixed lattice step (KV append, tests);
+                          -1 (hq_encode only) = the step and k that the preceding hq_rate on the
+                          same workspace and stream left there                                     */
   int32_t rice_k;      /* -1 = automatic; 0..15 = fixed Rice parameter                              */
 } hq_params;
 
@@ -104,7 +106,10 @@ int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t 
 
 /* Rate control alone (component 3's rate targeting): chooses the lattice step and Rice parameter
  * for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles meets
- * params->target_bps.  Blocking.  info->payload_bps is the sample estimate. */
+ * params->target_bps.  With info != NULL the call blocks and fills info (payload_bps is the target);
+ * with info == NULL it only enqueues work, and a following hq_encode with params->step == -1 on the
+ * same workspace and stream encodes at the chosen point (the pair then does exactly what one
+ * hq_encode with rate control does). */
 int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, hq_info *info,
             void *workspace, size_t workspace_bytes, hq_stream_t stream);
 
@@ -112,8 +117,9 @@ int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, h
  * With out_bytes != NULL the call blocks, stores the stream size in *out_bytes (also when the
  * result is HQ_ERR_CAPACITY: the size needed) and fills *info (may be NULL).  With out_bytes == NULL
  * the call only enqueues work on `stream`; the size is in the stream header (total_bytes) and
- * device-side errors are returned later by hq_status(workspace).  Rate control runs unless
- * params->step > 0. */
+ * device-side errors are returned later by hq_status(workspace).  Rate control runs when
+ * params->step == 0; step > 0 fixes the step; step == -1 takes the point a preceding asynchronous
+ * hq_rate left in the workspace. */
 int hq_encode(const void *x, int32_t dtype, uint64_t n, const hq_params *params, void *out,
               uint64_t out_capacity, uint64_t *out_bytes, hq_info *info, void *workspace,
               size_t workspace_bytes, hq_stream_t stream);

@@ -196,16 +196,20 @@ def hq_decode(stream_bytes, n: int, out_dtype=None, out=None, ws=None, stream=No
     return out
 
 
-def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None):
+def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None,
+            blocking=True):
+    """Rate control alone.  blocking=False only enqueues it; a following hq_encode(..., step=-1,
+    ws=<same workspace>) then encodes at the chosen operating point."""
     assert x.is_cuda and x.is_contiguous()
     n = x.numel()
     p = make_params(lattice, target_bps, seed, dither, step, rice_k)
     if ws is None:
         ws = workspace(n, x.device)
     info = HqInfo()
-    _check(lib().hq_rate(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p), ctypes.byref(info),
-                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_handle(stream)), "hq_rate")
-    return info.as_dict()
+    _check(lib().hq_rate(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
+                         ctypes.byref(info) if blocking else None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                         _stream_handle(stream)), "hq_rate")
+    return info.as_dict() if blocking else None
 
 
 def hq_codes(x, step: float, lattice="e8", seed=0, dither=False, ws=None, stream=None):

@@ -18,6 +18,9 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # workgroup reductions through LDS atomics at a uniform address become DPP reductions instead
+    # of a per-lane read-back loop
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",
     "-Wall",
 ]
 

@@ -41,6 +41,7 @@ int check_params(const hq_params* p, uint64_t n) {
   if (n > (1ull << 35)) return HQ_ERR_INVALID_ARG;  // the encoder's look-back packs 28-bit padding sums
   if (p->dither > 1) return HQ_ERR_INVALID_ARG;
   if (p->rice_k < -1 || p->rice_k > 15) return HQ_ERR_INVALID_ARG;
+  if (p->step == -1.0f) return HQ_OK;  // operating point left in the workspace by hq_rate
   if (!(p->step >= 0.0f)) return HQ_ERR_INVALID_ARG;  // also rejects NaN
   if (p->step > 0.0f) {
     const uint32_t b = f32_bits(p->step);
@@ -61,7 +62,7 @@ int status_from_flags(uint32_t f) {
   return HQ_OK;
 }
 
-size_t workspace_bytes_for(uint64_t n) { return kWsHeader + align256h(8ull * (chunks_of(n) + 1)); }
+size_t workspace_bytes_for(uint64_t n) { return kWsHeader + kWsPartials + align256h(8ull * (chunks_of(n) + 1)); }
 
 EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, void* out, uint64_t cap,
                      void* ws, hq_stream_t s) {
@@ -76,7 +77,7 @@ EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, v
   a.seed = p->seed;
   a.target = p->target_bps;
   a.rice_k = p->rice_k;
-  a.fixed_step_bits = p->step > 0.0f ? f32_bits(p->step) : 0u;
+  a.fixed_step_bits = p->step > 0.0f ? f32_bits(p->step) : 0u;  // 0 also for step == -1
   a.out = static_cast<uint8_t*>(out);
   a.cap = cap;
   a.ws = static_cast<Workspace*>(ws);
@@ -188,9 +189,11 @@ int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, h
   if (rc) return rc;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < workspace_bytes_for(n) || (n && !x)) return HQ_ERR_INVALID_ARG;
+  if (params->step == -1.0f) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
   rc = run_rate_control(a);
   if (rc) return rc;
+  if (!info) return HQ_OK;  // asynchronous: the operating point stays in the workspace
   Workspace h;
   if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
       hipStreamSynchronize(a.stream) != hipSuccess)
@@ -215,8 +218,10 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
   if (!workspace || workspace_bytes < workspace_bytes_for(n) || (n && !x) || !out) return HQ_ERR_INVALID_ARG;
   if (((uintptr_t)out & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, out, out_capacity, workspace, stream);
-  rc = run_rate_control(a);
-  if (rc) return rc;
+  if (params->step != -1.0f) {
+    rc = run_rate_control(a);
+    if (rc) return rc;
+  }
   if (launch_encode(a) != hipSuccess) return HQ_ERR_HIP;
   if (!out_bytes) return HQ_OK;
   Results r;

@@ -67,17 +67,35 @@ __device__ __forceinline__ void fwht_lane(float a[8]) {
   }
 }
 
-__device__ __forceinline__ void fwht_cross(float a[8], int lane16) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const bool high = (lane16 & m) != 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __shfl_xor(a[i], m, 64);
-      a[i] = high ? (p - a[i]) : (a[i] + p);
-    }
-  }
+// Partner value for the cross-lane stages: ds_swizzle in bit-mask mode (and 0x1F, xor m) inside
+// 32 lanes.  It runs in the LDS pipe, so a stage costs one VALU operation per value (the fused
+// multiply-add below).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
 }
+
+// The four cross-lane stages.  Each lane computes own + s * partner with s = +1 on the low lane
+// and -1 on the high lane, as one fused multiply-add: the product by +-1 is exact, so the result
+// is the sum or difference rounded once, exactly as the plain butterfly.  The high lane then holds
+// the negated value; after the four stages lane l holds sigma(l) * y with
+// sigma(l) = (-1)^popcount(l & 15) (lane_sign_bit), which callers fold into the quantiser's
+// multiplier (encode) or into the sign diagonal (decode).
+template <int M>
+__device__ __forceinline__ void fwht_stage(float a[8], int lane16) {
+  const float sgn = (lane16 & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(lane_xor<M>(a[i]), sgn, a[i]);
+}
+
+__device__ __forceinline__ void fwht_cross(float a[8], int lane16) {
+  fwht_stage<1>(a, lane16);
+  fwht_stage<2>(a, lane16);
+  fwht_stage<4>(a, lane16);
+  fwht_stage<8>(a, lane16);
+}
+
+__device__ __forceinline__ uint32_t lane_sign_bit(int lane16) { return (uint32_t)__popc(lane16 & 15) & 1u; }
 
 // Sum of squares of the tile as a balanced pairwise tree in index order: squares, pairs inside
 // the lane, then lane xor 1, 2, 4, 8 (each add is commutative, so both lanes get equal sums).
@@ -86,8 +104,10 @@ __device__ __forceinline__ float tile_sumsq(const float a[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = a[i] * a[i];
   float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) t = t + __shfl_xor(t, m, 64);
+  t = t + lane_xor<1>(t);
+  t = t + lane_xor<2>(t);
+  t = t + lane_xor<4>(t);
+  t = t + lane_xor<8>(t);
   return t;
 }
 
@@ -99,10 +119,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Tile scale s = bfloat16 nearest to sqrt(S / 128), ties to even, decided exactly: start from the
-// rounded square root, then compare S against 128 m^2 for the two neighbouring rounding midpoints
-// m (9 significant bits, so m^2 and 128 m^2 are exact in binary32).  S is brought into
-// [2^-60, 2^60] by an exact power-of-two factor first so that no square under- or overflows.
+// Tile scale s = bfloat16 nearest to sqrt(S / 128), ties to even, decided exactly.  A hardware
+// square root r (within one binary32 ulp) gives the candidate c = bf16(r); the true result can only
+// be c's neighbour on r's side of c, across the rounding midpoint m between them, and that midpoint
+// has 9 significant bits, so S against 128 m^2 is an exact binary32 comparison.  S is first brought
+// into [2^-60, 2^60] by an exact power-of-two factor so that no square under- or overflows.
 __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
   if (!(S > 0.0f)) return 0u;
   float Ss = S;
@@ -114,22 +135,20 @@ __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
     Ss = S * 0x1p-100f;
     adj = -50;
   }
-  const float r = __fsqrt_rn(Ss * 0.0078125f);
+  const float r = __builtin_amdgcn_sqrtf(Ss * 0.0078125f);
   uint32_t c = f32_to_bf16_rne(r);
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const float cv = bf16_bits_to_f32(c);
-    const float mhi = (cv + bf16_bits_to_f32(c + 1u)) * 0.5f;
-    const float mlo = (cv + bf16_bits_to_f32(c - 1u)) * 0.5f;
-    const float thi = 128.0f * (mhi * mhi);
-    const float tlo = 128.0f * (mlo * mlo);
-    if (Ss > thi || (Ss == thi && (c & 1u)))
-      c += 1u;
-    else if (Ss < tlo || (Ss == tlo && (c & 1u)))
-      c -= 1u;
-  }
+  const float cv = bf16_bits_to_f32(c);
+  const bool up = r >= cv;
+  const uint32_t nb = up ? c + 1u : c - 1u;
+  const float m = (cv + bf16_bits_to_f32(nb)) * 0.5f;
+  const float tm = 128.0f * (m * m);
+  const bool cross = up ? (Ss > tm) : (Ss < tm);
+  if (cross || (Ss == tm && (c & 1u))) c = nb;
   return (uint32_t)((int32_t)c - adj * 128);
 }
+
+__device__ __forceinline__ uint32_t zigzag(int32_t a) { return ((uint32_t)a << 1) ^ (uint32_t)(a >> 31); }
+__device__ __forceinline__ int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u); }
 
 // ---------------------------------------------------------------------------------------------
 // Nearest lattice points (Conway-Sloane rules).  Ties: rint is round-half-even; the coordinate
@@ -210,6 +229,56 @@ __device__ __forceinline__ void e8_nearest(const float* v, int32_t* z) {
   }
 }
 
+// E8 nearest point and bit-stripping in one pass, producing the symbols and the coset bit
+// directly (same rule and ties as e8_nearest followed by strip_octet).  With r = rint v, e = v - r,
+// sigma_i = [e_i < 0]: the stripped coordinates are u = r for the D8 candidate and u = r - sigma for
+// the D8 + 1/2 candidate; the parity fix moves the first coordinate whose |e| equals the maximum
+// (D8) or the minimum (D8 + 1/2) of |e| by +1 or -1 (toward v in the lattice-point coordinates).
+__device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32_t* coset) {
+  float e[8];
+  int32_t r[8];
+  uint32_t xr = 0, xe = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ri = rintf(v[i]);
+    e[i] = v[i] - ri;
+    r[i] = (int32_t)ri;
+    xr ^= (uint32_t)r[i];
+    xe ^= __float_as_uint(e[i]);
+  }
+  const uint32_t pa = xr & 1u, pb = pa ^ (xe >> 31);
+  const float amax = fmaxf(fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))),
+                           fmaxf(fmaxf(fabsf(e[4]), fabsf(e[5])), fmaxf(fabsf(e[6]), fabsf(e[7]))));
+  const float amin = fminf(fminf(fminf(fabsf(e[0]), fabsf(e[1])), fminf(fabsf(e[2]), fabsf(e[3]))),
+                           fminf(fminf(fabsf(e[4]), fabsf(e[5])), fminf(fabsf(e[6]), fabsf(e[7]))));
+  const float d = ((fabsf(e[0]) + fabsf(e[1])) + (fabsf(e[2]) + fabsf(e[3]))) +
+                  ((fabsf(e[4]) + fabsf(e[5])) + (fabsf(e[6]) + fabsf(e[7])));
+  const float lhs = pa ? d + (1.0f - 2.0f * amax) : d;
+  const float rhs = pb ? 2.0f + 2.0f * amin : 2.0f;
+  const bool keep_a = lhs <= rhs;
+  const float t = keep_a ? amax : amin;
+  bool found = keep_a ? (pa == 0u) : (pb == 0u);  // no fix needed: nothing to find
+  const uint32_t bsub = keep_a ? 0u : 1u;
+  int32_t u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sg = __float_as_uint(e[i]) >> 31;
+    const int32_t base = r[i] - (int32_t)(sg & bsub);
+    const bool hit = !found && (fabsf(e[i]) == t);
+    found = found || hit;
+    const int32_t delta = ((uint32_t)keep_a ^ sg) ? 1 : -1;
+    u[i] = hit ? base + delta : base;
+  }
+  int32_t par = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    sym[i] = zigzag(u[i]);
+    par += u[i];
+  }
+  sym[7] = zigzag((u[7] - (par & 1)) >> 1);
+  *coset = bsub;
+}
+
 template <int LAT>
 __device__ __forceinline__ void nearest_octet(const float* v, int32_t* code) {
   if (LAT == kLatE8) {
@@ -250,8 +319,6 @@ __device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, f
 
 // ---------------------------------------------------------------------------------------------
 // Bit-stripping and zigzag (see the format description in hq.h).
-__device__ __forceinline__ uint32_t zigzag(int32_t a) { return ((uint32_t)a << 1) ^ (uint32_t)(a >> 31); }
-__device__ __forceinline__ int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u); }
 
 template <int LAT>
 __device__ __forceinline__ bool slot_halved(int s) {
@@ -332,6 +399,35 @@ __device__ __forceinline__ void unstrip_octet(const uint32_t* sym, uint32_t cose
 }
 
 // ---------------------------------------------------------------------------------------------
+// Loads of one lane's 8 values of tile t with the sign diagonal applied (DT 0: fp32, 1: bf16 bits).
+// smask[i] is 0x80000000 where D = -1: the sign flip is an xor (fp32) or an add into bit 31 of the
+// widened bf16 value, both exact.
+template <int DT>
+__device__ __forceinline__ void load_octet_signed(const void* x, uint64_t t, int o, const uint32_t* smask, float* v) {
+  if (DT == 1) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * o);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float((ws[i] << 16) + smask[2 * i]);
+      v[2 * i + 1] = __uint_as_float((ws[i] & 0xFFFF0000u) ^ smask[2 * i + 1]);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * o);
+    const float4 a = p[0], b = p[1];
+    const float vv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(vv[i]) ^ smask[i]);
+  }
+}
+
+// Broadcast inside the 16-lane group of a tile: every lane receives the value of lane `src` (0..15)
+// of its own group (ds_swizzle bit-mask mode: keep lane bit 4, set bits 0-3 to src).
+template <int SRC>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x10 | (SRC << 5));
+}
+
 // Loads of one lane's 8 values of tile t (DT 0: fp32, 1: bf16 bits).
 template <int DT>
 __device__ __forceinline__ void load_octet(const void* x, uint64_t t, int o, float* v) {

@@ -19,13 +19,12 @@ constexpr int kRcKwin = 4;
 // chunk, plus one) follow it.  Every field is (re)initialised by the first kernel of a call.
 struct alignas(256) Workspace {
   uint32_t pad_ticket;
-  uint32_t rc_ticket;    // last-workgroup detection of a rate pass
+  uint32_t pad_ticket2;
   uint32_t status;       // error flags (kErr*)
   uint32_t step_bits;    // operating point chosen so far (binary32 bits of the step)
   int32_t rice_k;
   uint32_t pad0;
   int64_t rc_centre;     // centre of the next rate pass (step bits)
-  uint64_t rc_sumq[kRcCand][kRcKwin];  // sum of (symbol >> width) per candidate and Rice k
   // encoder results, written by the chunk that finishes the look-back chain
   uint64_t res_total_bytes;
   uint64_t res_payload_bits;
@@ -50,9 +49,16 @@ struct alignas(256) Workspace {
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
+// Per-workgroup partial sums of a rate pass (one slot of kRcCand * kRcKwin counters per workgroup
+// of 16 sample tiles), then the encoder's look-back flags.
+constexpr size_t kRcSlots = kRcSampleTiles / 16;
+constexpr size_t kWsPartials = kRcSlots * kRcCand * kRcKwin * sizeof(uint32_t);
 
+inline uint32_t* rc_partials(void* ws) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + kWsHeader);
+}
 inline uint64_t* lookback_flags(void* ws) {
-  return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader);
+  return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader + kWsPartials);
 }
 
 struct EncodeArgs {

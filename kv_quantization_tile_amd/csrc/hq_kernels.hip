@@ -43,6 +43,40 @@ __device__ __forceinline__ uint32_t lds_get_bits(const uint32_t* s, uint32_t pos
   return (uint32_t)(v >> sh) & low_mask(nbits);
 }
 
+// Remainder field of one octet packed in registers: slot s at its offset, least significant bit
+// first, for fields of at most 64 bits (Rice k <= 8).  k is the same in every lane, so the
+// branches below are uniform.
+template <int LAT>
+__device__ __forceinline__ void pack_octet_remainders(const uint32_t* sym, int k, uint32_t* lo, uint32_t* hi) {
+  uint32_t l = 0, h = 0;
+  int off = 0;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) {
+    const int w = slot_width<LAT>(sl, k);
+    const uint32_t v = sym[sl] & low_mask(w);
+    if (off < 32) {
+      l |= v << off;
+      if (off + w > 32) h |= v >> (32 - off);
+    } else {
+      h |= v << (off - 32);
+    }
+    off += w;
+  }
+  *lo = l;
+  *hi = h;
+}
+
+// OR a field of at most 64 bits (lo, hi) into an LDS bit array at bit position pos.
+__device__ __forceinline__ void lds_put_field64(uint32_t* s, uint32_t pos, uint32_t lo, uint32_t hi) {
+  const uint32_t word = pos >> 5, sh = pos & 31u;
+  const uint32_t w0 = lo << sh;
+  const uint32_t w1 = sh ? ((lo >> (32u - sh)) | (hi << sh)) : hi;
+  const uint32_t w2 = sh ? (hi >> (32u - sh)) : 0u;
+  atomicOr(&s[word], w0);
+  atomicOr(&s[word + 1], w1);
+  if (w2) atomicOr(&s[word + 2], w2);
+}
+
 // Sample tile of stratum i (jittered stratified sampling, see rate control below).
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x = x * 0x9E3779B1u + 0x7F4A7C15u;
@@ -96,10 +130,12 @@ __device__ __forceinline__ uint32_t transform_octet(const void* x, uint64_t t, b
 }
 
 // v = y * m (+ U); m = 1 / (s * step) rounded once each (0 when s = 0); nearest lattice point.
+// y holds sigma(lane) times the transformed values (see fwht_cross); the sign is folded into m.
 template <int LAT, bool DITHER>
 __device__ __forceinline__ void quantize_octet(const float* y, float s, float step, const float* u,
-                                               int32_t* code) {
-  const float m = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
+                                               int32_t* code, uint32_t lane_neg) {
+  const float m0 = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
+  const float m = lane_neg ? -m0 : m0;
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -109,12 +145,38 @@ __device__ __forceinline__ void quantize_octet(const float* y, float s, float st
   nearest_octet<LAT>(v, code);
 }
 
+// Symbols of one octet at multiplier m (the lane's sign already folded into m): v = y * m (+ U),
+// nearest lattice point, bit-stripping.
+template <int LAT, bool DITHER>
+__device__ __forceinline__ void octet_symbols(const float* y, float m, const float* u, uint32_t* sym,
+                                              uint32_t* coset) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = y[i] * m;
+    if (DITHER) v[i] = v[i] + u[i];
+  }
+  if (LAT == kLatE8) {
+    e8_symbols(v, sym, coset);
+  } else {
+    int32_t code[8];
+    nearest_octet<LAT>(v, code);
+    strip_octet<LAT>(code, sym, coset);
+  }
+}
+
+// Per-tile multiplier m = 1 / (s * step) (0 when s = 0), with the lane's sign folded in.
+__device__ __forceinline__ float tile_multiplier(uint32_t sb, float step, uint32_t lane_neg) {
+  const float s = bf16_bits_to_f32(sb);
+  const float m0 = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
+  return lane_neg ? -m0 : m0;
+}
+
 // ---------------------------------------------------------------------------------------------
 __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int64_t centre,
                             uint32_t step_bits, int32_t k) {
   const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid == 0) {
-    ws->rc_ticket = 0;
     ws->status = 0;
     ws->step_bits = step_bits;
     ws->rice_k = k;
@@ -126,7 +188,6 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int
     ws->res_step_bits = step_bits;
     ws->res_k = k;
   }
-  if (gid < (uint64_t)(kRcCand * kRcKwin)) (&ws->rc_sumq[0][0])[gid] = 0;
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
 }
 
@@ -143,34 +204,33 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int
 //    pair, rounds, clamps, and stores the answer as the next centre together with the k of the
 //    candidate nearest to it.  Pass A (h = 21) starts at 2.05 - target octaves; pass B (h = 17)
 //    refines.  With a fixed step and automatic k one pass with the single candidate picks k.
+// Bits of candidate j over the Rice window (lane j of the solving wavefront computes its own).
 template <int LAT>
-__device__ void rate_solve(Workspace* ws, const uint64_t* sumq, int nc, int half_log2, int fixed_k, float target,
-                           uint32_t N) {
-  const int64_t centre = ws->rc_centre;
-  int64_t b[kRcCand];
-  double R[kRcCand];
-  int kc[kRcCand];
-  const double Nd = (double)N;
-  for (int j = 0; j < nc; ++j) {
-    b[j] = nc == 1 ? centre
-                   : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
-                               kStepBitsMax);
-    const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b[j]);
-    int best = 0;
-    double rb = 0.0;
-    for (int w = 0; w < kRcKwin; ++w) {
-      const int k = fixed_k >= 0 ? fixed_k : kb + w;
-      const uint64_t sq = sumq[j * kRcKwin + w];
-      const double per_tile = (double)(tile_fixed_bits<LAT>(k) - 16u) + 128.0;
-      const double bits = per_tile * Nd + (double)sq;
-      if (w == 0 || bits < rb) {
-        rb = bits;
-        best = w;
-      }
+__device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t centre, int j, int nc, int half_log2,
+                                               int fixed_k, uint32_t N, int64_t* b_out, double* R_out, int* k_out) {
+  const int64_t b = nc == 1 ? centre
+                            : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
+                                        kStepBitsMax);
+  const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
+  int best = 0;
+  double rb = 0.0;
+  for (int w = 0; w < kRcKwin; ++w) {
+    const int k = fixed_k >= 0 ? fixed_k : kb + w;
+    const double per_tile = (double)(tile_fixed_bits<LAT>(k) - 16u) + 128.0;
+    const double bits = per_tile * (double)N + (double)sumq[j * kRcKwin + w];
+    if (w == 0 || bits < rb) {
+      rb = bits;
+      best = w;
     }
-    R[j] = rb;
-    kc[j] = fixed_k >= 0 ? fixed_k : kb + best;
   }
+  *b_out = b;
+  *R_out = rb;
+  *k_out = fixed_k >= 0 ? fixed_k : kb + best;
+}
+
+// Bracket, interpolate and store the answer (one lane; b, R, kc per candidate).
+__device__ void rate_solve(Workspace* ws, const int64_t* b, const double* R, const int* kc, int nc, float target,
+                           uint32_t N) {
   const double Tb = (double)target * (double)((uint64_t)N * kTile);
   const double nominal = (double)((uint64_t)N * kTile) / 8388608.0;
   double xv;
@@ -213,16 +273,13 @@ __device__ void rate_solve(Workspace* ws, const uint64_t* sumq, int nc, int half
   ws->rc_centre = xb;
   ws->step_bits = (uint32_t)xb;
   ws->rice_k = kc[best];
-  ws->rc_ticket = 0;
 }
 
 template <int LAT, bool DITHER, int DT>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
-                                                      Workspace* ws, uint64_t seed, int nc, int half_log2,
-                                                      int fixed_k, float target) {
-  __shared__ uint32_t s_red[4][kRcCand * kRcKwin];
-  __shared__ uint64_t s_sumq[kRcCand * kRcKwin];
-  __shared__ uint32_t s_last;
+                                                      Workspace* ws, uint32_t* partials, uint64_t seed, int nc,
+                                                      int half_log2, int fixed_k, float target) {
+  __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
   const uint64_t i = (uint64_t)blockIdx.x * 16 + wave * 4 + tw;
   const bool valid = i < N;
@@ -232,10 +289,21 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   bool finite;
   const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
   if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
-  const float s = bf16_bits_to_f32(sb);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   const int64_t centre = ws->rc_centre;
+  // lane o computes the multiplier of candidate o mod 8; the group shares them by broadcast
+  const int jm = nc == 1 ? 0 : (o & 7);
+  const int64_t bm = nc == 1 ? centre
+                             : clamp_i64(centre + (int64_t)(2 * jm - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
+                                         kStepBitsMax);
+  const uint32_t m_mine = __float_as_uint(tile_multiplier(sb, __uint_as_float((uint32_t)bm), 0u));
+  const bool lane_neg = lane_sign_bit(o) != 0u;
+  float mj[kRcCand];
+  mj[0] = __uint_as_float(group_bcast<0>(m_mine)); mj[1] = __uint_as_float(group_bcast<1>(m_mine));
+  mj[2] = __uint_as_float(group_bcast<2>(m_mine)); mj[3] = __uint_as_float(group_bcast<3>(m_mine));
+  mj[4] = __uint_as_float(group_bcast<4>(m_mine)); mj[5] = __uint_as_float(group_bcast<5>(m_mine));
+  mj[6] = __uint_as_float(group_bcast<6>(m_mine)); mj[7] = __uint_as_float(group_bcast<7>(m_mine));
   uint32_t acc[kRcCand][kRcKwin];
 #pragma unroll
   for (int j = 0; j < kRcCand; ++j)
@@ -247,10 +315,9 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
       const int64_t b = nc == 1 ? centre
                                 : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2),
                                             kStepBitsMin, kStepBitsMax);
-      int32_t code[8];
-      quantize_octet<LAT, DITHER>(y, s, __uint_as_float((uint32_t)b), u, code);
+      const float m = lane_neg ? -mj[j] : mj[j];
       uint32_t sym[8], cos;
-      strip_octet<LAT>(code, sym, &cos);
+      octet_symbols<LAT, DITHER>(y, m, u, sym, &cos);
       const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
 #pragma unroll
       for (int w = 0; w < kRcKwin; ++w) {
@@ -262,35 +329,64 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
       }
     }
   }
-  // workgroup reduction, then one 64-bit atomic per counter
+  // workgroup reduction through LDS atomics (no dependent shuffle chains)
+  if (tid < kRcCand * kRcKwin) s_red[0][tid] = 0u;
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kRcCand; ++j)
 #pragma unroll
-    for (int w = 0; w < kRcKwin; ++w) {
-      uint32_t v = acc[j][w];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-      if (lane == 0) s_red[wave][j * kRcKwin + w] = v;
-    }
+    for (int w = 0; w < kRcKwin; ++w)
+      if (j < nc && acc[j][w]) atomicAdd(&s_red[0][j * kRcKwin + w], acc[j][w]);
   __syncthreads();
-  if (tid < kRcCand * kRcKwin) {
-    const uint64_t tot = (uint64_t)s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
-    if (tot) atomicAdd((unsigned long long*)&(&ws->rc_sumq[0][0])[tid], (unsigned long long)tot);
+  // this workgroup's partial sums go to its own slot; rate_solve_kernel, the next launch on the
+  // stream, adds them up (the kernel boundary orders the stores before its loads)
+  constexpr int kC = kRcCand * kRcKwin;
+  if (tid < kC) partials[(uint64_t)blockIdx.x * kC + tid] = s_red[0][tid];
+}
+
+// One workgroup: sum the partial counters of the rate pass over its nslots workgroups, then solve.
+template <int LAT>
+__global__ __launch_bounds__(kBlock) void rate_solve_kernel(Workspace* ws, const uint32_t* __restrict__ partials,
+                                                            uint32_t nslots, int nc, int half_log2, int fixed_k,
+                                                            float target, uint32_t N) {
+  constexpr int kC = kRcCand * kRcKwin;  // 32 counters = 8 uint4 per slot
+  __shared__ uint64_t s_acc[kBlock / 8][kC];
+  __shared__ uint64_t s_sumq[kC];
+  __shared__ int64_t s_b[kRcCand];
+  __shared__ double s_R[kRcCand];
+  __shared__ int s_k[kRcCand];
+  const int tid = threadIdx.x;
+  // lane t reads quad t mod 8 (counters 4 (t mod 8) .. +3) of slots t/8, t/8 + 32, ...
+  const int quad = tid & 7;
+  uint64_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  const uint4* p4 = reinterpret_cast<const uint4*>(partials);
+  for (uint32_t slot = tid >> 3; slot < nslots; slot += kBlock / 8) {
+    const uint4 v = p4[(uint64_t)slot * (kC / 4) + quad];
+    a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
   }
-  __threadfence();
+  s_acc[tid >> 3][4 * quad + 0] = a0;
+  s_acc[tid >> 3][4 * quad + 1] = a1;
+  s_acc[tid >> 3][4 * quad + 2] = a2;
+  s_acc[tid >> 3][4 * quad + 3] = a3;
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&ws->rc_ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
-  __syncthreads();
-  if (s_last) {  // last workgroup: gather the counters (and clear them for the next pass), solve
-    __threadfence();
-    uint64_t* cnt = &ws->rc_sumq[0][0];
-    if (tid < kRcCand * kRcKwin) {
-      s_sumq[tid] = __hip_atomic_load(&cnt[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&cnt[tid], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (tid == 0) rate_solve<LAT>(ws, s_sumq, nc, half_log2, fixed_k, target, N);
+  if (tid < kC) {
+    uint64_t t = 0;
+    for (int r = 0; r < kBlock / 8; ++r) t += s_acc[r][tid];
+    s_sumq[tid] = t;
   }
+  __syncthreads();
+  const int64_t centre = ws->rc_centre;
+  if (tid < nc) {
+    int64_t b;
+    double R;
+    int k;
+    rate_candidate<LAT>(s_sumq, centre, tid, nc, half_log2, fixed_k, N, &b, &R, &k);
+    s_b[tid] = b;
+    s_R[tid] = R;
+    s_k[tid] = k;
+  }
+  __syncthreads();
+  if (tid == 0) rate_solve(ws, s_b, s_R, s_k, nc, target, N);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -437,6 +533,49 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   }
 
   const uint32_t sgn = octet_sign_bits(P.seed, o);
+  uint32_t smask[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
+  const uint32_t lane_neg = lane_sign_bit(o);
+
+  // phase 1: every round's transform and tile energy
+  float y[4][8];
+  float S[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t t = (uint64_t)c * kChunkTiles + 16u * r + 4u * wave + tw;
+    if (t < P.T) {
+      load_octet_signed<DT>(P.x, t, o, smask, y[r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
+    }
+    fwht_lane(y[r]);
+    fwht_cross(y[r], o);
+    S[r] = tile_sumsq(y[r]);
+  }
+  // one scale and one division per lane (round o mod 4), broadcast inside the tile's lane group
+  uint32_t sb_mine;
+  float m_mine;
+  {
+    const int rr = o & 3;
+    const float Sr = rr == 0 ? S[0] : rr == 1 ? S[1] : rr == 2 ? S[2] : S[3];
+    const bool fin = isfinite(Sr);
+    const uint64_t t = (uint64_t)c * kChunkTiles + 16u * rr + 4u * wave + tw;
+    if (!fin && t < P.T && o < 4) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+    sb_mine = tile_scale_bits(fin ? Sr : 0.0f);
+    m_mine = tile_multiplier(sb_mine, step, 0u);
+  }
+  uint32_t sbr[4];
+  float mr[4];
+  sbr[0] = group_bcast<0>(sb_mine); sbr[1] = group_bcast<1>(sb_mine);
+  sbr[2] = group_bcast<2>(sb_mine); sbr[3] = group_bcast<3>(sb_mine);
+  mr[0] = __uint_as_float(group_bcast<0>(__float_as_uint(m_mine)));
+  mr[1] = __uint_as_float(group_bcast<1>(__float_as_uint(m_mine)));
+  mr[2] = __uint_as_float(group_bcast<2>(__float_as_uint(m_mine)));
+  mr[3] = __uint_as_float(group_bcast<3>(__float_as_uint(m_mine)));
+
+  // phase 2: quantise, strip, pack the fixed record, Rice lengths
   uint32_t sym[4][8];
   uint32_t L[4];
 #pragma unroll
@@ -444,32 +583,37 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const uint32_t tc = 16u * r + 4u * wave + tw;
     const uint64_t t = (uint64_t)c * kChunkTiles + tc;
     const bool valid = t < P.T;
-    float y[8];
-    bool finite;
-    const uint32_t sb = transform_octet<DT>(P.x, t, valid, o, sgn, y, &finite);
-    if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+    if (!isfinite(S[r])) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
+    }
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (DITHER) dither_octet<LAT>(P.seed, t, o, u);
-    int32_t code[8];
-    quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), step, u, code);
     uint32_t cos;
-    strip_octet<LAT>(code, sym[r], &cos);
+    octet_symbols<LAT, DITHER>(y[r], lane_neg ? -mr[r] : mr[r], u, sym[r], &cos);
     const uint64_t bal = __ballot(valid && cos != 0u);
     uint32_t len = 8;
     if (valid) {
       const uint32_t rec = tc * F;
       if (o == 0) {
-        lds_put_bits(s_fixed, rec, sb, 16);
+        lds_put_bits(s_fixed, rec, sbr[r], 16);
         if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (16 * tw)) & 0xFFFFu, 16);
       }
       uint32_t pos = rec + hdr + (uint32_t)o * RW;
+      if (k <= 8) {
+        uint32_t lo, hi;
+        pack_octet_remainders<LAT>(sym[r], k, &lo, &hi);
+        lds_put_field64(s_fixed, pos, lo, hi);
+      } else {
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int w = slot_width<LAT>(sl, k);
-        lds_put_bits(s_fixed, pos, sym[r][sl] & low_mask(w), w);
-        pos += w;
-        len += sym[r][sl] >> w;
+        for (int sl = 0; sl < 8; ++sl) {
+          const int w = slot_width<LAT>(sl, k);
+          lds_put_bits(s_fixed, pos, sym[r][sl] & low_mask(w), w);
+          pos += w;
+        }
       }
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) len += sym[r][sl] >> slot_width<LAT>(sl, k);
     }
     L[r] = valid ? len : 0u;
   }
@@ -521,16 +665,29 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
       __syncthreads();
     }
+    if (B <= kUnaryWinBits) {  // the common case: the whole segment fits one window
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (L[r] == 0) continue;
-      uint32_t p = off[r];
+      for (int r = 0; r < 4; ++r) {
+        uint32_t p = off[r];
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        p += sym[r][sl] >> slot_width<LAT>(sl, k);
-        const uint32_t rel = p - wb;
-        if (p >= wb && rel < kUnaryWinBits) atomicOr(&s_unary[rel >> 5], 1u << (rel & 31u));
-        p += 1;
+        for (int sl = 0; sl < 8; ++sl) {
+          p += sym[r][sl] >> slot_width<LAT>(sl, k);
+          if (L[r]) atomicOr(&s_unary[p >> 5], 1u << (p & 31u));
+          p += 1;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (L[r] == 0) continue;
+        uint32_t p = off[r];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          p += sym[r][sl] >> slot_width<LAT>(sl, k);
+          const uint32_t rel = p - wb;
+          if (p >= wb && rel < kUnaryWinBits) atomicOr(&s_unary[rel >> 5], 1u << (rel & 31u));
+          p += 1;
+        }
       }
     }
     __syncthreads();
@@ -579,7 +736,7 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   int32_t code[8];
-  quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), __uint_as_float(step_bits), u, code);
+  quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), __uint_as_float(step_bits), u, code, lane_sign_bit(o));
   if (valid) {
     int4* dst = reinterpret_cast<int4*>(codes + t * kTile + 8 * o);
     dst[0] = make_int4(code[0], code[1], code[2], code[3]);
@@ -591,24 +748,20 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
 // ---------------------------------------------------------------------------------------------
 // Decoder.
 __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  ws->status = 0;
-  ws->dec_valid = 0;
-  bool ok = in_bytes >= (uint64_t)kHeaderBytes;
-  uint32_t h[32];
-  if (ok) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(in);
-    for (int i = 0; i < 32; ++i) h[i] = p[i];
-  } else {
-    for (int i = 0; i < 32; ++i) h[i] = 0;
-  }
+  __shared__ uint32_t s_h[32];
+  __shared__ uint32_t s_idx[2];
+  const int tid = threadIdx.x;
+  const bool have = in_bytes >= (uint64_t)kHeaderBytes;
+  if (tid < 32) s_h[tid] = have ? reinterpret_cast<const uint32_t*>(in)[tid] : 0u;
+  __syncthreads();
+  const uint32_t* h = s_h;
   const uint64_t hn = ((uint64_t)h[7] << 32) | h[6];
   const uint64_t T = n / kTile;
   const uint32_t chunks = (uint32_t)((T + kChunkTiles - 1) / kChunkTiles);
   const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
-  ok = ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatE8 && flags <= 1 &&
-       (h[2] & 0xFFFFu) == (uint32_t)kTile && k <= 15 && (h[2] >> 24) == 6u && h[3] >= kStepBitsMin &&
-       h[3] <= kStepBitsMax && hn == n && (n % kTile) == 0;
+  bool ok = have && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatE8 && flags <= 1 &&
+            (h[2] & 0xFFFFu) == (uint32_t)kTile && k <= 15 && (h[2] >> 24) == 6u && h[3] >= kStepBitsMin &&
+            h[3] <= kStepBitsMax && hn == n && (n % kTile) == 0;
   uint32_t F = 0;
   if (ok) {
     const int kh = k > 0 ? k - 1 : 0;
@@ -622,14 +775,16 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
   ok = ok && (((uint64_t)h[9] << 32) | h[8]) == T && h[10] == chunks && h[11] == F &&
        (((uint64_t)h[13] << 32) | h[12]) == fixed_off && (((uint64_t)h[15] << 32) | h[14]) == unary_off &&
        total <= in_bytes && words <= (1ull << 32) && unary_off + 8ull * words == total;
-  if (ok) {
-    const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
-    ok = idx[0] == 0u && (uint64_t)idx[chunks] == words;
-  }
+  if (ok && tid < 2) s_idx[tid] = reinterpret_cast<const uint32_t*>(in + kHeaderBytes)[tid == 0 ? 0 : chunks];
+  __syncthreads();
+  if (tid != 0) return;
+  ok = ok && s_idx[0] == 0u && (uint64_t)s_idx[1] == words;
+  ws->dec_valid = 0;
   if (!ok) {
     ws->status = kErrCorrupt;
     return;
   }
+  ws->status = 0;
   ws->dec_lattice = (uint32_t)lattice;
   ws->dec_dither = (uint32_t)flags;
   ws->dec_k = k;
@@ -646,9 +801,22 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
 
 constexpr int kMaxSymsPerChunk = kChunkTiles * kTile;
 
+// One slot's remainder from an octet field held in (lo, hi) (at most 64 bits); off and w are the
+// same in every lane.
+__device__ __forceinline__ uint32_t field_slot(uint32_t lo, uint32_t hi, int off, int w) {
+  if (w == 0) return 0u;
+  if (off >= 32) return __builtin_amdgcn_ubfe(hi, (uint32_t)(off - 32), (uint32_t)w);
+  if (off + w <= 32) return __builtin_amdgcn_ubfe(lo, (uint32_t)off, (uint32_t)w);
+  return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)off) & low_mask(w);
+}
+
+typedef float hq_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 hq_b2 __attribute__((ext_vector_type(2)));
+
 template <int LAT, int DT_OUT>
-__device__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, uint32_t c,
-                             uint32_t tiles_c, const uint32_t* s_pos, const uint32_t* s_fixed) {
+__device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
+                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos,
+                                             const uint32_t* s_fixed) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
   const int k = ws->dec_k;
   const uint32_t F = ws->dec_F;
@@ -657,7 +825,12 @@ __device__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ 
   const float step = __uint_as_float(ws->dec_step_bits);
   const int RW = octet_rem_bits<LAT>(k);
   const int hdr = tile_hdr_bits<LAT>();
-  const uint32_t sgn = octet_sign_bits(seed, o);
+  // output factor per coordinate: +-2^-7 with the sign of D and of the lane's butterfly sign; the
+  // fused multiply-add with +0 below is exact and turns an exact zero into +0
+  const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit(o) ? 0xFFu : 0u);
+  float cmul[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -0.0078125f : 0.0078125f;
   bool bad = false;
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
@@ -669,30 +842,51 @@ __device__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ 
       const uint32_t rec = tc * F;
       const uint32_t sb = lds_get_bits(s_fixed, rec, 16);
       const uint32_t coset = LAT == kLatE8 ? lds_get_bits(s_fixed, rec + 16 + o, 1) : 0u;
-      uint32_t pos = rec + hdr + (uint32_t)o * RW;
+      const uint32_t P = rec + hdr + (uint32_t)o * RW;
       uint32_t sym[8];
       const uint32_t g0 = (16u * tc + o) * 8u;
       uint32_t prev = g0 ? s_pos[g0 - 1] + 1u : 0u;
+      if (k <= 8) {
+        const uint32_t word = P >> 5, sh = P & 31u;
+        const uint32_t w0 = s_fixed[word], w1 = s_fixed[word + 1], w2 = s_fixed[word + 2];
+        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh), hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+        int off = 0;
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int w = slot_width<LAT>(sl, k);
-        const uint32_t p = s_pos[g0 + sl];
-        const uint32_t q = p - prev;
-        prev = p + 1u;
-        if (q > (0xFFFFFFFFu >> w)) bad = true;
-        sym[sl] = (q << w) | lds_get_bits(s_fixed, pos, w);
-        pos += w;
+        for (int sl = 0; sl < 8; ++sl) {
+          const int w = slot_width<LAT>(sl, k);
+          const uint32_t p = s_pos[g0 + sl];
+          const uint32_t q = p - prev;
+          prev = p + 1u;
+          if (q > (0xFFFFFFFFu >> w)) bad = true;
+          sym[sl] = (q << w) | field_slot(lo, hi, off, w);
+          off += w;
+        }
+      } else {
+        uint32_t pos = P;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int w = slot_width<LAT>(sl, k);
+          const uint32_t p = s_pos[g0 + sl];
+          const uint32_t q = p - prev;
+          prev = p + 1u;
+          if (q > (0xFFFFFFFFu >> w)) bad = true;
+          sym[sl] = (q << w) | lds_get_bits(s_fixed, pos, w);
+          pos += w;
+        }
       }
       int32_t code[8];
       unstrip_octet<LAT>(sym, coset, code);
-      float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (dither) dither_octet<LAT>(seed, t, o, u);
       const float tsc = bf16_bits_to_f32(sb) * step;
+      if (dither) {
+        float u[8];
+        dither_octet<LAT>(seed, t, o, u);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float cc = code_coord<LAT>(code[i]);
-        const float cu = dither ? cc - u[i] : cc;
-        yv[i] = cu * tsc;
+        for (int i = 0; i < 8; ++i) yv[i] = (code_coord<LAT>(code[i]) - u[i]) * tsc;
+      } else {
+        // (z / 2) * tsc equals z * (tsc / 2): both are the same real product rounded once
+        const float f = LAT == kLatE8 ? tsc * 0.5f : tsc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yv[i] = (float)code[i] * f;
       }
     } else {
 #pragma unroll
@@ -703,16 +897,17 @@ __device__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ 
     if (valid) {
       float xo[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = yv[i] * 0.0078125f;
-        xo[i] = ((sgn >> i) & 1u) ? -v : v;
-      }
+      for (int i = 0; i < 8; ++i) xo[i] = __builtin_fmaf(yv[i], cmul[i], 0.0f);
       if (DT_OUT == 1) {
-        uint32_t pk[4];
+        hq_b2 pk[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = f32_to_bf16_rne(xo[2 * i]) | (f32_to_bf16_rne(xo[2 * i + 1]) << 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * kTile + 8 * o) =
-            make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        for (int i = 0; i < 4; ++i) pk[i] = __builtin_convertvector((hq_f2){xo[2 * i], xo[2 * i + 1]}, hq_b2);
+        uint4 st;
+        st.x = __builtin_bit_cast(uint32_t, pk[0]);
+        st.y = __builtin_bit_cast(uint32_t, pk[1]);
+        st.z = __builtin_bit_cast(uint32_t, pk[2]);
+        st.w = __builtin_bit_cast(uint32_t, pk[3]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * kTile + 8 * o) = st;
       } else {
         float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * kTile + 8 * o);
         dst[0] = make_float4(xo[0], xo[1], xo[2], xo[3]);
@@ -746,20 +941,21 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
     return;
   }
   const uint32_t nW = w1 - w0;
-  const uint64_t* seg = reinterpret_cast<const uint64_t*>(in + ws->dec_unary_off) + w0;
-  // terminator positions: popcount per word, workgroup scan, scatter of the set bits
+  const uint32_t* seg = reinterpret_cast<const uint32_t*>(in + ws->dec_unary_off + 8ull * w0);
+  const uint32_t nW32 = 2u * nW;
+  // terminator positions: popcount per 32-bit word, workgroup scan, scatter of the set bits
+  // (positions past nsym only occur in a corrupt segment, which is rejected below)
   uint32_t carry = 0;
-  for (uint32_t base = 0; base < nW; base += kBlock) {
+  for (uint32_t base = 0; base < nW32; base += kBlock) {
     const uint32_t j = base + tid;
-    const uint64_t word = j < nW ? seg[j] : 0ull;
-    const uint32_t cnt = (uint32_t)__popcll(word);
+    uint32_t bits = j < nW32 ? seg[j] : 0u;
     uint32_t tot;
-    uint32_t g = carry + block_excl_scan(cnt, s_scan, &tot);
-    uint64_t bits = word;
+    uint32_t g = carry + block_excl_scan((uint32_t)__popc(bits), s_scan, &tot);
+    const uint32_t bitbase = j * 32u;
     while (bits) {
-      const uint32_t b = (uint32_t)__ffsll((unsigned long long)bits) - 1u;
-      bits &= bits - 1ull;
-      if (g < nsym) s_pos[g] = j * 64u + b;
+      const uint32_t b = (uint32_t)__builtin_ctz(bits);
+      bits &= bits - 1u;
+      s_pos[min(g, (uint32_t)(kMaxSymsPerChunk - 1))] = bitbase + b;
       ++g;
     }
     carry += tot;
@@ -820,9 +1016,21 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
   if (blocks == 0) return hipSuccess;
 #define HQ_RATE(L, D, T)                                                                              \
   hipLaunchKernelGGL((rate_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
-                     a.seed, nc, half_log2, a.rice_k, a.target)
+                     rc_partials(a.ws), a.seed, nc, half_log2, a.rice_k, a.target)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_RATE);
 #undef HQ_RATE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define HQ_SOLVE(L)                                                                                   \
+  hipLaunchKernelGGL((rate_solve_kernel<L>), dim3(1), dim3(kBlock), 0, a.stream, a.ws, rc_partials(a.ws), \
+                     blocks, nc, half_log2, a.rice_k, a.target, N)
+  if (a.lattice == kLatE8)
+    HQ_SOLVE(kLatE8);
+  else if (a.lattice == kLatD4)
+    HQ_SOLVE(kLatD4);
+  else
+    HQ_SOLVE(kLatZ);
+#undef HQ_SOLVE
   return hipGetLastError();
 }
 

@@ -37,8 +37,9 @@ def test_sizes_match_oracle_layout(orc):
             for k in (0, 1, 3, 15):
                 fo, uo, F = orc.layout(n, orc.LATTICES[lat], k)
                 assert hq.hq_stream_fixed_bytes(n, lat, k) == uo
-    assert hq.hq_workspace_size(0) == 4096 + 256
-    assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + ((8 * 101 + 255) // 256) * 256
+    partials = 512 * 32 * 4
+    assert hq.hq_workspace_size(0) == 4096 + partials + 256
+    assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + partials + ((8 * 101 + 255) // 256) * 256
 
 
 def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 21):
@@ -52,7 +53,7 @@ def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 
     (dict(tile=64), hq.HQ_ERR_UNSUPPORTED),
     (dict(lattice=3), hq.HQ_ERR_INVALID_ARG),
     (dict(rice_k=16), hq.HQ_ERR_INVALID_ARG),
-    (dict(step=-1.0), hq.HQ_ERR_INVALID_ARG),
+    (dict(step=-2.0), hq.HQ_ERR_INVALID_ARG),          # -1 alone is a valid sentinel
     (dict(step=float("nan")), hq.HQ_ERR_INVALID_ARG),
     (dict(step=1e-6), hq.HQ_ERR_INVALID_ARG),
     (dict(step=1e6), hq.HQ_ERR_INVALID_ARG),
@@ -76,6 +77,13 @@ def test_encode_rejects_bad_buffers_on_host():
     assert _encode_rc(p, x=0) == hq.HQ_ERR_INVALID_ARG               # null input
     assert _encode_rc(p, out=0) == hq.HQ_ERR_INVALID_ARG             # null output
     assert _encode_rc(p, out=(1 << 20) + 4) == hq.HQ_ERR_INVALID_ARG  # misaligned output
+
+
+def test_rate_rejects_workspace_step_sentinel_on_host():
+    # step == -1 means "take the operating point from the workspace": meaningless for rate control
+    p = hq.make_params("e8", 4.0, step=-1.0)
+    assert hq.lib().hq_rate(ctypes.c_void_p(1 << 20), 1, 128, ctypes.byref(p), None, ctypes.c_void_p(1 << 21),
+                            1 << 20, None) == hq.HQ_ERR_INVALID_ARG
 
 
 def test_decode_and_codes_reject_bad_args_on_host():

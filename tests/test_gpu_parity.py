@@ -107,7 +107,7 @@ def test_stream_parity_fixed_point(orc, lattice, dither, T):
         s_gpu, info = hq.hq_encode(dev(x), lattice, 0.0, seed=9, dither=dither, step=step, rice_k=k)
         assert_same_stream(host_bytes(s_gpu), s_orc, f"step {step} k {k}")
         y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
-        assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.decode(s_orc, x.size).view(np.uint32))
 
 
 @pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
@@ -193,7 +193,9 @@ def test_zero_tiles_and_tiny_values(orc):
             s_gpu, _ = hq.hq_encode(dev(x), lat, 0.0, seed=1, dither=dither, step=0.25, rice_k=3)
             assert_same_stream(host_bytes(s_gpu), s_orc, f"{lat} dither={dither}")
             y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
-            assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.decode(s_orc, x.size).view(np.uint32))
+            yb = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)   # incl. bf16 denormal outputs
+            assert np.array_equal(bf16_host(yb), orc.decode(s_orc, x.size, out_dtype="bf16"))
 
 
 def test_long_unary_segments(orc):
@@ -257,6 +259,20 @@ def test_corrupt_streams_reported(orc):
         assert e.value.code == hq.HQ_ERR_CORRUPT, mutate
     y = hq.hq_decode(good, x.size, out_dtype=torch.float32)   # and the good one still decodes
     assert torch.isfinite(y).all()
+
+
+def test_async_rate_then_encode_equals_one_call(orc):
+    """hq_rate (asynchronous) + hq_encode(step=-1) on the same workspace = hq_encode with rate control."""
+    say("case: rate then encode")
+    w = synth.weight(rows=1024)
+    xd = dev(w)
+    a, _ = hq.hq_encode(xd, "e8", 3.5)
+    ws = hq.workspace(w.size)
+    hq.hq_rate(xd, "e8", 3.5, ws=ws, blocking=False)
+    b, _ = hq.hq_encode(xd, "e8", 3.5, step=-1.0, ws=ws)
+    assert torch.equal(a, b)
+    s_orc, _ = orc.encode(w, orc.LAT_E8, 3.5)
+    assert_same_stream(host_bytes(b), s_orc)
 
 
 def test_deterministic_repeat():
