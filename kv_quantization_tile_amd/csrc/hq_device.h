@@ -233,7 +233,12 @@ __device__ __forceinline__ void e8_nearest(const float* v, int32_t* z) {
 // directly (same rule and ties as e8_nearest followed by strip_octet).  With r = rint v, e = v - r,
 // sigma_i = [e_i < 0]: the stripped coordinates are u = r for the D8 candidate and u = r - sigma for
 // the D8 + 1/2 candidate; the parity fix moves the first coordinate whose |e| equals the maximum
-// (D8) or the minimum (D8 + 1/2) of |e| by +1 or -1 (toward v in the lattice-point coordinates).
+// (D8) or the minimum (D8 + 1/2) of |e| by one step toward v in the lattice-point coordinates.
+// Per coordinate, with the masks sg = -sigma and kb = -[D8 + 1/2 kept], u = r + adj where
+//   adj = kb & sg (no fix: 0 or -sigma), or (sg ^ kb) | (~kb & 1) at the fixed coordinate
+//   (D8: r - 1 or r + 1 toward v; D8 + 1/2: r - 1 + sigma).
+// 1 - 2 a_max and 2 + 2 a_min are formed by a fused multiply-add: the product by 2 is exact, so
+// the single rounding equals that of the separate multiply and add.
 __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32_t* coset) {
   float e[8];
   int32_t r[8];
@@ -253,21 +258,23 @@ __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32
                            fminf(fminf(fabsf(e[4]), fabsf(e[5])), fminf(fabsf(e[6]), fabsf(e[7]))));
   const float d = ((fabsf(e[0]) + fabsf(e[1])) + (fabsf(e[2]) + fabsf(e[3]))) +
                   ((fabsf(e[4]) + fabsf(e[5])) + (fabsf(e[6]) + fabsf(e[7])));
-  const float lhs = pa ? d + (1.0f - 2.0f * amax) : d;
-  const float rhs = pb ? 2.0f + 2.0f * amin : 2.0f;
-  const bool keep_a = lhs <= rhs;
+  const float lhs = d + (pa ? __builtin_fmaf(-2.0f, amax, 1.0f) : 0.0f);
+  const float rhs = pb ? __builtin_fmaf(2.0f, amin, 2.0f) : 2.0f;
+  // rhs - lhs is exact in sign (a difference of distinct finite floats is never zero), so its sign
+  // bit is [lhs > rhs]: kb is all ones when the D8 + 1/2 candidate is kept
+  const uint32_t kb = (uint32_t)((int32_t)__float_as_uint(rhs - lhs) >> 31);
+  const bool keep_a = kb == 0u;
   const float t = keep_a ? amax : amin;
   bool found = keep_a ? (pa == 0u) : (pb == 0u);  // no fix needed: nothing to find
-  const uint32_t bsub = keep_a ? 0u : 1u;
   int32_t u[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t sg = __float_as_uint(e[i]) >> 31;
-    const int32_t base = r[i] - (int32_t)(sg & bsub);
+    const uint32_t sg = (uint32_t)((int32_t)__float_as_uint(e[i]) >> 31);
     const bool hit = !found && (fabsf(e[i]) == t);
     found = found || hit;
-    const int32_t delta = ((uint32_t)keep_a ^ sg) ? 1 : -1;
-    u[i] = hit ? base + delta : base;
+    const uint32_t nofix = kb & sg;               // 0 (D8) or -sigma (D8 + 1/2)
+    const uint32_t fixv = (sg ^ kb) | (~kb & 1u);  // D8: sigma ? -1 : +1;  D8 + 1/2: sigma - 1
+    u[i] = r[i] + (int32_t)(hit ? fixv : nofix);
   }
   int32_t par = 0;
 #pragma unroll
@@ -276,7 +283,7 @@ __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32
     par += u[i];
   }
   sym[7] = zigzag((u[7] - (par & 1)) >> 1);
-  *coset = bsub;
+  *coset = kb & 1u;
 }
 
 template <int LAT>
@@ -470,6 +477,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   __syncthreads();
   *total = all;
   return before + inc - v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: four row shifts give the
+// prefix inside each row of 16 lanes, then row_bcast:15 adds row 0's (row 2's) total to row 1
+// (row 3) and row_bcast:31 adds the total of rows 0-1 to rows 2-3.  Lanes whose source is out of
+// range or whose row is masked receive 0 (old = 0, bound_ctrl), so the add leaves them unchanged.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+  return (uint32_t)v;
 }
 
 __device__ __forceinline__ uint64_t atomic_load_acq(const uint64_t* p) {

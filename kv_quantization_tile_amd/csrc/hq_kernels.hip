@@ -18,7 +18,7 @@
 namespace hq {
 
 constexpr int kFixedWordsMax = 3904;      // 2 F u32 words per chunk; F <= 1952 bits
-constexpr int kUnaryWinWords = 4096;      // 16 KiB unary staging window = 131072 bits
+constexpr int kUnaryWinWords = 1024;      // 4 KiB unary staging window = 32768 bits
 constexpr uint32_t kUnaryWinBits = kUnaryWinWords * 32u;
 constexpr uint64_t kFlagAgg = 1ull << 62, kFlagPrefix = 2ull << 62, kValMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 20;
@@ -43,27 +43,31 @@ __device__ __forceinline__ uint32_t lds_get_bits(const uint32_t* s, uint32_t pos
   return (uint32_t)(v >> sh) & low_mask(nbits);
 }
 
-// Remainder field of one octet packed in registers: slot s at its offset, least significant bit
-// first, for fields of at most 64 bits (Rice k <= 8).  k is the same in every lane, so the
-// branches below are uniform.
+// Remainder field of one octet in the low RW bits of (lo, hi), slot 0 lowest (least significant
+// bit first).  Each slot's low w bits enter at the top of a right-shifting accumulator through one
+// funnel shift (alignbit), which also drops the symbol's bits above w; a final shift moves the
+// field down.  k is the same in every lane, so the branch is uniform.  Fields up to 64 bits
+// (Rice k <= 8).
 template <int LAT>
 __device__ __forceinline__ void pack_octet_remainders(const uint32_t* sym, int k, uint32_t* lo, uint32_t* hi) {
+  const int RW = octet_rem_bits<LAT>(k);
   uint32_t l = 0, h = 0;
-  int off = 0;
+  if (RW <= 32) {
 #pragma unroll
-  for (int sl = 0; sl < 8; ++sl) {
-    const int w = slot_width<LAT>(sl, k);
-    const uint32_t v = sym[sl] & low_mask(w);
-    if (off < 32) {
-      l |= v << off;
-      if (off + w > 32) h |= v >> (32 - off);
-    } else {
-      h |= v << (off - 32);
+    for (int sl = 0; sl < 8; ++sl) l = __builtin_amdgcn_alignbit(sym[sl], l, (uint32_t)slot_width<LAT>(sl, k));
+    *lo = __builtin_amdgcn_alignbit(0u, l, (uint32_t)(32 - RW));  // shift 32 is 0: RW = 0 leaves l = 0
+    *hi = 0u;
+  } else {
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const uint32_t w = (uint32_t)slot_width<LAT>(sl, k);
+      l = __builtin_amdgcn_alignbit(h, l, w);
+      h = __builtin_amdgcn_alignbit(sym[sl], h, w);
     }
-    off += w;
+    const uint32_t sh = (uint32_t)(64 - RW);  // 1..31
+    *lo = __builtin_amdgcn_alignbit(h, l, sh);
+    *hi = h >> sh;
   }
-  *lo = l;
-  *hi = h;
 }
 
 // OR a field of at most 64 bits (lo, hi) into an LDS bit array at bit position pos.
@@ -391,6 +395,40 @@ __global__ __launch_bounds__(kBlock) void rate_solve_kernel(Workspace* ws, const
 
 // ---------------------------------------------------------------------------------------------
 // Header of the stream (see hq.h), written by the workgroup that completes the last chunk.
+// Symbols of one lane's octet in round r of chunk c, computed from the input again (load, sign,
+// FWHT, tile scale, multiplier, dither, lattice).  Used only for octets whose unary code is longer
+// than one word and for segments larger than the staging window; every lane of the wavefront must
+// call it together (the FWHT and the tile energy exchange values between lanes).
+template <int LAT, bool DITHER, int DT>
+__device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_t seed, uint32_t c, int r,
+                                              int wave, int tw, int o, uint32_t sgn, uint32_t lane_neg, float step,
+                                              uint32_t* sym) {
+  const uint64_t t = (uint64_t)c * kChunkTiles + 16u * r + 4u * wave + tw;
+  uint32_t smask[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
+  float y[8];
+  if (t < T) {
+    load_octet_signed<DT>(x, t, o, smask, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+  }
+  fwht_lane(y);
+  fwht_cross(y, o);
+  const float S = tile_sumsq(y);
+  const bool fin = isfinite(S);
+  if (!fin) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+  }
+  const float m = tile_multiplier(tile_scale_bits(fin ? S : 0.0f), step, lane_neg);
+  float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  uint32_t cos;
+  octet_symbols<LAT, DITHER>(y, m, u, sym, &cos);
+}
+
 __device__ void write_header(uint8_t* out, uint64_t cap, int lattice, int dither, int k, uint32_t step_bits,
                              uint64_t seed, uint64_t n, uint64_t T, uint32_t chunks, uint32_t F,
                              uint64_t fixed_off, uint64_t unary_off, uint64_t words, uint64_t ubits,
@@ -484,7 +522,7 @@ template <int LAT, bool DITHER, int DT>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
   __shared__ uint4 s_unary4[kUnaryWinWords / 4];
-  __shared__ uint32_t s_scan[8];
+  __shared__ uint4 s_wtot4[4];  // per round, the four wavefronts' Rice-length totals
   __shared__ uint64_t s_prefix;
   uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
   uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
@@ -575,9 +613,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   mr[2] = __uint_as_float(group_bcast<2>(__float_as_uint(m_mine)));
   mr[3] = __uint_as_float(group_bcast<3>(__float_as_uint(m_mine)));
 
-  // phase 2: quantise, strip, pack the fixed record, Rice lengths
+  // phase 2: quantise, strip, pack the fixed record, Rice lengths and unary patterns
   uint32_t sym[4][8];
-  uint32_t L[4];
+  uint32_t L[4], pat[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t tc = 16u * r + 4u * wave + tw;
@@ -612,20 +650,41 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
           pos += w;
         }
       }
+      // unary code of the octet relative to its start: the terminator of slot s sits at
+      // c_s = sum over s' <= s of (q_s' + 1), minus 1; bits at c >= 32 only matter when L > 32,
+      // and such octets are written terminator by terminator below
+      uint32_t cpos = 0xFFFFFFFFu, pt = 0;
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) len += sym[r][sl] >> slot_width<LAT>(sl, k);
+      for (int sl = 0; sl < 8; ++sl) {
+        cpos += (sym[r][sl] >> slot_width<LAT>(sl, k)) + 1u;
+        pt |= 1u << (cpos & 31u);
+      }
+      len = cpos + 1u;
+      pat[r] = pt;
+    } else {
+      pat[r] = 0;
     }
     L[r] = valid ? len : 0u;
   }
 
-  // unary offsets inside the chunk: octet index 256 r + tid is the symbol order
+  // unary offsets inside the chunk (octet index 256 r + tid is the symbol order): wavefront scans
+  // of every round, then one exchange of the 16 wavefront totals
+  uint32_t incl[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) incl[r] = wave_incl_scan(L[r]);
+  if (lane == 63) {
+    uint32_t* wt = reinterpret_cast<uint32_t*>(s_wtot4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wt[4 * r + wave] = incl[r];
+  }
+  __syncthreads();
   uint32_t off[4], B = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan(L[r], s_scan, &tot);
-    off[r] = B + ex;
-    B += tot;
+    const uint4 t4 = s_wtot4[r];
+    const uint32_t before = (wave > 0 ? t4.x : 0u) + (wave > 1 ? t4.y : 0u) + (wave > 2 ? t4.z : 0u);
+    off[r] = B + before + incl[r] - L[r];
+    B += (t4.x + t4.y) + (t4.z + t4.w);
   }
   const uint64_t W = (B + 63u) / 64u;
   if (wave == 0) {
@@ -655,35 +714,46 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       atomicOr(&ws->status, (uint32_t)kErrCapacity);
   }
 
-  // unary segment, staged through LDS in windows of kUnaryWinBits
+  // unary segment, staged through LDS in windows of kUnaryWinBits.  Common case: the segment fits
+  // one window and each octet's code (at most 32 bits) is ORed in as one pattern.  Otherwise the
+  // symbols of the rounds concerned are computed again and written terminator by terminator.
   const uint64_t ubase = unary_off + 8ull * prefix;
   const bool fits = ubase + 8ull * W <= P.cap;
   const uint32_t seg_words = (uint32_t)(2u * W);
+  const bool multi = B > kUnaryWinBits;
+  if (!multi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t p0 = off[r];
+      if (L[r] != 0u && L[r] <= 32u) {
+        const uint32_t sh = p0 & 31u;
+        atomicOr(&s_unary[p0 >> 5], pat[r] << sh);
+        if (sh + L[r] > 32u) atomicOr(&s_unary[(p0 >> 5) + 1], __builtin_amdgcn_alignbit(0u, pat[r], 32u - sh));
+      }
+    }
+  }
+  uint32_t slow = 0;  // rounds (bit r) in which some lane of this wavefront writes terminators
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (__ballot(multi ? L[r] != 0u : L[r] > 32u)) slow |= 1u << r;
   for (uint32_t wb = 0; wb < B; wb += kUnaryWinBits) {
     if (wb) {
       __syncthreads();
       for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
       __syncthreads();
     }
-    if (B <= kUnaryWinBits) {  // the common case: the whole segment fits one window
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t p = off[r];
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          p += sym[r][sl] >> slot_width<LAT>(sl, k);
-          if (L[r]) atomicOr(&s_unary[p >> 5], 1u << (p & 31u));
-          p += 1;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (L[r] == 0) continue;
-        uint32_t p = off[r];
+#pragma unroll 1
+    for (int r = 0; r < 4; ++r) {
+      if (!((slow >> r) & 1u)) continue;  // uniform in the wavefront
+      const uint32_t Lr = r == 0 ? L[0] : r == 1 ? L[1] : r == 2 ? L[2] : L[3];
+      const uint32_t offr = r == 0 ? off[0] : r == 1 ? off[1] : r == 2 ? off[2] : off[3];
+      uint32_t sy[8];
+      round_symbols<LAT, DITHER, DT>(P.x, P.T, P.seed, c, r, wave, tw, o, sgn, lane_neg, step, sy);
+      if (multi ? Lr != 0u : Lr > 32u) {
+        uint32_t p = offr;
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-          p += sym[r][sl] >> slot_width<LAT>(sl, k);
+          p += sy[sl] >> slot_width<LAT>(sl, k);
           const uint32_t rel = p - wb;
           if (p >= wb && rel < kUnaryWinBits) atomicOr(&s_unary[rel >> 5], 1u << (rel & 31u));
           p += 1;
