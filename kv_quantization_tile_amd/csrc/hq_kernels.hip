@@ -880,13 +880,31 @@ __device__ __forceinline__ uint32_t field_slot(uint32_t lo, uint32_t hi, int off
   return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)off) & low_mask(w);
 }
 
+// Bit field of `nbits` (<= 32) bits at bit position pos of a plane in global memory; both words
+// are read unconditionally (callers guarantee the second is inside the stream).
+__device__ __forceinline__ uint32_t plane_bits(const uint32_t* __restrict__ pl, uint32_t pos, int nbits) {
+  const uint32_t word = pos >> 5;
+  return __builtin_amdgcn_alignbit(pl[word + 1], pl[word], pos & 31u) & low_mask(nbits);
+}
+
 typedef float hq_f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 hq_b2 __attribute__((ext_vector_type(2)));
 
+// Twice the un-zigzagged value of a symbol: 2 unzz(s) = s ^ -(s & 1) (s for even s, -s - 1 for odd).
+__device__ __forceinline__ int32_t twice_unzz(uint32_t s) {
+  return (int32_t)(s ^ (uint32_t)__builtin_amdgcn_sbfe((int32_t)s, 0u, 1u));
+}
+
+// Decode of one chunk's tiles once the terminator positions of its unary segment are in s_pos.
+// Each lane rebuilds one octet per round: Rice symbols (unary part from consecutive terminator
+// positions, remainders from the fixed record read in place), lattice codes, rescale (and dither
+// removal), inverse FWHT, sign and 2^-7, store.  The fixed-record words of round r + 1 are loaded
+// while round r is computed.  Every read of the record stays inside the stream: a chunk's record
+// has room for 64 tiles, and at most two words past its end lie in the unary plane, which holds at
+// least one word per symbol's chunk once the chunk's terminator count has been checked.
 template <int LAT, int DT_OUT>
 __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
-                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos,
-                                             const uint32_t* s_fixed) {
+                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos, bool check_q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
   const int k = ws->dec_k;
   const uint32_t F = ws->dec_F;
@@ -894,7 +912,8 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
   const uint64_t seed = ws->dec_seed;
   const float step = __uint_as_float(ws->dec_step_bits);
   const int RW = octet_rem_bits<LAT>(k);
-  const int hdr = tile_hdr_bits<LAT>();
+  const uint32_t hdr = (uint32_t)tile_hdr_bits<LAT>();
+  const uint32_t* __restrict__ fw = reinterpret_cast<const uint32_t*>(in + ws->dec_fixed_off + (uint64_t)c * 8ull * F);
   // output factor per coordinate: +-2^-7 with the sign of D and of the lane's butterfly sign; the
   // fused multiply-add with +0 below is exact and turns an exact zero into +0
   const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit(o) ? 0xFFu : 0u);
@@ -902,32 +921,64 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
   for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -0.0078125f : 0.0078125f;
   bool bad = false;
+  // record words of a round: the tile header (scale, then E8 coset bits) and the octet's field
+  uint32_t hA, hB, f0, f1, f2;
+  auto issue = [&](int r) {
+    const uint32_t rec = (16u * r + 4u * wave + tw) * F;
+    const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
+    hA = fw[rec >> 5];
+    hB = fw[(rec >> 5) + 1];
+    f0 = fw[P >> 5];
+    f1 = fw[(P >> 5) + 1];
+    f2 = RW > 32 ? fw[(P >> 5) + 2] : 0u;
+  };
+  issue(0);
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
     const uint32_t tc = 16u * r + 4u * wave + tw;
     const bool valid = tc < tiles_c;
     const uint64_t t = (uint64_t)c * kChunkTiles + tc;
+    const uint32_t rec = tc * F;
+    const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
+    const uint32_t a0 = hA, a1 = hB, x0 = f0, x1 = f1, x2 = f2;
+    if (r < 3) issue(r + 1);
     float yv[8];
     if (valid) {
-      const uint32_t rec = tc * F;
-      const uint32_t sb = lds_get_bits(s_fixed, rec, 16);
-      const uint32_t coset = LAT == kLatE8 ? lds_get_bits(s_fixed, rec + 16 + o, 1) : 0u;
-      const uint32_t P = rec + hdr + (uint32_t)o * RW;
+      // rec is a multiple of 16: the 32 bits at rec are the scale (low half) and, for E8, the
+      // coset bits of the tile's 16 octets (high half)
+      const uint32_t th = __builtin_amdgcn_alignbit(a1, a0, rec & 31u);
+      const uint32_t sb = th & 0xFFFFu;
+      const uint32_t coset = LAT == kLatE8 ? (th >> (16 + o)) & 1u : 0u;
+      const uint32_t sh = P & 31u;
+      const uint32_t lo = __builtin_amdgcn_alignbit(x1, x0, sh), hi = __builtin_amdgcn_alignbit(x2, x1, sh);
+      // unary parts: q = p - p_prev - 1 = (p_prev ^ ~0) + p; the symbol before the chunk's first
+      // sits at -1
+      const uint32_t g0 = (16u * tc + (uint32_t)o) * 8u;
+      const uint32_t pv = s_pos[g0 ? g0 - 1 : 0];
+      uint32_t pprev = g0 ? pv : 0xFFFFFFFFu;
+      const uint4 pa = *reinterpret_cast<const uint4*>(s_pos + g0);
+      const uint4 pb = *reinterpret_cast<const uint4*>(s_pos + g0 + 4);
+      const uint32_t pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
       uint32_t sym[8];
-      const uint32_t g0 = (16u * tc + o) * 8u;
-      uint32_t prev = g0 ? s_pos[g0 - 1] + 1u : 0u;
-      if (k <= 8) {
-        const uint32_t word = P >> 5, sh = P & 31u;
-        const uint32_t w0 = s_fixed[word], w1 = s_fixed[word + 1], w2 = s_fixed[word + 2];
-        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh), hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+      if (RW <= 32) {  // uniform: every slot is one bit-field extract of lo
         int off = 0;
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int w = slot_width<LAT>(sl, k);
-          const uint32_t p = s_pos[g0 + sl];
-          const uint32_t q = p - prev;
-          prev = p + 1u;
-          if (q > (0xFFFFFFFFu >> w)) bad = true;
+          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
+          pprev = pp[sl];
+          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
+          sym[sl] = (q << w) | __builtin_amdgcn_ubfe(lo, (uint32_t)off, (uint32_t)w);
+          off += w;
+        }
+      } else if (k <= 8) {
+        int off = 0;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int w = slot_width<LAT>(sl, k);
+          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
+          pprev = pp[sl];
+          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
           sym[sl] = (q << w) | field_slot(lo, hi, off, w);
           off += w;
         }
@@ -936,27 +987,48 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int w = slot_width<LAT>(sl, k);
-          const uint32_t p = s_pos[g0 + sl];
-          const uint32_t q = p - prev;
-          prev = p + 1u;
-          if (q > (0xFFFFFFFFu >> w)) bad = true;
-          sym[sl] = (q << w) | lds_get_bits(s_fixed, pos, w);
-          pos += w;
+          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
+          pprev = pp[sl];
+          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
+          sym[sl] = (q << w) | plane_bits(fw, pos, w);
+          pos += (uint32_t)w;
         }
       }
-      int32_t code[8];
-      unstrip_octet<LAT>(sym, coset, code);
       const float tsc = bf16_bits_to_f32(sb) * step;
-      if (dither) {
-        float u[8];
-        dither_octet<LAT>(seed, t, o, u);
+      if (LAT == kLatE8) {
+        // z_i = 2 u_i + p for i < 7; the parity of u_0 + .. + u_6 is bit 1 of z_0 ^ .. ^ z_6;
+        // z_7 = 2 (2 unzz(s_7) + par) + p
+        int32_t z[8];
+        uint32_t xz = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) yv[i] = (code_coord<LAT>(code[i]) - u[i]) * tsc;
+        for (int i = 0; i < 7; ++i) {
+          z[i] = twice_unzz(sym[i]) + (int32_t)coset;
+          xz ^= (uint32_t)z[i];
+        }
+        z[7] = 2 * twice_unzz(sym[7]) + (int32_t)((xz & 2u) | coset);
+        if (dither) {
+          float u[8];
+          dither_octet<LAT>(seed, t, o, u);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) yv[i] = ((float)z[i] * 0.5f - u[i]) * tsc;
+        } else {
+          // (z / 2) * tsc equals z * (tsc / 2): both are the same real product rounded once
+          const float f = tsc * 0.5f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) yv[i] = (float)z[i] * f;
+        }
       } else {
-        // (z / 2) * tsc equals z * (tsc / 2): both are the same real product rounded once
-        const float f = LAT == kLatE8 ? tsc * 0.5f : tsc;
+        int32_t code[8];
+        unstrip_octet<LAT>(sym, coset, code);
+        if (dither) {
+          float u[8];
+          dither_octet<LAT>(seed, t, o, u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) yv[i] = (float)code[i] * f;
+          for (int i = 0; i < 8; ++i) yv[i] = (code_coord<LAT>(code[i]) - u[i]) * tsc;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) yv[i] = (float)code[i] * tsc;
+        }
       }
     } else {
 #pragma unroll
@@ -988,60 +1060,62 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
   if (bad) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
 }
 
+// One workgroup per chunk.  Terminator positions: thread i takes words [i m, i m + m) of the
+// chunk's unary segment (m = ceil(words / 256)), counts their set bits, a workgroup scan gives each
+// thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
+// count (so every write below stays inside s_pos), it writes the position of each set bit.
 template <int DT_OUT>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restrict__ in, void* __restrict__ out,
                                                         Workspace* ws) {
-  __shared__ uint32_t s_pos[kMaxSymsPerChunk];
-  __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
-  __shared__ uint32_t s_scan[8];
-  uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
+  __shared__ uint4 s_pos4[kMaxSymsPerChunk / 4];  // exactly 32 KiB: five workgroups fit one CU's LDS
+  uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
+  uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
   if (!ws->dec_valid) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t c = blockIdx.x;
   const uint32_t chunks = ws->dec_chunks;
   if (c >= chunks) return;
   const uint64_t T = ws->dec_tiles;
   const uint32_t tiles_c = (uint32_t)min((uint64_t)kChunkTiles, T - (uint64_t)c * kChunkTiles);
   const uint32_t nsym = tiles_c * kTile;
-  const uint32_t F = ws->dec_F;
   const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
   const uint32_t w0 = idx[c], w1 = idx[c + 1];
   if (w1 < w0 || (uint64_t)w1 > ws->dec_words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
     if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
     return;
   }
-  const uint32_t nW = w1 - w0;
-  const uint32_t* seg = reinterpret_cast<const uint32_t*>(in + ws->dec_unary_off + 8ull * w0);
-  const uint32_t nW32 = 2u * nW;
-  // terminator positions: popcount per 32-bit word, workgroup scan, scatter of the set bits
-  // (positions past nsym only occur in a corrupt segment, which is rejected below)
-  uint32_t carry = 0;
-  for (uint32_t base = 0; base < nW32; base += kBlock) {
-    const uint32_t j = base + tid;
-    uint32_t bits = j < nW32 ? seg[j] : 0u;
-    uint32_t tot;
-    uint32_t g = carry + block_excl_scan((uint32_t)__popc(bits), s_scan, &tot);
-    const uint32_t bitbase = j * 32u;
-    while (bits) {
-      const uint32_t b = (uint32_t)__builtin_ctz(bits);
-      bits &= bits - 1u;
-      s_pos[min(g, (uint32_t)(kMaxSymsPerChunk - 1))] = bitbase + b;
-      ++g;
-    }
-    carry += tot;
-  }
-  // stage the fixed record
-  const uint4* src = reinterpret_cast<const uint4*>(in + ws->dec_fixed_off + (uint64_t)c * 8ull * F);
-  for (uint32_t i = tid; i < F / 2; i += kBlock) s_fixed4[i] = src[i];
+  const uint32_t* __restrict__ seg = reinterpret_cast<const uint32_t*>(in + ws->dec_unary_off + 8ull * w0);
+  const uint32_t nW32 = 2u * (w1 - w0);
+  const uint32_t m = (nW32 + kBlock - 1) / kBlock;
+  const uint32_t j0 = min((uint32_t)tid * m, nW32), j1 = min(j0 + m, nW32);
+  uint32_t cnt = 0;
+  for (uint32_t j = j0; j < j1; ++j) cnt += (uint32_t)__popc(seg[j]);
+  const uint32_t incl = wave_incl_scan(cnt);
+  if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  if (carry != nsym) {
+  const uint32_t t0 = s_wsum[0], t1 = s_wsum[1], t2 = s_wsum[2], t3 = s_wsum[3];
+  const uint32_t total = (t0 + t1) + (t2 + t3);
+  __syncthreads();  // every lane has the totals before s_pos is overwritten
+  if (total != nsym) {  // uniform: the whole workgroup leaves
     if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
     return;
   }
+  uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
+  for (uint32_t j = j0; j < j1; ++j) {
+    uint32_t bits = seg[j];
+    const uint32_t bitbase = j * 32u;
+    while (bits) {
+      s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
+      bits &= bits - 1u;
+    }
+  }
+  __syncthreads();
+  // q of a corrupt segment can exceed what q << w holds only when the segment is that long
+  const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
   switch (ws->dec_lattice) {
-    case kLatE8: decode_chunk<kLatE8, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
-    case kLatD4: decode_chunk<kLatD4, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
-    default: decode_chunk<kLatZ, DT_OUT>(in, out, ws, c, tiles_c, s_pos, s_fixed); break;
+    case kLatE8: decode_chunk<kLatE8, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
+    case kLatD4: decode_chunk<kLatD4, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
+    default: decode_chunk<kLatZ, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
   }
 }
 
