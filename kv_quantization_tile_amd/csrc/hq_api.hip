@@ -62,7 +62,7 @@ int status_from_flags(uint32_t f) {
   return HQ_OK;
 }
 
-size_t workspace_bytes_for(uint64_t n) { return kWsHeader + kWsPartials + align256h(8ull * (chunks_of(n) + 1)); }
+size_t workspace_bytes_for(uint64_t n) { return kWsHeader + kWsRate + align256h(8ull * (chunks_of(n) + 1)); }
 
 EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, void* out, uint64_t cap,
                      void* ws, hq_stream_t s) {
@@ -100,7 +100,7 @@ int run_rate_control(const EncodeArgs& a) {
     e = launch_init(a, (int64_t)a.fixed_step_bits);
     if (e != hipSuccess) return HQ_ERR_HIP;
     if (a.rice_k < 0 && N > 0) {
-      e = launch_rate_pass(a, 1, 0, N);
+      e = launch_rate_pass(a, 1, 0, N, 0);
       if (e != hipSuccess) return HQ_ERR_HIP;
     }
     return HQ_OK;
@@ -108,9 +108,9 @@ int run_rate_control(const EncodeArgs& a) {
   e = launch_init(a, initial_centre(a.target));
   if (e != hipSuccess) return HQ_ERR_HIP;
   if (N == 0) return HQ_OK;
-  e = launch_rate_pass(a, kRcCand, 21, N);
+  e = launch_rate_pass(a, kRcCand, 21, N, 0);
   if (e != hipSuccess) return HQ_ERR_HIP;
-  e = launch_rate_pass(a, kRcCand, 17, N);
+  e = launch_rate_pass(a, kRcCand, 17, N, 1);
   if (e != hipSuccess) return HQ_ERR_HIP;
   return HQ_OK;
 }

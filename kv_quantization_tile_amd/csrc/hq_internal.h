@@ -18,8 +18,7 @@ constexpr int kRcKwin = 4;
 // Device workspace.  The fixed part is 4 KiB; the encoder's look-back flags (one 64-bit word per
 // chunk, plus one) follow it.  Every field is (re)initialised by the first kernel of a call.
 struct alignas(256) Workspace {
-  uint32_t pad_ticket;
-  uint32_t pad_ticket2;
+  uint32_t pad2[2];
   uint32_t status;       // error flags (kErr*)
   uint32_t step_bits;    // operating point chosen so far (binary32 bits of the step)
   int32_t rice_k;
@@ -49,16 +48,24 @@ struct alignas(256) Workspace {
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
-// Per-workgroup partial sums of a rate pass (one slot of kRcCand * kRcKwin counters per workgroup
-// of 16 sample tiles), then the encoder's look-back flags.
-constexpr size_t kRcSlots = kRcSampleTiles / 16;
-constexpr size_t kWsPartials = kRcSlots * kRcCand * kRcKwin * sizeof(uint32_t);
+// Counters of the two rate passes.  A workgroup of a pass adds its sums into one of kRcAccSlots
+// counter sets (workgroup index mod kRcAccSlots, so that few workgroups share an address); the
+// one-workgroup solve kernel that follows adds the sets up.  The init kernel of every call zeroes
+// both passes' counters.
+constexpr int kRcAccSlots = 16;
+constexpr int kRcCounters = kRcCand * kRcKwin;
+struct RateAcc {
+  uint32_t cnt[kRcAccSlots][kRcCounters];
+};
+constexpr size_t kWsRate = 2 * sizeof(RateAcc);  // pass A, pass B
+static_assert(kWsRate % 256 == 0, "rate counters keep the flags 256-byte aligned");
 
-inline uint32_t* rc_partials(void* ws) {
-  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + kWsHeader);
+inline RateAcc* rate_acc(void* ws, int pass) {
+  return reinterpret_cast<RateAcc*>(reinterpret_cast<char*>(ws) + kWsHeader) + pass;
 }
+// the encoder's look-back flags follow the rate counters
 inline uint64_t* lookback_flags(void* ws) {
-  return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader + kWsPartials);
+  return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader + kWsRate);
 }
 
 struct EncodeArgs {
@@ -79,7 +86,7 @@ struct EncodeArgs {
 };
 
 hipError_t launch_init(const EncodeArgs& a, int64_t centre);
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample);
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass);
 hipError_t launch_encode(const EncodeArgs& a);
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
                          Workspace* ws, hipStream_t stream);

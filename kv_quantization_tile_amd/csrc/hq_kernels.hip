@@ -6,8 +6,9 @@
 //
 // Kernels of one encode call, all on the caller's stream, with no host round trip in between:
 //   init_kernel     clears the workspace flags and seeds the rate search;
-//   rate_kernel x2  evaluates 8 candidate steps on a sample of tiles, and its last workgroup solves
-//                   for the next centre (pass A: half-octave spacing, pass B: 1/32 octave);
+//   rate_kernel x2  evaluates 8 candidate steps on a sample of tiles into per-pass counters, each
+//                   followed by rate_solve_kernel, which solves for the next centre (pass A:
+//                   half-octave spacing, pass B: 1/32 octave);
 //   encode_kernel   one workgroup per 64-tile chunk: load, sign, FWHT, scale, lattice, strip, Rice
 //                   lengths, workgroup scan, decoupled look-back over chunks for the unary offsets,
 //                   and coalesced stores of the chunk's fixed record and unary segment.
@@ -177,8 +178,8 @@ __device__ __forceinline__ float tile_multiplier(uint32_t sb, float step, uint32
 }
 
 // ---------------------------------------------------------------------------------------------
-__global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int64_t centre,
-                            uint32_t step_bits, int32_t k) {
+__global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uint32_t* acc, uint32_t nacc,
+                            int64_t centre, uint32_t step_bits, int32_t k) {
   const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid == 0) {
     ws->status = 0;
@@ -193,6 +194,7 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int
     ws->res_k = k;
   }
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
+  for (uint64_t i = gid; i < nacc; i += (uint64_t)gridDim.x * blockDim.x) acc[i] = 0;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -203,7 +205,7 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, int
 //  - the search variable is b, the binary32 bit pattern of the step;
 //  - a pass evaluates up to 8 candidates centre + (2j-7) 2^h (clamped to [2^-12, 2^12]); for each,
 //    the Rice k is the argmin (ties: smaller k) over kb..kb+3, kb = clamp(-exponent - 2, 0, 12);
-//  - its last workgroup interpolates linearly (IEEE double) between the two candidates that
+//  - the solve kernel interpolates linearly (IEEE double) between the two candidates that
 //    bracket the target bit count (first candidate at or below it) or extrapolates from the end
 //    pair, rounds, clamps, and stores the answer as the next centre together with the k of the
 //    candidate nearest to it.  Pass A (h = 21) starts at 2.05 - target octaves; pass B (h = 17)
@@ -281,7 +283,7 @@ __device__ void rate_solve(Workspace* ws, const int64_t* b, const double* R, con
 
 template <int LAT, bool DITHER, int DT>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
-                                                      Workspace* ws, uint32_t* partials, uint64_t seed, int nc,
+                                                      Workspace* ws, RateAcc* racc, uint64_t seed, int nc,
                                                       int half_log2, int fixed_k, float target) {
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
@@ -342,40 +344,26 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
     for (int w = 0; w < kRcKwin; ++w)
       if (j < nc && acc[j][w]) atomicAdd(&s_red[0][j * kRcKwin + w], acc[j][w]);
   __syncthreads();
-  // this workgroup's partial sums go to its own slot; rate_solve_kernel, the next launch on the
-  // stream, adds them up (the kernel boundary orders the stores before its loads)
-  constexpr int kC = kRcCand * kRcKwin;
-  if (tid < kC) partials[(uint64_t)blockIdx.x * kC + tid] = s_red[0][tid];
+  // this workgroup's sums go into counter set blockIdx mod kRcAccSlots; rate_solve_kernel, the next
+  // launch on the stream, adds the sets up (the kernel boundary orders the atomics before its loads)
+  if (tid < kRcCounters && s_red[0][tid])
+    __hip_atomic_fetch_add(&racc->cnt[blockIdx.x % kRcAccSlots][tid], s_red[0][tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup: sum the partial counters of the rate pass over its nslots workgroups, then solve.
+// One workgroup: add up the counter sets of a rate pass, evaluate the candidates, solve.
 template <int LAT>
-__global__ __launch_bounds__(kBlock) void rate_solve_kernel(Workspace* ws, const uint32_t* __restrict__ partials,
-                                                            uint32_t nslots, int nc, int half_log2, int fixed_k,
-                                                            float target, uint32_t N) {
-  constexpr int kC = kRcCand * kRcKwin;  // 32 counters = 8 uint4 per slot
-  __shared__ uint64_t s_acc[kBlock / 8][kC];
-  __shared__ uint64_t s_sumq[kC];
+__global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, const RateAcc* __restrict__ racc, int nc,
+                                                        int half_log2, int fixed_k, float target, uint32_t N) {
+  __shared__ uint64_t s_sumq[kRcCounters];
   __shared__ int64_t s_b[kRcCand];
   __shared__ double s_R[kRcCand];
   __shared__ int s_k[kRcCand];
   const int tid = threadIdx.x;
-  // lane t reads quad t mod 8 (counters 4 (t mod 8) .. +3) of slots t/8, t/8 + 32, ...
-  const int quad = tid & 7;
-  uint64_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-  const uint4* p4 = reinterpret_cast<const uint4*>(partials);
-  for (uint32_t slot = tid >> 3; slot < nslots; slot += kBlock / 8) {
-    const uint4 v = p4[(uint64_t)slot * (kC / 4) + quad];
-    a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
-  }
-  s_acc[tid >> 3][4 * quad + 0] = a0;
-  s_acc[tid >> 3][4 * quad + 1] = a1;
-  s_acc[tid >> 3][4 * quad + 2] = a2;
-  s_acc[tid >> 3][4 * quad + 3] = a3;
-  __syncthreads();
-  if (tid < kC) {
+  if (tid < kRcCounters) {
     uint64_t t = 0;
-    for (int r = 0; r < kBlock / 8; ++r) t += s_acc[r][tid];
+#pragma unroll
+    for (int sl = 0; sl < kRcAccSlots; ++sl) t += racc->cnt[sl][tid];
     s_sumq[tid] = t;
   }
   __syncthreads();
@@ -1138,7 +1126,9 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
 
 hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
   const uint64_t nflags = (uint64_t)a.chunks + 1;
-  uint64_t blocks = (nflags + kBlock - 1) / kBlock;
+  const uint32_t nacc = (uint32_t)(kWsRate / sizeof(uint32_t));
+  const uint64_t work = nflags > nacc ? nflags : nacc;
+  uint64_t blocks = (work + kBlock - 1) / kBlock;
   if (blocks > 1024) blocks = 1024;
   uint32_t step_bits;
   int32_t k;
@@ -1150,24 +1140,24 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
     step_bits = (uint32_t)c;
     k = a.rice_k >= 0 ? a.rice_k : kwin_base(centre) + 1;
   }
-  hipLaunchKernelGGL(init_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.ws,
-                     lookback_flags(a.ws), nflags, centre, step_bits, k);
+  hipLaunchKernelGGL(init_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.ws, lookback_flags(a.ws),
+                     nflags, reinterpret_cast<uint32_t*>(rate_acc(a.ws, 0)), nacc, centre, step_bits, k);
   return hipGetLastError();
 }
 
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N) {
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
   const uint32_t blocks = (N + 15) / 16;
   if (blocks == 0) return hipSuccess;
 #define HQ_RATE(L, D, T)                                                                              \
   hipLaunchKernelGGL((rate_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
-                     rc_partials(a.ws), a.seed, nc, half_log2, a.rice_k, a.target)
+                     rate_acc(a.ws, pass), a.seed, nc, half_log2, a.rice_k, a.target)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_RATE);
 #undef HQ_RATE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 #define HQ_SOLVE(L)                                                                                   \
-  hipLaunchKernelGGL((rate_solve_kernel<L>), dim3(1), dim3(kBlock), 0, a.stream, a.ws, rc_partials(a.ws), \
-                     blocks, nc, half_log2, a.rice_k, a.target, N)
+  hipLaunchKernelGGL((rate_solve_kernel<L>), dim3(1), dim3(64), 0, a.stream, a.ws, rate_acc(a.ws, pass), nc, \
+                     half_log2, a.rice_k, a.target, N)
   if (a.lattice == kLatE8)
     HQ_SOLVE(kLatE8);
   else if (a.lattice == kLatD4)

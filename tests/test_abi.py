@@ -37,9 +37,9 @@ def test_sizes_match_oracle_layout(orc):
             for k in (0, 1, 3, 15):
                 fo, uo, F = orc.layout(n, orc.LATTICES[lat], k)
                 assert hq.hq_stream_fixed_bytes(n, lat, k) == uo
-    partials = 512 * 32 * 4
-    assert hq.hq_workspace_size(0) == 4096 + partials + 256
-    assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + partials + ((8 * 101 + 255) // 256) * 256
+    rate = 2 * 16 * 32 * 4  # two rate passes, 16 sets of 32 counters each
+    assert hq.hq_workspace_size(0) == 4096 + rate + 256
+    assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + rate + ((8 * 101 + 255) // 256) * 256
 
 
 def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 21):
