@@ -31,7 +31,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", choices=["weight", "kv"], default="weight")
+    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all"], default="weight",
+                    help="weight / kv: one tensor, the headline line; sweep: Z, D4 and E8 on the weight; "
+                         "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
+                         "the 64 (layer, K|V) calls of the KV cache")
     ap.add_argument("--bps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -97,6 +100,144 @@ def profiled_traffic(profile_stem: str, kernel_prefix: str):
     return None
 
 
+def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=None, ws_dec=None, y=None):
+    """Events around rate control, encode and decode of one device tensor (steps timed, warmup
+    untimed).  Returns per-step means (ms), the stream header and the decoded tensor."""
+    dev = x.device
+    n = x.numel()
+    if out is None:
+        s_ref, _ = hq.hq_encode(x, lat, tb, seed=seed, dither=dither)
+        out = torch.empty(int(s_ref.numel() * 1.05) + 65536, dtype=torch.uint8, device=dev)
+        del s_ref
+    ws = hq.workspace(n, dev) if ws is None else ws
+    ws_dec = hq.workspace(0, dev) if ws_dec is None else ws_dec
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev) if y is None else y
+    stream = torch.cuda.current_stream()
+
+    def one():
+        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
+        return e1, e2
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        e1, e2 = one()
+        e3 = torch.cuda.Event(enable_timing=True)
+        e3.record(stream)
+        ev.append((e0, e1, e2, e3))
+    torch.cuda.synchronize()
+    st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
+    assert st == 0 and st2 == 0, (st, st2)
+    r = {"rate_ms": float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev])),
+         "encode_ms": float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev])),
+         "decode_ms": float(np.mean([c.elapsed_time(d) for _, _, c, d in ev])),
+         "step_ms": float(np.mean([a.elapsed_time(d) for a, _, _, d in ev]))}
+    return r, hq.header_fields(out[:128].cpu().numpy()), y
+
+
+def series(args):
+    """Many tensors or lattices, one JSON line: value = total bf16 input bytes over the summed step
+    times; per-item figures in extra."""
+    import torch
+
+    import kv_quantization_tile_amd as hq
+    dev = torch.device("cuda:0")
+    items = []
+    if args.config == "sweep":
+        import synth
+        xw = torch.from_numpy(synth.weight().reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+        tb = 4.0 if args.bps is None else args.bps
+        for lat in ("z", "d4", "e8"):
+            items.append((lat, lambda: xw, lat, tb, 0, False))
+        workload = f"lattice sweep on the mlp weight 14336x4096 bf16 at {tb:g} bps: Z, D4, E8, no dither"
+        steps, warmup = args.steps, args.warmup
+    elif args.config == "model":
+        import synth
+        tb = 4.0 if args.bps is None else args.bps
+
+        def gen(i, shape):
+            def f():
+                g = torch.Generator(device=dev)
+                g.manual_seed(1000 + i)
+                return (torch.randn(shape, generator=g, device=dev) * 0.02).to(torch.bfloat16).reshape(-1)
+            return f
+        for i, (name, shape) in enumerate(synth.model_shapes()):
+            items.append((name, gen(i, shape), "e8", tb, i, False))
+        workload = (f"224 linear weights of an 8B-shaped decoder (32 x q,k,v,o,gate,up,down) N(0, 0.02^2) bf16, "
+                    f"drawn on the GPU one at a time, E8 {tb:g} bps, no dither")
+        steps, warmup = 1, 1
+    else:  # kv_all
+        tb = 2.0 if args.bps is None else args.bps
+
+        def gen(layer, is_v):
+            def f():
+                g = torch.Generator(device=dev)
+                g.manual_seed(2_000_003 + layer * 2 + is_v)
+                x = torch.randn((8, 32768, 128), generator=g, device=dev)
+                if not is_v:
+                    gc = torch.Generator(device=dev)
+                    gc.manual_seed(7919 + layer)
+                    for h in range(8):
+                        ch = torch.randperm(128, generator=gc, device=dev)[:4]
+                        x[h, :, ch] *= 10.0
+                return x.to(torch.bfloat16).reshape(-1)
+            return f
+        for layer in range(32):
+            for is_v in (0, 1):
+                items.append((f"l{layer}.{'v' if is_v else 'k'}", gen(layer, is_v), "e8", tb,
+                              (layer << 1) | is_v, True))
+        workload = (f"KV cache, 32 layers x K|V calls of [8][32768][128] bf16 N(0,1) (4 K channels per head x10), "
+                    f"drawn on the GPU one call at a time, E8 + dither {tb:g} bps, per-layer seed (l<<1)|isV")
+        steps, warmup = 1, 1
+    total_in = 0
+    tot = {"rate_ms": 0.0, "encode_ms": 0.0, "decode_ms": 0.0, "step_ms": 0.0}
+    per = {}
+    worst_rate_err = 0.0
+    enc_alg = 0
+    for name, make, lat, tb, seed, dither in items:
+        x = make()
+        n = x.numel()
+        r, hdr, y = time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup)
+        for k in tot:
+            tot[k] += r[k]
+        total_in += 2 * n
+        enc_alg += 2 * n + hdr["total_bytes"]
+        rate_err = abs(hdr["payload_bits"] / n - tb)
+        worst_rate_err = max(worst_rate_err, rate_err)
+        if args.config == "sweep":
+            xf = x.float()
+            nmse = float(((y.float() - xf) ** 2).sum() / (xf ** 2).sum())
+            per[name] = {"payload_bps": round(hdr["payload_bits"] / n, 5),
+                         "total_bps": round(8 * hdr["total_bytes"] / n, 5), "nmse": nmse,
+                         "gbs": round(2 * n / (r["step_ms"] * 1e-3) / 1e9, 2),
+                         **{k: round(v, 5) for k, v in r.items()}}
+        del x, y
+    value = total_in / (tot["step_ms"] * 1e-3) / 1e9
+    enc_gbs = enc_alg / (tot["encode_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(tot["step_ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": workload, "items": len(items), "input_bytes": total_in},
+        "roofline": {"bound": "hbm", "achieved": round(enc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(enc_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "encode_kernel",
+                     "alg_bytes_per_launch": enc_alg // len(items), "launch_ms": round(tot["encode_ms"] / len(items), 5)},
+        "extra": {**{k: round(v, 4) for k, v in tot.items()}, "worst_payload_rate_error_bps": round(worst_rate_err, 5),
+                  **({"per_lattice": per} if per else {})},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -105,6 +246,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.config in ("sweep", "model", "kv_all"):
+        series(args)
         return
     import torch
 

@@ -147,6 +147,11 @@ __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
   return (uint32_t)((int32_t)c - adj * 128);
 }
 
+// Three-input XOR in one v_bitop3 (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ uint32_t zigzag(int32_t a) { return ((uint32_t)a << 1) ^ (uint32_t)(a >> 31); }
 __device__ __forceinline__ int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u); }
 
@@ -231,27 +236,28 @@ __device__ __forceinline__ void e8_nearest(const float* v, int32_t* z) {
 
 // E8 nearest point and bit-stripping in one pass, producing the symbols and the coset bit
 // directly (same rule and ties as e8_nearest followed by strip_octet).  With r = rint v, e = v - r,
-// sigma_i = [e_i < 0]: the stripped coordinates are u = r for the D8 candidate and u = r - sigma for
-// the D8 + 1/2 candidate; the parity fix moves the first coordinate whose |e| equals the maximum
-// (D8) or the minimum (D8 + 1/2) of |e| by one step toward v in the lattice-point coordinates.
-// Per coordinate, with the masks sg = -sigma and kb = -[D8 + 1/2 kept], u = r + adj where
-//   adj = kb & sg (no fix: 0 or -sigma), or (sg ^ kb) | (~kb & 1) at the fixed coordinate
-//   (D8: r - 1 or r + 1 toward v; D8 + 1/2: r - 1 + sigma).
+// sigma_i = [e_i < 0]: the stripped coordinates are u = r for the D8 candidate and
+// u = r - sigma = floor v for the D8 + 1/2 candidate; the parity fix moves the first coordinate
+// whose |e| equals the maximum (D8) or the minimum (D8 + 1/2) of |e| by one step: +-1 with the sign
+// of e for D8, against it for D8 + 1/2.  The stripped coordinates stay in binary32 (integers below
+// 2^22, so every step is exact), and zigzag is |2u + 1/2| truncated: 2u for u >= 0, -2u - 1 below.
 // 1 - 2 a_max and 2 + 2 a_min are formed by a fused multiply-add: the product by 2 is exact, so
 // the single rounding equals that of the separate multiply and add.
 __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32_t* coset) {
-  float e[8];
-  int32_t r[8];
-  uint32_t xr = 0, xe = 0;
+  float e[8], rf[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float ri = rintf(v[i]);
-    e[i] = v[i] - ri;
-    r[i] = (int32_t)ri;
-    xr ^= (uint32_t)r[i];
-    xe ^= __float_as_uint(e[i]);
+    rf[i] = rintf(v[i]);
+    e[i] = v[i] - rf[i];
   }
-  const uint32_t pa = xr & 1u, pb = pa ^ (xe >> 31);
+  // parity of sum r: the sum of eight integers below 2^18 is exact in binary32
+  const float rsum = ((rf[0] + rf[1]) + (rf[2] + rf[3])) + ((rf[4] + rf[5]) + (rf[6] + rf[7]));
+  // parity of the number of negative e: sign bit of the XOR of the eight patterns
+  const uint32_t xe =
+      xor3(xor3(__float_as_uint(e[0]), __float_as_uint(e[1]), __float_as_uint(e[2])),
+           xor3(__float_as_uint(e[3]), __float_as_uint(e[4]), __float_as_uint(e[5])),
+           __float_as_uint(e[6]) ^ __float_as_uint(e[7]));
+  const uint32_t pa = (uint32_t)(int32_t)rsum & 1u, pb = pa ^ (xe >> 31);
   const float amax = fmaxf(fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))),
                            fmaxf(fmaxf(fabsf(e[4]), fabsf(e[5])), fmaxf(fabsf(e[6]), fabsf(e[7]))));
   const float amin = fminf(fminf(fminf(fabsf(e[0]), fabsf(e[1])), fminf(fabsf(e[2]), fabsf(e[3]))),
@@ -266,23 +272,22 @@ __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32
   const bool keep_a = kb == 0u;
   const float t = keep_a ? amax : amin;
   bool found = keep_a ? (pa == 0u) : (pb == 0u);  // no fix needed: nothing to find
-  int32_t u[8];
+  float u[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t sg = (uint32_t)((int32_t)__float_as_uint(e[i]) >> 31);
+    const float base = keep_a ? rf[i] : floorf(v[i]);
     const bool hit = !found && (fabsf(e[i]) == t);
     found = found || hit;
-    const uint32_t nofix = kb & sg;               // 0 (D8) or -sigma (D8 + 1/2)
-    const uint32_t fixv = (sg ^ kb) | (~kb & 1u);  // D8: sigma ? -1 : +1;  D8 + 1/2: sigma - 1
-    u[i] = r[i] + (int32_t)(hit ? fixv : nofix);
+    // +-1 with the sign of e (D8) or against it (D8 + 1/2): sign bit of e ^ kb on 1.0
+    const float step1 = __uint_as_float(((__float_as_uint(e[i]) ^ kb) & 0x80000000u) | 0x3F800000u);
+    u[i] = base + (hit ? step1 : 0.0f);
   }
-  int32_t par = 0;
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
-    sym[i] = zigzag(u[i]);
-    par += u[i];
-  }
-  sym[7] = zigzag((u[7] - (par & 1)) >> 1);
+  for (int i = 0; i < 7; ++i) sym[i] = (uint32_t)fabsf(__builtin_fmaf(2.0f, u[i], 0.5f));
+  const uint32_t x = xor3(xor3(sym[0], sym[1], sym[2]), xor3(sym[3], sym[4], sym[5]), sym[6]);
+  // parity of u_0 + .. + u_6: u and zz(u) satisfy [u odd] = bit 1 ^ bit 0 of zz(u)
+  const int32_t par = (int32_t)(((x >> 1) ^ x) & 1u);
+  sym[7] = zigzag(((int32_t)u[7] - par) >> 1);
   *coset = kb & 1u;
 }
 

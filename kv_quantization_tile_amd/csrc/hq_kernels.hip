@@ -609,9 +609,11 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const uint32_t tc = 16u * r + 4u * wave + tw;
     const uint64_t t = (uint64_t)c * kChunkTiles + tc;
     const bool valid = t < P.T;
-    if (!isfinite(S[r])) {
+    if (__ballot(!isfinite(S[r]))) {  // uniform test: the common case skips the block entirely
+      if (!isfinite(S[r])) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
+      }
     }
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (DITHER) dither_octet<LAT>(P.seed, t, o, u);
@@ -626,7 +628,13 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
         if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (16 * tw)) & 0xFFFFu, 16);
       }
       uint32_t pos = rec + hdr + (uint32_t)o * RW;
-      if (k <= 8) {
+      if (RW <= 32) {  // uniform: the field is one word, ORed into at most two
+        uint32_t lo, hi;
+        pack_octet_remainders<LAT>(sym[r], k, &lo, &hi);
+        const uint32_t sh = pos & 31u;
+        atomicOr(&s_fixed[pos >> 5], lo << sh);
+        if (sh + (uint32_t)RW > 32u) atomicOr(&s_fixed[(pos >> 5) + 1], __builtin_amdgcn_alignbit(0u, lo, 32u - sh));
+      } else if (k <= 8) {
         uint32_t lo, hi;
         pack_octet_remainders<LAT>(sym[r], k, &lo, &hi);
         lds_put_field64(s_fixed, pos, lo, hi);
@@ -1053,7 +1061,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 // thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
 // count (so every write below stays inside s_pos), it writes the position of each set bit.
 template <int DT_OUT>
-__global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restrict__ in, void* __restrict__ out,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) void decode_kernel(const uint8_t* __restrict__ in, void* __restrict__ out,
                                                         Workspace* ws) {
   __shared__ uint4 s_pos4[kMaxSymsPerChunk / 4];  // exactly 32 KiB: five workgroups fit one CU's LDS
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);

@@ -165,6 +165,52 @@ def test_kv_call_full_size(orc, layer, is_v, target):
     assert np.array_equal(bf16_host(y), orc.decode(s_orc, x.size, out_dtype="bf16"))
 
 
+@pytest.mark.parametrize("lattice", ["z", "d4"])
+def test_lattice_sweep_weight(orc, lattice):
+    """Lattice sweep on the 14336 x 4096 weight at 4 bps (Z and D4; E8 is covered above): the same
+    step and Rice parameter as the oracle, identical stream and decode, rate within 0.01."""
+    say(f"case: weight 14336x4096 {lattice} 4 bps")
+    w = synth.weight()
+    s_orc, info_orc = orc.encode(w, orc.LATTICES[lattice], 4.0)
+    s_gpu, info = hq.hq_encode(dev(w), lattice, 4.0)
+    assert info["step"] == info_orc["step"] and info["rice_k"] == info_orc["k"]
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert abs(info["payload_bps"] - 4.0) <= 0.01
+    y = hq.hq_decode(s_gpu, w.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(y), orc.decode(s_orc, w.size, out_dtype="bf16"))
+
+
+def test_lattice_sweep_distortion_order():
+    """At an equal payload rate the lattice with the smaller normalized second moment gives the
+    smaller error: E8 < D4 < Z in normalized MSE on the weight at 4 bps."""
+    say("case: lattice sweep distortion order")
+    x = dev(synth.weight())
+    xf = x.float()
+    nmse = {}
+    for lat in ("z", "d4", "e8"):
+        s, info = hq.hq_encode(x, lat, 4.0)
+        assert abs(info["payload_bps"] - 4.0) <= 0.01
+        y = hq.hq_decode(s, x.numel(), out_dtype=torch.float32)
+        nmse[lat] = float(((y - xf) ** 2).sum() / (xf ** 2).sum())
+    say(f"nmse {nmse}")
+    assert nmse["e8"] < nmse["d4"] < nmse["z"]
+
+
+@pytest.mark.parametrize("index", [0, 1, 6])
+def test_model_tensor_full_size(orc, index):
+    """Linear weights of the 8B-shaped decoder (q [4096,4096], k [1024,4096], down [4096,14336]),
+    E8 at 4 bps: identical stream and decode."""
+    name, shape = synth.model_shapes()[index]
+    say(f"case: model tensor {index} {name} {shape}")
+    w = synth.model_tensor(index, shape)
+    s_orc, info_orc = orc.encode(w, orc.LAT_E8, 4.0, seed=index)
+    s_gpu, info = hq.hq_encode(dev(w), "e8", 4.0, seed=index)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert abs(info["payload_bps"] - 4.0) <= 0.01
+    y = hq.hq_decode(s_gpu, w.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(y), orc.decode(s_orc, w.size, out_dtype="bf16"))
+
+
 # ---- edge cases and error paths ---------------------------------------------------------------
 
 def test_empty_and_single_tile(orc):
