@@ -31,10 +31,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all"], default="weight",
+    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv"], default="weight",
                     help="weight / kv: one tensor, the headline line; sweep: Z, D4 and E8 on the weight; "
                          "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
-                         "the 64 (layer, K|V) calls of the KV cache")
+                         "the 64 (layer, K|V) calls of the KV cache; gemv: fused decode + matrix-vector "
+                         "product on the weight's stream")
     ap.add_argument("--bps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -238,6 +239,62 @@ def series(args):
     print(json.dumps(result), flush=True)
 
 
+def gemv_bench(args):
+    """Fused decode + matrix-vector product on the 14336 x 4096 weight's E8 stream, next to torch's
+    bf16 matrix-vector product on the uncompressed weight and to decode followed by that product."""
+    import torch
+
+    import kv_quantization_tile_amd as hq
+    import synth
+    dev = torch.device("cuda:0")
+    rows, cols = 14336, 4096
+    tb = 4.0 if args.bps is None else args.bps
+    w = torch.from_numpy(synth.weight().reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(synth.gaussian(cols, seed=31)).to(dev)
+    s, info = hq.hq_encode(w, "e8", tb)
+    nbytes = s.numel()
+    ws = torch.empty(hq.hq_gemv_workspace_size(rows, cols), dtype=torch.uint8, device=dev)
+    y = torch.empty(rows, dtype=torch.float32, device=dev)
+    wd = torch.empty(rows * cols, dtype=torch.bfloat16, device=dev)
+    ws_dec = hq.workspace(0, dev)
+    w2, xb = w.view(rows, cols), x.to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    fused_ms = timed(lambda: hq.hq_gemv(s, rows, cols, x, y=y, ws=ws, check=False))
+    assert hq.hq_status(ws) == 0
+    bf16_ms = timed(lambda: torch.mv(w2, xb))
+    dec_mv_ms = timed(lambda: (hq.hq_decode(s, rows * cols, out=wd, ws=ws_dec, check=False),
+                               torch.mv(wd.view(rows, cols), xb)))
+    alg = nbytes + 4 * cols + 4 * rows
+    achieved = alg / (fused_ms * 1e-3) / 1e9
+    result = {
+        "metric": "fused decode + matrix-vector product: bf16-equivalent weight GB/s, 1 GPU",
+        "value": round(2 * rows * cols / (fused_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(fused_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"mlp weight 14336x4096 bf16 as an E8 {tb:g} bps stream ({nbytes} B), "
+                               f"activation N(0,1) fp32 [4096]", "stream_bytes": nbytes,
+                   "payload_bps": round(info["payload_bps"], 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "hq_gemv (all launches)",
+                     "alg_bytes_per_launch": alg, "launch_ms": round(fused_ms, 5)},
+        "extra": {"torch_bf16_mv_ms": round(bf16_ms, 5), "decode_then_torch_mv_ms": round(dec_mv_ms, 5),
+                  "fused_vs_bf16": round(bf16_ms / fused_ms, 3), "fused_vs_decode_then_mv": round(dec_mv_ms / fused_ms, 3)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,6 +306,9 @@ def main():
         return
     if args.config in ("sweep", "model", "kv_all"):
         series(args)
+        return
+    if args.config == "gemv":
+        gemv_bench(args)
         return
     import torch
 

@@ -135,6 +135,25 @@ int hq_decode(const void *stream_data, uint64_t stream_bytes, void *out, int32_t
  * hq_encode / hq_decode / hq_rate that used it (HQ_OK when none). */
 int hq_status(void *workspace, hq_stream_t stream);
 
+/* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only). */
+int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
+
+/* Fused decode + matrix-vector product y = W_hat x, where the stream encodes a row-major
+ * [rows][cols] matrix (n = rows * cols; tiles of 128 along cols, so cols % 128 == 0) and W_hat is
+ * the decoder's reconstruction taken in exact arithmetic.  x: cols values of x_dtype (device),
+ * y: rows binary32 values (device).  Since tile (r, j) decodes to D H yhat / 128 (component 1's
+ * transform is orthogonal up to the factor 128 and H is symmetric), its contribution is
+ * <yhat, H D x_j> / 128: the activation is rotated once per column tile (binary32, the encoder's
+ * butterfly order) and no matrix tile is inverse-transformed.  Per tile, yhat = (c - U) * s * step
+ * rounded to binary32, the octet products are a fixed-order chain, the tile sum a fixed tree, and
+ * the row sum adds the tiles in column order, so results are deterministic; they differ from an
+ * exact product by rounding only (relative to sum |yhat| |x~|, a few hundred units of 2^-24).
+ * Components 1-3 of the HyperQuant technical summary (section "Methodology: the HyperQuant
+ * pipeline"); the fused product itself is the summary's future-work direction.  Asynchronous;
+ * stream validation as for hq_decode, errors through hq_status(workspace). */
+int hq_gemv(const void *stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void *x,
+            int32_t x_dtype, float *y, void *workspace, size_t workspace_bytes, hq_stream_t stream);
+
 /* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
  * E8 codes are twice the lattice point, D4 and Z codes are the point) and per-tile bf16 scale bits
  * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */

@@ -22,7 +22,7 @@ HQ_F32, HQ_BF16 = 0, 1
 LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
-           "hq_encode", "hq_decode", "hq_status", "hq_codes")
+           "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv")
 
 
 class HqParams(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib():
         L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
         L.hq_status.argtypes = [P, P]
         L.hq_codes.argtypes = [P, i32, u64, P, P, P, P, sz, P]
+        L.hq_gemv_workspace_size.argtypes = [u64, u64, ctypes.POINTER(sz)]
+        L.hq_gemv.argtypes = [P, u64, u64, u64, P, i32, P, P, sz, P]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         _lib = L
@@ -194,6 +196,30 @@ def hq_decode(stream_bytes, n: int, out_dtype=None, out=None, ws=None, stream=No
     if check:
         _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_decode")
     return out
+
+
+def hq_gemv_workspace_size(rows: int, cols: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().hq_gemv_workspace_size(rows, cols, ctypes.byref(out)), "hq_gemv_workspace_size")
+    return out.value
+
+
+def hq_gemv(stream_bytes, rows: int, cols: int, x, y=None, ws=None, stream=None, check=True):
+    """y = W_hat x for a stream of a [rows][cols] matrix: fused decode + matrix-vector product
+    (float32 output)."""
+    torch = _torch()
+    assert x.is_cuda and x.is_contiguous() and x.numel() == cols
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(hq_gemv_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
+    sh = _stream_handle(stream)
+    _check(lib().hq_gemv(ctypes.c_void_p(stream_bytes.data_ptr()), stream_bytes.numel(), rows, cols,
+                         ctypes.c_void_p(x.data_ptr()), _dtype_code(x), ctypes.c_void_p(y.data_ptr()),
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh), "hq_gemv")
+    if check:
+        _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_gemv")
+    return y
 
 
 def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None,

@@ -245,6 +245,32 @@ int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t
   return HQ_OK;
 }
 
+static size_t gemv_xt_bytes(uint64_t cols) { return align256h(4ull * cols); }
+
+int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t* bytes) {
+  if (!bytes || cols % 128 || (rows && cols && rows > (1ull << 35) / cols)) return HQ_ERR_INVALID_ARG;
+  *bytes = kWsHeader + gemv_xt_bytes(cols) + align256h(4ull * (rows * cols / 128));
+  return HQ_OK;
+}
+
+int hq_gemv(const void* stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void* x,
+            int32_t x_dtype, float* y, void* workspace, size_t workspace_bytes, hq_stream_t stream) {
+  size_t need = 0;
+  int rc = hq_gemv_workspace_size(rows, cols, &need);
+  if (rc) return rc;
+  if (x_dtype != HQ_F32 && x_dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
+  if (!stream_data || !workspace || workspace_bytes < need || (rows && cols && (!x || !y))) return HQ_ERR_INVALID_ARG;
+  if (((uintptr_t)stream_data & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)y & 3u) || ((uintptr_t)workspace & 255u))
+    return HQ_ERR_INVALID_ARG;
+  char* w = static_cast<char*>(workspace);
+  float* xt = reinterpret_cast<float*>(w + kWsHeader);
+  float* tp = reinterpret_cast<float*>(w + kWsHeader + gemv_xt_bytes(cols));
+  if (launch_gemv(static_cast<const uint8_t*>(stream_data), stream_bytes, rows, cols, x, x_dtype, y,
+                  static_cast<Workspace*>(workspace), xt, tp, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
 int hq_status(void* workspace, hq_stream_t stream) {
   if (!workspace) return HQ_ERR_INVALID_ARG;
   uint32_t f = 0;

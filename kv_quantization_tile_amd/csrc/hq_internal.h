@@ -91,5 +91,7 @@ hipError_t launch_encode(const EncodeArgs& a);
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
                          Workspace* ws, hipStream_t stream);
 hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales);
+hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
+                       float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream);
 
 }  // namespace hq

@@ -898,9 +898,19 @@ __device__ __forceinline__ int32_t twice_unzz(uint32_t s) {
 // while round r is computed.  Every read of the record stays inside the stream: a chunk's record
 // has room for 64 tiles, and at most two words past its end lie in the unary plane, which holds at
 // least one word per symbol's chunk once the chunk's terminator count has been checked.
-template <int LAT, int DT_OUT>
+// Extra arguments of the fused decode + matrix-vector product: the rotated activation (one
+// 128-value tile per column tile of the matrix), the number of column tiles, and the per-tile
+// partial products.
+struct GemvArgs {
+  const float* xt;
+  uint32_t ctiles;
+  float* tp;
+};
+
+template <int LAT, int DT_OUT, bool GEMV>
 __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
-                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos, bool check_q) {
+                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos, bool check_q,
+                                             GemvArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
   const int k = ws->dec_k;
   const uint32_t F = ws->dec_F;
@@ -1030,6 +1040,28 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
       for (int i = 0; i < 8; ++i) yv[i] = 0.0f;
     }
+    if constexpr (GEMV) {
+      // the tile's share of its row: 2^-7 <yhat, x~_j> (the lane's butterfly sign plays no part:
+      // yhat is not transformed here); the octet partial is a fixed-order chain, the tile sum a
+      // fixed xor tree
+      const uint32_t j = (uint32_t)(t % g.ctiles);
+      const float4* xp = reinterpret_cast<const float4*>(g.xt + (uint64_t)j * kTile + 8 * o);
+      const float4 a = valid ? xp[0] : make_float4(0, 0, 0, 0), b = valid ? xp[1] : make_float4(0, 0, 0, 0);
+      float part = yv[0] * a.x;
+      part = __builtin_fmaf(yv[1], a.y, part);
+      part = __builtin_fmaf(yv[2], a.z, part);
+      part = __builtin_fmaf(yv[3], a.w, part);
+      part = __builtin_fmaf(yv[4], b.x, part);
+      part = __builtin_fmaf(yv[5], b.y, part);
+      part = __builtin_fmaf(yv[6], b.z, part);
+      part = __builtin_fmaf(yv[7], b.w, part);
+      part = part + lane_xor<1>(part);
+      part = part + lane_xor<2>(part);
+      part = part + lane_xor<4>(part);
+      part = part + lane_xor<8>(part);
+      if (valid && o == 0) g.tp[t] = part * 0.0078125f;
+      continue;
+    }
     fwht_lane(yv);
     fwht_cross(yv, o);
     if (valid) {
@@ -1060,9 +1092,9 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 // chunk's unary segment (m = ceil(words / 256)), counts their set bits, a workgroup scan gives each
 // thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
 // count (so every write below stays inside s_pos), it writes the position of each set bit.
-template <int DT_OUT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) void decode_kernel(const uint8_t* __restrict__ in, void* __restrict__ out,
-                                                        Workspace* ws) {
+template <int DT_OUT, bool GEMV>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) void decode_kernel(
+    const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, GemvArgs gv) {
   __shared__ uint4 s_pos4[kMaxSymsPerChunk / 4];  // exactly 32 KiB: five workgroups fit one CU's LDS
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
   uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
@@ -1109,10 +1141,60 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   // q of a corrupt segment can exceed what q << w holds only when the segment is that long
   const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
   switch (ws->dec_lattice) {
-    case kLatE8: decode_chunk<kLatE8, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
-    case kLatD4: decode_chunk<kLatD4, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
-    default: decode_chunk<kLatZ, DT_OUT>(in, out, ws, c, tiles_c, s_pos, check_q); break;
+    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
+    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
+    default: decode_chunk<kLatZ, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fused decode + matrix-vector product.  For a stream of a [rows][cols] matrix (tiles of 128 along
+// cols), tile (r, j) decodes to D H yhat / 128, so its dot product with the activation's tile x_j
+// is <yhat, H D x_j> / 128 (H is symmetric, D diagonal): rotate each activation tile once, then
+// every matrix tile needs only its lattice values, no inverse transform.
+
+// x~_j = H D x_j for every column tile, binary32 in the encoder's butterfly order, stored with the
+// lanes' butterfly signs removed (an exact negation).  Runs after the header check (the seed of D
+// comes from the stream).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const void* __restrict__ x, uint32_t ctiles,
+                                                             const Workspace* ws, float* __restrict__ xt) {
+  if (!ws->dec_valid) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const uint64_t t = (uint64_t)blockIdx.x * 16 + 4 * wave + tw;
+  const bool valid = t < ctiles;
+  const uint32_t sgn = octet_sign_bits(ws->dec_seed, o);
+  uint32_t smask[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
+  float y[8];
+  if (valid) {
+    load_octet_signed<DT>(x, t, o, smask, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+  }
+  fwht_lane(y);
+  fwht_cross(y, o);
+  if (!valid) return;
+  const uint32_t neg = lane_sign_bit(o) << 31;
+  float4* dst = reinterpret_cast<float4*>(xt + t * kTile + 8 * o);
+  dst[0] = make_float4(__uint_as_float(__float_as_uint(y[0]) ^ neg), __uint_as_float(__float_as_uint(y[1]) ^ neg),
+                       __uint_as_float(__float_as_uint(y[2]) ^ neg), __uint_as_float(__float_as_uint(y[3]) ^ neg));
+  dst[1] = make_float4(__uint_as_float(__float_as_uint(y[4]) ^ neg), __uint_as_float(__float_as_uint(y[5]) ^ neg),
+                       __uint_as_float(__float_as_uint(y[6]) ^ neg), __uint_as_float(__float_as_uint(y[7]) ^ neg));
+}
+
+// y_r = sum over the row's column tiles of the tile partials, in column order (one lane per row).
+__global__ __launch_bounds__(kBlock) void gemv_rows_kernel(const float* __restrict__ tp, uint64_t rows,
+                                                           uint32_t ctiles, const Workspace* ws, float* __restrict__ y) {
+  if (!ws->dec_valid) return;
+  const uint64_t r = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (r >= rows) return;
+  const float* p = tp + r * ctiles;
+  float acc = 0.0f;
+  for (uint32_t j = 0; j < ctiles; ++j) acc += p[j];
+  y[r] = acc;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1213,10 +1295,37 @@ hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int ou
   const uint64_t T = n / kTile;
   const uint64_t chunks = (T + kChunkTiles - 1) / kChunkTiles;
   if (chunks == 0) return hipSuccess;
+  const GemvArgs none{nullptr, 1u, nullptr};
   if (out_dtype == 1)
-    hipLaunchKernelGGL(decode_kernel<1>, dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws);
+    hipLaunchKernelGGL((decode_kernel<1, false>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws, none);
   else
-    hipLaunchKernelGGL(decode_kernel<0>, dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws);
+    hipLaunchKernelGGL((decode_kernel<0, false>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
+                       float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream) {
+  const uint64_t n = rows * cols;
+  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t ctiles = (uint32_t)(cols / kTile);
+  const uint64_t T = n / kTile;
+  const uint64_t chunks = (T + kChunkTiles - 1) / kChunkTiles;
+  if (chunks == 0) return hipSuccess;
+  const uint32_t rblocks = (ctiles + 15) / 16;
+  if (x_dtype == 1)
+    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, x, ctiles, ws, xt);
+  else
+    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, x, ctiles, ws, xt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const GemvArgs g{xt, ctiles, tp};
+  hipLaunchKernelGGL((decode_kernel<1, true>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, nullptr, ws, g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemv_rows_kernel, dim3((uint32_t)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, tp,
+                     rows, ctiles, ws, y);
   return hipGetLastError();
 }
 

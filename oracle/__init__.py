@@ -74,6 +74,7 @@ def lib():
         L.hqo_encode_layout.argtypes = [u64, i32, i32, P, P, P]
         L.hqo_encode.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, u64, P, P]
         L.hqo_decode.argtypes = [P, u64, u64, P, i32]
+        L.hqo_decode_coords.argtypes = [P, u64, u64, P]
         _lib = L
     return _lib
 
@@ -270,6 +271,39 @@ def decode(stream, n: int, out_dtype: str = "f32"):
         code = 1
     _check(lib().hqo_decode(_p(s), s.size, n, _p(out), code), "decode")
     return out
+
+
+def decode_coords(stream, n: int) -> np.ndarray:
+    """yhat = (c - U) * (s * step) per value, binary64: the exact reconstruction of tile t is
+    D H yhat_t / 128."""
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(n, dtype=np.float64)
+    _check(lib().hqo_decode_coords(_p(s), s.size, n, _p(out)), "decode_coords")
+    return out
+
+
+def hadamard128() -> np.ndarray:
+    """Sylvester H_128 = H_2 (x) ... (x) H_2, entries +-1 (natural order)."""
+    h = np.array([[1.0]])
+    for _ in range(7):
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def gemv_reference(stream, rows: int, cols: int, x: np.ndarray, seed: int):
+    """Matrix-vector product with the decoded [rows][cols] matrix (tiles of 128 along cols), in
+    binary64, by the plain definition: W_hat = D H yhat / 128 per tile, y = W_hat x.
+    Also returns, per row, B_r = sum over the row's tiles of sum_i |yhat_i| * ||x_tile||_1, the
+    scale of the rounding error of any binary32 evaluation that rotates x per tile."""
+    n = rows * cols
+    yh = decode_coords(stream, n).reshape(rows, cols // 128, 128)
+    d = signs(seed).astype(np.float64)
+    h = hadamard128()
+    w = (yh @ h.T) * d / 128.0          # row-major tiles: w[r, j, :] = D H yhat[r, j, :] / 128
+    xf = np.asarray(x, dtype=np.float64).reshape(cols // 128, 128)
+    y = np.einsum("rji,ji->r", w, xf)
+    bound = np.einsum("rji,j->r", np.abs(yh), np.abs(xf).sum(axis=1))
+    return y, bound
 
 
 def decode_status(stream, n: int) -> int:

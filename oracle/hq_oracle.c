@@ -877,7 +877,11 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
 
 /* Full decoder: validates the header and every chunk, then reconstructs.  out_dtype 0 = fp32,
  * 1 = bf16 (round to nearest even). */
-int hqo_decode(const uint8_t *s, uint64_t bytes, uint64_t n, void *out, int out_dtype) {
+/* Stream reader shared by the decoders below: validates the header and index, and hands every tile's
+ * integer codes and scale bits to `sink` in tile order (format v1, see hqo_encode_layout). */
+typedef void (*tile_sink)(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step);
+
+static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink sink, void *ctx) {
   if (bytes < HEADER_BYTES) return ERR_CORRUPT;
   if (get_u32(s) != MAGIC || get_u16(s + 4) != VERSION) return ERR_CORRUPT;
   int lattice = s[6], dither = s[7] & 1, k = s[10];
@@ -928,17 +932,50 @@ int hqo_decode(const uint8_t *s, uint64_t bytes, uint64_t n, void *out, int out_
         int cos = lattice == LAT_E8 ? get_bit(fixed, coset_pos + (uint64_t)o) : 0;
         hqo_unstrip_octet(lattice, sym, cos, code + 8 * o);
       }
-      float xt[TILE];
-      dequantize_tile(&q, t, code, sb, st, xt);
-      if (out_dtype == 0) {
-        memcpy((float *)out + t * TILE, xt, sizeof(xt));
-      } else {
-        uint16_t *o16 = (uint16_t *)out + t * TILE;
-        for (int i = 0; i < TILE; ++i) o16[i] = f32_to_bf16_rne(xt[i]);
-      }
+      sink(ctx, &q, t, code, sb, st);
     }
     /* the rest of the segment must be padding */
     while (upos < uend) { if (get_bit(unary, upos)) return ERR_CORRUPT; ++upos; }
   }
   return OK;
+}
+
+typedef struct { void *out; int out_dtype; } decode_ctx;
+
+static void decode_sink(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step) {
+  const decode_ctx *d = (const decode_ctx *)ctx;
+  float xt[TILE];
+  dequantize_tile(q, t, code, sb, step, xt);
+  if (d->out_dtype == 0) {
+    memcpy((float *)d->out + t * TILE, xt, sizeof(xt));
+  } else {
+    uint16_t *o16 = (uint16_t *)d->out + t * TILE;
+    for (int i = 0; i < TILE; ++i) o16[i] = f32_to_bf16_rne(xt[i]);
+  }
+}
+
+int hqo_decode(const uint8_t *s, uint64_t bytes, uint64_t n, void *out, int out_dtype) {
+  decode_ctx d = {out, out_dtype};
+  return read_stream(s, bytes, n, decode_sink, &d);
+}
+
+/* The decoder's values before the inverse transform, in binary64: yhat_i = (c_i - U_i) * t with
+ * t = s * step the binary32 product both sides use (dequantize_tile), so that the exact
+ * reconstruction of tile t is D H yhat / 128.  Test infrastructure for products with the decoded
+ * matrix (the fused decode + matrix-vector product). */
+static void coords_sink(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step) {
+  double *out = (double *)ctx + t * TILE;
+  const float tsc = bf16_to_f32(sb) * step;
+  for (int o = 0; o < 16; ++o) {
+    float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
+    for (int i = 0; i < 8; ++i) {
+      const double c = (double)code_to_coord(q->lattice, code[8 * o + i]);
+      out[8 * o + i] = (c - (double)u[i]) * (double)tsc;
+    }
+  }
+}
+
+int hqo_decode_coords(const uint8_t *s, uint64_t bytes, uint64_t n, double *yhat) {
+  return read_stream(s, bytes, n, coords_sink, yhat);
 }

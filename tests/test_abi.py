@@ -109,3 +109,26 @@ def test_product_package_does_not_import_oracle():
     assert "import oracle" not in src and "from oracle" not in src
     for f in os.listdir(os.path.join(ROOT, "kv_quantization_tile_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "kv_quantization_tile_amd", "csrc", f)).read().lower(), f
+
+
+def test_gemv_rejects_bad_args_on_host():
+    L = hq.lib()
+    sz = ctypes.c_size_t(0)
+    assert L.hq_gemv_workspace_size(4, 100, ctypes.byref(sz)) == hq.HQ_ERR_INVALID_ARG   # cols % 128
+    assert L.hq_gemv_workspace_size(4, 1024, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_gemv_workspace_size(4, 1024, ctypes.byref(sz)) == hq.HQ_OK
+    assert sz.value == 4096 + 4096 + 256  # header, 1024 rotated values, 32 tile partials (aligned)
+    ws, big = ctypes.c_void_p(1 << 21), 1 << 20
+    args = dict(s=ctypes.c_void_p(1 << 20), rows=4, cols=1024, x=ctypes.c_void_p(1 << 22), dt=0,
+                y=ctypes.c_void_p(1 << 23), ws=ws, wsb=big)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.hq_gemv(a["s"], 4096, a["rows"], a["cols"], a["x"], a["dt"], a["y"], a["ws"], a["wsb"], None)
+    assert call(cols=1000) == hq.HQ_ERR_INVALID_ARG
+    assert call(dt=5) == hq.HQ_ERR_INVALID_ARG
+    assert call(s=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(x=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(y=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(wsb=16) == hq.HQ_ERR_INVALID_ARG
+    assert call(x=ctypes.c_void_p((1 << 22) + 4)) == hq.HQ_ERR_INVALID_ARG  # misaligned activation
