@@ -149,7 +149,8 @@ int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
  * the row sum adds the tiles in column order, so results are deterministic; they differ from an
  * exact product by rounding only (relative to sum |yhat| |x~|, a few hundred units of 2^-24).
  * Components 1-3 of the HyperQuant technical summary (section "Methodology: the HyperQuant
- * pipeline"); the fused product itself is the summary's future-work direction.  Asynchronous;
+ * pipeline"); fused decode + matrix products are the direction its section "Significance and
+ * claims" names for a wall-clock gain.  Asynchronous;
  * stream validation as for hq_decode, errors through hq_status(workspace). */
 int hq_gemv(const void *stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void *x,
             int32_t x_dtype, float *y, void *workspace, size_t workspace_bytes, hq_stream_t stream);
