@@ -92,9 +92,19 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   return x;
 }
+// N is min(T, kRcSampleTiles): for every tensor of at least that many tiles the divisions are
+// shifts; the stratum width hi - lo is below 2^32, so the pick is a 32-bit remainder.
+static_assert(kRcSampleTiles == 8192, "the stratum bounds below shift by 13");
 __device__ __forceinline__ uint64_t sample_tile(uint64_t i, uint64_t T, uint64_t N) {
-  const uint64_t lo = (i * T) / N, hi = ((i + 1) * T) / N;
-  return lo + (uint64_t)mix32((uint32_t)i) % (hi - lo);
+  uint64_t lo, hi;
+  if (N == kRcSampleTiles) {
+    lo = (i * T) >> 13;
+    hi = ((i + 1) * T) >> 13;
+  } else {
+    lo = (i * T) / N;
+    hi = ((i + 1) * T) / N;
+  }
+  return lo + (uint64_t)(mix32((uint32_t)i) % (uint32_t)(hi - lo));
 }
 
 __host__ __device__ inline int kwin_base(int64_t b) {
@@ -1116,8 +1126,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   const uint32_t nW32 = 2u * (w1 - w0);
   const uint32_t m = (nW32 + kBlock - 1) / kBlock;
   const uint32_t j0 = min((uint32_t)tid * m, nW32), j1 = min(j0 + m, nW32);
+  // segments of up to 1024 words (4 bits per symbol): the run is loaded once, all words at once,
+  // and kept in registers for the scatter
+  const bool small = m <= 4u;
+  uint32_t wd[4] = {0u, 0u, 0u, 0u};
   uint32_t cnt = 0;
-  for (uint32_t j = j0; j < j1; ++j) cnt += (uint32_t)__popc(seg[j]);
+  if (small) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (j0 + (uint32_t)i < j1) wd[i] = seg[j0 + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt += (uint32_t)__popc(wd[i]);
+  } else {
+    for (uint32_t j = j0; j < j1; ++j) cnt += (uint32_t)__popc(seg[j]);
+  }
   const uint32_t incl = wave_incl_scan(cnt);
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
@@ -1129,12 +1151,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
     return;
   }
   uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
-  for (uint32_t j = j0; j < j1; ++j) {
-    uint32_t bits = seg[j];
-    const uint32_t bitbase = j * 32u;
-    while (bits) {
-      s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
-      bits &= bits - 1u;
+  if (small) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t bits = wd[i];
+      const uint32_t bitbase = (j0 + (uint32_t)i) * 32u;
+      while (bits) {
+        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
+        bits &= bits - 1u;
+      }
+    }
+  } else {
+    for (uint32_t j = j0; j < j1; ++j) {
+      uint32_t bits = seg[j];
+      const uint32_t bitbase = j * 32u;
+      while (bits) {
+        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
+        bits &= bits - 1u;
+      }
     }
   }
   __syncthreads();
