@@ -75,6 +75,8 @@ def lib():
         L.hqo_encode.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, u64, P, P]
         L.hqo_decode.argtypes = [P, u64, u64, P, i32]
         L.hqo_decode_coords.argtypes = [P, u64, u64, P]
+        L.hqo_haar_matrix.argtypes = [u64, P]
+        L.hqo_haar_gaussians.argtypes = [u64, P]
         _lib = L
     return _lib
 
@@ -304,6 +306,26 @@ def gemv_reference(stream, rows: int, cols: int, x: np.ndarray, seed: int):
     y = np.einsum("rji,ji->r", w, xf)
     bound = np.einsum("rji,j->r", np.abs(yh), np.abs(xf).sum(axis=1))
     return y, bound
+
+
+def haar_gaussians(seed: int) -> np.ndarray:
+    g = np.zeros(128 * 128, dtype=np.float64)
+    lib().hqo_haar_gaussians(seed, _p(g))
+    return g.reshape(128, 128)
+
+
+def haar_matrix(seed: int) -> np.ndarray:
+    """The per-layer Haar-uniform rotation Q (128 x 128, binary64): G = Q R, diag(R) > 0."""
+    q = np.zeros(128 * 128, dtype=np.float64)
+    lib().hqo_haar_matrix(seed, _p(q))
+    return q.reshape(128, 128)
+
+
+def rotate_reference(x, q: np.ndarray, transpose: bool = False) -> np.ndarray:
+    """y_v = Q x_v (or Q^T x_v) for every 128-value vector v of x, binary64."""
+    xv = np.asarray(x, dtype=np.float64).reshape(-1, 128)
+    m = q.T if transpose else q
+    return (xv @ m.T).reshape(-1)
 
 
 def decode_status(stream, n: int) -> int:

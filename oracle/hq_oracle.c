@@ -273,6 +273,51 @@ void hqo_dither_octet(uint64_t seed, uint64_t tile, int octet, int lattice, floa
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Per-layer Haar-uniform rotation for KV caches (HyperQuant summary, Methodology component 4: the
+ * per-layer rotation is either a full Haar-uniform matrix or the cheap +-1 sign diagonal).  The
+ * pages give no construction; the reading taken is the textbook one: G with independent N(0,1)
+ * entries, G = Q R with the diagonal of R positive, and Q is Haar-distributed on O(128).
+ *   Gaussians: entry e = 128 i + j of G comes from Philox4x32-10 with key = seed and counter
+ *   (e / 4, 0, 0, 2); the call's words w0..w3 give two Box-Muller pairs, u(w) = (w + 1/2) 2^-32,
+ *   r = sqrt(-2 ln u(w0)), (r cos 2 pi u(w1), r sin 2 pi u(w1)), then the same for (w2, w3); entry
+ *   e takes number e mod 4 of those four.  All in binary64.
+ *   Q: modified Gram-Schmidt on the columns of G (which makes the diagonal of R positive directly).
+ * Output: q[128 i + j] = Q[i][j], binary64. */
+static void haar_gaussians(uint64_t seed, double g[TILE * TILE]) {
+  const double two_pi = 6.283185307179586476925286766559;
+  for (uint32_t c = 0; c < TILE * TILE / 4; ++c) {
+    uint32_t ctr[4] = {c, 0u, 0u, 2u}, key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[4];
+    hqo_philox4x32_10(ctr, key, w);
+    for (int pair = 0; pair < 2; ++pair) {
+      double u1 = ((double)w[2 * pair] + 0.5) * 0x1p-32, u2 = ((double)w[2 * pair + 1] + 0.5) * 0x1p-32;
+      double r = sqrt(-2.0 * log(u1));
+      g[4 * c + 2 * pair] = r * cos(two_pi * u2);
+      g[4 * c + 2 * pair + 1] = r * sin(two_pi * u2);
+    }
+  }
+}
+
+void hqo_haar_gaussians(uint64_t seed, double *g) { haar_gaussians(seed, g); }
+
+void hqo_haar_matrix(uint64_t seed, double *q) {
+  double *a = (double *)malloc(sizeof(double) * TILE * TILE);
+  haar_gaussians(seed, a);  /* a[i][j]: column j is the vector being orthonormalised */
+  for (int j = 0; j < TILE; ++j) {
+    for (int p = 0; p < j; ++p) { /* remove the component along the finished column p */
+      double dot = 0.0;
+      for (int i = 0; i < TILE; ++i) dot += a[i * TILE + p] * a[i * TILE + j];
+      for (int i = 0; i < TILE; ++i) a[i * TILE + j] -= dot * a[i * TILE + p];
+    }
+    double nrm = 0.0;
+    for (int i = 0; i < TILE; ++i) nrm += a[i * TILE + j] * a[i * TILE + j];
+    nrm = sqrt(nrm);
+    for (int i = 0; i < TILE; ++i) a[i * TILE + j] /= nrm;
+  }
+  memcpy(q, a, sizeof(double) * TILE * TILE);
+  free(a);
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Bit-stripping (HyperQuant summary, Methodology component 3: bits that lattice membership fixes */
 /* are removed losslessly before coding).  Per octet the integer codes become one raw coset bit   */
 /* (E8 only) and eight symbols in slots 0..7; "halved" slots use Rice width max(k-1, 0).          */
