@@ -31,11 +31,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv"], default="weight",
+    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv", "kv_haar"],
+                    default="weight",
                     help="weight / kv: one tensor, the headline line; sweep: Z, D4 and E8 on the weight; "
                          "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
                          "the 64 (layer, K|V) calls of the KV cache; gemv: fused decode + matrix-vector "
-                         "product on the weight's stream")
+                         "product on the weight's stream; kv_haar: one KV call with the full per-layer "
+                         "Haar rotation before encode and after decode")
     ap.add_argument("--bps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -295,6 +297,91 @@ def gemv_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def kv_haar_bench(args):
+    """One KV call ([8][32768][128] bf16, E8 + dither) with the per-layer Haar-uniform rotation:
+    rotate (MFMA), rate control, encode, decode, rotate back; the rotation kernel's roofline."""
+    import torch
+
+    import kv_quantization_tile_amd as hq
+    import synth
+    dev = torch.device("cuda:0")
+    tb = 2.0 if args.bps is None else args.bps
+    layer, is_v = 0, 0
+    x_host = synth.kv(layer, is_v)
+    n = x_host.size
+    seed = synth.kv_seed(layer, is_v)
+    x = torch.from_numpy(x_host.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(hq.hq_haar_matrix(layer)).to(dev)
+    xr = hq.hq_rotate(x, q)
+    s_ref, _ = hq.hq_encode(xr, "e8", tb, seed=seed, dither=True)
+    out = torch.empty(int(s_ref.numel() * 1.05) + 65536, dtype=torch.uint8, device=dev)
+    ws, ws_dec = hq.workspace(n, dev), hq.workspace(0, dev)
+    yr, y = torch.empty_like(x), torch.empty_like(x)
+
+    def step(ev):
+        ev[0].record()
+        hq.hq_rotate(x, q, out=xr)
+        ev[1].record()
+        hq.hq_rate(xr, "e8", tb, seed=seed, dither=True, ws=ws, blocking=False)
+        hq.hq_encode(xr, "e8", tb, seed=seed, dither=True, step=-1.0, out=out, ws=ws, blocking=False)
+        ev[2].record()
+        hq.hq_decode(out, n, out=yr, ws=ws_dec, check=False)
+        ev[3].record()
+        hq.hq_rotate(yr, q, transpose=True, out=y)
+        ev[4].record()
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for ev in evs:
+        step(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    assert hq.hq_status(ws) == 0 and hq.hq_status(ws_dec) == 0
+    m = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    codec_enc_ms, dec_ms, back_ms = m(1, 2), m(2, 3), m(3, 4)
+    step_ms = t0.elapsed_time(t1) / args.steps
+
+    # the rotation kernel alone, launched back to back over four buffer pairs (512 MiB touched per
+    # round, twice what the on-package cache holds) so every launch reads and writes HBM
+    nb = 4
+    xs = [x.clone() for _ in range(nb)]
+    ys = [torch.empty_like(x) for _ in range(nb)]
+    for i in range(nb):
+        hq.hq_rotate(xs[i], q, out=ys[i])
+    torch.cuda.synchronize()
+    rounds = max(args.steps, 4)
+    t0.record()
+    for _ in range(rounds):
+        for i in range(nb):
+            hq.hq_rotate(xs[i], q, out=ys[i])
+    t1.record()
+    torch.cuda.synchronize()
+    rot_ms = t0.elapsed_time(t1) / (rounds * nb)
+    assert torch.equal(ys[0], xr)
+    del xs, ys
+    rot_alg = 4 * n  # bf16 in + bf16 out
+    achieved = rot_alg / (rot_ms * 1e-3) / 1e9
+    xf, yf = x.float(), y.float()
+    nmse = float(((yf - xf) ** 2).sum() / (xf ** 2).sum())
+    result = {
+        "metric": METRIC + " (KV path with the full per-layer rotation)", "value": round(2 * n / (step_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"kv cache layer 0 K [8][32768][128] bf16, Haar rotation (seed 0) + E8 + dither "
+                               f"{tb:g} bps"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "rotate_kernel",
+                     "alg_bytes_per_launch": rot_alg, "launch_ms": round(rot_ms, 5)},
+        "extra": {"rotate_ms": round(rot_ms, 5), "rate_and_encode_ms": round(codec_enc_ms, 5),
+                  "decode_ms": round(dec_ms, 5), "rotate_back_ms": round(back_ms, 5), "nmse": nmse},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -309,6 +396,9 @@ def main():
         return
     if args.config == "gemv":
         gemv_bench(args)
+        return
+    if args.config == "kv_haar":
+        kv_haar_bench(args)
         return
     import torch
 

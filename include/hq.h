@@ -155,6 +155,22 @@ int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 int hq_gemv(const void *stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void *x,
             int32_t x_dtype, float *y, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 
+/* The per-layer Haar-uniform rotation of a seed (component 4: the full-matrix alternative to the
+ * +-1 sign diagonal), written to q (HOST pointer, 128 * 128 floats, q[128 i + j] = Q[i][j]).
+ * Construction (the pages give none; the textbook one): G with independent N(0,1) entries, entry
+ * e = 128 i + j from Philox4x32-10 with key = seed and counter (e / 4, 0, 0, 2), two Box-Muller
+ * pairs per call (u(w) = (w + 1/2) 2^-32; r = sqrt(-2 ln u(w0)); (r cos 2pi u(w1), r sin 2pi u(w1)),
+ * then (w2, w3)); G = Q R with diag(R) > 0, computed in binary64 and rounded to binary32.
+ * Host only, deterministic. */
+int hq_haar_matrix(uint64_t seed, float *q);
+
+/* y_v = Q x_v (transpose = 0; the rotation before hq_encode) or Q^T x_v (transpose = 1; after
+ * hq_decode) for every 128-value vector v of x.  x, y: DEVICE, n bf16 values each (n % 128 == 0),
+ * 16-byte aligned, may not overlap; q: DEVICE, 128 * 128 binary32 as from hq_haar_matrix.
+ * On MFMA (bf16 inputs, Q split into two bf16 parts, binary32 accumulation); y is rounded to bf16
+ * (nearest even).  Asynchronous on `stream`. */
+int hq_rotate(const void *x, uint64_t n, const float *q, int32_t transpose, void *y, hq_stream_t stream);
+
 /* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
  * E8 codes are twice the lattice point, D4 and Z codes are the point) and per-tile bf16 scale bits
  * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */

@@ -22,7 +22,8 @@ HQ_F32, HQ_BF16 = 0, 1
 LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
-           "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv")
+           "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
+           "hq_haar_matrix", "hq_rotate")
 
 
 class HqParams(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib():
         L.hq_codes.argtypes = [P, i32, u64, P, P, P, P, sz, P]
         L.hq_gemv_workspace_size.argtypes = [u64, u64, ctypes.POINTER(sz)]
         L.hq_gemv.argtypes = [P, u64, u64, u64, P, i32, P, P, sz, P]
+        L.hq_haar_matrix.argtypes = [u64, P]
+        L.hq_rotate.argtypes = [P, u64, P, i32, P, P]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         _lib = L
@@ -220,6 +223,27 @@ def hq_gemv(stream_bytes, rows: int, cols: int, x, y=None, ws=None, stream=None,
     if check:
         _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_gemv")
     return y
+
+
+def hq_haar_matrix(seed: int):
+    """The per-layer Haar-uniform rotation Q of a seed, as a float32 numpy array [128, 128]."""
+    import numpy as np
+    q = np.zeros(128 * 128, dtype=np.float32)
+    _check(lib().hq_haar_matrix(seed, ctypes.c_void_p(q.ctypes.data)), "hq_haar_matrix")
+    return q.reshape(128, 128)
+
+
+def hq_rotate(x, q, transpose: bool = False, out=None, stream=None):
+    """y_v = Q x_v (or Q^T x_v) for the 128-value bf16 vectors of x; q a float32 CUDA tensor [128, 128]."""
+    torch = _torch()
+    assert x.is_cuda and x.is_contiguous() and x.dtype == torch.bfloat16
+    assert q.is_cuda and q.is_contiguous() and q.dtype == torch.float32 and q.numel() == 128 * 128
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().hq_rotate(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(q.data_ptr()),
+                           1 if transpose else 0, ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
+           "hq_rotate")
+    return out
 
 
 def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None,

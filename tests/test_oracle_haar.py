@@ -1,8 +1,10 @@
 """Pins of the per-layer Haar-uniform rotation (HyperQuant summary, Methodology component 4: the full
-Haar-uniform matrix alternative to the +-1 sign diagonal)."""
+Haar-uniform matrix alternative to the +-1 sign diagonal), and agreement of the library's host
+construction (Householder) with the oracle's (Gram-Schmidt)."""
 import numpy as np
 import pytest
 
+import kv_quantization_tile_amd as hq
 
 
 def test_gaussians_look_standard_normal(orc):
@@ -59,3 +61,12 @@ def test_haar_statistics(orc):
     assert abs(qs.var() - 1.0 / 128) < 2e-4
     tr = np.trace(qs, axis1=1, axis2=2)
     assert abs(tr.mean()) < 0.25 and abs(tr.var() - 1.0) < 0.35
+
+
+@pytest.mark.parametrize("seed", [0, 3, 999])
+def test_library_matrix_matches_oracle(orc, seed):
+    """hq_haar_matrix (host code of the library, Householder) equals the oracle's Gram-Schmidt
+    construction of the same definition, to binary32 rounding."""
+    q_lib = hq.hq_haar_matrix(seed).astype(np.float64)
+    q_orc = orc.haar_matrix(seed)
+    assert np.abs(q_lib - q_orc).max() < 2e-7
