@@ -78,15 +78,21 @@ def workload(cfg: str, bps):
                    seed=synth.kv_seed(0, 0), profile=f"kv_8x32768x128_e8_dither_{tb:g}bps"), synth.kv_seed(0, 0)
 
 
-def kernel_source_hash() -> str:
+CODEC_SOURCES = ("csrc/hq_kernels.hip", "csrc/hq_device.h", "csrc/hq_internal.h")
+ROTATE_SOURCES = ("csrc/hq_rotate.hip",)
+
+
+def kernel_source_hash(sources=CODEC_SOURCES) -> str:
+    """Hash of the kernels' sources and the compile flags: counter summaries taken under another
+    hash describe other code."""
     import hashlib
+    from kv_quantization_tile_amd.build import FLAGS
     pkg = os.path.join(ROOT, "kv_quantization_tile_amd")
-    src = b"".join(open(os.path.join(pkg, f), "rb").read() for f in
-                   ("csrc/hq_kernels.hip", "csrc/hq_device.h", "csrc/hq_internal.h", "build.py"))
+    src = b"".join(open(os.path.join(pkg, f), "rb").read() for f in sources) + json.dumps(FLAGS).encode()
     return hashlib.sha256(src).hexdigest()[:16]
 
 
-def profiled_traffic(profile_stem: str, kernel_prefix: str):
+def profiled_traffic(profile_stem: str, kernel_prefix: str, sources=CODEC_SOURCES, namespace: str = "hq::"):
     """HBM bytes per dispatch of the named kernel, from the committed FETCH_SIZE / WRITE_SIZE summary
     of this workload (copy-calibrated); None when there is none or the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", profile_stem + "_hbm_traffic.md")
@@ -95,10 +101,10 @@ def profiled_traffic(profile_stem: str, kernel_prefix: str):
     text = open(path).read()
     blob = text.split("```json", 1)[-1].split("```", 1)[0]
     data = json.loads(blob)
-    if data.get("source_sha256_16") != kernel_source_hash():
+    if data.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     for name, rec in data["kernels"].items():
-        if name.startswith("hq::" + kernel_prefix):
+        if name.startswith(namespace + kernel_prefix):
             return int(rec["traffic_bytes"])
     return None
 
@@ -354,13 +360,15 @@ def kv_haar_bench(args):
         hq.hq_rotate(xs[i], q, out=ys[i])
     torch.cuda.synchronize()
     rounds = max(args.steps, 4)
-    t0.record()
-    for _ in range(rounds):
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(rounds * nb)]
+    for r in range(rounds):
         for i in range(nb):
+            pairs[r * nb + i][0].record()
             hq.hq_rotate(xs[i], q, out=ys[i])
-    t1.record()
+            pairs[r * nb + i][1].record()
     torch.cuda.synchronize()
-    rot_ms = t0.elapsed_time(t1) / (rounds * nb)
+    rot_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
     assert torch.equal(ys[0], xr)
     del xs, ys
     rot_alg = 4 * n  # bf16 in + bf16 out
@@ -374,7 +382,10 @@ def kv_haar_bench(args):
         "config": {"workload": f"kv cache layer 0 K [8][32768][128] bf16, Haar rotation (seed 0) + E8 + dither "
                                f"{tb:g} bps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "rotate_kernel",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("rotate_kv_8x32768x128_bf16", "rotate_kernel", ROTATE_SOURCES,
+                                                 "hq_rot::"),
+                     "kernel": "rotate_kernel",
                      "alg_bytes_per_launch": rot_alg, "launch_ms": round(rot_ms, 5)},
         "extra": {"rotate_ms": round(rot_ms, 5), "rate_and_encode_ms": round(codec_enc_ms, 5),
                   "decode_ms": round(dec_ms, 5), "rotate_back_ms": round(back_ms, 5), "nmse": nmse},
