@@ -20,7 +20,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "hq_oracle.c")
+_SRC = [os.path.join(_HERE, "hq_oracle.c"), os.path.join(_HERE, "srft_oracle.c")]
 _LIB = os.path.join(_HERE, "libhq_oracle.so")
 
 LAT_Z, LAT_D4, LAT_E8 = 0, 1, 2
@@ -33,7 +33,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle into ``oracle/libhq_oracle.so`` with gcc."""
     if force or not os.path.exists(_LIB):
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+               "-Wall", "-Wextra", "-o", _LIB + ".tmp", *_SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -77,6 +77,11 @@ def lib():
         L.hqo_decode_coords.argtypes = [P, u64, u64, P]
         L.hqo_haar_matrix.argtypes = [u64, P]
         L.hqo_haar_gaussians.argtypes = [u64, P]
+        L.hqo_srft_twiddle.argtypes = [u32, u32, P]
+        L.hqo_srft_forward.argtypes = [P, u64, P, P]
+        L.hqo_srft_inverse.argtypes = [P, u64, P]
+        L.hqo_srft_encode.argtypes = [P, i32, u64, u64, P, i32, P, P]
+        L.hqo_srft_decode.argtypes = [P, P, u64, u64, P, i32, P, i32]
         _lib = L
     return _lib
 
@@ -326,6 +331,67 @@ def rotate_reference(x, q: np.ndarray, transpose: bool = False) -> np.ndarray:
     xv = np.asarray(x, dtype=np.float64).reshape(-1, 128)
     m = q.T if transpose else q
     return (xv @ m.T).reshape(-1)
+
+
+# ---------------------------------------------------------------------------------------------
+# SRFT fixed-rate KV codec ("When quantization is free" summary, Methodology 1-3), srft_oracle.c
+
+
+def srft_twiddle(n: int, k: int):
+    cs = np.zeros(2, dtype=np.float32)
+    lib().hqo_srft_twiddle(n, k, _p(cs))
+    return float(cs[0]), float(cs[1])
+
+
+def _lam(lam):
+    if lam is None:
+        return None, None
+    a = np.ascontiguousarray(lam, dtype=np.float32)
+    assert a.size == 128
+    return a, _p(a)
+
+
+def srft_forward(x, seed: int, lam=None) -> np.ndarray:
+    """v = SRFT(x) / lambda of one 128-value vector, binary32."""
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    v = np.zeros(128, dtype=np.float32)
+    la, lp = _lam(lam)
+    assert lib().hqo_srft_forward(_p(xa), seed, lp, _p(v)) == 0
+    return v
+
+
+def srft_inverse(y, seed: int) -> np.ndarray:
+    ya = np.ascontiguousarray(y, dtype=np.float32)
+    x = np.zeros(128, dtype=np.float32)
+    lib().hqo_srft_inverse(_p(ya), seed, _p(x))
+    return x
+
+
+def srft_encode(x, seed: int, bits: int = 4, lam=None):
+    """(codes uint8 [vectors][64 or 128], scales uint16 binary16 bits [vectors][16]) of a bf16 (uint16
+    bits) or float32 array."""
+    xa = np.ascontiguousarray(x).reshape(-1)
+    dtype = 1 if xa.dtype == np.uint16 else 0
+    if dtype == 0:
+        xa = xa.astype(np.float32)
+    n = xa.size
+    nv = n // 128
+    codes = np.zeros((nv, 64 if bits == 4 else 128), dtype=np.uint8)
+    scales = np.zeros((nv, 16), dtype=np.uint16)
+    la, lp = _lam(lam)
+    rc = lib().hqo_srft_encode(_p(xa), dtype, n, seed, lp, bits, _p(codes), _p(scales))
+    assert rc == 0, rc
+    return codes, scales
+
+
+def srft_decode(codes, scales, n: int, seed: int, bits: int = 4, lam=None, out_dtype: str = "bf16"):
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    out = np.zeros(n, dtype=np.uint16 if out_dtype == "bf16" else np.float32)
+    la, lp = _lam(lam)
+    rc = lib().hqo_srft_decode(_p(c), _p(s), n, seed, lp, bits, _p(out), 1 if out_dtype == "bf16" else 0)
+    assert rc == 0, rc
+    return out
 
 
 def decode_status(stream, n: int) -> int:
