@@ -31,13 +31,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv", "kv_haar"],
+    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv", "kv_haar", "srft"],
                     default="weight",
                     help="weight / kv: one tensor, the headline line; sweep: Z, D4 and E8 on the weight; "
                          "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
                          "the 64 (layer, K|V) calls of the KV cache; gemv: fused decode + matrix-vector "
                          "product on the weight's stream; kv_haar: one KV call with the full per-layer "
-                         "Haar rotation before encode and after decode")
+                         "Haar rotation before encode and after decode; srft: the SRFT fixed-rate codec "
+                         "(int4, or int8 with --bps 8) on the KV call")
     ap.add_argument("--bps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -80,6 +81,7 @@ def workload(cfg: str, bps):
 
 CODEC_SOURCES = ("csrc/hq_kernels.hip", "csrc/hq_device.h", "csrc/hq_internal.h")
 ROTATE_SOURCES = ("csrc/hq_rotate.hip",)
+SRFT_SOURCES = ("csrc/hq_srft.hip", "csrc/hq_device.h")
 
 
 def kernel_source_hash(sources=CODEC_SOURCES) -> str:
@@ -393,6 +395,112 @@ def kv_haar_bench(args):
     print(json.dumps(result), flush=True)
 
 
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # binary32 VALU operations per second, packed forms unused
+
+
+def srft_ops_per_vector(bits: int):
+    """Binary32 operations of the SRFT codec's definition per 128-value vector (each add, multiply,
+    division, abs-max, rounding, clamp, conversion counted once; products by the exact twiddles 1 and
+    -+i not counted).  Returns (encode, decode)."""
+    fft = 6 * 32 * 4 + 98 * 6          # 384 complex adds; 98 products by non-trivial twiddles
+    unpack = 2 + 63 * 12                # E, G, W^k (-i G), E + ...
+    enc = 128 + fft + unpack + 128 + 128 + 16 * 3 + 128 * 4 + 128  # signs, multipliers, abs-max,
+    # scale (division, binary16 rounding, reciprocal), codes (multiply, rint, clamp, convert), finiteness
+    dec = 128 * 3 + 16 + (4 + 63 * 12) + fft + 128 * 3 + 128       # dequantise, unpack, FFT, output
+    return enc, dec
+
+
+def srft_bench(args):
+    """The SRFT fixed-rate codec (sign, FFT, Hermitian pack, per-group int4 / int8) on one KV call
+    [8][32768][128] bf16: encode + decode per step, per-launch events, the dominant kernel's ALU
+    roofline, the oracle on the whole tensor as the CPU baseline and parity of codes and decode."""
+    import torch
+
+    import kv_quantization_tile_amd as hq
+    import synth
+    bits = 4 if args.bps is None else int(args.bps)
+    if bits not in (4, 8):
+        raise SystemExit("--config srft takes --bps 4 or 8")
+    dev = torch.device("cuda:0")
+    x_host = synth.kv(0, 0)
+    n = x_host.size
+    nv = n // 128
+    seed = synth.kv_seed(0, 0)
+    x = torch.from_numpy(x_host.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = torch.empty((nv, 64 if bits == 4 else 128), dtype=torch.uint8, device=dev)
+    scales = torch.empty((nv, 16), dtype=torch.int16, device=dev)
+    y = torch.empty_like(x)
+
+    def step(ev):
+        ev[0].record()
+        hq.hq_srft_encode(x, seed=seed, bits=bits, codes=codes, scales=scales)
+        ev[1].record()
+        ev[2].record()
+        hq.hq_srft_decode(codes, scales, n, seed=seed, bits=bits, out=y)
+        ev[3].record()
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for ev in evs:
+        step(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    step_ms = t0.elapsed_time(t1) / args.steps
+    ops_enc, ops_dec = srft_ops_per_vector(bits)
+    code_bytes = nv * (64 if bits == 4 else 128) + nv * 32
+    if enc_ms >= dec_ms:
+        dom, ms, ops, hbm = "srft_encode_kernel", enc_ms, ops_enc * nv, 2 * n + code_bytes
+    else:
+        dom, ms, ops, hbm = "srft_decode_kernel", dec_ms, ops_dec * nv, 2 * n + code_bytes
+    tops = ops / (ms * 1e-3) / 1e12
+    xf = x.float()
+    nmse = float(((y.float() - xf) ** 2).sum() / (xf ** 2).sum())
+    traffic = profiled_traffic(f"srft_kv_8x32768x128_int{bits}", dom, SRFT_SOURCES, "hq_srft::")
+    result = {
+        "metric": "encode+decode GB/s of bf16 input (SRFT fixed-rate codec), 1 GPU", "value": round(2 * n / (step_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"kv cache layer 0 K [8][32768][128] bf16, SRFT int{bits} + 16 binary16 group "
+                               f"scales per vector"},
+        "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TFLOP/s",
+                     "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": traffic, "kernel": dom,
+                     "alg_ops_per_launch": ops, "launch_ms": round(ms, 5),
+                     "hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "extra": {"encode_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5), "nmse": nmse,
+                  "bits_per_value": (64 if bits == 4 else 128) * 8 / 128 + 16 * 16 / 128,
+                  "ops_per_vector_encode": ops_enc, "ops_per_vector_decode": ops_dec},
+    }
+    if not args.no_cpu_baseline or not args.no_parity:
+        import oracle
+        if not os.path.exists(os.path.join(ROOT, "oracle", "libhq_oracle.so")):
+            oracle.build()
+        t1h = time.perf_counter()
+        c_orc, s_orc = oracle.srft_encode(x_host, seed, bits)
+        t2h = time.perf_counter()
+        y_orc = oracle.srft_decode(c_orc, s_orc, n, seed, bits)
+        t3h = time.perf_counter()
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {"value": round(2 * n / (t3h - t1h) / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                      "kind": "oracle",
+                                      "sample": f"the whole workload ({n} values), one encode + one bf16 decode, "
+                                                f"single host thread: encode {t2h - t1h:.2f} s, decode "
+                                                f"{t3h - t2h:.2f} s"}
+        if not args.no_parity:
+            result["extra"]["parity_codes_equal"] = bool(np.array_equal(codes.cpu().numpy(), c_orc))
+            result["extra"]["parity_scales_equal"] = bool(
+                np.array_equal(scales.cpu().numpy().view(np.uint16), s_orc))
+            result["extra"]["parity_decoded_equal"] = bool(
+                np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), y_orc))
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -410,6 +518,9 @@ def main():
         return
     if args.config == "kv_haar":
         kv_haar_bench(args)
+        return
+    if args.config == "srft":
+        srft_bench(args)
         return
     import torch
 

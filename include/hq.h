@@ -171,6 +171,30 @@ int hq_haar_matrix(uint64_t seed, float *q);
  * (nearest even).  Asynchronous on `stream`. */
 int hq_rotate(const void *x, uint64_t n, const float *q, int32_t transpose, void *y, hq_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * SRFT fixed-rate KV codec ("When quantization is free" technical summary,
+ * gist.science/ko/paper/2605.05699, section "Methodology" 1-3): per 128-value vector,
+ * v = pack(F diag(s) x) / lambda with F the unitary DFT, s the sign diagonal of `seed` (the same
+ * signs as the lattice codec's D), pack the orthogonal real form (X_0, X_64, sqrt 2 Re X_1,
+ * sqrt 2 Im X_1, ...), lambda a per-coordinate calibration scale; then 16 groups of 8 coordinates,
+ * scale Delta = binary16(absmax / L) (L = 7 for int4, 127 for int8; nearest even, saturating at
+ * 65504) and codes q = clamp(rint(v * (1 / Delta)), -L, L).  Fixed rate: 4 (or 8) bits per value
+ * plus 16 binary16 scales per vector (96 bytes per vector at int4, 2.67x smaller than bf16).
+ *
+ * codes: DEVICE, n / 2 bytes (bits = 4: codes 2j and 2j + 1 of a vector in the low and high nibble
+ * of its byte j, two's complement) or n bytes (bits = 8, int8); scales: DEVICE, n / 128 * 16
+ * binary16 values (vector-major).  x / out: DEVICE, n values of `dtype` / `out_dtype` (HQ_F32 or
+ * HQ_BF16), n % 128 == 0.  All device pointers 16-byte aligned.  lambda: HOST, 128 binary32 values,
+ * each finite and > 0 (HQ_ERR_INVALID_ARG otherwise), or NULL for all ones; encoder and decoder
+ * must be given the same lambda and seed.  A vector whose packed coordinates are not all finite is
+ * stored with zero codes and NaN (0x7E00) scales and decodes to NaN.  Decode outputs bf16 rounded
+ * to nearest even (or binary32), exact zeros as +0.  Both calls are asynchronous on `stream`, use
+ * no workspace and allocate nothing. */
+int hq_srft_encode(const void *x, int32_t dtype, uint64_t n, uint64_t seed, const float *lambda, int32_t bits,
+                   void *codes, void *scales, hq_stream_t stream);
+int hq_srft_decode(const void *codes, const void *scales, uint64_t n, uint64_t seed, const float *lambda,
+                   int32_t bits, void *out, int32_t out_dtype, hq_stream_t stream);
+
 /* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
  * E8 codes are twice the lattice point, D4 and Z codes are the point) and per-tile bf16 scale bits
  * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */

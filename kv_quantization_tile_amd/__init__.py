@@ -23,7 +23,7 @@ LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
            "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
-           "hq_haar_matrix", "hq_rotate")
+           "hq_haar_matrix", "hq_rotate", "hq_srft_encode", "hq_srft_decode")
 
 
 class HqParams(ctypes.Structure):
@@ -72,6 +72,8 @@ def lib():
         L.hq_gemv.argtypes = [P, u64, u64, u64, P, i32, P, P, sz, P]
         L.hq_haar_matrix.argtypes = [u64, P]
         L.hq_rotate.argtypes = [P, u64, P, i32, P, P]
+        L.hq_srft_encode.argtypes = [P, i32, u64, u64, P, i32, P, P, P]
+        L.hq_srft_decode.argtypes = [P, P, u64, u64, P, i32, P, i32, P]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         _lib = L
@@ -243,6 +245,48 @@ def hq_rotate(x, q, transpose: bool = False, out=None, stream=None):
     _check(lib().hq_rotate(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(q.data_ptr()),
                            1 if transpose else 0, ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
            "hq_rotate")
+    return out
+
+
+def _host_lambda(lam):
+    import numpy as np
+    if lam is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(lam, dtype=np.float32).reshape(-1))
+    if a.size != 128:
+        raise ValueError("lambda holds one scale per coordinate: 128 values")
+    return a, ctypes.c_void_p(a.ctypes.data)
+
+
+def hq_srft_encode(x, seed: int = 0, bits: int = 4, lam=None, codes=None, scales=None, stream=None):
+    """SRFT fixed-rate codes of x (bf16 or float32 CUDA tensor, numel % 128 == 0): returns (codes
+    uint8 [vectors][64 | 128], scales int16 view of binary16 [vectors][16]).  lam: 128 host floats."""
+    torch = _torch()
+    assert x.is_cuda and x.is_contiguous()
+    n = x.numel()
+    nv = n // 128
+    if codes is None:
+        codes = torch.empty((nv, 64 if bits == 4 else 128), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((nv, 16), dtype=torch.int16, device=x.device)
+    keep, lp = _host_lambda(lam)
+    _check(lib().hq_srft_encode(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, int(seed), lp, int(bits),
+                                ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                _stream_handle(stream)), "hq_srft_encode")
+    return codes, scales
+
+
+def hq_srft_decode(codes, scales, n: int, seed: int = 0, bits: int = 4, lam=None, out=None,
+                   out_dtype=None, stream=None):
+    """Decode n values from SRFT codes and scales (CUDA tensors) into bf16 (default) or float32."""
+    torch = _torch()
+    assert codes.is_cuda and scales.is_cuda and codes.is_contiguous() and scales.is_contiguous()
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype or torch.bfloat16, device=codes.device)
+    keep, lp = _host_lambda(lam)
+    _check(lib().hq_srft_decode(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), n,
+                                int(seed), lp, int(bits), ctypes.c_void_p(out.data_ptr()), _dtype_code(out),
+                                _stream_handle(stream)), "hq_srft_decode")
     return out
 
 

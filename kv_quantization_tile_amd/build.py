@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhq.so")
-SOURCES = ["hq_kernels.hip", "hq_api.hip", "hq_rotate.hip"]
+SOURCES = ["hq_kernels.hip", "hq_api.hip", "hq_rotate.hip", "hq_srft.hip"]
 
 # Floating-point flags: every binary32 operation that decides an integer code must be rounded
 # exactly once in program order (no contraction into FMA, no fast-math, denormals kept, correctly

@@ -132,3 +132,25 @@ def test_gemv_rejects_bad_args_on_host():
     assert call(y=None) == hq.HQ_ERR_INVALID_ARG
     assert call(wsb=16) == hq.HQ_ERR_INVALID_ARG
     assert call(x=ctypes.c_void_p((1 << 22) + 4)) == hq.HQ_ERR_INVALID_ARG  # misaligned activation
+
+
+def test_srft_rejects_bad_args_on_host():
+    L = hq.lib()
+    P = ctypes.c_void_p
+    ok = P(1 << 20)
+    lam_bad = (ctypes.c_float * 128)(*([1.0] * 127 + [-1.0]))
+    lam_nan = (ctypes.c_float * 128)(*([1.0] * 127 + [float("nan")]))
+    E = hq.HQ_ERR_INVALID_ARG
+    assert L.hq_srft_encode(ok, 1, 100, 0, None, 4, ok, ok, None) == E           # n % 128
+    assert L.hq_srft_encode(ok, 2, 128, 0, None, 4, ok, ok, None) == E           # dtype
+    assert L.hq_srft_encode(ok, 1, 128, 0, None, 5, ok, ok, None) == E           # bits
+    assert L.hq_srft_encode(None, 1, 128, 0, None, 4, ok, ok, None) == E         # null
+    assert L.hq_srft_encode(P((1 << 20) + 8), 1, 128, 0, None, 4, ok, ok, None) == E  # alignment
+    assert L.hq_srft_encode(ok, 1, 128, 0, lam_bad, 4, ok, ok, None) == E        # lambda <= 0
+    assert L.hq_srft_encode(ok, 1, 128, 0, lam_nan, 4, ok, ok, None) == E        # lambda NaN
+    assert L.hq_srft_encode(ok, 1, 0, 0, None, 4, None, None, None) == hq.HQ_OK  # empty: nothing to do
+    assert L.hq_srft_decode(ok, ok, 100, 0, None, 4, ok, 1, None) == E
+    assert L.hq_srft_decode(ok, ok, 128, 0, None, 8, ok, 3, None) == E           # out dtype
+    assert L.hq_srft_decode(ok, None, 128, 0, None, 4, ok, 1, None) == E
+    assert L.hq_srft_decode(ok, ok, 128, 0, lam_bad, 4, ok, 1, None) == E
+    assert L.hq_srft_decode(None, None, 0, 0, None, 4, None, 1, None) == hq.HQ_OK
