@@ -274,11 +274,13 @@ __global__ __launch_bounds__(kBlock) void srft_decode_kernel(const uint8_t* __re
                                                              const uint16_t* __restrict__ scales, uint64_t nvec,
                                                              uint64_t seed, Consts K, void* __restrict__ out,
                                                              int f32_out) {
+  // every thread stays to the end (the bf16 store goes through LDS with workgroup barriers); a
+  // thread past the last vector decodes the last vector again and stores nothing
   const uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (v >= nvec) return;
+  const uint64_t vl = v < nvec ? v : nvec - 1;
   constexpr int kWords = BITS == 4 ? 16 : 32;
   uint32_t cw[kWords];
-  const uint4* csrc = reinterpret_cast<const uint4*>(codes + v * (BITS == 4 ? kD / 2 : kD));
+  const uint4* csrc = reinterpret_cast<const uint4*>(codes + vl * (BITS == 4 ? kD / 2 : kD));
 #pragma unroll
   for (int i = 0; i < kWords / 4; ++i) {
     const uint4 u = csrc[i];
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(kBlock) void srft_decode_kernel(const uint8_t* __re
     cw[4 * i + 2] = u.z;
     cw[4 * i + 3] = u.w;
   }
-  const uint4* ssrc = reinterpret_cast<const uint4*>(scales + v * kGroups);
+  const uint4* ssrc = reinterpret_cast<const uint4*>(scales + vl * kGroups);
   const uint4 s0 = ssrc[0], s1 = ssrc[1];
   const uint32_t sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   // y_c = (q_c Delta_g) lambda_c, formed where the unpack needs it
@@ -334,10 +336,30 @@ __global__ __launch_bounds__(kBlock) void srft_decode_kernel(const uint8_t* __re
       // v_cvt_pk_bf16_f32: round to nearest even (a NaN stays a NaN)
       ow[n] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
     }
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + v * kD);
+    // Through LDS, half a vector (128 bytes) per row and 64 rows per wavefront, so that each store
+    // instruction writes 8 whole 128-byte lines; row r's 16-byte chunk c sits at slot c ^ (r & 7).
+    __shared__ uint4 s_out[kBlock / 64][64 * 8];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint64_t wbase = (uint64_t)blockIdx.x * kBlock + (uint64_t)wv * 64;
+    uint4* dst = reinterpret_cast<uint4*>(out);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dst[i] = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int w = 32 * h + 4 * c;
+        s_out[wv][lane * 8 + (c ^ (lane & 7))] = make_uint4(ow[w], ow[w + 1], ow[w + 2], ow[w + 3]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const uint64_t vec = wbase + (uint64_t)r;
+        if (vec < nvec) dst[vec * 16 + 8 * h + c] = s_out[wv][r * 8 + (c ^ (r & 7))];
+      }
+      __syncthreads();
+    }
   } else {
+    if (v >= nvec) return;
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + v * kD);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
