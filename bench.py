@@ -112,8 +112,8 @@ def profiled_traffic(profile_stem: str, kernel_prefix: str, sources=CODEC_SOURCE
 
 
 def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=None, ws_dec=None, y=None):
-    """Events around rate control, encode and decode of one device tensor (steps timed, warmup
-    untimed).  Returns per-step means (ms), the stream header and the decoded tensor."""
+    """Events around encode (with rate control) and decode of one device tensor (steps timed,
+    warmup untimed).  Returns per-step means (ms), the stream header and the decoded tensor."""
     dev = x.device
     n = x.numel()
     if out is None:
@@ -126,33 +126,37 @@ def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=N
     stream = torch.cuda.current_stream()
 
     def one():
-        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(stream)
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e2.record(stream)
         hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
-        return e1, e2
+        return e1
 
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+        hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
     ev = []
     for _ in range(steps):
         e0 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        e1, e2 = one()
-        e3 = torch.cuda.Event(enable_timing=True)
-        e3.record(stream)
-        ev.append((e0, e1, e2, e3))
+        e1 = one()
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        ev.append((e0, e1, e2))
     torch.cuda.synchronize()
     st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
-    r = {"rate_ms": float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev])),
-         "encode_ms": float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev])),
-         "decode_ms": float(np.mean([c.elapsed_time(d) for _, _, c, d in ev])),
-         "step_ms": float(np.mean([a.elapsed_time(d) for a, _, _, d in ev]))}
+    r = {"encode_ms": float(np.mean([a.elapsed_time(b) for a, b, _ in ev])),
+         "decode_ms": float(np.mean([b.elapsed_time(c) for _, b, c in ev])),
+         "step_ms": step_ms}
     return r, hq.header_fields(out[:128].cpu().numpy()), y
 
 
@@ -211,7 +215,7 @@ def series(args):
                     f"drawn on the GPU one call at a time, E8 + dither {tb:g} bps, per-layer seed (l<<1)|isV")
         steps, warmup = 1, 1
     total_in = 0
-    tot = {"rate_ms": 0.0, "encode_ms": 0.0, "decode_ms": 0.0, "step_ms": 0.0}
+    tot = {"encode_ms": 0.0, "decode_ms": 0.0, "step_ms": 0.0}
     per = {}
     worst_rate_err = 0.0
     enc_alg = 0
@@ -241,7 +245,7 @@ def series(args):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload, "items": len(items), "input_bytes": total_in},
         "roofline": {"bound": "hbm", "achieved": round(enc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(enc_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "encode_kernel",
+                     "frac": round(enc_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "rate passes + encode_kernel",
                      "alg_bytes_per_launch": enc_alg // len(items), "launch_ms": round(tot["encode_ms"] / len(items), 5)},
         "extra": {**{k: round(v, 4) for k, v in tot.items()}, "worst_payload_rate_error_bps": round(worst_rate_err, 5),
                   **({"per_lattice": per} if per else {})},
@@ -327,31 +331,35 @@ def kv_haar_bench(args):
     yr, y = torch.empty_like(x), torch.empty_like(x)
 
     def step(ev):
-        ev[0].record()
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
         hq.hq_rotate(x, q, out=xr)
-        ev[1].record()
-        hq.hq_rate(xr, "e8", tb, seed=seed, dither=True, ws=ws, blocking=False)
-        hq.hq_encode(xr, "e8", tb, seed=seed, dither=True, step=-1.0, out=out, ws=ws, blocking=False)
-        ev[2].record()
+        rec(1)
+        hq.hq_encode(xr, "e8", tb, seed=seed, dither=True, out=out, ws=ws, blocking=False)
+        rec(2)
         hq.hq_decode(out, n, out=yr, ws=ws_dec, check=False)
-        ev[3].record()
+        rec(3)
         hq.hq_rotate(yr, q, transpose=True, out=y)
-        ev[4].record()
+        rec(4)
 
     for _ in range(args.warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: steps back to back, events only at its ends; then a breakdown loop
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
+    for _ in range(args.steps):
+        step(None)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for ev in evs:
         step(ev)
-    t1.record()
     torch.cuda.synchronize()
     assert hq.hq_status(ws) == 0 and hq.hq_status(ws_dec) == 0
     m = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
     codec_enc_ms, dec_ms, back_ms = m(1, 2), m(2, 3), m(3, 4)
-    step_ms = t0.elapsed_time(t1) / args.steps
 
     # the rotation kernel alone, launched back to back over four buffer pairs (512 MiB touched per
     # round, twice what the on-package cache holds) so every launch reads and writes HBM
@@ -432,26 +440,31 @@ def srft_bench(args):
     y = torch.empty_like(x)
 
     def step(ev):
-        ev[0].record()
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
         hq.hq_srft_encode(x, seed=seed, bits=bits, codes=codes, scales=scales)
-        ev[1].record()
-        ev[2].record()
+        rec(1)
+        rec(2)
         hq.hq_srft_decode(codes, scales, n, seed=seed, bits=bits, out=y)
-        ev[3].record()
+        rec(3)
 
     for _ in range(args.warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        step(None)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: steps back to back, events only at its ends; then a breakdown loop
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
+    for _ in range(args.steps):
+        step(None)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for ev in evs:
         step(ev)
-    t1.record()
     torch.cuda.synchronize()
     enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    step_ms = t0.elapsed_time(t1) / args.steps
     ops_enc, ops_dec = srft_ops_per_vector(bits)
     code_bytes = nv * (64 if bits == 4 else 128) + nv * 32
     if enc_ms >= dec_ms:
@@ -542,43 +555,70 @@ def main():
     y = torch.empty(n, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    # one step = rate control, encode and decode; the encode is issued as an asynchronous hq_rate
-    # followed by hq_encode at the operating point it chose (exactly the kernels of one hq_encode
-    # with rate control), so that events can bracket the encode kernel alone
-    def rate():
-        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
-
+    # one step = hq_encode with rate control (two sample passes, then the encode kernel, whose
+    # workgroup 0 solves the second pass) and hq_decode
     def encode():
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
 
     def decode():
         hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
 
+    # the encode kernel alone, for its roofline: an asynchronous hq_rate leaves the operating point
+    # (its passes and a one-workgroup solve), and hq_encode at that point launches only the kernel
+    def rate():
+        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
+
+    def encode_at_point():
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
+
     for _ in range(args.warmup):
-        rate(); encode(); decode()
+        encode(); decode()
+        rate(); encode_at_point()
     torch.cuda.synchronize()
 
+    # the timed region: K steps back to back, events only at its two ends (an event recorded
+    # between two kernels delays the second by several microseconds)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
-        rate()
-        ev[i][1].record(stream)
         encode()
-        ev[i][2].record(stream)
         decode()
-        ev[i][3].record(stream)
+    t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rate_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
-    enc_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
-    dec_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
-    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]))
+    step_ms = t_start.elapsed_time(t_end) / K
     st = hq.hq_status(ws)
     st2 = hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
+    g_step = out[:128].clone()
+
+    # breakdown (separate loops): encode with rate control, decode, the encode kernel alone
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        encode()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    enc_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    dec_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+
+    ek = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ek[i][0].record(stream)
+        rate()
+        ek[i][1].record(stream)
+        encode_at_point()
+        ek[i][2].record(stream)
+    torch.cuda.synchronize()
+    assert hq.hq_status(ws) == 0
+    rate_ms = float(np.mean([ek[i][0].elapsed_time(ek[i][1]) for i in range(K)]))
+    enc_kernel_ms = float(np.mean([ek[i][1].elapsed_time(ek[i][2]) for i in range(K)]))
+    assert torch.equal(out[:128], g_step), "hq_rate + hq_encode(step=-1) differs from hq_encode"
 
     hdr = hq.header_fields(out[:128].cpu().numpy())
     total_bytes = hdr["total_bytes"]
@@ -591,10 +631,10 @@ def main():
     # check launch, which makes the decode figure slightly conservative)
     dec_alg = total_bytes + input_bytes
     enc_alg = input_bytes + total_bytes
-    if dec_ms >= enc_ms:
+    if dec_ms >= enc_kernel_ms:
         dom, dom_ms, dom_bytes = "decode_kernel", dec_ms, dec_alg
     else:
-        dom, dom_ms, dom_bytes = "encode_kernel", enc_ms, enc_alg
+        dom, dom_ms, dom_bytes = "encode_kernel", enc_kernel_ms, enc_alg
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = profiled_traffic(profile_stem, dom)
 
@@ -619,9 +659,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                      "alg_bytes_per_launch": dom_bytes, "launch_ms": round(dom_ms, 5)},
-        "extra": {"rate_control_ms": round(rate_ms, 5), "encode_ms": round(enc_ms, 5),
-                  "decode_ms": round(dec_ms, 5),
-                  "encode_kernel_gbs": round(enc_alg / (enc_ms * 1e-3) / 1e9, 1),
+        "extra": {"encode_with_rate_control_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5),
+                  "encode_kernel_ms": round(enc_kernel_ms, 5), "hq_rate_alone_ms": round(rate_ms, 5),
+                  "encode_kernel_gbs": round(enc_alg / (enc_kernel_ms * 1e-3) / 1e9, 1),
                   "decode_kernel_gbs": round(dec_alg / (dec_ms * 1e-3) / 1e9, 1),
                   "step_alg_bytes": alg_step,
                   "step_hbm_gbs": round(alg_step / (step_ms * 1e-3) / 1e9, 1),

@@ -109,7 +109,8 @@ int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t 
  * params->target_bps.  With info != NULL the call blocks and fills info (payload_bps is the target);
  * with info == NULL it only enqueues work, and a following hq_encode with params->step == -1 on the
  * same workspace and stream encodes at the chosen point (the pair then does exactly what one
- * hq_encode with rate control does). */
+ * hq_encode with rate control does).  x must be 16-byte aligned and the workspace 256-byte aligned
+ * (HQ_ERR_INVALID_ARG otherwise), as for hq_encode. */
 int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, hq_info *info,
             void *workspace, size_t workspace_bytes, hq_stream_t stream);
 

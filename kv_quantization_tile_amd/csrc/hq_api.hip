@@ -189,6 +189,7 @@ int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, h
   if (rc) return rc;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < workspace_bytes_for(n) || (n && !x)) return HQ_ERR_INVALID_ARG;
+  if (((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   if (params->step == -1.0f) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
   rc = run_rate_control(a);

@@ -86,6 +86,16 @@ def test_rate_rejects_workspace_step_sentinel_on_host():
                             1 << 20, None) == hq.HQ_ERR_INVALID_ARG
 
 
+def test_rate_rejects_misaligned_buffers_on_host():
+    # the rate passes read the input with 16-byte loads and the workspace is 256-byte aligned
+    p = hq.make_params("e8", 4.0)
+    L = hq.lib()
+    assert L.hq_rate(ctypes.c_void_p((1 << 20) + 8), 1, 128, ctypes.byref(p), None, ctypes.c_void_p(1 << 21),
+                     1 << 20, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_rate(ctypes.c_void_p(1 << 20), 1, 128, ctypes.byref(p), None, ctypes.c_void_p((1 << 21) + 64),
+                     1 << 20, None) == hq.HQ_ERR_INVALID_ARG
+
+
 def test_decode_and_codes_reject_bad_args_on_host():
     L = hq.lib()
     assert L.hq_decode(ctypes.c_void_p(1 << 20), 4096, ctypes.c_void_p(1 << 20), 1, 100,
