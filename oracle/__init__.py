@@ -23,8 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = [os.path.join(_HERE, "hq_oracle.c"), os.path.join(_HERE, "srft_oracle.c")]
 _LIB = os.path.join(_HERE, "libhq_oracle.so")
 
-LAT_Z, LAT_D4, LAT_E8 = 0, 1, 2
-LATTICES = {"z": LAT_Z, "d4": LAT_D4, "e8": LAT_E8}
+LAT_Z, LAT_D4, LAT_E8, LAT_A2 = 0, 1, 2, 3
+LATTICES = {"z": LAT_Z, "d4": LAT_D4, "e8": LAT_E8, "a2": LAT_A2}
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NONFINITE, ERR_CAPACITY, ERR_CORRUPT, ERR_RATE = (
     0, -1, -2, -3, -4, -5, -6)
 

@@ -8,7 +8,8 @@
  * What it computes follows the HyperQuant technical summaries (gist.science/ko/paper/2606.23406 and
  * gist.science/ja/paper/2606.23406), section "Methodology: the HyperQuant pipeline":
  *   component 1 (per-tile randomized Hadamard transform  RHT_n(x) = H_n D x, tiles of 128),
- *   component 2 (nearest-point quantisation onto E8 / D4 / Z with an integer embedding and a scale),
+ *   component 2 (nearest-point quantisation onto E8 / D4 / A2 / Z with an integer embedding and a
+ *   scale),
  *   component 3 (bit-stripping of lattice-fixed bits, then Rice coding; rate within ~0.01 bps),
  *   component 4 (KV bias correction: per-layer +-1 rotation, subtractive dither U ~ Unif(V(L))).
  * Where the pages leave a step open (butterfly order, scale rounding, tie breaks, bit layout,
@@ -34,7 +35,11 @@
 #define MAGIC 0x31305148u /* bytes 'H' 'Q' '0' '1' */
 #define VERSION 1
 
-enum { LAT_Z = 0, LAT_D4 = 1, LAT_E8 = 2 };
+enum { LAT_Z = 0, LAT_D4 = 1, LAT_E8 = 2, LAT_A2 = 3 };
+
+/* A2 works in coordinates where the second coordinate of each pair is divided by sqrt 3 (see
+ * a2_nearest): R3 is binary32 sqrt(3) rounded to nearest, 0x3FDDB3D7. */
+#define A2_R3_BITS 0x3FDDB3D7u
 enum {
   OK = 0,
   ERR_INVALID_ARG = -1,
@@ -219,8 +224,36 @@ static void e8_nearest(const float v[8], int32_t z[8]) {
   }
 }
 
+/* A2, the hexagonal lattice (the summary's 2-dimensional lattice), with minimal distance 1:
+ *   A2 = (Z x sqrt3 Z)  u  ((Z + 1/2) x (sqrt3 Z + sqrt3/2)),
+ * the union of a rectangular lattice and its shift by a deep hole.  Reading: a pair (v0, v1) is
+ * quantised in "stretched" coordinates w = (v0, v1 / sqrt 3), where the lattice is
+ * Z^2 u (Z + 1/2)^2 and the squared distance is dw0^2 + 3 dw1^2; the codec's scaling folds the
+ * 1/sqrt 3 into the multiplier of odd slots (quantize_tile), so the input here is w.  Candidate A
+ * rounds both coordinates (r = rint w, a = |w - r|), candidate B is the nearest point of the shifted
+ * set, at distance 1/2 - a_i per coordinate.  Then
+ *   |w-A|^2 - |w-B|^2 = a0^2 + 3 a1^2 - (1/2 - a0)^2 - 3 (1/2 - a1)^2 = a0 + 3 a1 - 1,
+ * and A is kept iff fl(a0 + 3 a1) <= 1, the sum formed by one fused multiply-add (one rounding).
+ * Integer code: z = 2c (the lattice point in stretched coordinates is z/2), so z0 = z1 (mod 2). */
+static void a2_nearest(const float w[2], int32_t z[2]) {
+  float r[2], a[2];
+  int sgn[2];
+  for (int i = 0; i < 2; ++i) {
+    r[i] = rintf(w[i]);
+    float e = w[i] - r[i];
+    a[i] = fabsf(e);
+    sgn[i] = signbit(e) ? -1 : 1;
+  }
+  if (fmaf(3.0f, a[1], a[0]) <= 1.0f) {
+    for (int i = 0; i < 2; ++i) z[i] = 2 * (int32_t)r[i];
+  } else {
+    for (int i = 0; i < 2; ++i) z[i] = 2 * (int32_t)r[i] + sgn[i];
+  }
+}
+
 /* Nearest point for one octet (8 consecutive coordinates) under `lattice`.  Output integer codes:
- * Z: z_i = rint(v_i);  D4: two D4 points;  E8: z in 2*E8 (the lattice point is z/2). */
+ * Z: z_i = rint(v_i);  D4: two D4 points;  E8: z in 2*E8 (the lattice point is z/2);
+ * A2: four pairs (slots 2j, 2j+1) in stretched coordinates, z = 2c. */
 int hqo_nearest_octet(int lattice, const float v[8], int32_t code[8]) {
   switch (lattice) {
     case LAT_Z:
@@ -232,6 +265,9 @@ int hqo_nearest_octet(int lattice, const float v[8], int32_t code[8]) {
       return OK;
     case LAT_E8:
       e8_nearest(v, code);
+      return OK;
+    case LAT_A2:
+      for (int j = 0; j < 4; ++j) a2_nearest(v + 2 * j, code + 2 * j);
       return OK;
   }
   return ERR_INVALID_ARG;
@@ -246,18 +282,20 @@ int hqo_nearest_batch(int lattice, const float *v, uint64_t count, int32_t *code
   return OK;
 }
 
-/* Lattice coordinate (as a float) of an integer code: E8 codes are twice the lattice point. */
+/* Lattice coordinate (as a float) of an integer code: E8 and A2 codes are twice the lattice
+ * point (A2: in stretched coordinates). */
 static float code_to_coord(int lattice, int32_t c) {
-  return lattice == LAT_E8 ? (float)c * 0.5f : (float)c;
+  return (lattice == LAT_E8 || lattice == LAT_A2) ? (float)c * 0.5f : (float)c;
 }
 
 /* Subtractive dither (HyperQuant summary, Methodology component 4: add a fresh U ~ Unif(V(L))
  * before quantising and subtract it after).  Reading: for tile t and octet o, one Philox call
  * with counter (o, t low word, t high word, 1) and the call's key gives four 32-bit words; their
  * eight 16-bit halves (low half first) h_i give b_i = 2 h_i / 65536 in [0, 2).  [0,2)^8 is a
- * fundamental domain of 2Z^8, a sublattice of E8, D4 x D4 and Z^8, so b is (to 16-bit
- * resolution) uniform on a union of whole cells and U = b - Q(b) is uniform on the Voronoi cell
- * V(L).  Every operation here is exact in binary32. */
+ * fundamental domain of 2Z^8, a sublattice of E8, D4 x D4, Z^8 and (in stretched coordinates)
+ * A2^4, so b is (to 16-bit resolution) uniform on a union of whole cells and U = b - Q(b) is
+ * uniform on the Voronoi cell V(L) (for A2 in stretched coordinates, i.e. U_1 sqrt 3 is the data-
+ * space offset).  Every operation here is exact in binary32. */
 void hqo_dither_octet(uint64_t seed, uint64_t tile, int octet, int lattice, float u[8]) {
   uint32_t ctr[4] = {(uint32_t)octet, (uint32_t)tile, (uint32_t)(tile >> 32), 1u};
   uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[4];
@@ -325,6 +363,10 @@ void hqo_haar_matrix(uint64_t seed, double *q) {
 /*       is fixed by u0..u6 (1 more bit): w = (u7 - (u0+..+u6 & 1))/2; symbols u0..u6, w.        */
 /*       8 bits per octet are stripped = log2 [Z^8 : 2 E8].                                       */
 /*   D4: per 4-block, w = (x3 - (x0+x1+x2 & 1))/2; symbols x0, x1, x2, w (1 bit stripped).       */
+/*   A2: per pair j, p_j = z_2j & 1 is shared by both coordinates (1 bit stripped = log2 [Z^2 :  */
+/*       2 A2] in stretched integer form); raw coset bit j of the octet's 4; u = (z - p_j)/2.     */
+/*       The odd slots hold the stretched coordinate (1/sqrt 3 ~ 2^-0.79 of the spread of the    */
+/*       even ones), so they are "halved" slots too (reading).                                   */
 /*   Z : no fixed bits; symbols z0..z7.                                                          */
 /* Signed symbols are mapped to unsigned by zigzag: 0,-1,1,-2,.. -> 0,1,2,3,..                    */
 /* ------------------------------------------------------------------------------------------ */
@@ -334,6 +376,7 @@ static int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 
 static int slot_halved(int lattice, int slot) {
   if (lattice == LAT_E8) return slot == 7;
   if (lattice == LAT_D4) return (slot & 3) == 3;
+  if (lattice == LAT_A2) return slot & 1;
   return 0;
 }
 static int slot_width(int lattice, int slot, int k) {
@@ -364,6 +407,15 @@ int hqo_strip_octet(int lattice, const int32_t code[8], uint32_t sym[8], int *co
     *coset = p;
     return OK;
   }
+  if (lattice == LAT_A2) {
+    for (int j = 0; j < 4; ++j) {
+      int32_t p = code[2 * j] & 1;
+      sym[2 * j] = zigzag((code[2 * j] - p) / 2);
+      sym[2 * j + 1] = zigzag((code[2 * j + 1] - p) / 2);
+      *coset |= p << j;
+    }
+    return OK;
+  }
   return ERR_INVALID_ARG;
 }
 
@@ -387,18 +439,23 @@ int hqo_unstrip_octet(int lattice, const uint32_t sym[8], int coset, int32_t cod
     for (int i = 0; i < 8; ++i) code[i] = 2 * u[i] + coset;
     return OK;
   }
+  if (lattice == LAT_A2) {
+    for (int i = 0; i < 8; ++i) code[i] = 2 * unzigzag(sym[i]) + ((coset >> (i / 2)) & 1);
+    return OK;
+  }
   return ERR_INVALID_ARG;
 }
 
 /* Remainder bits per octet and fixed bits per tile record F:
- * 16 (scale) + 16 (coset bits, E8 only) + 16 * (sum of slot widths). */
+ * 16 (scale) + coset bits (E8: 16, one per octet; A2: 64, one per pair) + 16 * (sum of slot
+ * widths). */
 static int octet_rem_bits(int lattice, int k) {
   int b = 0;
   for (int s = 0; s < 8; ++s) b += slot_width(lattice, s, k);
   return b;
 }
 uint32_t hqo_tile_fixed_bits(int lattice, int k) {
-  return 16u + (lattice == LAT_E8 ? 16u : 0u) + 16u * (uint32_t)octet_rem_bits(lattice, k);
+  return 16u + (lattice == LAT_E8 ? 16u : lattice == LAT_A2 ? 64u : 0u) + 16u * (uint32_t)octet_rem_bits(lattice, k);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -417,10 +474,27 @@ static void qctx_init(qctx *q, int lattice, int dither, uint64_t seed) {
   hqo_signs(seed, q->d);
 }
 
+/* Reconstruction factor t and multiplier m of a tile, per slot parity.  Every lattice:
+ * t = s * step, m = 1 / t (each rounded once in binary32; m = 0 when s = 0).  A2 odd slots (the
+ * second coordinate of a pair): t' = t * R3 and m' = 1 / t', which takes that coordinate into the
+ * stretched coordinates of a2_nearest on the way in and back on the way out. */
+static void tile_factors(int lattice, float s, float step, float m[2], float t[2]) {
+  t[0] = s * step;
+  m[0] = (s != 0.0f) ? 1.0f / t[0] : 0.0f;
+  if (lattice == LAT_A2) {
+    t[1] = t[0] * f32_from_bits(A2_R3_BITS);
+    m[1] = (s != 0.0f) ? 1.0f / t[1] : 0.0f;
+  } else {
+    t[1] = t[0];
+    m[1] = m[0];
+  }
+}
+
 /* Quantise tile `t` (values x[0..127]) at step `step`: returns the scale bits and 128 integer
  * codes; returns ERR_NONFINITE if the transformed tile's energy is not finite.
  *   y = H (D x);  S = sumsq(y);  s = bf16(sqrt(S/128));
- *   m = 1 / (s * step)  (binary32 product then division; m = 0 when s = 0);
+ *   m = 1 / (s * step)  (binary32 product then division; m = 0 when s = 0; A2's odd slots use
+ *   the m' of tile_factors);
  *   v = y * m  (+ U for the dithered path);  codes = nearest lattice point per octet. */
 static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float step,
                          uint16_t *scale_out, int32_t code[TILE]) {
@@ -431,14 +505,11 @@ static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float s
   if (!isfinite(S)) return ERR_NONFINITE;
   uint16_t sb = hqo_scale_bits(S);
   float s = bf16_to_f32(sb);
-  float m = 0.0f;
-  if (s != 0.0f) {
-    float tsc = s * step;
-    m = 1.0f / tsc;
-  }
+  float m[2], tf[2];
+  tile_factors(q->lattice, s, step, m, tf);
   for (int o = 0; o < 16; ++o) {
     float v[8];
-    for (int i = 0; i < 8; ++i) v[i] = y[8 * o + i] * m;
+    for (int i = 0; i < 8; ++i) v[i] = y[8 * o + i] * m[i & 1];
     if (q->dither) {
       float u[8];
       hqo_dither_octet(q->seed, t, o, q->lattice, u);
@@ -457,7 +528,8 @@ static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float s
 static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb,
                             float step, float out[TILE]) {
   float s = bf16_to_f32(sb);
-  float tsc = s * step;
+  float m[2], tf[2];
+  tile_factors(q->lattice, s, step, m, tf);
   float y[TILE];
   for (int o = 0; o < 16; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -465,7 +537,7 @@ static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE],
     for (int i = 0; i < 8; ++i) {
       float c = code_to_coord(q->lattice, code[8 * o + i]);
       float cu = q->dither ? c - u[i] : c;
-      y[8 * o + i] = cu * tsc;
+      y[8 * o + i] = cu * tf[i & 1];
     }
   }
   hqo_fwht128(y);
@@ -489,7 +561,7 @@ static void load_tile(const void *x, int dtype, uint64_t t, float out[TILE]) {
 int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
                  float step, int32_t *codes, uint16_t *scales) {
   if (n % TILE) return ERR_INVALID_ARG;
-  if (lattice < LAT_Z || lattice > LAT_E8) return ERR_INVALID_ARG;
+  if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   qctx q;
   qctx_init(&q, lattice, dither, seed);
   uint64_t T = n / TILE;
@@ -517,16 +589,13 @@ int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int di
     float S = hqo_sumsq128(y);
     if (!isfinite(S)) return ERR_NONFINITE;
     float s = bf16_to_f32(hqo_scale_bits(S));
-    float m = 0.0f;
-    if (s != 0.0f) {
-      float tsc = s * step;
-      m = 1.0f / tsc;
-    }
+    float m[2], tf[2];
+    tile_factors(lattice, s, step, m, tf);
     for (int o = 0; o < 16; ++o) {
       float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (dither) hqo_dither_octet(seed, t, o, lattice, u);
       for (int i = 0; i < 8; ++i) {
-        float v = y[8 * o + i] * m;
+        float v = y[8 * o + i] * m[i & 1];
         v_out[t * TILE + 8 * o + i] = dither ? v + u[i] : v;
       }
     }
@@ -658,6 +727,12 @@ static int rc_eval(const qctx *q, const void *x, int dtype, uint64_t T, uint64_t
 }
 
 /* Total payload bits of a candidate for Rice parameter k. */
+/* Lowest reachable payload rate: one unary bit per value plus the raw coset bits (E8: 1/8, A2:
+ * 1/2 bit per value). */
+static float min_bps(int lattice) {
+  return lattice == LAT_E8 ? 1.125f : lattice == LAT_A2 ? 1.5f : 1.0f;
+}
+
 static double rc_bits(int lattice, uint64_t N, int k, uint64_t sumq) {
   double per_tile = (double)(hqo_tile_fixed_bits(lattice, k) - 16u) + 128.0;
   return per_tile * (double)N + (double)sumq;
@@ -667,7 +742,7 @@ static double rc_bits(int lattice, uint64_t N, int k, uint64_t sumq) {
 int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
              float target_bps, float step, int rice_k, uint32_t *step_bits_out, int *k_out) {
   if (n % TILE) return ERR_INVALID_ARG;
-  if (lattice < LAT_Z || lattice > LAT_E8) return ERR_INVALID_ARG;
+  if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   if (rice_k < -1 || rice_k > 15) return ERR_INVALID_ARG;
   qctx q;
   qctx_init(&q, lattice, dither, seed);
@@ -696,7 +771,7 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
     *k_out = kb + best;
     return OK;
   }
-  if (!(target_bps >= (lattice == LAT_E8 ? 1.125f : 1.0f)) || !(target_bps <= 12.0f)) return ERR_RATE;
+  if (!(target_bps >= min_bps(lattice)) || !(target_bps <= 12.0f)) return ERR_RATE;
   int64_t b0 = (int64_t)(127u << 23) + (int64_t)floor((2.05 - (double)target_bps) * 8388608.0 + 0.5);
   if (N == 0) {
     *step_bits_out = (uint32_t)clamp64(b0, STEP_BITS_MIN, STEP_BITS_MAX);
@@ -747,8 +822,9 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
 /*    unary_words u64 | unary_bits u64 | payload_bits u64 | total_bytes u64 | 32 B zero        */
 /*  chunk index at byte 128: chunks+1 u32 word offsets (64-bit words) into the unary plane       */
 /*  fixed plane at fixed_off = align256(128 + 4 (chunks+1)): chunk c holds tiles 64c..64c+63,    */
-/*    8F bytes; tile record t at bit t F: scale bf16 (16) | E8 coset bits, bit o = octet o (16)  */
-/*    | for octet 0..15, slot 0..7: remainder (slot width bits, least significant first);       */
+/*    8F bytes; tile record t at bit t F: scale bf16 (16) | E8 coset bits, bit o = octet o (16), */
+/*    or A2 coset bits, bit 4o + j = pair j of octet o (64) | for octet 0..15, slot 0..7:        */
+/*    remainder (slot width bits, least significant first);                                      */
 /*    tiles past the end of the tensor are zero bits                                             */
 /*  unary plane at unary_off = align256(fixed_off + 8F chunks): chunk c's segment starts at     */
 /*    64-bit word index[c]; for each symbol in (tile, octet, slot) order: q = symbol >> width    */
@@ -832,7 +908,7 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
                float target_bps, float step, int rice_k, uint8_t *out, uint64_t cap,
                uint64_t *out_bytes, uint64_t info[4]) {
   if (n % TILE) return ERR_INVALID_ARG;
-  if (lattice < LAT_Z || lattice > LAT_E8) return ERR_INVALID_ARG;
+  if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   uint32_t sbits;
   int k;
   int rc = hqo_rate(x, dtype, n, lattice, dither, seed, target_bps, step, rice_k, &sbits, &k);
@@ -898,11 +974,13 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
       fp += 16;
       uint64_t coset_pos = fp;
       if (lattice == LAT_E8) fp += 16;
+      if (lattice == LAT_A2) fp += 64;
       for (int o = 0; o < 16; ++o) {
         uint32_t sym[8];
         int cos;
         hqo_strip_octet(lattice, codes + t * TILE + 8 * o, sym, &cos);
         if (lattice == LAT_E8) put_bit(fixed, coset_pos + (uint64_t)o, cos);
+        if (lattice == LAT_A2) put_bits(fixed, coset_pos + 4u * (uint64_t)o, (uint32_t)cos, 4);
         for (int s = 0; s < 8; ++s) {
           int w = slot_width(lattice, s, k);
           put_bits(fixed, fp, sym[s] & low_mask(w), w);
@@ -930,7 +1008,7 @@ static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink s
   if (bytes < HEADER_BYTES) return ERR_CORRUPT;
   if (get_u32(s) != MAGIC || get_u16(s + 4) != VERSION) return ERR_CORRUPT;
   int lattice = s[6], dither = s[7] & 1, k = s[10];
-  if (lattice > LAT_E8 || (s[7] & ~1u) || get_u16(s + 8) != TILE || k > 15 || s[11] != 6) return ERR_CORRUPT;
+  if (lattice > LAT_A2 || (s[7] & ~1u) || get_u16(s + 8) != TILE || k > 15 || s[11] != 6) return ERR_CORRUPT;
   if (get_u64(s + 24) != n || n % TILE) return ERR_CORRUPT;
   uint32_t sbits = get_u32(s + 12);
   if (sbits < STEP_BITS_MIN || sbits > STEP_BITS_MAX) return ERR_CORRUPT;
@@ -957,6 +1035,7 @@ static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink s
       fp += 16;
       uint64_t coset_pos = fp;
       if (lattice == LAT_E8) fp += 16;
+      if (lattice == LAT_A2) fp += 64;
       int32_t code[TILE];
       for (int o = 0; o < 16; ++o) {
         uint32_t sym[8];
@@ -974,7 +1053,9 @@ static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink s
           ++upos;
           sym[sl] = (qv << w) | r;
         }
-        int cos = lattice == LAT_E8 ? get_bit(fixed, coset_pos + (uint64_t)o) : 0;
+        int cos = lattice == LAT_E8   ? get_bit(fixed, coset_pos + (uint64_t)o)
+                  : lattice == LAT_A2 ? (int)get_bits(fixed, coset_pos + 4u * (uint64_t)o, 4)
+                                      : 0;
         hqo_unstrip_octet(lattice, sym, cos, code + 8 * o);
       }
       sink(ctx, &q, t, code, sb, st);

@@ -20,6 +20,8 @@ CASES = [
     ("tiny_d4_4bps", "tiny", "d4", 4.0, 0, False),
     ("tiny_z_4bps", "tiny", "z", 4.0, 0, False),
     ("tiny_e8_2bps_dither", "tiny", "e8", 2.0, 5, True),
+    ("tiny_a2_4bps", "tiny", "a2", 4.0, 0, False),
+    ("tiny_a2_3bps_dither", "tiny", "a2", 3.0, 5, True),
     ("weight16x4096_e8_3bps", "weight16", "e8", 3.0, 0, False),
 ]
 

@@ -19,7 +19,7 @@ def test_rice_exhaustive_roundtrip_and_length(orc):
         assert ulen == int(np.sum(vals >> k)) + vals.size     # unary part: q zeros + a one
 
 
-@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
 @pytest.mark.parametrize("dither", [False, True])
 def test_stream_roundtrip_equals_dequantisation(orc, lattice, dither):
     L = orc.LATTICES[lattice]

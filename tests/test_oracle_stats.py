@@ -2,7 +2,7 @@
 
 * Methodology component 3 / contributions: the realised rate lands within ~0.01 bps of the target;
 * component 4: subtractive dither gives strict per-vector inner-product unbiasedness;
-* component 2: lattice gain (E8 < D4 < Z distortion at equal rate); and the Shannon bound
+* component 2: lattice gain (E8 < D4 < Z, and A2 < Z, distortion at equal rate); and the Shannon bound
   D >= 2^(-2R) for Gaussian sources as a sanity floor;
 * dithered distortion equals the closed form G(L) V^(2/d) step^2 (relative to the tile energy).
 """
@@ -11,10 +11,11 @@ import pytest
 
 import synth
 
-G = {"e8": (929.0 / 12960.0, 8, 1.0), "d4": (0.0766032346, 4, 2.0), "z": (1.0 / 12.0, 1, 1.0)}
+G = {"e8": (929.0 / 12960.0, 8, 1.0), "d4": (0.0766032346, 4, 2.0), "z": (1.0 / 12.0, 1, 1.0),
+     "a2": (5.0 / (36.0 * 3.0 ** 0.5), 2, 3.0 ** 0.5 / 2.0)}
 
 
-@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
 @pytest.mark.parametrize("target", [2.0, 3.0, 4.0, 5.0])
 def test_rate_within_0p01_tiny(orc, lattice, target):
     x = synth.tiny()
@@ -37,7 +38,7 @@ def test_rate_within_0p01_kv_slice_dithered(orc, target):
     assert abs(info["payload_bps"] - target) <= 0.01
 
 
-@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
 def test_dithered_mse_closed_form(orc, lattice):
     """With dither the error in lattice units is uniform on the Voronoi cell, so per tile
     E|xhat - x|^2 / |x|^2 = G V^(2/d) step^2 (up to the bf16 rounding of the scale)."""
@@ -54,7 +55,7 @@ def test_dithered_mse_closed_form(orc, lattice):
     assert abs(r.mean() - want) < 5 * se, (r.mean(), want, se)
 
 
-@pytest.mark.parametrize("lattice", ["e8", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "a2", "z"])
 def test_dither_per_vector_unbiased(orc, lattice):
     """One fixed tile x, repeated M times: every copy gets its own dither draw (the dither counter
     holds the tile index) and the same D.  The mean reconstruction converges to x, so
@@ -80,12 +81,13 @@ def test_dither_per_vector_unbiased(orc, lattice):
 def test_shannon_floor_and_lattice_ordering(orc):
     x = synth.gaussian(128 * 2048, seed=31)
     mse = {}
-    for lat in ("e8", "d4", "z"):
+    for lat in ("e8", "d4", "a2", "z"):
         s, info = orc.encode(x, orc.LATTICES[lat], 4.0)
         y = orc.decode(s, x.size)
         mse[lat] = float(np.mean((y.astype(np.float64) - x) ** 2) / np.mean(x.astype(np.float64) ** 2))
         assert mse[lat] >= 2.0 ** (-2 * info["payload_bps"])
     assert mse["e8"] < mse["d4"] < mse["z"]
+    assert mse["a2"] < mse["z"]
 
 
 def test_sample_tiles_cover_each_stratum(orc):
