@@ -5,8 +5,8 @@
  * (gist.science/ko/paper/2606.23406; Japanese version gist.science/ja/paper/2606.23406), section
  * "Methodology: the HyperQuant pipeline":
  *   component 1  per-tile randomized Hadamard transform RHT_128(x) = H_128 D x (D: random +-1),
- *   component 2  nearest-point quantisation onto E8 (or D4, or scalar Z) in an integer embedding,
- *                scaled so the rotated tile matches the lattice,
+ *   component 2  nearest-point quantisation onto E8 (or D4, A2, or scalar Z) in an integer
+ *                embedding, scaled so the rotated tile matches the lattice,
  *   component 3  stripping of the bits that lattice membership fixes, then Rice coding, with the
  *                realised rate within ~0.01 bits per value of the target,
  *   component 4  for KV caches: a per-layer +-1 rotation (folded into D through the seed) and a
@@ -31,14 +31,20 @@
  *   chunk index at byte 128: chunks+1 u32 offsets, in 64-bit words, into the unary plane
  *   fixed plane at fixed_off = align256(128 + 4 (chunks+1)); chunk c = tiles 64c..64c+63, 8F bytes;
  *     tile record at bit t F (bit i of a plane = bit i%8 of byte i/8): bf16 tile scale (16) |
- *     E8 only: coset bit of octet o at bit o (16) | octet 0..15, slot 0..7: Rice remainder, width
- *     k (full slots) or max(k-1,0) (the parity-fixed slot: 7 of E8, 3 and 7 of D4), LSB first
+ *     coset bits (E8: octet o at bit o, 16; A2: pair j of octet o at bit 4o+j, 64; none for D4 and
+ *     Z) | octet 0..15, slot 0..7: Rice remainder, width k (full slots) or max(k-1,0) (halved
+ *     slots: the parity-fixed slot 7 of E8, 3 and 7 of D4; the stretched odd slots of A2), LSB first
  *   unary plane at unary_off = align256(fixed_off + 8 F chunks): chunk c's segment starts at word
  *     index[c]; each symbol in (tile, octet, slot) order contributes (symbol >> width) zero bits
  *     and a one; segments are zero-padded to 64 bits.
  *   Symbols per octet (8 consecutive coordinates): E8: z in 2E8, p = z0 & 1, u = (z-p)/2,
  *     slots zz(u0..u6), zz((u7 - (u0+..+u6 & 1))/2); D4 (two blocks): zz(x0..x2),
- *     zz((x3 - (x0+x1+x2 & 1))/2); Z: zz(z0..z7); zz(a) = (a << 1) ^ (a >> 31).
+ *     zz((x3 - (x0+x1+x2 & 1))/2); A2 (four pairs, stretched coordinates, z = 2c with
+ *     z_2j = z_2j+1 mod 2): p_j = z_2j & 1, slots zz((z_2j - p_j)/2), zz((z_2j+1 - p_j)/2);
+ *     Z: zz(z0..z7); zz(a) = (a << 1) ^ (a >> 31).
+ *   A2 is the hexagonal lattice with minimal distance 1; each pair (v0, v1) is quantised as
+ *     (v0, v1 / sqrt 3) onto Z^2 u (Z+1/2)^2 under the distance dw0^2 + 3 dw1^2: its odd slots use
+ *     the multiplier 1 / ((s step) R) and reconstruct with (s step) R, R = binary32 sqrt 3.
  */
 #ifndef HQ_H_
 #define HQ_H_
@@ -59,12 +65,12 @@ typedef enum {
   HQ_ERR_NONFINITE = -3,   /* a tile whose transformed energy is NaN or Inf                         */
   HQ_ERR_CAPACITY = -4,    /* output buffer too small; *out_bytes holds the size needed            */
   HQ_ERR_CORRUPT = -5,     /* stream fails validation (header, index, segment, terminator count)   */
-  HQ_ERR_RATE = -6,        /* target rate outside [1.125 (E8) or 1.0 (D4, Z), 12] bits per value    */
+  HQ_ERR_RATE = -6,        /* target outside [1.125 (E8), 1.5 (A2) or 1.0 (D4, Z), 12] bits / value */
   HQ_ERR_HIP = -7,         /* a HIP runtime call failed                                             */
   HQ_ERR_TIMEOUT = -8      /* the encoder's cross-workgroup wait exceeded its bound (never expected) */
 } hq_status_code;
 
-typedef enum { HQ_Z = 0, HQ_D4 = 1, HQ_E8 = 2 } hq_lattice;
+typedef enum { HQ_Z = 0, HQ_D4 = 1, HQ_E8 = 2, HQ_A2 = 3 } hq_lattice;
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 
 typedef struct {
@@ -197,7 +203,8 @@ int hq_srft_decode(const void *codes, const void *scales, uint64_t n, uint64_t s
                    int32_t bits, void *out, int32_t out_dtype, hq_stream_t stream);
 
 /* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
- * E8 codes are twice the lattice point, D4 and Z codes are the point) and per-tile bf16 scale bits
+ * E8 and A2 codes are twice the lattice point (A2 in stretched coordinates), D4 and Z codes are the
+ * point) and per-tile bf16 scale bits
  * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */
 int hq_codes(const void *x, int32_t dtype, uint64_t n, const hq_params *params, int32_t *codes,
              uint16_t *scales, void *workspace, size_t workspace_bytes, hq_stream_t stream);

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libhq.so")
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_NONFINITE = 0, -1, -2, -3
 HQ_ERR_CAPACITY, HQ_ERR_CORRUPT, HQ_ERR_RATE, HQ_ERR_HIP, HQ_ERR_TIMEOUT = -4, -5, -6, -7, -8
-HQ_Z, HQ_D4, HQ_E8 = 0, 1, 2
+HQ_Z, HQ_D4, HQ_E8, HQ_A2 = 0, 1, 2, 3
 HQ_F32, HQ_BF16 = 0, 1
-LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8}
+LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8, "a2": HQ_A2}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
            "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",

@@ -25,18 +25,21 @@ uint64_t align256h(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
 
 int octet_rem_bits_h(int lattice, int k) {
   const int kh = k > 0 ? k - 1 : 0;
-  return lattice == HQ_E8 ? 7 * k + kh : lattice == HQ_D4 ? 6 * k + 2 * kh : 8 * k;
+  return lattice == HQ_E8 ? 7 * k + kh : lattice == HQ_D4 ? 6 * k + 2 * kh : lattice == HQ_A2 ? 4 * k + 4 * kh : 8 * k;
 }
 uint32_t tile_fixed_bits_h(int lattice, int k) {
-  return (uint32_t)((lattice == HQ_E8 ? 32 : 16) + 16 * octet_rem_bits_h(lattice, k));
+  return (uint32_t)((lattice == HQ_E8 ? 32 : lattice == HQ_A2 ? 80 : 16) + 16 * octet_rem_bits_h(lattice, k));
 }
+
+// Lowest payload rate a lattice reaches: one unary bit per value plus its raw coset bits.
+float min_bps(int lattice) { return lattice == HQ_E8 ? 1.125f : lattice == HQ_A2 ? 1.5f : 1.0f; }
 
 uint64_t chunks_of(uint64_t n) { return (n / 128 + 63) / 64; }
 
 int check_params(const hq_params* p, uint64_t n) {
   if (!p) return HQ_ERR_INVALID_ARG;
   if (p->tile != 128) return HQ_ERR_UNSUPPORTED;
-  if (p->lattice < HQ_Z || p->lattice > HQ_E8) return HQ_ERR_INVALID_ARG;
+  if (p->lattice < HQ_Z || p->lattice > HQ_A2) return HQ_ERR_INVALID_ARG;
   if (n % 128) return HQ_ERR_INVALID_ARG;
   if (n > (1ull << 35)) return HQ_ERR_INVALID_ARG;  // the encoder's look-back packs 28-bit padding sums
   if (p->dither > 1) return HQ_ERR_INVALID_ARG;
@@ -47,8 +50,7 @@ int check_params(const hq_params* p, uint64_t n) {
     const uint32_t b = f32_bits(p->step);
     if (b < kStepMin || b > kStepMax) return HQ_ERR_INVALID_ARG;
   } else {
-    const float lo = p->lattice == HQ_E8 ? 1.125f : 1.0f;
-    if (!(p->target_bps >= lo) || !(p->target_bps <= 12.0f)) return HQ_ERR_RATE;
+    if (!(p->target_bps >= min_bps(p->lattice)) || !(p->target_bps <= 12.0f)) return HQ_ERR_RATE;
   }
   return HQ_OK;
 }
@@ -176,7 +178,7 @@ int hq_workspace_size(uint64_t n, const hq_params* params, size_t* bytes) {
 }
 
 int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t* bytes) {
-  if (!bytes || n % 128 || lattice < HQ_Z || lattice > HQ_E8 || rice_k < 0 || rice_k > 15) return HQ_ERR_INVALID_ARG;
+  if (!bytes || n % 128 || lattice < HQ_Z || lattice > HQ_A2 || rice_k < 0 || rice_k > 15) return HQ_ERR_INVALID_ARG;
   const uint64_t chunks = chunks_of(n);
   const uint64_t fixed_off = align256h(128 + 4 * (chunks + 1));
   *bytes = align256h(fixed_off + chunks * 8ull * tile_fixed_bits_h(lattice, rice_k));

@@ -20,7 +20,11 @@ constexpr uint32_t kVersion = 1;
 constexpr uint32_t kStepBitsMin = (127u - 12u) << 23;
 constexpr uint32_t kStepBitsMax = (127u + 12u) << 23;
 
-enum { kLatZ = 0, kLatD4 = 1, kLatE8 = 2 };
+enum { kLatZ = 0, kLatD4 = 1, kLatE8 = 2, kLatA2 = 3 };
+// A2 quantises each pair in stretched coordinates (second coordinate / sqrt 3); its reconstruction
+// factor on odd slots is the tile's times this binary32 sqrt(3) (nearest), and its multiplier the
+// reciprocal of that.
+constexpr uint32_t kA2R3Bits = 0x3FDDB3D7u;
 
 
 // ---------------------------------------------------------------------------------------------
@@ -291,10 +295,27 @@ __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32
   *coset = kb & 1u;
 }
 
+// A2 (hexagonal, minimal distance 1) in stretched coordinates w = (v0, v1 / sqrt 3), where it is
+// Z^2 u (Z + 1/2)^2 under the squared distance dw0^2 + 3 dw1^2.  With r = rint w and a = |w - r|,
+// |w - A|^2 - |w - B|^2 = a0 + 3 a1 - 1 for the rounded point A and the nearest point B of the
+// shifted coset, so A is kept iff fma(3, a1, a0) <= 1 (one rounding).  Codes z = 2c: B moves each
+// coordinate half a step toward w (up for an exact integer).
+__device__ __forceinline__ void a2_nearest(const float* w, int32_t* z) {
+  const float r0 = rintf(w[0]), r1 = rintf(w[1]);
+  const float e0 = w[0] - r0, e1 = w[1] - r1;
+  const bool keep_a = __builtin_fmaf(3.0f, fabsf(e1), fabsf(e0)) <= 1.0f;
+  const int32_t s0 = (__float_as_uint(e0) >> 31) ? -1 : 1, s1 = (__float_as_uint(e1) >> 31) ? -1 : 1;
+  z[0] = 2 * (int32_t)r0 + (keep_a ? 0 : s0);
+  z[1] = 2 * (int32_t)r1 + (keep_a ? 0 : s1);
+}
+
 template <int LAT>
 __device__ __forceinline__ void nearest_octet(const float* v, int32_t* code) {
   if (LAT == kLatE8) {
     e8_nearest(v, code);
+  } else if (LAT == kLatA2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a2_nearest(v + 2 * j, code + 2 * j);
   } else if (LAT == kLatD4) {
     d4_nearest(v, code);
     d4_nearest(v + 4, code + 4);
@@ -306,7 +327,7 @@ __device__ __forceinline__ void nearest_octet(const float* v, int32_t* code) {
 
 template <int LAT>
 __device__ __forceinline__ float code_coord(int32_t c) {
-  return LAT == kLatE8 ? (float)c * 0.5f : (float)c;
+  return (LAT == kLatE8 || LAT == kLatA2) ? (float)c * 0.5f : (float)c;
 }
 
 // Subtractive dither of octet o of tile t: one Philox call, counter (o, t lo, t hi, 1); the eight
@@ -334,7 +355,7 @@ __device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, f
 
 template <int LAT>
 __device__ __forceinline__ bool slot_halved(int s) {
-  return LAT == kLatE8 ? (s == 7) : LAT == kLatD4 ? ((s & 3) == 3) : false;
+  return LAT == kLatE8 ? (s == 7) : LAT == kLatD4 ? ((s & 3) == 3) : LAT == kLatA2 ? ((s & 1) == 1) : false;
 }
 template <int LAT>
 __device__ __forceinline__ int slot_width(int s, int k) {
@@ -343,11 +364,13 @@ __device__ __forceinline__ int slot_width(int s, int k) {
 template <int LAT>
 __device__ __forceinline__ int octet_rem_bits(int k) {
   const int kh = k > 0 ? k - 1 : 0;
-  return LAT == kLatE8 ? 7 * k + kh : LAT == kLatD4 ? 6 * k + 2 * kh : 8 * k;
+  return LAT == kLatE8 ? 7 * k + kh : LAT == kLatD4 ? 6 * k + 2 * kh : LAT == kLatA2 ? 4 * k + 4 * kh : 8 * k;
 }
+// Tile record header: 16 scale bits, then the raw coset bits (E8: one per octet; A2: one per pair,
+// bit 4 o + j for pair j of octet o).
 template <int LAT>
 __device__ __forceinline__ int tile_hdr_bits() {
-  return LAT == kLatE8 ? 32 : 16;
+  return LAT == kLatE8 ? 32 : LAT == kLatA2 ? 80 : 16;
 }
 template <int LAT>
 __device__ __forceinline__ uint32_t tile_fixed_bits(int k) {
@@ -368,6 +391,16 @@ __device__ __forceinline__ void strip_octet(const int32_t* code, uint32_t* sym, 
     for (int i = 0; i < 7; ++i) sym[i] = zigzag(u[i]);
     sym[7] = zigzag((u[7] - (r & 1)) >> 1);
     *coset = (uint32_t)p;
+  } else if (LAT == kLatA2) {
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t p = code[2 * j] & 1;
+      sym[2 * j] = zigzag((code[2 * j] - p) >> 1);
+      sym[2 * j + 1] = zigzag((code[2 * j + 1] - p) >> 1);
+      cs |= (uint32_t)p << j;
+    }
+    *coset = cs;
   } else if (LAT == kLatD4) {
 #pragma unroll
     for (int b = 0; b < 8; b += 4) {
@@ -395,6 +428,9 @@ __device__ __forceinline__ void unstrip_octet(const uint32_t* sym, uint32_t cose
     u[7] = 2 * unzigzag(sym[7]) + (r & 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) code[i] = 2 * u[i] + (int32_t)coset;
+  } else if (LAT == kLatA2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = 2 * unzigzag(sym[i]) + (int32_t)((coset >> (i / 2)) & 1u);
   } else if (LAT == kLatD4) {
 #pragma unroll
     for (int b = 0; b < 8; b += 4) {

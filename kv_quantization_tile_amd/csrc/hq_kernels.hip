@@ -144,31 +144,45 @@ __device__ __forceinline__ uint32_t transform_octet(const void* x, uint64_t t, b
   return tile_scale_bits(S);
 }
 
-// v = y * m (+ U); m = 1 / (s * step) rounded once each (0 when s = 0); nearest lattice point.
+// Per-tile multiplier m = 1 / (s * step) (0 when s = 0), with the lane's sign folded in.  A2's
+// odd slots use m' = 1 / ((s * step) * sqrt3) instead (each product and quotient rounded once),
+// which takes the pair's second coordinate into the lattice's stretched coordinates.
+template <bool ODD>
+__device__ __forceinline__ float tile_multiplier(uint32_t sb, float step, uint32_t lane_neg) {
+  const float s = bf16_bits_to_f32(sb);
+  const float t = ODD ? (s * step) * __uint_as_float(kA2R3Bits) : s * step;
+  const float m0 = (s != 0.0f) ? __fdiv_rn(1.0f, t) : 0.0f;
+  return lane_neg ? -m0 : m0;
+}
+__device__ __forceinline__ float tile_multiplier(uint32_t sb, float step, uint32_t lane_neg) {
+  return tile_multiplier<false>(sb, step, lane_neg);
+}
+
+// v = y * m (+ U); m as above (A2: m' on odd slots); nearest lattice point.
 // y holds sigma(lane) times the transformed values (see fwht_cross); the sign is folded into m.
 template <int LAT, bool DITHER>
-__device__ __forceinline__ void quantize_octet(const float* y, float s, float step, const float* u,
+__device__ __forceinline__ void quantize_octet(const float* y, uint32_t sb, float step, const float* u,
                                                int32_t* code, uint32_t lane_neg) {
-  const float m0 = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
-  const float m = lane_neg ? -m0 : m0;
+  const float m = tile_multiplier<false>(sb, step, lane_neg);
+  const float m1 = LAT == kLatA2 ? tile_multiplier<true>(sb, step, lane_neg) : m;
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v[i] = y[i] * m;
+    v[i] = y[i] * ((i & 1) ? m1 : m);
     if (DITHER) v[i] = v[i] + u[i];
   }
   nearest_octet<LAT>(v, code);
 }
 
-// Symbols of one octet at multiplier m (the lane's sign already folded into m): v = y * m (+ U),
-// nearest lattice point, bit-stripping.
+// Symbols of one octet at multipliers m (even slots) and m1 (odd slots; equal to m except for A2),
+// the lane's sign already folded in: v = y * m (+ U), nearest lattice point, bit-stripping.
 template <int LAT, bool DITHER>
-__device__ __forceinline__ void octet_symbols(const float* y, float m, const float* u, uint32_t* sym,
+__device__ __forceinline__ void octet_symbols(const float* y, float m, float m1, const float* u, uint32_t* sym,
                                               uint32_t* coset) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v[i] = y[i] * m;
+    v[i] = y[i] * ((i & 1) ? m1 : m);
     if (DITHER) v[i] = v[i] + u[i];
   }
   if (LAT == kLatE8) {
@@ -178,13 +192,6 @@ __device__ __forceinline__ void octet_symbols(const float* y, float m, const flo
     nearest_octet<LAT>(v, code);
     strip_octet<LAT>(code, sym, coset);
   }
-}
-
-// Per-tile multiplier m = 1 / (s * step) (0 when s = 0), with the lane's sign folded in.
-__device__ __forceinline__ float tile_multiplier(uint32_t sb, float step, uint32_t lane_neg) {
-  const float s = bf16_bits_to_f32(sb);
-  const float m0 = (s != 0.0f) ? __fdiv_rn(1.0f, s * step) : 0.0f;
-  return lane_neg ? -m0 : m0;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -308,18 +315,30 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   const int64_t centre = ws->rc_centre;
-  // lane o computes the multiplier of candidate o mod 8; the group shares them by broadcast
+  // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots);
+  // the group shares them by broadcast
   const int jm = nc == 1 ? 0 : (o & 7);
   const int64_t bm = nc == 1 ? centre
                              : clamp_i64(centre + (int64_t)(2 * jm - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
                                          kStepBitsMax);
-  const uint32_t m_mine = __float_as_uint(tile_multiplier(sb, __uint_as_float((uint32_t)bm), 0u));
+  const float stepm = __uint_as_float((uint32_t)bm);
+  const uint32_t m_mine = __float_as_uint((LAT == kLatA2 && o >= 8) ? tile_multiplier<true>(sb, stepm, 0u)
+                                                                     : tile_multiplier<false>(sb, stepm, 0u));
   const bool lane_neg = lane_sign_bit(o) != 0u;
-  float mj[kRcCand];
+  float mj[kRcCand], mo[kRcCand];
   mj[0] = __uint_as_float(group_bcast<0>(m_mine)); mj[1] = __uint_as_float(group_bcast<1>(m_mine));
   mj[2] = __uint_as_float(group_bcast<2>(m_mine)); mj[3] = __uint_as_float(group_bcast<3>(m_mine));
   mj[4] = __uint_as_float(group_bcast<4>(m_mine)); mj[5] = __uint_as_float(group_bcast<5>(m_mine));
   mj[6] = __uint_as_float(group_bcast<6>(m_mine)); mj[7] = __uint_as_float(group_bcast<7>(m_mine));
+  if (LAT == kLatA2) {
+    mo[0] = __uint_as_float(group_bcast<8>(m_mine)); mo[1] = __uint_as_float(group_bcast<9>(m_mine));
+    mo[2] = __uint_as_float(group_bcast<10>(m_mine)); mo[3] = __uint_as_float(group_bcast<11>(m_mine));
+    mo[4] = __uint_as_float(group_bcast<12>(m_mine)); mo[5] = __uint_as_float(group_bcast<13>(m_mine));
+    mo[6] = __uint_as_float(group_bcast<14>(m_mine)); mo[7] = __uint_as_float(group_bcast<15>(m_mine));
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRcCand; ++j) mo[j] = mj[j];
+  }
   uint32_t acc[kRcCand][kRcKwin];
 #pragma unroll
   for (int j = 0; j < kRcCand; ++j)
@@ -332,8 +351,9 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
                                 : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2),
                                             kStepBitsMin, kStepBitsMax);
       const float m = lane_neg ? -mj[j] : mj[j];
+      const float m1 = lane_neg ? -mo[j] : mo[j];
       uint32_t sym[8], cos;
-      octet_symbols<LAT, DITHER>(y, m, u, sym, &cos);
+      octet_symbols<LAT, DITHER>(y, m, m1, u, sym, &cos);
       const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
 #pragma unroll
       for (int w = 0; w < kRcKwin; ++w) {
@@ -420,11 +440,13 @@ __device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
   }
-  const float m = tile_multiplier(tile_scale_bits(fin ? S : 0.0f), step, lane_neg);
+  const uint32_t sb = tile_scale_bits(fin ? S : 0.0f);
+  const float m = tile_multiplier<false>(sb, step, lane_neg);
+  const float m1 = LAT == kLatA2 ? tile_multiplier<true>(sb, step, lane_neg) : m;
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   uint32_t cos;
-  octet_symbols<LAT, DITHER>(y, m, u, sym, &cos);
+  octet_symbols<LAT, DITHER>(y, m, m1, u, sym, &cos);
 }
 
 __device__ void write_header(uint8_t* out, uint64_t cap, int lattice, int dither, int k, uint32_t step_bits,
@@ -590,7 +612,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     fwht_cross(y[r], o);
     S[r] = tile_sumsq(y[r]);
   }
-  // one scale and one division per lane (round o mod 4), broadcast inside the tile's lane group
+  // one scale and one division per lane (round o mod 4; A2: lanes with bit 2 of o set divide for
+  // the odd slots), broadcast inside the tile's lane group
   uint32_t sb_mine;
   float m_mine;
   {
@@ -600,16 +623,26 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const uint64_t t = (uint64_t)c * kChunkTiles + 16u * rr + 4u * wave + tw;
     if (!fin && t < P.T && o < 4) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
     sb_mine = tile_scale_bits(fin ? Sr : 0.0f);
-    m_mine = tile_multiplier(sb_mine, step, 0u);
+    m_mine = (LAT == kLatA2 && (o & 4)) ? tile_multiplier<true>(sb_mine, step, 0u)
+                                        : tile_multiplier<false>(sb_mine, step, 0u);
   }
   uint32_t sbr[4];
-  float mr[4];
+  float mr[4], mr1[4];
   sbr[0] = group_bcast<0>(sb_mine); sbr[1] = group_bcast<1>(sb_mine);
   sbr[2] = group_bcast<2>(sb_mine); sbr[3] = group_bcast<3>(sb_mine);
   mr[0] = __uint_as_float(group_bcast<0>(__float_as_uint(m_mine)));
   mr[1] = __uint_as_float(group_bcast<1>(__float_as_uint(m_mine)));
   mr[2] = __uint_as_float(group_bcast<2>(__float_as_uint(m_mine)));
   mr[3] = __uint_as_float(group_bcast<3>(__float_as_uint(m_mine)));
+  if (LAT == kLatA2) {
+    mr1[0] = __uint_as_float(group_bcast<4>(__float_as_uint(m_mine)));
+    mr1[1] = __uint_as_float(group_bcast<5>(__float_as_uint(m_mine)));
+    mr1[2] = __uint_as_float(group_bcast<6>(__float_as_uint(m_mine)));
+    mr1[3] = __uint_as_float(group_bcast<7>(__float_as_uint(m_mine)));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mr1[r] = mr[r];
+  }
 
   // phase 2: quantise, strip, pack the fixed record, Rice lengths and unary patterns
   uint32_t sym[4][8];
@@ -628,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (DITHER) dither_octet<LAT>(P.seed, t, o, u);
     uint32_t cos;
-    octet_symbols<LAT, DITHER>(y[r], lane_neg ? -mr[r] : mr[r], u, sym[r], &cos);
+    octet_symbols<LAT, DITHER>(y[r], lane_neg ? -mr[r] : mr[r], lane_neg ? -mr1[r] : mr1[r], u, sym[r], &cos);
     const uint64_t bal = __ballot(valid && cos != 0u);
     uint32_t len = 8;
     if (valid) {
@@ -637,6 +670,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
         lds_put_bits(s_fixed, rec, sbr[r], 16);
         if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (16 * tw)) & 0xFFFFu, 16);
       }
+      // A2: the octet's four pair cosets, bits 4 o .. 4 o + 3 after the scale (never across a word)
+      if (LAT == kLatA2) lds_put_bits(s_fixed, rec + 16 + 4u * (uint32_t)o, cos, 4);
       uint32_t pos = rec + hdr + (uint32_t)o * RW;
       if (RW <= 32) {  // uniform: the field is one word, ORed into at most two
         uint32_t lo, hi;
@@ -812,7 +847,7 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   int32_t code[8];
-  quantize_octet<LAT, DITHER>(y, bf16_bits_to_f32(sb), __uint_as_float(step_bits), u, code, lane_sign_bit(o));
+  quantize_octet<LAT, DITHER>(y, sb, __uint_as_float(step_bits), u, code, lane_sign_bit(o));
   if (valid) {
     int4* dst = reinterpret_cast<int4*>(codes + t * kTile + 8 * o);
     dst[0] = make_int4(code[0], code[1], code[2], code[3]);
@@ -835,14 +870,17 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
   const uint64_t T = n / kTile;
   const uint32_t chunks = (uint32_t)((T + kChunkTiles - 1) / kChunkTiles);
   const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
-  bool ok = have && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatE8 && flags <= 1 &&
+  bool ok = have && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags <= 1 &&
             (h[2] & 0xFFFFu) == (uint32_t)kTile && k <= 15 && (h[2] >> 24) == 6u && h[3] >= kStepBitsMin &&
             h[3] <= kStepBitsMax && hn == n && (n % kTile) == 0;
   uint32_t F = 0;
   if (ok) {
     const int kh = k > 0 ? k - 1 : 0;
-    const int rem = lattice == kLatE8 ? 7 * k + kh : lattice == kLatD4 ? 6 * k + 2 * kh : 8 * k;
-    F = (uint32_t)((lattice == kLatE8 ? 32 : 16) + 16 * rem);
+    const int rem = lattice == kLatE8 ? 7 * k + kh
+                    : lattice == kLatD4 ? 6 * k + 2 * kh
+                    : lattice == kLatA2 ? 4 * k + 4 * kh
+                                        : 8 * k;
+    F = (uint32_t)((lattice == kLatE8 ? 32 : lattice == kLatA2 ? 80 : 16) + 16 * rem);
   }
   const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (chunks + 1));
   const uint64_t unary_off = align256(fixed_off + (uint64_t)chunks * 8ull * F);
@@ -937,13 +975,15 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
   for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -0.0078125f : 0.0078125f;
   bool bad = false;
-  // record words of a round: the tile header (scale, then E8 coset bits) and the octet's field
-  uint32_t hA, hB, f0, f1, f2;
+  // record words of a round: the tile header (scale, then E8 coset bits), A2's word with the
+  // octet's four coset bits, and the octet's field
+  uint32_t hA, hB, hC, f0, f1, f2;
   auto issue = [&](int r) {
     const uint32_t rec = (16u * r + 4u * wave + tw) * F;
     const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
     hA = fw[rec >> 5];
     hB = fw[(rec >> 5) + 1];
+    hC = LAT == kLatA2 ? fw[(rec + 16u + 4u * (uint32_t)o) >> 5] : 0u;
     f0 = fw[P >> 5];
     f1 = fw[(P >> 5) + 1];
     f2 = RW > 32 ? fw[(P >> 5) + 2] : 0u;
@@ -956,7 +996,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
     const uint64_t t = (uint64_t)c * kChunkTiles + tc;
     const uint32_t rec = tc * F;
     const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
-    const uint32_t a0 = hA, a1 = hB, x0 = f0, x1 = f1, x2 = f2;
+    const uint32_t a0 = hA, a1 = hB, a2w = hC, x0 = f0, x1 = f1, x2 = f2;
     if (r < 3) issue(r + 1);
     float yv[8];
     if (valid) {
@@ -964,7 +1004,9 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       // coset bits of the tile's 16 octets (high half)
       const uint32_t th = __builtin_amdgcn_alignbit(a1, a0, rec & 31u);
       const uint32_t sb = th & 0xFFFFu;
-      const uint32_t coset = LAT == kLatE8 ? (th >> (16 + o)) & 1u : 0u;
+      const uint32_t coset = LAT == kLatE8   ? (th >> (16 + o)) & 1u
+                             : LAT == kLatA2 ? (a2w >> ((rec + 16u + 4u * (uint32_t)o) & 31u)) & 0xFu
+                                             : 0u;
       const uint32_t sh = P & 31u;
       const uint32_t lo = __builtin_amdgcn_alignbit(x1, x0, sh), hi = __builtin_amdgcn_alignbit(x2, x1, sh);
       // unary parts: q = p - p_prev - 1 = (p_prev ^ ~0) + p; the symbol before the chunk's first
@@ -1032,6 +1074,18 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
           const float f = tsc * 0.5f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] = (float)z[i] * f;
+        }
+      } else if (LAT == kLatA2) {
+        // odd slots: the stretched coordinate, reconstructed with (s * step) * sqrt3
+        int32_t code[8];
+        unstrip_octet<LAT>(sym, coset, code);
+        const float tsc1 = tsc * __uint_as_float(kA2R3Bits);
+        float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (dither) dither_octet<LAT>(seed, t, o, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float cc = code_coord<LAT>(code[i]);
+          yv[i] = (dither ? cc - u[i] : cc) * ((i & 1) ? tsc1 : tsc);
         }
       } else {
         int32_t code[8];
@@ -1176,6 +1230,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
   switch (ws->dec_lattice) {
     case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
+    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
     case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
     default: decode_chunk<kLatZ, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
   }
@@ -1239,6 +1294,9 @@ __global__ __launch_bounds__(kBlock) void gemv_rows_kernel(const float* __restri
     if ((LATV) == kLatE8) {                                                   \
       if (DITHV) { if ((DTV) == 1) CALL(kLatE8, true, 1); else CALL(kLatE8, true, 0); }   \
       else { if ((DTV) == 1) CALL(kLatE8, false, 1); else CALL(kLatE8, false, 0); }       \
+    } else if ((LATV) == kLatA2) {                                            \
+      if (DITHV) { if ((DTV) == 1) CALL(kLatA2, true, 1); else CALL(kLatA2, true, 0); }   \
+      else { if ((DTV) == 1) CALL(kLatA2, false, 1); else CALL(kLatA2, false, 0); }       \
     } else if ((LATV) == kLatD4) {                                            \
       if (DITHV) { if ((DTV) == 1) CALL(kLatD4, true, 1); else CALL(kLatD4, true, 0); }   \
       else { if ((DTV) == 1) CALL(kLatD4, false, 1); else CALL(kLatD4, false, 0); }       \
@@ -1284,6 +1342,8 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
                      half_log2, a.rice_k, a.target, N)
   if (a.lattice == kLatE8)
     HQ_SOLVE(kLatE8);
+  else if (a.lattice == kLatA2)
+    HQ_SOLVE(kLatA2);
   else if (a.lattice == kLatD4)
     HQ_SOLVE(kLatD4);
   else

@@ -1086,18 +1086,19 @@ int hqo_decode(const uint8_t *s, uint64_t bytes, uint64_t n, void *out, int out_
 }
 
 /* The decoder's values before the inverse transform, in binary64: yhat_i = (c_i - U_i) * t with
- * t = s * step the binary32 product both sides use (dequantize_tile), so that the exact
- * reconstruction of tile t is D H yhat / 128.  Test infrastructure for products with the decoded
- * matrix (the fused decode + matrix-vector product). */
+ * t = s * step the binary32 product both sides use (dequantize_tile; A2's odd slots take its t'),
+ * so that the exact reconstruction of tile t is D H yhat / 128.  Test infrastructure for products
+ * with the decoded matrix (the fused decode + matrix-vector product). */
 static void coords_sink(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step) {
   double *out = (double *)ctx + t * TILE;
-  const float tsc = bf16_to_f32(sb) * step;
+  float m[2], tf[2];
+  tile_factors(q->lattice, bf16_to_f32(sb), step, m, tf);
   for (int o = 0; o < 16; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
     for (int i = 0; i < 8; ++i) {
       const double c = (double)code_to_coord(q->lattice, code[8 * o + i]);
-      out[8 * o + i] = (c - (double)u[i]) * (double)tsc;
+      out[8 * o + i] = (c - (double)u[i]) * (double)tf[i & 1];
     }
   }
 }

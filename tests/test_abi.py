@@ -33,7 +33,7 @@ def test_strerror_codes():
 
 def test_sizes_match_oracle_layout(orc):
     for n in (0, 128, 128 * 65, 128 * 458752):
-        for lat in ("z", "d4", "e8"):
+        for lat in ("z", "d4", "e8", "a2"):
             for k in (0, 1, 3, 15):
                 fo, uo, F = orc.layout(n, orc.LATTICES[lat], k)
                 assert hq.hq_stream_fixed_bytes(n, lat, k) == uo
@@ -51,13 +51,14 @@ def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(tile=64), hq.HQ_ERR_UNSUPPORTED),
-    (dict(lattice=3), hq.HQ_ERR_INVALID_ARG),
+    (dict(lattice=4), hq.HQ_ERR_INVALID_ARG),
     (dict(rice_k=16), hq.HQ_ERR_INVALID_ARG),
     (dict(step=-2.0), hq.HQ_ERR_INVALID_ARG),          # -1 alone is a valid sentinel
     (dict(step=float("nan")), hq.HQ_ERR_INVALID_ARG),
     (dict(step=1e-6), hq.HQ_ERR_INVALID_ARG),
     (dict(step=1e6), hq.HQ_ERR_INVALID_ARG),
     (dict(target_bps=1.0), hq.HQ_ERR_RATE),          # below E8's floor of 1.125
+    (dict(lattice="a2", target_bps=1.4), hq.HQ_ERR_RATE),  # below A2's floor of 1.5 (coset bits)
     (dict(target_bps=13.0), hq.HQ_ERR_RATE),
     (dict(dither=True, lattice="z", target_bps=0.5), hq.HQ_ERR_RATE),
 ])

@@ -18,7 +18,7 @@ hq = pytest.importorskip("kv_quantization_tile_amd")
 
 pytestmark = pytest.mark.gpu
 
-LAT = {"z": 0, "d4": 1, "e8": 2}
+LAT = {"z": 0, "d4": 1, "e8": 2, "a2": 3}
 
 
 def dev(a: np.ndarray):
@@ -60,12 +60,14 @@ def boundary_check(orc, x, lattice, step, seed, dither, codes_gpu, codes_orc):
     if bad.size == 0:
         return 0
     v = orc.lattice_inputs(x, LAT[lattice], step, seed, dither).reshape(-1, 8).astype(np.float64)
-    half = 0.5 if lattice == "e8" else 1.0
+    half = 0.5 if lattice in ("e8", "a2") else 1.0
+    # squared-distance weights: A2 is quantised in stretched coordinates (odd slots / sqrt 3)
+    wm = np.tile([1.0, 3.0], 4) if lattice == "a2" else np.ones(8)
     for i in bad:
         cg = codes_gpu.reshape(-1, 8)[i] * half
         co = codes_orc.reshape(-1, 8)[i] * half
-        dg, do = ((v[i] - cg) ** 2).sum(), ((v[i] - co) ** 2).sum()
-        dist = abs(dg - do) / (2 * np.linalg.norm(cg - co))
+        dg, do = (wm * (v[i] - cg) ** 2).sum(), (wm * (v[i] - co) ** 2).sum()
+        dist = abs(dg - do) / (2 * np.sqrt((wm * (cg - co) ** 2).sum()))
         assert dist <= 1e-5, (i, dist)
     assert bad.size <= max(1, int(1e-6 * codes_orc.size / 8)), bad.size
     return bad.size
@@ -96,7 +98,7 @@ def _scaled_gaussian_tiles(T, seed):
     return x
 
 
-@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
 @pytest.mark.parametrize("dither", [False, True])
 @pytest.mark.parametrize("T", [1, 65, 130, 1000])
 def test_stream_parity_fixed_point(orc, lattice, dither, T):
@@ -110,7 +112,7 @@ def test_stream_parity_fixed_point(orc, lattice, dither, T):
         assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.decode(s_orc, x.size).view(np.uint32))
 
 
-@pytest.mark.parametrize("lattice", ["e8", "d4", "z"])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
 @pytest.mark.parametrize("dither", [False, True])
 def test_codes_parity_weight_slice(orc, lattice, dither):
     say(f"case: codes {lattice} dither={dither} weight 512x4096")
@@ -122,13 +124,17 @@ def test_codes_parity_weight_slice(orc, lattice, dither):
         boundary_check(orc, w, lattice, step, 3, dither, c_gpu.cpu().numpy(), c_orc)
 
 
-@pytest.mark.parametrize("case", ["tiny", "weight2048", "kv_dither"])
+@pytest.mark.parametrize("case", ["tiny", "weight2048", "kv_dither", "tiny_a2", "kv_dither_a2"])
 def test_rate_control_parity(orc, case):
     say(f"case: rate control {case}")
     if case == "tiny":
         x, lat, tb, seed, dither = synth.tiny(), "e8", 3.0, 0, False
     elif case == "weight2048":
         x, lat, tb, seed, dither = synth.weight(rows=2048), "e8", 4.0, 0, False
+    elif case == "tiny_a2":
+        x, lat, tb, seed, dither = synth.tiny(), "a2", 3.0, 0, False
+    elif case == "kv_dither_a2":
+        x, lat, tb, seed, dither = synth.kv(1, 0, heads=2, tokens=8192), "a2", 2.5, synth.kv_seed(1, 0), True
     else:
         x, lat, tb, seed, dither = synth.kv(1, 0, heads=2, tokens=8192), "e8", 2.0, synth.kv_seed(1, 0), True
     st, sb, k = orc.rate(x, LAT[lat], tb, seed=seed, dither=dither)
@@ -165,9 +171,9 @@ def test_kv_call_full_size(orc, layer, is_v, target):
     assert np.array_equal(bf16_host(y), orc.decode(s_orc, x.size, out_dtype="bf16"))
 
 
-@pytest.mark.parametrize("lattice", ["z", "d4"])
+@pytest.mark.parametrize("lattice", ["z", "d4", "a2"])
 def test_lattice_sweep_weight(orc, lattice):
-    """Lattice sweep on the 14336 x 4096 weight at 4 bps (Z and D4; E8 is covered above): the same
+    """Lattice sweep on the 14336 x 4096 weight at 4 bps (Z, D4, A2; E8 is covered above): the same
     step and Rice parameter as the oracle, identical stream and decode, rate within 0.01."""
     say(f"case: weight 14336x4096 {lattice} 4 bps")
     w = synth.weight()
@@ -182,18 +188,19 @@ def test_lattice_sweep_weight(orc, lattice):
 
 def test_lattice_sweep_distortion_order():
     """At an equal payload rate the lattice with the smaller normalized second moment gives the
-    smaller error: E8 < D4 < Z in normalized MSE on the weight at 4 bps."""
+    smaller error: E8 < D4 < Z, and A2 < Z, in normalized MSE on the weight at 4 bps."""
     say("case: lattice sweep distortion order")
     x = dev(synth.weight())
     xf = x.float()
     nmse = {}
-    for lat in ("z", "d4", "e8"):
+    for lat in ("z", "d4", "a2", "e8"):
         s, info = hq.hq_encode(x, lat, 4.0)
         assert abs(info["payload_bps"] - 4.0) <= 0.01
         y = hq.hq_decode(s, x.numel(), out_dtype=torch.float32)
         nmse[lat] = float(((y - xf) ** 2).sum() / (xf ** 2).sum())
     say(f"nmse {nmse}")
     assert nmse["e8"] < nmse["d4"] < nmse["z"]
+    assert nmse["a2"] < nmse["z"]
 
 
 @pytest.mark.parametrize("index", [0, 1, 6])
@@ -233,7 +240,7 @@ def test_zero_tiles_and_tiny_values(orc):
     x[10] = np.float32(1e-30) * x[10]
     x[11] = np.float32(1e-42)
     x[20] = np.float32(1e15) * x[20]
-    for lat in ("e8", "d4", "z"):
+    for lat in ("e8", "d4", "a2", "z"):
         for dither in (False, True):
             s_orc, _ = orc.encode(x, LAT[lat], 0.0, seed=1, dither=dither, step=0.25, rice_k=3)
             s_gpu, _ = hq.hq_encode(dev(x), lat, 0.0, seed=1, dither=dither, step=0.25, rice_k=3)

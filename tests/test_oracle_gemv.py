@@ -16,7 +16,7 @@ def test_hadamard128_is_sylvester(orc):
 
 
 @pytest.mark.parametrize("lattice,dither,target", [("e8", False, 4.0), ("e8", True, 2.0), ("d4", False, 3.0),
-                                                    ("z", False, 5.0)])
+                                                    ("a2", True, 3.0), ("z", False, 5.0)])
 def test_decode_coords_reconstruct_the_decode(orc, lattice, dither, target):
     """D H yhat / 128 in binary64 equals the oracle's binary32 decode up to the seven butterfly
     roundings: |difference| <= 8 u ||yhat_tile||_1 / 128 per value."""
