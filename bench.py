@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv", "kv_haar", "srft"],
                     default="weight",
-                    help="weight / kv: one tensor, the headline line; sweep: Z, D4 and E8 on the weight; "
+                    help="weight / kv: one tensor, the headline line; sweep: Z, A2, D4 and E8 on the weight; "
                          "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
                          "the 64 (layer, K|V) calls of the KV cache; gemv: fused decode + matrix-vector "
                          "product on the weight's stream; kv_haar: one KV call with the full per-layer "
@@ -172,9 +172,9 @@ def series(args):
         import synth
         xw = torch.from_numpy(synth.weight().reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
         tb = 4.0 if args.bps is None else args.bps
-        for lat in ("z", "d4", "e8"):
+        for lat in ("z", "a2", "d4", "e8"):
             items.append((lat, lambda: xw, lat, tb, 0, False))
-        workload = f"lattice sweep on the mlp weight 14336x4096 bf16 at {tb:g} bps: Z, D4, E8, no dither"
+        workload = f"lattice sweep on the mlp weight 14336x4096 bf16 at {tb:g} bps: Z, A2, D4, E8, no dither"
         steps, warmup = args.steps, args.warmup
     elif args.config == "model":
         import synth
