@@ -53,8 +53,10 @@ enum {
 /* Step range accepted by the codec: 2^-12 .. 2^12 (as binary32 bit patterns). */
 #define STEP_BITS_MIN ((uint32_t)(127 - 12) << 23)
 #define STEP_BITS_MAX ((uint32_t)(127 + 12) << 23)
-#define RC_SAMPLE_TILES 8192
-#define RC_CANDIDATES 8
+#define RC_SAMPLE_TILES 8192   /* pass B (and a fixed step's k choice) */
+#define RC_SAMPLE_TILES_A 2048 /* pass A */
+#define RC_CANDIDATES 8        /* pass A; pass B evaluates RC_CANDIDATES_B */
+#define RC_CANDIDATES_B 4
 #define RC_KWIN 4
 
 static float f32_from_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
@@ -618,12 +620,16 @@ int hqo_dequantize(const int32_t *codes, const uint16_t *scales, uint64_t n, int
 /* ~0.01 bps of the target").  The pages give no algorithm; reading:                              */
 /*  - payload rate = (coset bits + Rice bits) / values; the 16-bit tile scales, the chunk index  */
 /*    and padding are side information, reported apart;                                          */
-/*  - a jittered stratified sample of min(T, 8192) tiles: stratum i = [floor(iT/N),              */
-/*    floor((i+1)T/N)), one tile per stratum chosen by a 32-bit integer hash of i;               */
+/*  - a jittered stratified sample of N = min(T, 2048) tiles for pass A and min(T, 8192) for pass */
+/*    B: stratum i = [floor(iT/N), floor((i+1)T/N)), one tile per stratum chosen by a 32-bit      */
+/*    integer hash of i;                                                                          */
 /*  - the search variable is b = the binary32 bit pattern of the step (b / 2^23 - 127 is a        */
 /*    piecewise-linear log2 of the step);                                                         */
-/*  - pass A evaluates 8 candidates b0 + (2j-7) 2^21 around the Gaussian high-rate guess          */
-/*    log2 step = 2.05 - target; pass B 8 candidates (2j-7) 2^17 around pass A's answer;           */
+/*  - pass A evaluates 8 candidates b0 + (2j-7) 2^21 (quarter-octave spacing) around the Gaussian */
+/*    high-rate guess log2 step = 2.05 - target; pass B 4 candidates (2j-3) 2^18 (1/16 octave)     */
+/*    around pass A's answer.  Pass A lands within a few hundredths of an octave of the final     */
+/*    answer, well inside pass B's +-3/32 octave, and its result hardly depends on its sample     */
+/*    size, so the coarse pass uses the smaller sample;                                           */
 /*  - each candidate's Rice parameter is the argmin (ties to the smaller k) over the window        */
 /*    kb..kb+3, kb = clamp(-e - 2, 0, 12), e = the step's binary exponent;                        */
 /*  - after a pass, the answer is the linear interpolation between the two candidates that        */
@@ -778,33 +784,37 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
     *k_out = rice_k >= 0 ? rice_k : kwin_base(b0) + 1;
     return OK;
   }
-  double Tb = (double)target_bps * (double)(N * TILE);
-  double nominal = (double)(N * TILE) / 8388608.0;
   int64_t centre = b0;
-  const int spacing_log2[2] = {22, 18};
+  const uint64_t np[2] = {T < RC_SAMPLE_TILES_A ? T : RC_SAMPLE_TILES_A, N};
+  const int ncand[2] = {RC_CANDIDATES, RC_CANDIDATES_B};
+  const int half_log2[2] = {21, 18};
   for (int pass = 0; pass < 2; ++pass) {
+    const uint64_t Np = np[pass];
+    const int nc = ncand[pass];
+    const double Tb = (double)target_bps * (double)(Np * TILE);
+    const double nominal = (double)(Np * TILE) / 8388608.0;
     int64_t b[RC_CANDIDATES];
-    for (int j = 0; j < RC_CANDIDATES; ++j)
-      b[j] = clamp64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << (spacing_log2[pass] - 1)),
+    for (int j = 0; j < nc; ++j)
+      b[j] = clamp64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2[pass]),
                      STEP_BITS_MIN, STEP_BITS_MAX);
     uint64_t sumq[RC_CANDIDATES][RC_KWIN];
-    int rc = rc_eval(&q, x, dtype, T, N, RC_CANDIDATES, b, rice_k, sumq);
+    int rc = rc_eval(&q, x, dtype, T, Np, nc, b, rice_k, sumq);
     if (rc) return rc;
     double R[RC_CANDIDATES];
     int kc[RC_CANDIDATES];
-    for (int j = 0; j < RC_CANDIDATES; ++j) {
+    for (int j = 0; j < nc; ++j) {
       int kb = rice_k >= 0 ? rice_k : kwin_base(b[j]);
       int best = 0;
-      double rb = rc_bits(lattice, N, rice_k >= 0 ? rice_k : kb, sumq[j][0]);
+      double rb = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb, sumq[j][0]);
       for (int w = 1; w < RC_KWIN; ++w) {
-        double rw = rc_bits(lattice, N, rice_k >= 0 ? rice_k : kb + w, sumq[j][w]);
+        double rw = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb + w, sumq[j][w]);
         if (rw < rb) { rb = rw; best = w; }
       }
       R[j] = rb;
       kc[j] = rice_k >= 0 ? rice_k : kb + best;
     }
     int jn;
-    rc_solve(RC_CANDIDATES, b, R, Tb, nominal, &centre, &jn);
+    rc_solve(nc, b, R, Tb, nominal, &centre, &jn);
     k_ans = kc[jn];
   }
   b_ans = centre;
