@@ -112,7 +112,7 @@ int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t 
 
 /* Rate control alone (component 3's rate targeting): chooses the lattice step and Rice parameter
  * for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles meets
- * params->target_bps.  With info != NULL the call blocks and fills info (payload_bps is the target);
+ * params->target_bps (a coarse pass on min(T, 2048) tiles first).  With info != NULL the call blocks and fills info (payload_bps is the target);
  * with info == NULL it only enqueues work, and a following hq_encode with params->step == -1 on the
  * same workspace and stream encodes at the chosen point (the pair then does exactly what one
  * hq_encode with rate control does).  x must be 16-byte aligned and the workspace 256-byte aligned

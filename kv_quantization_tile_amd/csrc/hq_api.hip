@@ -93,27 +93,44 @@ int64_t initial_centre(float target) {
   return (int64_t)(127u << 23) + (int64_t)floor((2.05 - (double)target) * 8388608.0 + 0.5);
 }
 
-// init + rate passes (when needed); leaves step and k in the workspace.
-int run_rate_control(const EncodeArgs& a) {
+// The rate pass whose solve is still to be done after run_rate_control (pass < 0: none; the
+// workspace holds the operating point).
+struct LastPass {
+  int pass = -1, nc = 0, half_log2 = 0;
+  uint32_t N = 0;
+};
+
+// init + rate passes (when needed).  Pass B solves pass A inside its own launch; the caller solves
+// the last pass with one more launch (launch_rate_solve).
+int run_rate_control(const EncodeArgs& a, LastPass* last) {
   const uint64_t T = a.tiles;
   const uint32_t N = (uint32_t)(T < kRcSampleTiles ? T : kRcSampleTiles);
+  const uint32_t NA = (uint32_t)(T < kRcSampleTilesA ? T : kRcSampleTilesA);
   hipError_t e;
+  *last = LastPass{};
   if (a.fixed_step_bits) {
     e = launch_init(a, (int64_t)a.fixed_step_bits);
     if (e != hipSuccess) return HQ_ERR_HIP;
     if (a.rice_k < 0 && N > 0) {
       e = launch_rate_pass(a, 1, 0, N, 0);
       if (e != hipSuccess) return HQ_ERR_HIP;
+      last->pass = 0;
+      last->nc = 1;
+      last->N = N;
     }
     return HQ_OK;
   }
   e = launch_init(a, initial_centre(a.target));
   if (e != hipSuccess) return HQ_ERR_HIP;
   if (N == 0) return HQ_OK;
-  e = launch_rate_pass(a, kRcCand, 21, N, 0);
+  e = launch_rate_pass(a, kRcCand, 21, NA, 0);
   if (e != hipSuccess) return HQ_ERR_HIP;
-  e = launch_rate_pass(a, kRcCand, 17, N, 1);
+  e = launch_rate_pass(a, kRcCandB, 18, N, 1, kRcCand, 21, NA);
   if (e != hipSuccess) return HQ_ERR_HIP;
+  last->pass = 1;
+  last->nc = kRcCandB;
+  last->half_log2 = 18;
+  last->N = N;
   return HQ_OK;
 }
 
@@ -194,8 +211,11 @@ int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, h
   if (((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   if (params->step == -1.0f) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
-  rc = run_rate_control(a);
+  LastPass last;
+  rc = run_rate_control(a, &last);
   if (rc) return rc;
+  if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
+    return HQ_ERR_HIP;
   if (!info) return HQ_OK;  // asynchronous: the operating point stays in the workspace
   Workspace h;
   if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
@@ -222,8 +242,11 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
   if (((uintptr_t)out & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, out, out_capacity, workspace, stream);
   if (params->step != -1.0f) {
-    rc = run_rate_control(a);
+    LastPass last;
+    rc = run_rate_control(a, &last);
     if (rc) return rc;
+    if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
+      return HQ_ERR_HIP;
   }
   if (launch_encode(a) != hipSuccess) return HQ_ERR_HIP;
   if (!out_bytes) return HQ_OK;

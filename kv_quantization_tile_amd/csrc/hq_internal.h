@@ -11,8 +11,10 @@ enum { kErrNonfinite = 1u, kErrCapacity = 2u, kErrCorrupt = 4u, kErrTimeout = 8u
 
 // Rate control (the pages ask for a realised rate within ~0.01 bits per value and give no
 // algorithm; see hq_kernels.hip for the search).
-constexpr uint32_t kRcSampleTiles = 8192;
-constexpr int kRcCand = 8;
+constexpr uint32_t kRcSampleTiles = 8192;   // pass B (and a fixed step's Rice choice)
+constexpr uint32_t kRcSampleTilesA = 2048;  // pass A
+constexpr int kRcCand = 8;                  // pass A; the most a pass evaluates
+constexpr int kRcCandB = 4;
 constexpr int kRcKwin = 4;
 
 // Device workspace.  The fixed part is 4 KiB; the encoder's look-back flags (one 64-bit word per
@@ -45,6 +47,10 @@ struct alignas(256) Workspace {
   uint64_t dec_fixed_off;
   uint64_t dec_unary_off;
   uint64_t dec_words;
+  // pass B's centre, which its workgroup 0 solves from pass A and publishes to the rest of the
+  // launch (bit 63 set = published, the centre in the low 32 bits; relaxed agent-scope atomics,
+  // the value travels in the word itself).  init_kernel clears it.
+  uint64_t sync_centre;
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
@@ -86,7 +92,13 @@ struct EncodeArgs {
 };
 
 hipError_t launch_init(const EncodeArgs& a, int64_t centre);
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass);
+// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its workgroup 0, with pass 0's
+// candidates (nc0, half_spacing_log2_0, sample0); pass 0 reads the centre init_kernel stored.
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass,
+                            int nc0 = 0, int half_spacing_log2_0 = 0, uint32_t sample0 = 0);
+// One-workgroup solve of a rate pass into the workspace's step and k (hq_rate's last launch).
+hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass);
+// The encoder, at the operating point the workspace holds.
 hipError_t launch_encode(const EncodeArgs& a);
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
                          Workspace* ws, hipStream_t stream);

@@ -92,14 +92,14 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   return x;
 }
-// N is min(T, kRcSampleTiles): for every tensor of at least that many tiles the divisions are
+// N is min(T, the pass's sample size), a power of two whenever N < T: then the divisions are
 // shifts; the stratum width hi - lo is below 2^32, so the pick is a 32-bit remainder.
-static_assert(kRcSampleTiles == 8192, "the stratum bounds below shift by 13");
 __device__ __forceinline__ uint64_t sample_tile(uint64_t i, uint64_t T, uint64_t N) {
   uint64_t lo, hi;
-  if (N == kRcSampleTiles) {
-    lo = (i * T) >> 13;
-    hi = ((i + 1) * T) >> 13;
+  if (N < T && (N & (N - 1)) == 0) {
+    const uint32_t sh = (uint32_t)__builtin_ctzll(N);
+    lo = (i * T) >> sh;
+    hi = ((i + 1) * T) >> sh;
   } else {
     lo = (i * T) / N;
     hi = ((i + 1) * T) / N;
@@ -209,6 +209,7 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
     ws->res_words = 0;
     ws->res_step_bits = step_bits;
     ws->res_k = k;
+    ws->sync_centre = 0;
   }
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
   for (uint64_t i = gid; i < nacc; i += (uint64_t)gridDim.x * blockDim.x) acc[i] = 0;
@@ -217,22 +218,23 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
 // ---------------------------------------------------------------------------------------------
 // Rate control.  The pages fix only the outcome (realised rate within ~0.01 bits per value); the
 // search is this codec's reading:
-//  - sample: N = min(T, 8192) tiles, one per stratum [floor(iT/N), floor((i+1)T/N)), picked by a
-//    32-bit hash of i;
+//  - sample: N = min(T, 2048) tiles for pass A, min(T, 8192) for pass B, one per stratum
+//    [floor(iT/N), floor((i+1)T/N)), picked by a 32-bit hash of i;
 //  - the search variable is b, the binary32 bit pattern of the step;
-//  - a pass evaluates up to 8 candidates centre + (2j-7) 2^h (clamped to [2^-12, 2^12]); for each,
-//    the Rice k is the argmin (ties: smaller k) over kb..kb+3, kb = clamp(-exponent - 2, 0, 12);
+//  - a pass evaluates nc candidates centre + (2j-(nc-1)) 2^h (clamped to [2^-12, 2^12]); for
+//    each, the Rice k is the argmin (ties: smaller k) over kb..kb+3, kb = clamp(-exponent - 2, 0, 12);
 //  - the solve kernel interpolates linearly (IEEE double) between the two candidates that
 //    bracket the target bit count (first candidate at or below it) or extrapolates from the end
 //    pair, rounds, clamps, and stores the answer as the next centre together with the k of the
-//    candidate nearest to it.  Pass A (h = 21) starts at 2.05 - target octaves; pass B (h = 17)
-//    refines.  With a fixed step and automatic k one pass with the single candidate picks k.
+//    candidate nearest to it.  Pass A (8 candidates, h = 21: quarter octaves) starts at
+//    2.05 - target octaves; pass B (4 candidates, h = 18: 1/16 octave) refines.  With a fixed step
+//    and automatic k one pass (8192 tiles) with the single candidate picks k.
 // Bits of candidate j over the Rice window (lane j of the solving wavefront computes its own).
 template <int LAT>
 __device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t centre, int j, int nc, int half_log2,
                                                int fixed_k, uint32_t N, int64_t* b_out, double* R_out, int* k_out) {
   const int64_t b = nc == 1 ? centre
-                            : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
+                            : clamp_i64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2), kStepBitsMin,
                                         kStepBitsMax);
   const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
   int best = 0;
@@ -251,9 +253,10 @@ __device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t cen
   *k_out = fixed_k >= 0 ? fixed_k : kb + best;
 }
 
-// Bracket, interpolate and store the answer (one lane; b, R, kc per candidate).
-__device__ void rate_solve(Workspace* ws, const int64_t* b, const double* R, const int* kc, int nc, float target,
-                           uint32_t N) {
+// Bracket, interpolate and round: the next centre (or the final step bits) and the k of the
+// candidate nearest to it (one lane; b, R, kc per candidate).
+__device__ void rate_solve(const int64_t* b, const double* R, const int* kc, int nc, float target, uint32_t N,
+                           int64_t* xb_out, int* k_out) {
   const double Tb = (double)target * (double)((uint64_t)N * kTile);
   const double nominal = (double)((uint64_t)N * kTile) / 8388608.0;
   double xv;
@@ -293,33 +296,133 @@ __device__ void rate_solve(Workspace* ws, const int64_t* b, const double* R, con
     const int64_t db = b[best] > xb ? b[best] - xb : xb - b[best];
     if (di < db) best = i;
   }
-  ws->rc_centre = xb;
-  ws->step_bits = (uint32_t)xb;
-  ws->rice_k = kc[best];
+  *xb_out = xb;
+  *k_out = kc[best];
 }
 
+// One rate pass's counters and candidates, for its solver.
+struct PassDesc {
+  const RateAcc* racc;
+  int nc, half_log2, fixed_k;
+  float target;
+  uint32_t N;
+};
+
+struct SolveLds {
+  uint64_t sumq[kRcCounters];
+  int64_t b[kRcCand];
+  double R[kRcCand];
+  int k[kRcCand];
+  int64_t xb;
+  int kres;
+};
+
+// Solve a rate pass around `centre` with the first lanes of a workgroup (every lane of the
+// workgroup calls it: it holds two barriers).  The counter sets are added in a fixed order; every
+// lane gets the result, and the workspace's step, k and centre are set to it.
+template <int LAT>
+__device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, SolveLds* L, int64_t* xb, int* k) {
+  const int tid = threadIdx.x;
+  if (tid < kRcCounters) {
+    uint64_t t = 0;
+#pragma unroll
+    for (int sl = 0; sl < kRcAccSlots; ++sl) t += pd.racc->cnt[sl][tid];
+    L->sumq[tid] = t;
+  }
+  __syncthreads();
+  if (tid < pd.nc) {
+    int64_t b;
+    double R;
+    int kk;
+    rate_candidate<LAT>(L->sumq, centre, tid, pd.nc, pd.half_log2, pd.fixed_k, pd.N, &b, &R, &kk);
+    L->b[tid] = b;
+    L->R[tid] = R;
+    L->k[tid] = kk;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, &L->xb, &L->kres);
+    ws->rc_centre = L->xb;
+    ws->step_bits = (uint32_t)L->xb;
+    ws->rice_k = L->kres;
+  }
+  __syncthreads();
+  *xb = L->xb;
+  *k = L->kres;
+}
+
+// Waits (one lane per wavefront, bounded) until workgroup 0 of this launch has published `word`
+// (bit 63 set) and returns it, wave-uniform; 0 after the bound, with kErrTimeout recorded.
+// Workgroup 0 is dispatched first and publishes without waiting on anyone, so the wait ends.
+__device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
+  uint64_t v = 0;
+  if ((threadIdx.x & 63) == 0) {
+    uint32_t spins = 0;
+    while (true) {
+      v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v >> 63) break;
+      if (++spins > kSpinLimit) {
+        atomicOr(status, (uint32_t)kErrTimeout);
+        v = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// A wavefront takes 4 sample tiles and cpw of the pass's candidates; the cw = ceil(nc / cpw)
+// wavefronts that share a group of 4 tiles sit in the same workgroup, which therefore holds 4 / cw
+// tile groups (cw is 1, 2 or 4).  Splitting the candidates over wavefronts keeps each wavefront's
+// chain short and the pass latency low; every wavefront repeats its tiles' transform.
+// With solve_prev, workgroup 0 first solves the previous pass (prev) for this pass's centre and
+// publishes it in Workspace::sync_centre; the other workgroups transform their tiles meanwhile and
+// then wait for it.
 template <int LAT, bool DITHER, int DT>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
                                                       Workspace* ws, RateAcc* racc, uint64_t seed, int nc,
-                                                      int half_log2, int fixed_k, float target) {
+                                                      int half_log2, int fixed_k, float target, int cpw,
+                                                      int solve_prev, PassDesc prev) {
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
+  __shared__ SolveLds s_solve;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
-  const uint64_t i = (uint64_t)blockIdx.x * 16 + wave * 4 + tw;
+  int64_t centre_solved = 0;
+  if (solve_prev && blockIdx.x == 0) {
+    int kk;
+    solve_pass<LAT>(prev, ws->rc_centre, ws, &s_solve, &centre_solved, &kk);
+    if (tid == 0)
+      __hip_atomic_store(&ws->sync_centre, (1ull << 63) | (uint64_t)(uint32_t)centre_solved, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int cw = (nc + cpw - 1) / cpw;
+  const int jlo = (wave % cw) * cpw, jhi = jlo + cpw;
+  const uint64_t i = ((uint64_t)blockIdx.x * (4 / cw) + wave / cw) * 4 + tw;
   const bool valid = i < N;
   const uint64_t t = valid ? sample_tile(i, T, N) : 0;
   const uint32_t sgn = octet_sign_bits(seed, o);
   float y[8];
   bool finite;
   const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
-  if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+  if (valid && !finite && o == 0 && jlo == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
-  const int64_t centre = ws->rc_centre;
+  int64_t centre;
+  if (!solve_prev) {
+    centre = ws->rc_centre;  // stored by init_kernel
+  } else if (blockIdx.x == 0) {
+    centre = centre_solved;
+  } else {
+    const uint64_t w = wait_published(&ws->sync_centre, &ws->status);
+    centre = (w >> 63) ? (int64_t)(uint32_t)w : ws->rc_centre;
+  }
   // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots);
   // the group shares them by broadcast
   const int jm = nc == 1 ? 0 : (o & 7);
   const int64_t bm = nc == 1 ? centre
-                             : clamp_i64(centre + (int64_t)(2 * jm - 7) * ((int64_t)1 << half_log2), kStepBitsMin,
+                             : clamp_i64(centre + (int64_t)(2 * jm - (nc - 1)) * ((int64_t)1 << half_log2), kStepBitsMin,
                                          kStepBitsMax);
   const float stepm = __uint_as_float((uint32_t)bm);
   const uint32_t m_mine = __float_as_uint((LAT == kLatA2 && o >= 8) ? tile_multiplier<true>(sb, stepm, 0u)
@@ -346,9 +449,9 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
     for (int w = 0; w < kRcKwin; ++w) acc[j][w] = 0;
 #pragma unroll
   for (int j = 0; j < kRcCand; ++j) {
-    if (j < nc) {
+    if (j < nc && j >= jlo && j < jhi) {  // uniform
       const int64_t b = nc == 1 ? centre
-                                : clamp_i64(centre + (int64_t)(2 * j - 7) * ((int64_t)1 << half_log2),
+                                : clamp_i64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2),
                                             kStepBitsMin, kStepBitsMax);
       const float m = lane_neg ? -mj[j] : mj[j];
       const float m1 = lane_neg ? -mo[j] : mo[j];
@@ -372,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   for (int j = 0; j < kRcCand; ++j)
 #pragma unroll
     for (int w = 0; w < kRcKwin; ++w)
-      if (j < nc && acc[j][w]) atomicAdd(&s_red[0][j * kRcKwin + w], acc[j][w]);
+      if (j < nc && j >= jlo && j < jhi && acc[j][w]) atomicAdd(&s_red[0][j * kRcKwin + w], acc[j][w]);
   __syncthreads();
   // this workgroup's sums go into counter set blockIdx mod kRcAccSlots; rate_solve_kernel, the next
   // launch on the stream, adds the sets up (the kernel boundary orders the atomics before its loads)
@@ -383,32 +486,11 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
 
 // One workgroup: add up the counter sets of a rate pass, evaluate the candidates, solve.
 template <int LAT>
-__global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, const RateAcc* __restrict__ racc, int nc,
-                                                        int half_log2, int fixed_k, float target, uint32_t N) {
-  __shared__ uint64_t s_sumq[kRcCounters];
-  __shared__ int64_t s_b[kRcCand];
-  __shared__ double s_R[kRcCand];
-  __shared__ int s_k[kRcCand];
-  const int tid = threadIdx.x;
-  if (tid < kRcCounters) {
-    uint64_t t = 0;
-#pragma unroll
-    for (int sl = 0; sl < kRcAccSlots; ++sl) t += racc->cnt[sl][tid];
-    s_sumq[tid] = t;
-  }
-  __syncthreads();
-  const int64_t centre = ws->rc_centre;
-  if (tid < nc) {
-    int64_t b;
-    double R;
-    int k;
-    rate_candidate<LAT>(s_sumq, centre, tid, nc, half_log2, fixed_k, N, &b, &R, &k);
-    s_b[tid] = b;
-    s_R[tid] = R;
-    s_k[tid] = k;
-  }
-  __syncthreads();
-  if (tid == 0) rate_solve(ws, s_b, s_R, s_k, nc, target, N);
+__global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, PassDesc pd) {
+  __shared__ SolveLds s_solve;
+  int64_t xb;
+  int k;
+  solve_pass<LAT>(pd, ws->rc_centre, ws, &s_solve, &xb, &k);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1327,28 +1409,47 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
   return hipGetLastError();
 }
 
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
-  const uint32_t blocks = (N + 15) / 16;
+static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
+  PassDesc d;
+  d.racc = rate_acc(a.ws, pass);
+  d.nc = nc;
+  d.half_log2 = half_log2;
+  d.fixed_k = a.rice_k;
+  d.target = a.target;
+  d.N = N;
+  return d;
+}
+
+hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass, int nc0,
+                            int half_log2_0, uint32_t N0) {
+  // pass A (8 candidates, a small sample): two candidates per wavefront, so that the pass is not
+  // one long chain per wavefront; otherwise every wavefront takes all candidates of its tiles
+  const int cpw = nc == kRcCand ? 2 : nc;
+  const int cw = (nc + cpw - 1) / cpw;  // 1, 2 or 4 wavefronts per group of 4 tiles
+  if (cw != 1 && cw != 2 && cw != 4) return hipErrorInvalidValue;  // nc is 1, 2, 4 or 8
+  const uint32_t tiles_per_block = 4u * (uint32_t)(4 / cw);
+  const uint32_t blocks = (N + tiles_per_block - 1) / tiles_per_block;
   if (blocks == 0) return hipSuccess;
+  const int solve_prev = pass > 0 ? 1 : 0;
+  const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1) : PassDesc{};
 #define HQ_RATE(L, D, T)                                                                              \
   hipLaunchKernelGGL((rate_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
-                     rate_acc(a.ws, pass), a.seed, nc, half_log2, a.rice_k, a.target)
+                     rate_acc(a.ws, pass), a.seed, nc, half_log2, a.rice_k, a.target, cpw, solve_prev, prev)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_RATE);
 #undef HQ_RATE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-#define HQ_SOLVE(L)                                                                                   \
-  hipLaunchKernelGGL((rate_solve_kernel<L>), dim3(1), dim3(64), 0, a.stream, a.ws, rate_acc(a.ws, pass), nc, \
-                     half_log2, a.rice_k, a.target, N)
+  return hipGetLastError();
+}
+
+hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
+  const PassDesc pd = pass_desc(a, nc, half_log2, N, pass);
   if (a.lattice == kLatE8)
-    HQ_SOLVE(kLatE8);
+    hipLaunchKernelGGL((rate_solve_kernel<kLatE8>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
   else if (a.lattice == kLatA2)
-    HQ_SOLVE(kLatA2);
+    hipLaunchKernelGGL((rate_solve_kernel<kLatA2>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
   else if (a.lattice == kLatD4)
-    HQ_SOLVE(kLatD4);
+    hipLaunchKernelGGL((rate_solve_kernel<kLatD4>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
   else
-    HQ_SOLVE(kLatZ);
-#undef HQ_SOLVE
+    hipLaunchKernelGGL((rate_solve_kernel<kLatZ>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
   return hipGetLastError();
 }
 
