@@ -52,11 +52,17 @@ def lib():
         u64, u32, i32, f32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float
         L.hqo_philox4x32_10.argtypes = [P, P, P]
         L.hqo_signs.argtypes = [u64, P]
+        L.hqo_signs_n.argtypes = [u64, i32, P]
         L.hqo_fwht128.argtypes = [P]
+        L.hqo_fwht_n.argtypes = [P, i32]
         L.hqo_sumsq128.argtypes = [P]
         L.hqo_sumsq128.restype = f32
+        L.hqo_sumsq_n.argtypes = [P, i32]
+        L.hqo_sumsq_n.restype = f32
         L.hqo_scale_bits.argtypes = [f32]
         L.hqo_scale_bits.restype = ctypes.c_uint16
+        L.hqo_scale_bits_n.argtypes = [f32, i32]
+        L.hqo_scale_bits_n.restype = ctypes.c_uint16
         L.hqo_nearest_octet.argtypes = [i32, P, P]
         L.hqo_nearest_batch.argtypes = [i32, P, u64, P]
         L.hqo_dither_octet.argtypes = [u64, u64, i32, i32, P]
@@ -64,15 +70,17 @@ def lib():
         L.hqo_unstrip_octet.argtypes = [i32, P, i32, P]
         L.hqo_tile_fixed_bits.argtypes = [i32, i32]
         L.hqo_tile_fixed_bits.restype = u32
-        L.hqo_quantize.argtypes = [P, i32, u64, i32, i32, u64, f32, P, P]
-        L.hqo_dequantize.argtypes = [P, P, u64, i32, i32, u64, f32, P]
-        L.hqo_lattice_inputs.argtypes = [P, i32, u64, i32, i32, u64, f32, P]
+        L.hqo_tile_fixed_bits_n.argtypes = [i32, i32, i32]
+        L.hqo_tile_fixed_bits_n.restype = u32
+        L.hqo_quantize.argtypes = [P, i32, u64, i32, i32, u64, f32, P, P, i32]
+        L.hqo_dequantize.argtypes = [P, P, u64, i32, i32, u64, f32, P, i32]
+        L.hqo_lattice_inputs.argtypes = [P, i32, u64, i32, i32, u64, f32, P, i32]
         L.hqo_sample_tile.argtypes = [u64, u64, u64]
         L.hqo_sample_tile.restype = u64
-        L.hqo_rate.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, P]
+        L.hqo_rate.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, P, i32]
         L.hqo_rice_roundtrip.argtypes = [P, u64, i32, P, P, P, u64, P]
-        L.hqo_encode_layout.argtypes = [u64, i32, i32, P, P, P]
-        L.hqo_encode.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, u64, P, P]
+        L.hqo_encode_layout.argtypes = [u64, i32, i32, P, P, P, i32]
+        L.hqo_encode.argtypes = [P, i32, u64, i32, i32, u64, f32, f32, i32, P, u64, P, P, i32]
         L.hqo_decode.argtypes = [P, u64, u64, P, i32]
         L.hqo_decode_coords.argtypes = [P, u64, u64, P]
         L.hqo_haar_matrix.argtypes = [u64, P]
@@ -119,9 +127,15 @@ def philox4x32_10(counter, key) -> np.ndarray:
     return out
 
 
-def signs(seed: int) -> np.ndarray:
-    d = np.zeros(128, dtype=np.float32)
-    lib().hqo_signs(seed, _p(d))
+TILES = (64, 128, 256)
+
+
+def signs(seed: int, tile: int = 128) -> np.ndarray:
+    d = np.zeros(tile, dtype=np.float32)
+    if tile == 128:
+        lib().hqo_signs(seed, _p(d))
+    else:
+        lib().hqo_signs_n(seed, tile, _p(d))
     return d
 
 
@@ -132,13 +146,28 @@ def fwht128(x) -> np.ndarray:
     return y
 
 
+def fwht(x) -> np.ndarray:
+    """The unnormalised transform of one tile of 64, 128 or 256 values."""
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    assert y.shape in ((64,), (128,), (256,))
+    lib().hqo_fwht_n(_p(y), y.size)
+    return y
+
+
 def sumsq128(y) -> float:
     y = np.ascontiguousarray(y, dtype=np.float32)
     return float(lib().hqo_sumsq128(_p(y)))
 
 
-def scale_bits(S: float) -> int:
-    return int(lib().hqo_scale_bits(ctypes.c_float(S)))
+def sumsq(y) -> float:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    return float(lib().hqo_sumsq_n(_p(y), y.size))
+
+
+def scale_bits(S: float, tile: int = 128) -> int:
+    if tile == 128:
+        return int(lib().hqo_scale_bits(ctypes.c_float(S)))
+    return int(lib().hqo_scale_bits_n(ctypes.c_float(S), tile))
 
 
 def nearest(lattice: int, v) -> np.ndarray:
@@ -170,8 +199,10 @@ def unstrip_octet(lattice: int, sym, coset: int) -> np.ndarray:
     return out
 
 
-def tile_fixed_bits(lattice: int, k: int) -> int:
-    return int(lib().hqo_tile_fixed_bits(lattice, k))
+def tile_fixed_bits(lattice: int, k: int, tile: int = 128) -> int:
+    if tile == 128:
+        return int(lib().hqo_tile_fixed_bits(lattice, k))
+    return int(lib().hqo_tile_fixed_bits_n(lattice, k, tile))
 
 
 def sample_tile(i: int, T: int, N: int) -> int:
@@ -193,56 +224,58 @@ def rice_roundtrip(vals, k: int):
 
 # ---- the codec ----------------------------------------------------------------------------------
 
-def quantize(x: np.ndarray, lattice: int, step: float, seed: int = 0, dither: bool = False):
+def quantize(x: np.ndarray, lattice: int, step: float, seed: int = 0, dither: bool = False, tile: int = 128):
     """Per-value integer codes (int32) and per-tile bf16 scale bits (uint16) at a fixed step."""
     x = np.ascontiguousarray(x).reshape(-1)
     n = x.size
     codes = np.zeros(n, dtype=np.int32)
-    scales = np.zeros(max(n // 128, 1), dtype=np.uint16)
+    scales = np.zeros(max(n // tile, 1), dtype=np.uint16)
     _check(lib().hqo_quantize(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
-                              ctypes.c_float(step), _p(codes), _p(scales)), "quantize")
-    return codes, scales[: n // 128]
+                              ctypes.c_float(step), _p(codes), _p(scales), tile), "quantize")
+    return codes, scales[: n // tile]
 
 
-def lattice_inputs(x, lattice: int, step: float, seed: int = 0, dither: bool = False) -> np.ndarray:
+def lattice_inputs(x, lattice: int, step: float, seed: int = 0, dither: bool = False,
+                   tile: int = 128) -> np.ndarray:
     """The binary32 values fed to the nearest-point step (y * m, plus U with dither)."""
     x = np.ascontiguousarray(x).reshape(-1)
     v = np.zeros(x.size, dtype=np.float32)
     _check(lib().hqo_lattice_inputs(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
-                                    ctypes.c_float(step), _p(v)), "lattice_inputs")
+                                    ctypes.c_float(step), _p(v), tile), "lattice_inputs")
     return v
 
 
-def dequantize(codes, scales, lattice: int, step: float, seed: int = 0, dither: bool = False):
+def dequantize(codes, scales, lattice: int, step: float, seed: int = 0, dither: bool = False, tile: int = 128):
     codes = np.ascontiguousarray(codes, dtype=np.int32)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     out = np.zeros(codes.size, dtype=np.float32)
     _check(lib().hqo_dequantize(_p(codes), _p(scales), codes.size, lattice, int(bool(dither)), seed,
-                                ctypes.c_float(step), _p(out)), "dequantize")
+                                ctypes.c_float(step), _p(out), tile), "dequantize")
     return out
 
 
 def rate(x, lattice: int, target_bps: float, seed: int = 0, dither: bool = False, step: float = 0.0,
-         rice_k: int = -1):
+         rice_k: int = -1, tile: int = 128):
     """Rate control only: returns (step as float32, step bit pattern, k)."""
     x = np.ascontiguousarray(x).reshape(-1)
     sb = ctypes.c_uint32(0)
     k = ctypes.c_int(0)
     _check(lib().hqo_rate(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
                           ctypes.c_float(target_bps), ctypes.c_float(step), rice_k,
-                          ctypes.byref(sb), ctypes.byref(k)), "rate")
+                          ctypes.byref(sb), ctypes.byref(k), tile), "rate")
     step_f = np.array([sb.value], dtype=np.uint32).view(np.float32)[0]
     return float(step_f), sb.value, k.value
 
 
-def layout(n: int, lattice: int, k: int):
+def layout(n: int, lattice: int, k: int, tile: int = 128):
     fo, uo, F = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint32(0)
-    lib().hqo_encode_layout(n, lattice, k, ctypes.byref(fo), ctypes.byref(uo), ctypes.byref(F))
+    _check(lib().hqo_encode_layout(n, lattice, k, ctypes.byref(fo), ctypes.byref(uo), ctypes.byref(F), tile),
+           "layout")
     return fo.value, uo.value, F.value
 
 
 def encode(x, lattice: int, target_bps: float = 4.0, seed: int = 0, dither: bool = False,
-           step: float = 0.0, rice_k: int = -1, capacity: int | None = None):
+           step: float = 0.0, rice_k: int = -1, capacity: int | None = None, tile: int = 128):
     """Full encoder.  Returns (stream bytes as uint8 array, info dict)."""
     x = np.ascontiguousarray(x).reshape(-1)
     n = x.size
@@ -254,7 +287,7 @@ def encode(x, lattice: int, target_bps: float = 4.0, seed: int = 0, dither: bool
         out = np.zeros(capacity, dtype=np.uint8)
         rc = lib().hqo_encode(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
                               ctypes.c_float(target_bps), ctypes.c_float(step), rice_k, _p(out),
-                              capacity, ctypes.byref(nbytes), _p(info))
+                              capacity, ctypes.byref(nbytes), _p(info), tile)
         if rc == ERR_CAPACITY and nbytes.value > capacity:
             capacity = int(nbytes.value)
             continue
@@ -282,32 +315,36 @@ def decode(stream, n: int, out_dtype: str = "f32"):
 
 def decode_coords(stream, n: int) -> np.ndarray:
     """yhat = (c - U) * (s * step) per value, binary64: the exact reconstruction of tile t is
-    D H yhat_t / 128."""
+    D H yhat_t / tile."""
     s = np.ascontiguousarray(stream, dtype=np.uint8)
     out = np.zeros(n, dtype=np.float64)
     _check(lib().hqo_decode_coords(_p(s), s.size, n, _p(out)), "decode_coords")
     return out
 
 
-def hadamard128() -> np.ndarray:
-    """Sylvester H_128 = H_2 (x) ... (x) H_2, entries +-1 (natural order)."""
+def hadamard(n: int = 128) -> np.ndarray:
+    """Sylvester H_n = H_2 (x) ... (x) H_2, entries +-1 (natural order)."""
     h = np.array([[1.0]])
-    for _ in range(7):
+    while h.shape[0] < n:
         h = np.block([[h, h], [h, -h]])
     return h
 
 
-def gemv_reference(stream, rows: int, cols: int, x: np.ndarray, seed: int):
-    """Matrix-vector product with the decoded [rows][cols] matrix (tiles of 128 along cols), in
-    binary64, by the plain definition: W_hat = D H yhat / 128 per tile, y = W_hat x.
+def hadamard128() -> np.ndarray:
+    return hadamard(128)
+
+
+def gemv_reference(stream, rows: int, cols: int, x: np.ndarray, seed: int, tile: int = 128):
+    """Matrix-vector product with the decoded [rows][cols] matrix (tiles of `tile` values along
+    cols), in binary64, by the plain definition: W_hat = D H yhat / tile per tile, y = W_hat x.
     Also returns, per row, B_r = sum over the row's tiles of sum_i |yhat_i| * ||x_tile||_1, the
     scale of the rounding error of any binary32 evaluation that rotates x per tile."""
     n = rows * cols
-    yh = decode_coords(stream, n).reshape(rows, cols // 128, 128)
-    d = signs(seed).astype(np.float64)
-    h = hadamard128()
-    w = (yh @ h.T) * d / 128.0          # row-major tiles: w[r, j, :] = D H yhat[r, j, :] / 128
-    xf = np.asarray(x, dtype=np.float64).reshape(cols // 128, 128)
+    yh = decode_coords(stream, n).reshape(rows, cols // tile, tile)
+    d = signs(seed, tile).astype(np.float64)
+    h = hadamard(tile)
+    w = (yh @ h.T) * d / float(tile)    # row-major tiles: w[r, j, :] = D H yhat[r, j, :] / tile
+    xf = np.asarray(x, dtype=np.float64).reshape(cols // tile, tile)
     y = np.einsum("rji,ji->r", w, xf)
     bound = np.einsum("rji,j->r", np.abs(yh), np.abs(xf).sum(axis=1))
     return y, bound

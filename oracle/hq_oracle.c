@@ -7,7 +7,8 @@
  *
  * What it computes follows the HyperQuant technical summaries (gist.science/ko/paper/2606.23406 and
  * gist.science/ja/paper/2606.23406), section "Methodology: the HyperQuant pipeline":
- *   component 1 (per-tile randomized Hadamard transform  RHT_n(x) = H_n D x, tiles of 128),
+ *   component 1 (per-tile randomized Hadamard transform  RHT_n(x) = H_n D x, tiles of 128, or of
+ *   64 or 256: the summary gives 128 as an example size),
  *   component 2 (nearest-point quantisation onto E8 / D4 / A2 / Z with an integer embedding and a
  *   scale),
  *   component 3 (bit-stripping of lattice-fixed bits, then Rice coding; rate within ~0.01 bps),
@@ -29,9 +30,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define TILE 128
-#define CHUNK_TILES 64
+#define TILE 128            /* the default tile length; 64 and 256 are the other lengths */
+#define TILE_MAX 256
+#define CHUNK_VALUES 8192   /* a chunk holds 8192 / tile tiles: 128, 64 or 32 */
 #define HEADER_BYTES 128
+#define HAAR_N 128          /* dimension of the per-layer rotation */
 #define MAGIC 0x31305148u /* bytes 'H' 'Q' '0' '1' */
 #define VERSION 1
 
@@ -88,25 +91,30 @@ void hqo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint3
 }
 
 /* Sign diagonal D of the RHT (HyperQuant summary, Methodology component 1: "D is a random sign
- * diagonal").  Reading: one D per call, shared by every tile, drawn from one Philox call with
- * key = (seed low word, seed high word) and counter (0,0,0,0); D_i = -1 iff bit (i mod 32) of
- * output word floor(i/32) is set.  The KV path's per-layer +-1 rotation (component 4) is the
- * same kind of diagonal, so it is folded into D by giving each (layer, K|V) call its own seed. */
-void hqo_signs(uint64_t seed, float d[TILE]) {
-  uint32_t ctr[4] = {0, 0, 0, 0}, key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[4];
-  hqo_philox4x32_10(ctr, key, w);
-  for (int i = 0; i < TILE; ++i) d[i] = ((w[i >> 5] >> (i & 31)) & 1u) ? -1.0f : 1.0f;
+ * diagonal").  Reading: one D per call, shared by every tile, drawn from Philox calls with
+ * key = (seed low word, seed high word) and counters (c,0,0,0), c = 0, 1, ...: the output words of
+ * call c are words 4c..4c+3; D_i = -1 iff bit (i mod 32) of word floor(i/32) is set (one call
+ * for tiles of 64 or 128, two for 256; shorter tiles use a prefix).  The KV path's per-layer +-1
+ * rotation (component 4) is the same kind of diagonal, so it is folded into D by giving each
+ * (layer, K|V) call its own seed. */
+void hqo_signs_n(uint64_t seed, int tl, float *d) {
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[8];
+  for (uint32_t c = 0; c < 2; ++c) {
+    uint32_t ctr[4] = {c, 0, 0, 0};
+    hqo_philox4x32_10(ctr, key, w + 4 * c);
+  }
+  for (int i = 0; i < tl; ++i) d[i] = ((w[i >> 5] >> (i & 31)) & 1u) ? -1.0f : 1.0f;
 }
+void hqo_signs(uint64_t seed, float d[TILE]) { hqo_signs_n(seed, TILE, d); }
 
 /* Unnormalised fast Walsh-Hadamard transform, Sylvester (natural) order, in place:
- * y = H_128 x with H entries +-1.  Seven radix-2 stages j = 0..6; stage j pairs index i (bit j
- * clear) with i + 2^j, the low element becomes a + b and the high element a - b, each rounded
- * once in binary32.  The factor 1/sqrt(128) that makes H orthogonal is carried by the tile scale,
- * and the inverse uses H H = 128 I. */
-void hqo_fwht128(float x[TILE]) {
-  for (int j = 0; j < 7; ++j) {
-    int h = 1 << j;
-    for (int i = 0; i < TILE; ++i) {
+ * y = H_n x with H entries +-1 (n = 64, 128 or 256).  Radix-2 stages j = 0..log2(n)-1; stage j
+ * pairs index i (bit j clear) with i + 2^j, the low element becomes a + b and the high element
+ * a - b, each rounded once in binary32.  The factor 1/sqrt(n) that makes H orthogonal is carried by
+ * the tile scale, and the inverse uses H H = n I. */
+void hqo_fwht_n(float *x, int n) {
+  for (int h = 1; h < n; h <<= 1) {
+    for (int i = 0; i < n; ++i) {
       if (i & h) continue;
       float a = x[i], b = x[i + h];
       x[i] = a + b;
@@ -114,16 +122,18 @@ void hqo_fwht128(float x[TILE]) {
     }
   }
 }
+void hqo_fwht128(float x[TILE]) { hqo_fwht_n(x, TILE); }
 
-/* Sum of squares of a tile as a balanced pairwise tree in index order: the 128 squares (each
- * rounded once), then pairs (2i, 2i+1), then pairs of those, ... seven levels. */
-float hqo_sumsq128(const float y[TILE]) {
-  float s[TILE];
-  for (int i = 0; i < TILE; ++i) s[i] = y[i] * y[i];
-  for (int len = TILE; len > 1; len >>= 1)
+/* Sum of squares of a tile as a balanced pairwise tree in index order: the n squares (each
+ * rounded once), then pairs (2i, 2i+1), then pairs of those, ... log2(n) levels. */
+float hqo_sumsq_n(const float *y, int n) {
+  float s[TILE_MAX];
+  for (int i = 0; i < n; ++i) s[i] = y[i] * y[i];
+  for (int len = n; len > 1; len >>= 1)
     for (int i = 0; i < len / 2; ++i) s[i] = s[2 * i] + s[2 * i + 1];
   return s[0];
 }
+float hqo_sumsq128(const float y[TILE]) { return hqo_sumsq_n(y, TILE); }
 
 /* Round a positive finite double to the nearest bfloat16 (8 significant bits), ties to even,
  * and return the bfloat16 bit pattern.  Written with frexp/ldexp so that it is plainly the
@@ -141,11 +151,12 @@ static uint16_t bf16_rne_from_double(double r) {
 }
 
 /* Tile scale (reading of the scaling factor alpha, HyperQuant summary Methodology component 2):
- * s = bf16_rne( sqrt(S / 128) ), the root-mean-square of the unnormalised transformed tile,
- * i.e. the l2 norm of the input tile.  The square root is exact (double sqrt is correctly
- * rounded and S/128 is exact in double; no double-rounding case exists because a bfloat16
+ * s = bf16_rne( sqrt(S / n) ), the root-mean-square of the unnormalised transformed tile of n
+ * values, i.e. the l2 norm of the input tile.  The square root is exact (double sqrt is correctly
+ * rounded and S/n is exact in double; no double-rounding case exists because a bfloat16
  * rounding midpoint squared has at most 18 significant bits).  s is stored as 16 bits per tile. */
-uint16_t hqo_scale_bits(float S) { return bf16_rne_from_double(sqrt((double)S / 128.0)); }
+uint16_t hqo_scale_bits_n(float S, int n) { return bf16_rne_from_double(sqrt((double)S / (double)n)); }
+uint16_t hqo_scale_bits(float S) { return hqo_scale_bits_n(S, TILE); }
 
 static float bf16_to_f32(uint16_t b) { return f32_from_bits((uint32_t)b << 16); }
 
@@ -323,9 +334,9 @@ void hqo_dither_octet(uint64_t seed, uint64_t tile, int octet, int lattice, floa
  *   e takes number e mod 4 of those four.  All in binary64.
  *   Q: modified Gram-Schmidt on the columns of G (which makes the diagonal of R positive directly).
  * Output: q[128 i + j] = Q[i][j], binary64. */
-static void haar_gaussians(uint64_t seed, double g[TILE * TILE]) {
+static void haar_gaussians(uint64_t seed, double g[HAAR_N * HAAR_N]) {
   const double two_pi = 6.283185307179586476925286766559;
-  for (uint32_t c = 0; c < TILE * TILE / 4; ++c) {
+  for (uint32_t c = 0; c < HAAR_N * HAAR_N / 4; ++c) {
     uint32_t ctr[4] = {c, 0u, 0u, 2u}, key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[4];
     hqo_philox4x32_10(ctr, key, w);
     for (int pair = 0; pair < 2; ++pair) {
@@ -340,20 +351,20 @@ static void haar_gaussians(uint64_t seed, double g[TILE * TILE]) {
 void hqo_haar_gaussians(uint64_t seed, double *g) { haar_gaussians(seed, g); }
 
 void hqo_haar_matrix(uint64_t seed, double *q) {
-  double *a = (double *)malloc(sizeof(double) * TILE * TILE);
+  double *a = (double *)malloc(sizeof(double) * HAAR_N * HAAR_N);
   haar_gaussians(seed, a);  /* a[i][j]: column j is the vector being orthonormalised */
-  for (int j = 0; j < TILE; ++j) {
+  for (int j = 0; j < HAAR_N; ++j) {
     for (int p = 0; p < j; ++p) { /* remove the component along the finished column p */
       double dot = 0.0;
-      for (int i = 0; i < TILE; ++i) dot += a[i * TILE + p] * a[i * TILE + j];
-      for (int i = 0; i < TILE; ++i) a[i * TILE + j] -= dot * a[i * TILE + p];
+      for (int i = 0; i < HAAR_N; ++i) dot += a[i * HAAR_N + p] * a[i * HAAR_N + j];
+      for (int i = 0; i < HAAR_N; ++i) a[i * HAAR_N + j] -= dot * a[i * HAAR_N + p];
     }
     double nrm = 0.0;
-    for (int i = 0; i < TILE; ++i) nrm += a[i * TILE + j] * a[i * TILE + j];
+    for (int i = 0; i < HAAR_N; ++i) nrm += a[i * HAAR_N + j] * a[i * HAAR_N + j];
     nrm = sqrt(nrm);
-    for (int i = 0; i < TILE; ++i) a[i * TILE + j] /= nrm;
+    for (int i = 0; i < HAAR_N; ++i) a[i * HAAR_N + j] /= nrm;
   }
-  memcpy(q, a, sizeof(double) * TILE * TILE);
+  memcpy(q, a, sizeof(double) * HAAR_N * HAAR_N);
   free(a);
 }
 
@@ -448,32 +459,38 @@ int hqo_unstrip_octet(int lattice, const uint32_t sym[8], int coset, int32_t cod
   return ERR_INVALID_ARG;
 }
 
-/* Remainder bits per octet and fixed bits per tile record F:
- * 16 (scale) + coset bits (E8: 16, one per octet; A2: 64, one per pair) + 16 * (sum of slot
- * widths). */
+/* Remainder bits per octet and fixed bits per tile record F of a tile of tl values (tl/8 octets):
+ * 16 (scale) + coset bits (E8: one per octet; A2: one per pair) + tl/8 * (sum of slot widths). */
 static int octet_rem_bits(int lattice, int k) {
   int b = 0;
   for (int s = 0; s < 8; ++s) b += slot_width(lattice, s, k);
   return b;
 }
-uint32_t hqo_tile_fixed_bits(int lattice, int k) {
-  return 16u + (lattice == LAT_E8 ? 16u : lattice == LAT_A2 ? 64u : 0u) + 16u * (uint32_t)octet_rem_bits(lattice, k);
+uint32_t hqo_tile_fixed_bits_n(int lattice, int k, int tl) {
+  const uint32_t oct = (uint32_t)tl / 8u;
+  const uint32_t coset = lattice == LAT_E8 ? oct : lattice == LAT_A2 ? 4u * oct : 0u;
+  return 16u + coset + oct * (uint32_t)octet_rem_bits(lattice, k);
 }
+uint32_t hqo_tile_fixed_bits(int lattice, int k) { return hqo_tile_fixed_bits_n(lattice, k, TILE); }
+
+static int valid_tile(int tl) { return tl == 64 || tl == 128 || tl == 256; }
+static int log2_int(uint64_t v) { int l = 0; while (v > 1) { v >>= 1; ++l; } return l; }
 
 /* ------------------------------------------------------------------------------------------ */
 /* Per-tile quantiser (the front half of the encoder).                                          */
 /* ------------------------------------------------------------------------------------------ */
 typedef struct {
-  int lattice, dither;
+  int lattice, dither, tl;
   uint64_t seed;
-  float d[TILE];
+  float d[TILE_MAX];
 } qctx;
 
-static void qctx_init(qctx *q, int lattice, int dither, uint64_t seed) {
+static void qctx_init(qctx *q, int lattice, int dither, uint64_t seed, int tl) {
   q->lattice = lattice;
   q->dither = dither;
   q->seed = seed;
-  hqo_signs(seed, q->d);
+  q->tl = tl;
+  hqo_signs_n(seed, tl, q->d);
 }
 
 /* Reconstruction factor t and multiplier m of a tile, per slot parity.  Every lattice:
@@ -492,24 +509,24 @@ static void tile_factors(int lattice, float s, float step, float m[2], float t[2
   }
 }
 
-/* Quantise tile `t` (values x[0..127]) at step `step`: returns the scale bits and 128 integer
+/* Quantise tile `t` (values x[0..tl-1]) at step `step`: returns the scale bits and tl integer
  * codes; returns ERR_NONFINITE if the transformed tile's energy is not finite.
- *   y = H (D x);  S = sumsq(y);  s = bf16(sqrt(S/128));
+ *   y = H (D x);  S = sumsq(y);  s = bf16(sqrt(S/tl));
  *   m = 1 / (s * step)  (binary32 product then division; m = 0 when s = 0; A2's odd slots use
  *   the m' of tile_factors);
  *   v = y * m  (+ U for the dithered path);  codes = nearest lattice point per octet. */
-static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float step,
-                         uint16_t *scale_out, int32_t code[TILE]) {
-  float y[TILE];
-  for (int i = 0; i < TILE; ++i) y[i] = q->d[i] * x[i];
-  hqo_fwht128(y);
-  float S = hqo_sumsq128(y);
+static int quantize_tile(const qctx *q, uint64_t t, const float *x, float step, uint16_t *scale_out,
+                         int32_t *code) {
+  float y[TILE_MAX];
+  for (int i = 0; i < q->tl; ++i) y[i] = q->d[i] * x[i];
+  hqo_fwht_n(y, q->tl);
+  float S = hqo_sumsq_n(y, q->tl);
   if (!isfinite(S)) return ERR_NONFINITE;
-  uint16_t sb = hqo_scale_bits(S);
+  uint16_t sb = hqo_scale_bits_n(S, q->tl);
   float s = bf16_to_f32(sb);
   float m[2], tf[2];
   tile_factors(q->lattice, s, step, m, tf);
-  for (int o = 0; o < 16; ++o) {
+  for (int o = 0; o < q->tl / 8; ++o) {
     float v[8];
     for (int i = 0; i < 8; ++i) v[i] = y[8 * o + i] * m[i & 1];
     if (q->dither) {
@@ -524,16 +541,16 @@ static int quantize_tile(const qctx *q, uint64_t t, const float x[TILE], float s
 }
 
 /* Inverse of the quantiser for one tile: c = code coordinate; yhat = (c - U) * (s * step);
- * xhat = D (H yhat) * 2^-7 (exact power-of-two factor because H H = 128 I).  Reading: a decoded
+ * xhat = D (H yhat) / tl (an exact power-of-two factor because H H = tl I).  Reading: a decoded
  * value that is exactly zero is +0 (the pages do not speak of signed zeros; the sign of an exact
  * cancellation depends on the order of the butterflies, not on the data). */
-static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb,
-                            float step, float out[TILE]) {
+static void dequantize_tile(const qctx *q, uint64_t t, const int32_t *code, uint16_t sb, float step,
+                            float *out) {
   float s = bf16_to_f32(sb);
   float m[2], tf[2];
   tile_factors(q->lattice, s, step, m, tf);
-  float y[TILE];
-  for (int o = 0; o < 16; ++o) {
+  float y[TILE_MAX];
+  for (int o = 0; o < q->tl / 8; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
     for (int i = 0; i < 8; ++i) {
@@ -542,35 +559,36 @@ static void dequantize_tile(const qctx *q, uint64_t t, const int32_t code[TILE],
       y[8 * o + i] = cu * tf[i & 1];
     }
   }
-  hqo_fwht128(y);
-  for (int i = 0; i < TILE; ++i) {
-    float o = q->d[i] * (y[i] * 0.0078125f);
+  hqo_fwht_n(y, q->tl);
+  const float inv = 1.0f / (float)q->tl;  /* 2^-6, 2^-7 or 2^-8: exact */
+  for (int i = 0; i < q->tl; ++i) {
+    float o = q->d[i] * (y[i] * inv);
     out[i] = (o == 0.0f) ? 0.0f : o;
   }
 }
 
-static void load_tile(const void *x, int dtype, uint64_t t, float out[TILE]) {
+static void load_tile(const void *x, int dtype, uint64_t t, int tl, float *out) {
   if (dtype == 0) {
-    memcpy(out, (const float *)x + t * TILE, sizeof(float) * TILE);
+    memcpy(out, (const float *)x + t * (uint64_t)tl, sizeof(float) * (size_t)tl);
   } else {
-    const uint16_t *p = (const uint16_t *)x + t * TILE;
-    for (int i = 0; i < TILE; ++i) out[i] = bf16_to_f32(p[i]);
+    const uint16_t *p = (const uint16_t *)x + t * (uint64_t)tl;
+    for (int i = 0; i < tl; ++i) out[i] = bf16_to_f32(p[i]);
   }
 }
 
 /* Per-value integer codes and per-tile scale bits at a fixed step (diagnostic form of the
  * encoder's front half; the GPU exposes the same thing for code-level parity). */
 int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
-                 float step, int32_t *codes, uint16_t *scales) {
-  if (n % TILE) return ERR_INVALID_ARG;
+                 float step, int32_t *codes, uint16_t *scales, int tl) {
+  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
-  uint64_t T = n / TILE;
+  qctx_init(&q, lattice, dither, seed, tl);
+  uint64_t T = n / (uint64_t)tl;
   for (uint64_t t = 0; t < T; ++t) {
-    float xt[TILE];
-    load_tile(x, dtype, t, xt);
-    int rc = quantize_tile(&q, t, xt, step, &scales[t], codes + t * TILE);
+    float xt[TILE_MAX];
+    load_tile(x, dtype, t, tl, xt);
+    int rc = quantize_tile(&q, t, xt, step, &scales[t], codes + t * (uint64_t)tl);
     if (rc) return rc;
   }
   return OK;
@@ -579,26 +597,26 @@ int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, 
 /* The binary32 inputs v of the nearest-point step at a fixed step (for locating a code mismatch
  * relative to the Voronoi boundary in the tests). */
 int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
-                       float step, float *v_out) {
-  if (n % TILE) return ERR_INVALID_ARG;
+                       float step, float *v_out, int tl) {
+  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
-  for (uint64_t t = 0; t < n / TILE; ++t) {
-    float y[TILE];
-    load_tile(x, dtype, t, y);
-    for (int i = 0; i < TILE; ++i) y[i] = q.d[i] * y[i];
-    hqo_fwht128(y);
-    float S = hqo_sumsq128(y);
+  qctx_init(&q, lattice, dither, seed, tl);
+  for (uint64_t t = 0; t < n / (uint64_t)tl; ++t) {
+    float y[TILE_MAX];
+    load_tile(x, dtype, t, tl, y);
+    for (int i = 0; i < tl; ++i) y[i] = q.d[i] * y[i];
+    hqo_fwht_n(y, tl);
+    float S = hqo_sumsq_n(y, tl);
     if (!isfinite(S)) return ERR_NONFINITE;
-    float s = bf16_to_f32(hqo_scale_bits(S));
+    float s = bf16_to_f32(hqo_scale_bits_n(S, tl));
     float m[2], tf[2];
     tile_factors(lattice, s, step, m, tf);
-    for (int o = 0; o < 16; ++o) {
+    for (int o = 0; o < tl / 8; ++o) {
       float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (dither) hqo_dither_octet(seed, t, o, lattice, u);
       for (int i = 0; i < 8; ++i) {
         float v = y[8 * o + i] * m[i & 1];
-        v_out[t * TILE + 8 * o + i] = dither ? v + u[i] : v;
+        v_out[t * (uint64_t)tl + 8 * o + i] = dither ? v + u[i] : v;
       }
     }
   }
@@ -606,12 +624,12 @@ int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int di
 }
 
 int hqo_dequantize(const int32_t *codes, const uint16_t *scales, uint64_t n, int lattice,
-                   int dither, uint64_t seed, float step, float *out) {
-  if (n % TILE) return ERR_INVALID_ARG;
+                   int dither, uint64_t seed, float step, float *out, int tl) {
+  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
-  for (uint64_t t = 0; t < n / TILE; ++t)
-    dequantize_tile(&q, t, codes + t * TILE, scales[t], step, out + t * TILE);
+  qctx_init(&q, lattice, dither, seed, tl);
+  for (uint64_t t = 0; t < n / (uint64_t)tl; ++t)
+    dequantize_tile(&q, t, codes + t * (uint64_t)tl, scales[t], step, out + t * (uint64_t)tl);
   return OK;
 }
 
@@ -710,15 +728,15 @@ static int rc_eval(const qctx *q, const void *x, int dtype, uint64_t T, uint64_t
     for (int w = 0; w < RC_KWIN; ++w) sumq[c][w] = 0;
   for (uint64_t i = 0; i < N; ++i) {
     uint64_t t = hqo_sample_tile(i, T, N);
-    float xt[TILE];
-    load_tile(x, dtype, t, xt);
+    float xt[TILE_MAX];
+    load_tile(x, dtype, t, q->tl, xt);
     for (int c = 0; c < nc; ++c) {
       uint16_t sb;
-      int32_t code[TILE];
+      int32_t code[TILE_MAX];
       int rc = quantize_tile(q, t, xt, f32_from_bits((uint32_t)b[c]), &sb, code);
       if (rc) return rc;
       int kb = fixed_k >= 0 ? fixed_k : kwin_base(b[c]);
-      for (int o = 0; o < 16; ++o) {
+      for (int o = 0; o < q->tl / 8; ++o) {
         uint32_t sym[8];
         int cos;
         hqo_strip_octet(q->lattice, code + 8 * o, sym, &cos);
@@ -739,20 +757,20 @@ static float min_bps(int lattice) {
   return lattice == LAT_E8 ? 1.125f : lattice == LAT_A2 ? 1.5f : 1.0f;
 }
 
-static double rc_bits(int lattice, uint64_t N, int k, uint64_t sumq) {
-  double per_tile = (double)(hqo_tile_fixed_bits(lattice, k) - 16u) + 128.0;
+static double rc_bits(int lattice, uint64_t N, int k, uint64_t sumq, int tl) {
+  double per_tile = (double)(hqo_tile_fixed_bits_n(lattice, k, tl) - 16u) + (double)tl;
   return per_tile * (double)N + (double)sumq;
 }
 
 /* Output: chosen step bits, Rice k, and the sample payload estimate (bits/value) by interpolation. */
 int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
-             float target_bps, float step, int rice_k, uint32_t *step_bits_out, int *k_out) {
-  if (n % TILE) return ERR_INVALID_ARG;
+             float target_bps, float step, int rice_k, uint32_t *step_bits_out, int *k_out, int tl) {
+  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   if (rice_k < -1 || rice_k > 15) return ERR_INVALID_ARG;
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
-  uint64_t T = n / TILE;
+  qctx_init(&q, lattice, dither, seed, tl);
+  uint64_t T = n / (uint64_t)tl;
   uint64_t N = T < RC_SAMPLE_TILES ? T : RC_SAMPLE_TILES;
   int64_t b_ans;
   int k_ans;
@@ -771,7 +789,7 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
     if (rc) return rc;
     int kb = kwin_base(b_ans), best = 0;
     for (int w = 1; w < RC_KWIN; ++w)
-      if (rc_bits(lattice, N, kb + w, sumq[0][w]) < rc_bits(lattice, N, kb + best, sumq[0][best]))
+      if (rc_bits(lattice, N, kb + w, sumq[0][w], tl) < rc_bits(lattice, N, kb + best, sumq[0][best], tl))
         best = w;
     *step_bits_out = (uint32_t)b_ans;
     *k_out = kb + best;
@@ -791,8 +809,8 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
   for (int pass = 0; pass < 2; ++pass) {
     const uint64_t Np = np[pass];
     const int nc = ncand[pass];
-    const double Tb = (double)target_bps * (double)(Np * TILE);
-    const double nominal = (double)(Np * TILE) / 8388608.0;
+    const double Tb = (double)target_bps * (double)(Np * (uint64_t)tl);
+    const double nominal = (double)(Np * (uint64_t)tl) / 8388608.0;
     int64_t b[RC_CANDIDATES];
     for (int j = 0; j < nc; ++j)
       b[j] = clamp64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2[pass]),
@@ -805,9 +823,9 @@ int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint
     for (int j = 0; j < nc; ++j) {
       int kb = rice_k >= 0 ? rice_k : kwin_base(b[j]);
       int best = 0;
-      double rb = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb, sumq[j][0]);
+      double rb = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb, sumq[j][0], tl);
       for (int w = 1; w < RC_KWIN; ++w) {
-        double rw = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb + w, sumq[j][w]);
+        double rw = rc_bits(lattice, Np, rice_k >= 0 ? rice_k : kb + w, sumq[j][w], tl);
         if (rw < rb) { rb = rw; best = w; }
       }
       R[j] = rb;
@@ -865,17 +883,20 @@ static uint64_t align256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
 
 /* Byte layout helpers shared by encoder and decoder of this file. */
 typedef struct {
-  uint64_t T, chunks, fixed_off, unary_off;
+  uint64_t T, chunks, fixed_off, unary_off, ctiles;
   uint32_t F;
+  int tl;
 } layout;
 
-static layout make_layout(uint64_t n, int lattice, int k) {
+static layout make_layout(uint64_t n, int lattice, int k, int tl) {
   layout L;
-  L.T = n / TILE;
-  L.chunks = (L.T + CHUNK_TILES - 1) / CHUNK_TILES;
-  L.F = hqo_tile_fixed_bits(lattice, k);
+  L.tl = tl;
+  L.T = n / (uint64_t)tl;
+  L.ctiles = CHUNK_VALUES / (uint64_t)tl;
+  L.chunks = (L.T + L.ctiles - 1) / L.ctiles;
+  L.F = hqo_tile_fixed_bits_n(lattice, k, tl);
   L.fixed_off = align256(HEADER_BYTES + 4u * (L.chunks + 1));
-  L.unary_off = align256(L.fixed_off + L.chunks * 8u * L.F);
+  L.unary_off = align256(L.fixed_off + L.chunks * L.ctiles * L.F / 8u);
   return L;
 }
 
@@ -904,8 +925,9 @@ int hqo_rice_roundtrip(const uint32_t *vals, uint64_t count, int k, uint32_t *ou
 }
 
 int hqo_encode_layout(uint64_t n, int lattice, int k, uint64_t *fixed_off, uint64_t *unary_off,
-                      uint32_t *F) {
-  layout L = make_layout(n, lattice, k);
+                      uint32_t *F, int tl) {
+  if (!valid_tile(tl)) return ERR_INVALID_ARG;
+  layout L = make_layout(n, lattice, k, tl);
   *fixed_off = L.fixed_off;
   *unary_off = L.unary_off;
   *F = L.F;
@@ -916,32 +938,32 @@ int hqo_encode_layout(uint64_t n, int lattice, int k, uint64_t *fixed_off, uint6
  * the required size when it does not fit.  info[0..3] = step bits, k, payload bits, unary bits. */
 int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
                float target_bps, float step, int rice_k, uint8_t *out, uint64_t cap,
-               uint64_t *out_bytes, uint64_t info[4]) {
-  if (n % TILE) return ERR_INVALID_ARG;
+               uint64_t *out_bytes, uint64_t info[4], int tl) {
+  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   uint32_t sbits;
   int k;
-  int rc = hqo_rate(x, dtype, n, lattice, dither, seed, target_bps, step, rice_k, &sbits, &k);
+  int rc = hqo_rate(x, dtype, n, lattice, dither, seed, target_bps, step, rice_k, &sbits, &k, tl);
   if (rc) return rc;
   float st = f32_from_bits(sbits);
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
-  layout L = make_layout(n, lattice, k);
+  qctx_init(&q, lattice, dither, seed, tl);
+  layout L = make_layout(n, lattice, k, tl);
   int32_t *codes = (int32_t *)malloc(sizeof(int32_t) * (n ? n : 1));
   uint16_t *scales = (uint16_t *)malloc(sizeof(uint16_t) * (L.T ? L.T : 1));
   uint64_t *chunk_bits = (uint64_t *)calloc(L.chunks + 1, sizeof(uint64_t));
   if (!codes || !scales || !chunk_bits) { free(codes); free(scales); free(chunk_bits); return ERR_INVALID_ARG; }
   /* quantise and measure each chunk's unary length */
   for (uint64_t t = 0; t < L.T; ++t) {
-    float xt[TILE];
-    load_tile(x, dtype, t, xt);
-    rc = quantize_tile(&q, t, xt, st, &scales[t], codes + t * TILE);
+    float xt[TILE_MAX];
+    load_tile(x, dtype, t, tl, xt);
+    rc = quantize_tile(&q, t, xt, st, &scales[t], codes + t * (uint64_t)tl);
     if (rc) { free(codes); free(scales); free(chunk_bits); return rc; }
-    for (int o = 0; o < 16; ++o) {
+    for (int o = 0; o < tl / 8; ++o) {
       uint32_t sym[8];
       int cos;
-      hqo_strip_octet(lattice, codes + t * TILE + 8 * o, sym, &cos);
-      for (int s = 0; s < 8; ++s) chunk_bits[t / CHUNK_TILES] += (sym[s] >> slot_width(lattice, s, k)) + 1u;
+      hqo_strip_octet(lattice, codes + t * (uint64_t)tl + 8 * o, sym, &cos);
+      for (int s = 0; s < 8; ++s) chunk_bits[t / L.ctiles] += (sym[s] >> slot_width(lattice, s, k)) + 1u;
     }
   }
   uint64_t words = 0, ubits = 0;
@@ -957,9 +979,9 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
   put_u16(out + 4, VERSION);
   out[6] = (uint8_t)lattice;
   out[7] = (uint8_t)(dither ? 1 : 0);
-  put_u16(out + 8, TILE);
+  put_u16(out + 8, (uint16_t)tl);
   out[10] = (uint8_t)k;
-  out[11] = 6;
+  out[11] = (uint8_t)log2_int(L.ctiles);
   put_u32(out + 12, sbits);
   put_u64(out + 16, seed);
   put_u64(out + 24, n);
@@ -978,17 +1000,17 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
   for (uint64_t c = 0; c < L.chunks; ++c) {
     put_u32(out + HEADER_BYTES + 4u * c, (uint32_t)wpos);
     uint64_t upos = wpos * 64u;
-    for (uint64_t t = c * CHUNK_TILES; t < (c + 1) * CHUNK_TILES && t < L.T; ++t) {
+    for (uint64_t t = c * L.ctiles; t < (c + 1) * L.ctiles && t < L.T; ++t) {
       uint64_t fp = t * (uint64_t)L.F;
       put_bits(fixed, fp, scales[t], 16);
       fp += 16;
       uint64_t coset_pos = fp;
-      if (lattice == LAT_E8) fp += 16;
-      if (lattice == LAT_A2) fp += 64;
-      for (int o = 0; o < 16; ++o) {
+      if (lattice == LAT_E8) fp += (uint64_t)(tl / 8);
+      if (lattice == LAT_A2) fp += (uint64_t)(tl / 2);
+      for (int o = 0; o < tl / 8; ++o) {
         uint32_t sym[8];
         int cos;
-        hqo_strip_octet(lattice, codes + t * TILE + 8 * o, sym, &cos);
+        hqo_strip_octet(lattice, codes + t * (uint64_t)tl + 8 * o, sym, &cos);
         if (lattice == LAT_E8) put_bit(fixed, coset_pos + (uint64_t)o, cos);
         if (lattice == LAT_A2) put_bits(fixed, coset_pos + 4u * (uint64_t)o, (uint32_t)cos, 4);
         for (int s = 0; s < 8; ++s) {
@@ -1012,18 +1034,19 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
  * 1 = bf16 (round to nearest even). */
 /* Stream reader shared by the decoders below: validates the header and index, and hands every tile's
  * integer codes and scale bits to `sink` in tile order (format v1, see hqo_encode_layout). */
-typedef void (*tile_sink)(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step);
+typedef void (*tile_sink)(void *ctx, const qctx *q, uint64_t t, const int32_t *code, uint16_t sb, float step);
 
 static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink sink, void *ctx) {
   if (bytes < HEADER_BYTES) return ERR_CORRUPT;
   if (get_u32(s) != MAGIC || get_u16(s + 4) != VERSION) return ERR_CORRUPT;
-  int lattice = s[6], dither = s[7] & 1, k = s[10];
-  if (lattice > LAT_A2 || (s[7] & ~1u) || get_u16(s + 8) != TILE || k > 15 || s[11] != 6) return ERR_CORRUPT;
-  if (get_u64(s + 24) != n || n % TILE) return ERR_CORRUPT;
+  int lattice = s[6], dither = s[7] & 1, k = s[10], tl = get_u16(s + 8);
+  if (lattice > LAT_A2 || (s[7] & ~1u) || !valid_tile(tl) || k > 15) return ERR_CORRUPT;
+  if (s[11] != log2_int(CHUNK_VALUES / (uint64_t)tl)) return ERR_CORRUPT;
+  if (get_u64(s + 24) != n || n % (uint64_t)tl) return ERR_CORRUPT;
   uint32_t sbits = get_u32(s + 12);
   if (sbits < STEP_BITS_MIN || sbits > STEP_BITS_MAX) return ERR_CORRUPT;
   uint64_t seed = get_u64(s + 16);
-  layout L = make_layout(n, lattice, k);
+  layout L = make_layout(n, lattice, k, tl);
   if (get_u64(s + 32) != L.T || get_u32(s + 40) != (uint32_t)L.chunks || get_u32(s + 44) != L.F ||
       get_u64(s + 48) != L.fixed_off || get_u64(s + 56) != L.unary_off)
     return ERR_CORRUPT;
@@ -1033,21 +1056,21 @@ static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink s
   if (get_u32(s + HEADER_BYTES) != 0 || get_u32(s + HEADER_BYTES + 4u * L.chunks) != words) return ERR_CORRUPT;
   float st = f32_from_bits(sbits);
   qctx q;
-  qctx_init(&q, lattice, dither, seed);
+  qctx_init(&q, lattice, dither, seed, tl);
   const uint8_t *fixed = s + L.fixed_off, *unary = s + L.unary_off;
   for (uint64_t c = 0; c < L.chunks; ++c) {
     uint32_t w0 = get_u32(s + HEADER_BYTES + 4u * c), w1 = get_u32(s + HEADER_BYTES + 4u * (c + 1));
     if (w1 < w0 || w1 > words) return ERR_CORRUPT;
     uint64_t upos = (uint64_t)w0 * 64u, uend = (uint64_t)w1 * 64u;
-    for (uint64_t t = c * CHUNK_TILES; t < (c + 1) * CHUNK_TILES && t < L.T; ++t) {
+    for (uint64_t t = c * L.ctiles; t < (c + 1) * L.ctiles && t < L.T; ++t) {
       uint64_t fp = t * (uint64_t)L.F;
       uint16_t sb = (uint16_t)get_bits(fixed, fp, 16);
       fp += 16;
       uint64_t coset_pos = fp;
-      if (lattice == LAT_E8) fp += 16;
-      if (lattice == LAT_A2) fp += 64;
-      int32_t code[TILE];
-      for (int o = 0; o < 16; ++o) {
+      if (lattice == LAT_E8) fp += (uint64_t)(tl / 8);
+      if (lattice == LAT_A2) fp += (uint64_t)(tl / 2);
+      int32_t code[TILE_MAX];
+      for (int o = 0; o < tl / 8; ++o) {
         uint32_t sym[8];
         for (int sl = 0; sl < 8; ++sl) {
           int w = slot_width(lattice, sl, k);
@@ -1078,15 +1101,16 @@ static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink s
 
 typedef struct { void *out; int out_dtype; } decode_ctx;
 
-static void decode_sink(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step) {
+static void decode_sink(void *ctx, const qctx *q, uint64_t t, const int32_t *code, uint16_t sb, float step) {
   const decode_ctx *d = (const decode_ctx *)ctx;
-  float xt[TILE];
+  const int tl = q->tl;
+  float xt[TILE_MAX];
   dequantize_tile(q, t, code, sb, step, xt);
   if (d->out_dtype == 0) {
-    memcpy((float *)d->out + t * TILE, xt, sizeof(xt));
+    memcpy((float *)d->out + t * (uint64_t)tl, xt, sizeof(float) * (size_t)tl);
   } else {
-    uint16_t *o16 = (uint16_t *)d->out + t * TILE;
-    for (int i = 0; i < TILE; ++i) o16[i] = f32_to_bf16_rne(xt[i]);
+    uint16_t *o16 = (uint16_t *)d->out + t * (uint64_t)tl;
+    for (int i = 0; i < tl; ++i) o16[i] = f32_to_bf16_rne(xt[i]);
   }
 }
 
@@ -1097,13 +1121,13 @@ int hqo_decode(const uint8_t *s, uint64_t bytes, uint64_t n, void *out, int out_
 
 /* The decoder's values before the inverse transform, in binary64: yhat_i = (c_i - U_i) * t with
  * t = s * step the binary32 product both sides use (dequantize_tile; A2's odd slots take its t'),
- * so that the exact reconstruction of tile t is D H yhat / 128.  Test infrastructure for products
+ * so that the exact reconstruction of tile t is D H yhat / tl.  Test infrastructure for products
  * with the decoded matrix (the fused decode + matrix-vector product). */
-static void coords_sink(void *ctx, const qctx *q, uint64_t t, const int32_t code[TILE], uint16_t sb, float step) {
-  double *out = (double *)ctx + t * TILE;
+static void coords_sink(void *ctx, const qctx *q, uint64_t t, const int32_t *code, uint16_t sb, float step) {
+  double *out = (double *)ctx + t * (uint64_t)q->tl;
   float m[2], tf[2];
   tile_factors(q->lattice, bf16_to_f32(sb), step, m, tf);
-  for (int o = 0; o < 16; ++o) {
+  for (int o = 0; o < q->tl / 8; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
     for (int i = 0; i < 8; ++i) {

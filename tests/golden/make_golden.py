@@ -23,6 +23,8 @@ CASES = [
     ("tiny_a2_4bps", "tiny", "a2", 4.0, 0, False),
     ("tiny_a2_3bps_dither", "tiny", "a2", 3.0, 5, True),
     ("weight16x4096_e8_3bps", "weight16", "e8", 3.0, 0, False),
+    ("tiny_e8_4bps_tile64", "tiny", "e8", 4.0, 0, False, 64),
+    ("tiny_e8_3bps_dither_tile256", "tiny", "e8", 3.0, 5, True, 256),
 ]
 
 
@@ -36,9 +38,9 @@ def make_input(name):
 
 def digest_rows():
     rows = []
-    for name, inp, lat, tb, seed, dither in CASES:
+    for name, inp, lat, tb, seed, dither, *tile in CASES:
         x = make_input(inp)
-        s, info = oracle.encode(x, oracle.LATTICES[lat], tb, seed=seed, dither=dither)
+        s, info = oracle.encode(x, oracle.LATTICES[lat], tb, seed=seed, dither=dither, tile=(tile or [128])[0])
         y = oracle.decode(s, x.size)
         rows.append((name, info["step_bits"], info["k"], info["payload_bits"], s.size,
                      hashlib.sha256(s.tobytes()).hexdigest(), hashlib.sha256(y.tobytes()).hexdigest()))

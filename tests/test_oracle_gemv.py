@@ -63,3 +63,16 @@ def test_gemv_reference_tracks_the_original_matrix(orc):
     y, _ = orc.gemv_reference(s, rows, cols, x, seed=1)
     exact = w.astype(np.float64) @ x
     assert np.linalg.norm(y - exact) <= 0.05 * np.linalg.norm(exact)
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+def test_decode_coords_other_tiles(orc, tile):
+    """D H_n yhat / n reconstructs the oracle's binary32 decode at tiles of 64 and 256 values."""
+    x = synth.tiny(seed=4, tiles=64)
+    s, _ = orc.encode(x, orc.LAT_E8, 3.0, seed=2, dither=True, tile=tile)
+    n = x.size
+    yh = orc.decode_coords(s, n).reshape(-1, tile)
+    exact = (yh @ scipy.linalg.hadamard(tile).astype(np.float64)) * orc.signs(2, tile).astype(np.float64) / tile
+    got = orc.decode(s, n).reshape(-1, tile).astype(np.float64)
+    tol = 9 * U * np.abs(yh).sum(axis=1, keepdims=True) / tile
+    assert np.all(np.abs(got - exact) <= tol + 1e-300)

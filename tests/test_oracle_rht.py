@@ -104,3 +104,69 @@ def test_scale_is_exact_rne_of_sqrt(orc):
         assert best is not None
         assert orc.scale_bits(float(S)) == best, S
     assert orc.scale_bits(0.0) == 0
+
+
+# ---- tiles of 64 and 256 values (the summary gives 128 as an example tile size) ----------------
+
+import pytest  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [64, 256])
+def test_fwht_other_tile_lengths(orc, n):
+    """H_n e_i is column i of scipy's Sylvester matrix; exact on integers; H_n H_n = n I."""
+    Hn = scipy.linalg.hadamard(n).astype(np.int64)
+    for i in range(n):
+        e = np.zeros(n, dtype=np.float32)
+        e[i] = 1.0
+        assert np.array_equal(orc.fwht(e), Hn[:, i].astype(np.float32))
+    rng = np.random.default_rng(n)
+    for _ in range(20):
+        x = rng.integers(-2**14, 2**14, size=n)
+        y = orc.fwht(x.astype(np.float32))
+        assert np.array_equal(y.astype(np.int64), Hn @ x)
+        assert np.array_equal(orc.fwht(y).astype(np.int64), n * x)
+    x = rng.standard_normal(n).astype(np.float32)
+    y = orc.fwht(x).astype(np.float64)
+    assert abs(np.sum(y * y) / (n * np.sum(x.astype(np.float64) ** 2)) - 1) < 1e-6
+    # the 128-value transform is the same routine
+    x = rng.standard_normal(128).astype(np.float32)
+    assert np.array_equal(orc.fwht(x), orc.fwht128(x))
+
+
+@pytest.mark.parametrize("n", [64, 256])
+def test_sumsq_and_scale_other_lengths(orc, n):
+    rng = np.random.default_rng(n + 1)
+    for _ in range(50):
+        y = (rng.standard_normal(n) * 10.0 ** rng.uniform(-5, 5)).astype(np.float32)
+        ref = float(np.sum(y.astype(np.float64) ** 2))
+        assert abs(orc.sumsq(y) / ref - 1) < 9 * 2.0 ** -24
+        yi = rng.integers(-200, 200, size=n).astype(np.float32)
+        assert orc.sumsq(yi) == float(np.sum(yi.astype(np.int64) ** 2))
+    # the scale is sqrt(S / n) rounded to bfloat16: S = n m^2 for an exact bfloat16 m gives m
+    for c in (0x3F80, 0x4049, 0x3A12, 0x4611):
+        m = np.array([c << 16], dtype=np.uint32).view(np.float32)[0]
+        S = np.float32(np.float64(m) * np.float64(m) * n)
+        assert orc.scale_bits(float(S), n) == c
+
+
+def test_signs_of_other_lengths_extend_the_128_diagonal(orc):
+    """Tiles of 64 use the first 64 signs of the 128-value diagonal; tiles of 256 append the 128
+    signs of the next Philox counter (1, 0, 0, 0), bit i mod 32 of word i/32 as before."""
+    for seed in (0, 7, 2**40 + 3):
+        d128 = orc.signs(seed)
+        assert np.array_equal(orc.signs(seed, 64), d128[:64])
+        d256 = orc.signs(seed, 256)
+        assert np.array_equal(d256[:128], d128)
+        w = orc.philox4x32_10([1, 0, 0, 0], [seed & 0xFFFFFFFF, seed >> 32])
+        bits = np.array([(int(w[i >> 5]) >> (i & 31)) & 1 for i in range(128)])
+        assert np.array_equal(d256[128:], np.where(bits == 1, -1.0, 1.0).astype(np.float32))
+        assert 40 < np.sum(d256 < 0) < 216
+
+
+@pytest.mark.parametrize("n", [64, 256])
+def test_rht_inverse_other_lengths(orc, n):
+    rng = np.random.default_rng(n + 2)
+    d = orc.signs(3, n)
+    x = rng.standard_normal(n).astype(np.float32)
+    back = d * (orc.fwht(orc.fwht(d * x)) * np.float32(1.0 / n))
+    assert np.max(np.abs(back - x)) <= 2.0 ** -19 * np.linalg.norm(x)

@@ -77,3 +77,31 @@ def test_nonfinite_input(orc):
     with pytest.raises(orc.OracleError) as e:
         orc.encode(x, orc.LAT_E8, 4.0, step=0.3, rice_k=2)
     assert e.value.code == orc.ERR_NONFINITE
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+@pytest.mark.parametrize("lattice", ["e8", "a2", "z"])
+def test_stream_roundtrip_other_tiles(orc, tile, lattice):
+    """Tiles of 64 and 256 values: decode(encode(x)) equals the direct dequantisation, a chunk holds
+    8192 / tile tiles, and the tile record has 16 scale bits, the lattice's coset bits and the
+    remainders of tile / 8 octets."""
+    L = orc.LATTICES[lattice]
+    x = synth.tiny(seed=5, tiles=130).reshape(-1)        # 16640 values: ragged last chunk
+    for dither in (False, True):
+        s, info = orc.encode(x, L, 3.0, seed=4, dither=dither, tile=tile)
+        y = orc.decode(s, x.size)
+        codes, scales = orc.quantize(x, L, info["step"], seed=4, dither=dither, tile=tile)
+        assert np.array_equal(y, orc.dequantize(codes, scales, L, info["step"], seed=4, dither=dither, tile=tile))
+        h = s[:128]
+        assert int(h[8]) | (int(h[9]) << 8) == tile and int(h[11]) == {64: 7, 256: 5}[tile]
+        fo, uo, F = orc.layout(x.size, L, info["k"], tile)
+        oct_bits = {"e8": 8 * info["k"] - (1 if info["k"] else 0), "a2": 8 * info["k"] - (4 if info["k"] else 0),
+                    "z": 8 * info["k"]}[lattice]
+        coset = {"e8": tile // 8, "a2": tile // 2, "z": 0}[lattice]
+        assert F == 16 + coset + (tile // 8) * oct_bits
+        assert info["payload_bits"] == (x.size // tile) * (F - 16) + info["unary_bits"]
+        # a stream is decoded only at its own tile size: another n or a damaged tile field fails
+        bad = s.copy()
+        bad[8] ^= 0xC0
+        with pytest.raises(orc.OracleError):
+            orc.decode(bad, x.size)

@@ -99,3 +99,28 @@ def test_sample_tiles_cover_each_stratum(orc):
     # positions within a 32-tile row are spread over all residues (no aliasing with row length)
     assert len(set(t % 32 for t in ts)) == 32
     assert [orc.sample_tile(i, 100, 100) for i in range(100)] == list(range(100))
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+@pytest.mark.parametrize("target", [2.0, 4.0])
+def test_rate_within_0p01_other_tiles(orc, tile, target):
+    x = synth.tiny()
+    for lat in ("e8", "d4"):
+        s, info = orc.encode(x, orc.LATTICES[lat], target, tile=tile)
+        assert abs(info["payload_bps"] - target) <= 0.01
+
+
+@pytest.mark.parametrize("tile", [64, 256])
+def test_dithered_mse_closed_form_other_tiles(orc, tile):
+    """The per-tile dithered error |xhat - x|^2 / s^2 = G V^(2/d) step^2 holds at every tile length
+    (x - xhat = D H (y - yhat) / n and |H z|^2 = n |z|^2)."""
+    g, d, vol = G["e8"]
+    x = synth.gaussian(tile * 3000, seed=22).reshape(-1, tile)
+    step = 0.5
+    codes, scales = orc.quantize(x, orc.LAT_E8, step, seed=3, dither=True, tile=tile)
+    y = orc.dequantize(codes, scales, orc.LAT_E8, step, seed=3, dither=True, tile=tile).reshape(x.shape)
+    s = synth.bf16_to_f32(scales).astype(np.float64)
+    r = ((y - x).astype(np.float64) ** 2).sum(axis=1) / (s * s)
+    want = g * vol ** (2.0 / d) * step ** 2
+    se = r.std() / np.sqrt(r.size)
+    assert abs(r.mean() - want) < 5 * se, (r.mean(), want, se)
