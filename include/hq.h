@@ -4,7 +4,8 @@
  * The method is the per-tile pipeline of the HyperQuant technical summary
  * (gist.science/ko/paper/2606.23406; Japanese version gist.science/ja/paper/2606.23406), section
  * "Methodology: the HyperQuant pipeline":
- *   component 1  per-tile randomized Hadamard transform RHT_128(x) = H_128 D x (D: random +-1),
+ *   component 1  per-tile randomized Hadamard transform RHT_n(x) = H_n D x (D: random +-1), on
+ *                tiles of n = 128 values (the summary's example size), or of 64 or 256,
  *   component 2  nearest-point quantisation onto E8 (or D4, A2, or scalar Z) in an integer
  *                embedding, scaled so the rotated tile matches the lattice,
  *   component 3  stripping of the bits that lattice membership fixes, then Rice coding, with the
@@ -18,25 +19,28 @@
  *    hq_stream_t are hipStream_t values (0 = the null stream).
  *  - The caller owns every buffer.  The library allocates no device memory and keeps no state
  *    between calls apart from immutable constants; one workspace serves one call in flight.
- *  - Tensors are flat arrays of n values, n a multiple of 128; tile t is values [128 t, 128 t + 128).
+ *  - Tensors are flat arrays of n values, n a multiple of the tile length TL (64, 128 or 256; 128
+ *    by default); tile t is values [TL t, TL t + TL).
  *  - Every call returns HQ_OK (0) or a negative hq_status code; no exception crosses the ABI.
  *  - Errors found on the device (non-finite input, too small an output buffer, corrupt stream) are
  *    recorded in the workspace; blocking calls return them, hq_status() reads them otherwise.
  *
  * Bitstream (format version 1, little-endian; the pages give no format, this is the codec's own):
  *   header, 128 bytes: u32 magic 'HQ01' | u16 version | u8 lattice | u8 flags (bit0 dither) |
- *     u16 tile (128) | u8 rice k | u8 log2 tiles per chunk (6) | u32 step (binary32 bits) |
+ *     u16 tile TL | u8 rice k | u8 log2 tiles per chunk (log2(8192 / TL)) | u32 step (binary32 bits) |
  *     u64 seed | u64 n | u64 tiles | u32 chunks | u32 F (fixed bits per tile) | u64 fixed_off |
  *     u64 unary_off | u64 unary_words | u64 unary_bits | u64 payload_bits | u64 total_bytes | 32 B 0
- *   chunk index at byte 128: chunks+1 u32 offsets, in 64-bit words, into the unary plane
- *   fixed plane at fixed_off = align256(128 + 4 (chunks+1)); chunk c = tiles 64c..64c+63, 8F bytes;
+ *   chunk index at byte 128: chunks+1 u32 offsets, in 64-bit words, into the unary plane; a chunk
+ *     is 8192 values (8192 / TL tiles)
+ *   fixed plane at fixed_off = align256(128 + 4 (chunks+1)); chunk c = its tiles' records;
  *     tile record at bit t F (bit i of a plane = bit i%8 of byte i/8): bf16 tile scale (16) |
- *     coset bits (E8: octet o at bit o, 16; A2: pair j of octet o at bit 4o+j, 64; none for D4 and
- *     Z) | octet 0..15, slot 0..7: Rice remainder, width k (full slots) or max(k-1,0) (halved
- *     slots: the parity-fixed slot 7 of E8, 3 and 7 of D4; the stretched odd slots of A2), LSB first
- *   unary plane at unary_off = align256(fixed_off + 8 F chunks): chunk c's segment starts at word
- *     index[c]; each symbol in (tile, octet, slot) order contributes (symbol >> width) zero bits
- *     and a one; segments are zero-padded to 64 bits.
+ *     coset bits (E8: octet o at bit o, TL/8 bits; A2: pair j of octet o at bit 4o+j, TL/2 bits;
+ *     none for D4 and Z) | octet 0..TL/8-1, slot 0..7: Rice remainder, width k (full slots) or
+ *     max(k-1,0) (halved slots: the parity-fixed slot 7 of E8, 3 and 7 of D4; the stretched odd
+ *     slots of A2), LSB first
+ *   unary plane at unary_off = align256(fixed_off + chunks (8192 / TL) F / 8): chunk c's segment
+ *     starts at word index[c]; each symbol in (tile, octet, slot) order contributes
+ *     (symbol >> width) zero bits and a one; segments are zero-padded to 64 bits.
  *   Symbols per octet (8 consecutive coordinates): E8: z in 2E8, p = z0 & 1, u = (z-p)/2,
  *     slots zz(u0..u6), zz((u7 - (u0+..+u6 & 1))/2); D4 (two blocks): zz(x0..x2),
  *     zz((x3 - (x0+x1+x2 & 1))/2); A2 (four pairs, stretched coordinates, z = 2c with
@@ -60,8 +64,8 @@ typedef void *hq_stream_t; /* a hipStream_t */
 
 typedef enum {
   HQ_OK = 0,
-  HQ_ERR_INVALID_ARG = -1, /* null pointer, bad enum, n % 128 != 0, n > 2^35, step outside 2^+-12 */
-  HQ_ERR_UNSUPPORTED = -2, /* tile size other than 128; or a unary plane of 2^32 words or more      */
+  HQ_ERR_INVALID_ARG = -1, /* null pointer, bad enum, n % TL != 0, n > 2^35, step outside 2^+-12  */
+  HQ_ERR_UNSUPPORTED = -2, /* tile size other than 64, 128, 256; or a unary plane of 2^32 words+     */
   HQ_ERR_NONFINITE = -3,   /* a tile whose transformed energy is NaN or Inf                         */
   HQ_ERR_CAPACITY = -4,    /* output buffer too small; *out_bytes holds the size needed            */
   HQ_ERR_CORRUPT = -5,     /* stream fails validation (header, index, segment, terminator count)   */
@@ -74,7 +78,7 @@ typedef enum { HQ_Z = 0, HQ_D4 = 1, HQ_E8 = 2, HQ_A2 = 3 } hq_lattice;
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 
 typedef struct {
-  uint32_t tile;       /* values per tile; 128 is the only size (component 1: "tiles, e.g. 128")   */
+  uint32_t tile;       /* values per tile: 64, 128 or 256 (component 1: "tiles, e.g. 128")         */
   int32_t lattice;     /* hq_lattice                                                                */
   float target_bps;    /* payload bits per value (coset + Rice bits / n); used when step == 0       */
   uint64_t seed;       /* Philox key of the sign diagonal D and of the dither                        */
@@ -105,10 +109,10 @@ const char *hq_strerror(int code);
  * (host only; no device call).  The workspace needs no initialisation. */
 int hq_workspace_size(uint64_t n, const hq_params *params, size_t *bytes);
 
-/* Stream size for n values at a fixed step and Rice k, without the unary plane (host only):
- * the header, index and fixed plane.  The unary plane adds (symbol >> width) + 1 bits per value,
+/* Stream size for n values at a fixed step, Rice k and tile length, without the unary plane (host
+ * only): the header, index and fixed plane.  The unary plane adds (symbol >> width) + 1 bits per value,
  * which depends on the data; hq_encode reports the exact size needed when a buffer is too small. */
-int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t *bytes);
+int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint32_t tile, uint64_t *bytes);
 
 /* Rate control alone (component 3's rate targeting): chooses the lattice step and Rice parameter
  * for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles meets
@@ -142,15 +146,15 @@ int hq_decode(const void *stream_data, uint64_t stream_bytes, void *out, int32_t
  * hq_encode / hq_decode / hq_rate that used it (HQ_OK when none). */
 int hq_status(void *workspace, hq_stream_t stream);
 
-/* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only). */
+/* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only; enough for any tile length). */
 int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 
 /* Fused decode + matrix-vector product y = W_hat x, where the stream encodes a row-major
- * [rows][cols] matrix (n = rows * cols; tiles of 128 along cols, so cols % 128 == 0) and W_hat is
- * the decoder's reconstruction taken in exact arithmetic.  x: cols values of x_dtype (device),
- * y: rows binary32 values (device).  Since tile (r, j) decodes to D H yhat / 128 (component 1's
- * transform is orthogonal up to the factor 128 and H is symmetric), its contribution is
- * <yhat, H D x_j> / 128: the activation is rotated once per column tile (binary32, the encoder's
+ * [rows][cols] matrix (n = rows * cols; tiles of TL values along cols, so cols % TL == 0) and W_hat
+ * is the decoder's reconstruction taken in exact arithmetic.  x: cols values of x_dtype (device),
+ * y: rows binary32 values (device).  Since tile (r, j) decodes to D H yhat / TL (component 1's
+ * transform is orthogonal up to the factor TL and H is symmetric), its contribution is
+ * <yhat, H D x_j> / TL: the activation is rotated once per column tile (binary32, the encoder's
  * butterfly order) and no matrix tile is inverse-transformed.  Per tile, yhat = (c - U) * s * step
  * rounded to binary32, the octet products are a fixed-order chain, the tile sum a fixed tree, and
  * the row sum adds the tiles in column order, so results are deterministic; they differ from an
@@ -158,7 +162,8 @@ int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
  * Components 1-3 of the HyperQuant technical summary (section "Methodology: the HyperQuant
  * pipeline"); fused decode + matrix products are the direction its section "Significance and
  * claims" names for a wall-clock gain.  Asynchronous;
- * stream validation as for hq_decode, errors through hq_status(workspace). */
+ * stream validation as for hq_decode (a stream whose tile length does not divide cols is corrupt
+ * for this call), errors through hq_status(workspace). */
 int hq_gemv(const void *stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void *x,
             int32_t x_dtype, float *y, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 

@@ -62,7 +62,7 @@ def lib():
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_workspace_size.argtypes = [u64, P, ctypes.POINTER(sz)]
-        L.hq_stream_fixed_bytes.argtypes = [u64, i32, i32, ctypes.POINTER(u64)]
+        L.hq_stream_fixed_bytes.argtypes = [u64, i32, i32, ctypes.c_uint32, ctypes.POINTER(u64)]
         L.hq_rate.argtypes = [P, i32, u64, P, P, P, sz, P]
         L.hq_encode.argtypes = [P, i32, u64, P, P, u64, P, P, P, sz, P]
         L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
@@ -106,10 +106,10 @@ def hq_workspace_size(n: int, params: HqParams | None = None) -> int:
     return out.value
 
 
-def hq_stream_fixed_bytes(n: int, lattice, rice_k: int) -> int:
+def hq_stream_fixed_bytes(n: int, lattice, rice_k: int, tile: int = 128) -> int:
     out = ctypes.c_uint64(0)
     lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
-    _check(lib().hq_stream_fixed_bytes(n, lat, rice_k, ctypes.byref(out)), "hq_stream_fixed_bytes")
+    _check(lib().hq_stream_fixed_bytes(n, lat, rice_k, tile, ctypes.byref(out)), "hq_stream_fixed_bytes")
     return out.value
 
 
@@ -140,7 +140,8 @@ def workspace(n: int, device="cuda"):
     return torch.empty(hq_workspace_size(n), dtype=torch.uint8, device=device)
 
 
-def capacity_estimate(n: int, lattice, target_bps: float, rice_k: int = -1, step: float = 0.0) -> int:
+def capacity_estimate(n: int, lattice, target_bps: float, rice_k: int = -1, step: float = 0.0,
+                      tile: int = 128) -> int:
     """A starting output size: the fixed plane at a generous Rice k plus 4 unary bits per value."""
     if rice_k >= 0:
         k = rice_k
@@ -148,23 +149,24 @@ def capacity_estimate(n: int, lattice, target_bps: float, rice_k: int = -1, step
         k = 15
     else:
         k = min(15, int(target_bps) + 3)
-    return hq_stream_fixed_bytes(n, lattice, k) + n // 2 + 4096
+    return hq_stream_fixed_bytes(n, lattice, k, tile) + n // 2 + 4096
 
 
 def hq_encode(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, out=None,
-              ws=None, stream=None, blocking=True):
-    """Encode a contiguous CUDA tensor (fp32 or bf16, numel % 128 == 0).
+              ws=None, stream=None, blocking=True, tile=128):
+    """Encode a contiguous CUDA tensor (fp32 or bf16, numel a multiple of the tile length 64, 128
+    or 256).
 
     Returns (stream bytes as a uint8 CUDA tensor, info dict).  With blocking=False the call only
     enqueues work and returns (out, None); the size is then in the stream header."""
     torch = _torch()
     assert x.is_cuda and x.is_contiguous()
     n = x.numel()
-    p = make_params(lattice, target_bps, seed, dither, step, rice_k)
+    p = make_params(lattice, target_bps, seed, dither, step, rice_k, tile)
     if ws is None:
         ws = workspace(n, x.device)
     if out is None:
-        out = torch.empty(capacity_estimate(n, p.lattice, target_bps, rice_k, step), dtype=torch.uint8,
+        out = torch.empty(capacity_estimate(n, p.lattice, target_bps, rice_k, step, tile), dtype=torch.uint8,
                           device=x.device)
     sh = _stream_handle(stream)
     if not blocking:
@@ -291,12 +293,12 @@ def hq_srft_decode(codes, scales, n: int, seed: int = 0, bits: int = 4, lam=None
 
 
 def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, ws=None, stream=None,
-            blocking=True):
+            blocking=True, tile=128):
     """Rate control alone.  blocking=False only enqueues it; a following hq_encode(..., step=-1,
     ws=<same workspace>) then encodes at the chosen operating point."""
     assert x.is_cuda and x.is_contiguous()
     n = x.numel()
-    p = make_params(lattice, target_bps, seed, dither, step, rice_k)
+    p = make_params(lattice, target_bps, seed, dither, step, rice_k, tile)
     if ws is None:
         ws = workspace(n, x.device)
     info = HqInfo()
@@ -306,22 +308,22 @@ def hq_rate(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, ric
     return info.as_dict() if blocking else None
 
 
-def hq_codes(x, step: float, lattice="e8", seed=0, dither=False, ws=None, stream=None):
+def hq_codes(x, step: float, lattice="e8", seed=0, dither=False, ws=None, stream=None, tile=128):
     """Integer lattice codes (int32, per value) and bf16 tile-scale bits (int16 view, per tile)."""
     torch = _torch()
     assert x.is_cuda and x.is_contiguous()
     n = x.numel()
-    p = make_params(lattice, 4.0, seed, dither, step, -1)
+    p = make_params(lattice, 4.0, seed, dither, step, -1, tile)
     if ws is None:
         ws = workspace(0, x.device)
     codes = torch.empty(n, dtype=torch.int32, device=x.device)
-    scales = torch.empty(max(n // 128, 1), dtype=torch.int16, device=x.device)
+    scales = torch.empty(max(n // tile, 1), dtype=torch.int16, device=x.device)
     sh = _stream_handle(stream)
     _check(lib().hq_codes(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
                           ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh), "hq_codes")
     _check(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), sh), "hq_codes")
-    return codes, scales[: n // 128]
+    return codes, scales[: n // tile]
 
 
 def hq_status(ws, stream=None) -> int:

@@ -27,20 +27,25 @@ int octet_rem_bits_h(int lattice, int k) {
   const int kh = k > 0 ? k - 1 : 0;
   return lattice == HQ_E8 ? 7 * k + kh : lattice == HQ_D4 ? 6 * k + 2 * kh : lattice == HQ_A2 ? 4 * k + 4 * kh : 8 * k;
 }
-uint32_t tile_fixed_bits_h(int lattice, int k) {
-  return (uint32_t)((lattice == HQ_E8 ? 32 : lattice == HQ_A2 ? 80 : 16) + 16 * octet_rem_bits_h(lattice, k));
+// Fixed bits of a tile record: 16 scale bits, the coset bits (E8: one per octet; A2: one per pair)
+// and the remainders of tile / 8 octets.
+uint32_t tile_fixed_bits_h(int lattice, int k, uint32_t tile) {
+  const uint32_t oct = tile / 8u;
+  return 16u + (lattice == HQ_E8 ? oct : lattice == HQ_A2 ? 4u * oct : 0u) + oct * (uint32_t)octet_rem_bits_h(lattice, k);
 }
+bool valid_tile(uint32_t tile) { return tile == 64u || tile == 128u || tile == 256u; }
 
 // Lowest payload rate a lattice reaches: one unary bit per value plus its raw coset bits.
 float min_bps(int lattice) { return lattice == HQ_E8 ? 1.125f : lattice == HQ_A2 ? 1.5f : 1.0f; }
 
-uint64_t chunks_of(uint64_t n) { return (n / 128 + 63) / 64; }
+// A chunk holds 8192 values at every tile length (8192 / tile tiles).
+uint64_t chunks_of(uint64_t n) { return (n + 8191) / 8192; }
 
 int check_params(const hq_params* p, uint64_t n) {
   if (!p) return HQ_ERR_INVALID_ARG;
-  if (p->tile != 128) return HQ_ERR_UNSUPPORTED;
+  if (!valid_tile(p->tile)) return HQ_ERR_UNSUPPORTED;
   if (p->lattice < HQ_Z || p->lattice > HQ_A2) return HQ_ERR_INVALID_ARG;
-  if (n % 128) return HQ_ERR_INVALID_ARG;
+  if (n % p->tile) return HQ_ERR_INVALID_ARG;
   if (n > (1ull << 35)) return HQ_ERR_INVALID_ARG;  // the encoder's look-back packs 28-bit padding sums
   if (p->dither > 1) return HQ_ERR_INVALID_ARG;
   if (p->rice_k < -1 || p->rice_k > 15) return HQ_ERR_INVALID_ARG;
@@ -72,7 +77,8 @@ EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, v
   a.x = x;
   a.dtype = dtype;
   a.n = n;
-  a.tiles = n / 128;
+  a.tile = (int)p->tile;
+  a.tiles = n / p->tile;
   a.chunks = (uint32_t)chunks_of(n);
   a.lattice = p->lattice;
   a.dither = (int)p->dither;
@@ -189,16 +195,18 @@ const char* hq_strerror(int code) {
 
 int hq_workspace_size(uint64_t n, const hq_params* params, size_t* bytes) {
   (void)params;
-  if (!bytes || n % 128) return HQ_ERR_INVALID_ARG;
+  if (!bytes || n % 64) return HQ_ERR_INVALID_ARG;
   *bytes = workspace_bytes_for(n);
   return HQ_OK;
 }
 
-int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint64_t* bytes) {
-  if (!bytes || n % 128 || lattice < HQ_Z || lattice > HQ_A2 || rice_k < 0 || rice_k > 15) return HQ_ERR_INVALID_ARG;
+int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint32_t tile, uint64_t* bytes) {
+  if (!bytes || lattice < HQ_Z || lattice > HQ_A2 || rice_k < 0 || rice_k > 15) return HQ_ERR_INVALID_ARG;
+  if (!valid_tile(tile)) return HQ_ERR_UNSUPPORTED;
+  if (n % tile) return HQ_ERR_INVALID_ARG;
   const uint64_t chunks = chunks_of(n);
   const uint64_t fixed_off = align256h(128 + 4 * (chunks + 1));
-  *bytes = align256h(fixed_off + chunks * 8ull * tile_fixed_bits_h(lattice, rice_k));
+  *bytes = align256h(fixed_off + chunks * (8192ull / tile) * tile_fixed_bits_h(lattice, rice_k, tile) / 8ull);
   return HQ_OK;
 }
 
@@ -260,7 +268,7 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
 
 int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t out_dtype, uint64_t n,
               void* workspace, size_t workspace_bytes, hq_stream_t stream) {
-  if (n % 128 || (n / 128 + 63) / 64 >= 0xFFFFFFFFull) return HQ_ERR_INVALID_ARG;
+  if (n % 64 || chunks_of(n) >= 0xFFFFFFFFull) return HQ_ERR_INVALID_ARG;
   if (out_dtype != HQ_F32 && out_dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
   if (!stream_data || !workspace || workspace_bytes < kWsHeader || (n && !out)) return HQ_ERR_INVALID_ARG;
   if (((uintptr_t)stream_data & 15u) || ((uintptr_t)out & 15u) || ((uintptr_t)workspace & 255u))
@@ -274,8 +282,9 @@ int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t
 static size_t gemv_xt_bytes(uint64_t cols) { return align256h(4ull * cols); }
 
 int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t* bytes) {
-  if (!bytes || cols % 128 || (rows && cols && rows > (1ull << 35) / cols)) return HQ_ERR_INVALID_ARG;
-  *bytes = kWsHeader + gemv_xt_bytes(cols) + align256h(4ull * (rows * cols / 128));
+  if (!bytes || cols % 64 || (rows && cols && rows > (1ull << 35) / cols)) return HQ_ERR_INVALID_ARG;
+  // per-tile partial products for the shortest tile (64 values), whatever the stream's tile length
+  *bytes = kWsHeader + gemv_xt_bytes(cols) + align256h(4ull * (rows * cols / 64));
   return HQ_OK;
 }
 

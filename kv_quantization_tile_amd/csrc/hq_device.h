@@ -1,9 +1,10 @@
 // hq_device.h -- device building blocks of the gfx950 codec kernels.
 //
-// Thread layout used by every kernel: a workgroup has 256 lanes in 4 wavefronts of 64.  Lane
-// (wave w, lane l) owns octet o = l % 16 (coordinates 8o..8o+7) of tile 4 w + l / 16 of the
-// workgroup's current group of 16 tiles.  A tile therefore lives in 16 consecutive lanes, 8 values
-// per lane: three Hadamard stages run inside the lane and four across lanes (lane xor 1, 2, 4, 8).
+// Thread layout used by every kernel: a workgroup has 256 lanes in 4 wavefronts of 64.  A tile of
+// TL values (64, 128 or 256) lives in LPT = TL / 8 consecutive lanes, 8 values per lane: lane
+// (wave w, lane l) owns octet o = l % LPT (coordinates 8o..8o+7) of tile TPW w + l / LPT of the
+// workgroup's current group of 4 TPW tiles, TPW = 64 / LPT tiles per wavefront.  Three Hadamard
+// stages run inside the lane and log2(LPT) across lanes (lane xor 1, 2, 4, ...).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,7 +12,8 @@
 
 namespace hq {
 
-constexpr int kTile = 128;
+constexpr int kTile = 128;            // the default tile length; 64 and 256 are the others
+constexpr int kChunkValues = 8192;    // a chunk holds kChunkValues / TL tiles
 constexpr int kChunkTiles = 64;
 constexpr int kBlock = 256;
 constexpr int kHeaderBytes = 128;
@@ -46,18 +48,20 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
   return c;
 }
 
-// Sign word of octet o: bit i (0..7) set means D_{8o+i} = -1.  D comes from one Philox call with
-// counter 0 and key = seed; the 128 sign bits are the output words, least significant bit first.
+// Sign word of octet o: bit i (0..7) set means D_{8o+i} = -1.  D comes from Philox calls with key
+// = seed and counters (c, 0, 0, 0): octets 0..15 use call 0, octets 16..31 (tiles of 256) call 1;
+// the sign bits are the output words, least significant bit first.
 __device__ __forceinline__ uint32_t octet_sign_bits(uint64_t seed, int o) {
-  const U4 w = philox4x32_10(U4{0u, 0u, 0u, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32));
-  const uint32_t word = (o >> 2) == 0 ? w.x : (o >> 2) == 1 ? w.y : (o >> 2) == 2 ? w.z : w.w;
+  const U4 w = philox4x32_10(U4{(uint32_t)(o >> 4), 0u, 0u, 0u}, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const int q = (o >> 2) & 3;
+  const uint32_t word = q == 0 ? w.x : q == 1 ? w.y : q == 2 ? w.z : w.w;
   return (word >> ((o & 3) * 8)) & 0xFFu;
 }
 
 // ---------------------------------------------------------------------------------------------
-// Unnormalised Walsh-Hadamard transform of the 128 values held by 16 lanes (8 per lane), stage j
-// pairing index i with i + 2^j in the order j = 0..6; the low element becomes a + b, the high
-// a - b.  Stages 0-2 are in registers, 3-6 exchange with lane xor 1, 2, 4, 8.
+// Unnormalised Walsh-Hadamard transform of the TL values held by LPT lanes (8 per lane), stage j
+// pairing index i with i + 2^j in the order j = 0..log2(TL)-1; the low element becomes a + b, the
+// high a - b.  Stages 0-2 are in registers, the others exchange with lane xor 1, 2, 4, ...
 __device__ __forceinline__ void fwht_lane(float a[8]) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -79,11 +83,11 @@ __device__ __forceinline__ float lane_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
 }
 
-// The four cross-lane stages.  Each lane computes own + s * partner with s = +1 on the low lane
-// and -1 on the high lane, as one fused multiply-add: the product by +-1 is exact, so the result
-// is the sum or difference rounded once, exactly as the plain butterfly.  The high lane then holds
-// the negated value; after the four stages lane l holds sigma(l) * y with
-// sigma(l) = (-1)^popcount(l & 15) (lane_sign_bit), which callers fold into the quantiser's
+// The cross-lane stages.  Each lane computes own + s * partner with s = +1 on the low lane and -1
+// on the high lane, as one fused multiply-add: the product by +-1 is exact, so the result is the
+// sum or difference rounded once, exactly as the plain butterfly.  The high lane then holds the
+// negated value; after the stages lane l holds sigma(l) * y with
+// sigma(l) = (-1)^popcount(l mod LPT) (lane_sign_bit), which callers fold into the quantiser's
 // multiplier (encode) or into the sign diagonal (decode).
 template <int M>
 __device__ __forceinline__ void fwht_stage(float a[8], int lane16) {
@@ -92,17 +96,21 @@ __device__ __forceinline__ void fwht_stage(float a[8], int lane16) {
   for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(lane_xor<M>(a[i]), sgn, a[i]);
 }
 
-__device__ __forceinline__ void fwht_cross(float a[8], int lane16) {
-  fwht_stage<1>(a, lane16);
-  fwht_stage<2>(a, lane16);
-  fwht_stage<4>(a, lane16);
-  fwht_stage<8>(a, lane16);
+template <int LPT = 16>
+__device__ __forceinline__ void fwht_cross(float a[8], int o) {
+  fwht_stage<1>(a, o);
+  fwht_stage<2>(a, o);
+  fwht_stage<4>(a, o);
+  if (LPT >= 16) fwht_stage<8>(a, o);
+  if (LPT >= 32) fwht_stage<16>(a, o);
 }
 
-__device__ __forceinline__ uint32_t lane_sign_bit(int lane16) { return (uint32_t)__popc(lane16 & 15) & 1u; }
+template <int LPT = 16>
+__device__ __forceinline__ uint32_t lane_sign_bit(int o) { return (uint32_t)__popc(o & (LPT - 1)) & 1u; }
 
 // Sum of squares of the tile as a balanced pairwise tree in index order: squares, pairs inside
-// the lane, then lane xor 1, 2, 4, 8 (each add is commutative, so both lanes get equal sums).
+// the lane, then lane xor 1, 2, 4, ... (each add is commutative, so both lanes get equal sums).
+template <int LPT = 16>
 __device__ __forceinline__ float tile_sumsq(const float a[8]) {
   float s[8];
 #pragma unroll
@@ -111,7 +119,8 @@ __device__ __forceinline__ float tile_sumsq(const float a[8]) {
   t = t + lane_xor<1>(t);
   t = t + lane_xor<2>(t);
   t = t + lane_xor<4>(t);
-  t = t + lane_xor<8>(t);
+  if (LPT >= 16) t = t + lane_xor<8>(t);
+  if (LPT >= 32) t = t + lane_xor<16>(t);
   return t;
 }
 
@@ -123,11 +132,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Tile scale s = bfloat16 nearest to sqrt(S / 128), ties to even, decided exactly.  A hardware
+// Tile scale s = bfloat16 nearest to sqrt(S / TL), ties to even, decided exactly.  A hardware
 // square root r (within one binary32 ulp) gives the candidate c = bf16(r); the true result can only
 // be c's neighbour on r's side of c, across the rounding midpoint m between them, and that midpoint
-// has 9 significant bits, so S against 128 m^2 is an exact binary32 comparison.  S is first brought
+// has 9 significant bits, so S against TL m^2 is an exact binary32 comparison.  S is first brought
 // into [2^-60, 2^60] by an exact power-of-two factor so that no square under- or overflows.
+template <int TL = 128>
 __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
   if (!(S > 0.0f)) return 0u;
   float Ss = S;
@@ -139,13 +149,13 @@ __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
     Ss = S * 0x1p-100f;
     adj = -50;
   }
-  const float r = __builtin_amdgcn_sqrtf(Ss * 0.0078125f);
+  const float r = __builtin_amdgcn_sqrtf(Ss * (1.0f / (float)TL));
   uint32_t c = f32_to_bf16_rne(r);
   const float cv = bf16_bits_to_f32(c);
   const bool up = r >= cv;
   const uint32_t nb = up ? c + 1u : c - 1u;
   const float m = (cv + bf16_bits_to_f32(nb)) * 0.5f;
-  const float tm = 128.0f * (m * m);
+  const float tm = (float)TL * (m * m);
   const bool cross = up ? (Ss > tm) : (Ss < tm);
   if (cross || (Ss == tm && (c & 1u))) c = nb;
   return (uint32_t)((int32_t)c - adj * 128);
@@ -366,15 +376,15 @@ __device__ __forceinline__ int octet_rem_bits(int k) {
   const int kh = k > 0 ? k - 1 : 0;
   return LAT == kLatE8 ? 7 * k + kh : LAT == kLatD4 ? 6 * k + 2 * kh : LAT == kLatA2 ? 4 * k + 4 * kh : 8 * k;
 }
-// Tile record header: 16 scale bits, then the raw coset bits (E8: one per octet; A2: one per pair,
-// bit 4 o + j for pair j of octet o).
-template <int LAT>
+// Tile record header: 16 scale bits, then the raw coset bits (E8: one per octet, bit o; A2: one
+// per pair, bit 4 o + j for pair j of octet o); then the remainders of the TL / 8 octets.
+template <int LAT, int TL = kTile>
 __device__ __forceinline__ int tile_hdr_bits() {
-  return LAT == kLatE8 ? 32 : LAT == kLatA2 ? 80 : 16;
+  return 16 + (LAT == kLatE8 ? TL / 8 : LAT == kLatA2 ? TL / 2 : 0);
 }
-template <int LAT>
+template <int LAT, int TL = kTile>
 __device__ __forceinline__ uint32_t tile_fixed_bits(int k) {
-  return (uint32_t)(tile_hdr_bits<LAT>() + 16 * octet_rem_bits<LAT>(k));
+  return (uint32_t)(tile_hdr_bits<LAT, TL>() + (TL / 8) * octet_rem_bits<LAT>(k));
 }
 
 template <int LAT>
@@ -450,10 +460,10 @@ __device__ __forceinline__ void unstrip_octet(const uint32_t* sym, uint32_t cose
 // Loads of one lane's 8 values of tile t with the sign diagonal applied (DT 0: fp32, 1: bf16 bits).
 // smask[i] is 0x80000000 where D = -1: the sign flip is an xor (fp32) or an add into bit 31 of the
 // widened bf16 value, both exact.
-template <int DT>
+template <int DT, int TL = kTile>
 __device__ __forceinline__ void load_octet_signed(const void* x, uint64_t t, int o, const uint32_t* smask, float* v) {
   if (DT == 1) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * o);
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * TL + 8 * o);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -461,7 +471,7 @@ __device__ __forceinline__ void load_octet_signed(const void* x, uint64_t t, int
       v[2 * i + 1] = __uint_as_float((ws[i] & 0xFFFF0000u) ^ smask[2 * i + 1]);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * o);
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * TL + 8 * o);
     const float4 a = p[0], b = p[1];
     const float vv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -469,18 +479,20 @@ __device__ __forceinline__ void load_octet_signed(const void* x, uint64_t t, int
   }
 }
 
-// Broadcast inside the 16-lane group of a tile: every lane receives the value of lane `src` (0..15)
-// of its own group (ds_swizzle bit-mask mode: keep lane bit 4, set bits 0-3 to src).
-template <int SRC>
+// Broadcast inside the LPT-lane group of a tile: every lane receives the value of lane SRC of its
+// own group (ds_swizzle bit-mask mode inside 32 lanes: keep the lane bits above the group, set
+// the low bits to SRC).
+template <int SRC, int LPT = 16>
 __device__ __forceinline__ uint32_t group_bcast(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x10 | (SRC << 5));
+  static_assert(SRC < LPT, "source lane inside the group");
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (0x1F & ~(LPT - 1)) | (SRC << 5));
 }
 
 // Loads of one lane's 8 values of tile t (DT 0: fp32, 1: bf16 bits).
-template <int DT>
+template <int DT, int TL = kTile>
 __device__ __forceinline__ void load_octet(const void* x, uint64_t t, int o, float* v) {
   if (DT == 1) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * o);
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * TL + 8 * o);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -488,7 +500,7 @@ __device__ __forceinline__ void load_octet(const void* x, uint64_t t, int o, flo
       v[2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * o);
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * TL + 8 * o);
     const float4 a = p[0], b = p[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;

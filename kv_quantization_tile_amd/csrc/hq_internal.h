@@ -41,7 +41,7 @@ struct alignas(256) Workspace {
   uint32_t dec_step_bits;
   uint32_t dec_F;
   uint32_t dec_chunks;
-  uint32_t pad1;
+  uint32_t dec_tile;
   uint64_t dec_seed;
   uint64_t dec_tiles;
   uint64_t dec_fixed_off;
@@ -79,6 +79,7 @@ struct EncodeArgs {
   int dtype;
   uint64_t n, tiles;
   uint32_t chunks;
+  int tile;            // values per tile: 64, 128 or 256
   int lattice;
   int dither;
   uint64_t seed;

@@ -118,14 +118,27 @@ __device__ __forceinline__ int64_t clamp_i64(int64_t v, int64_t lo, int64_t hi) 
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Lane layout of a tile length TL: LPT lanes per tile, TPW tiles per wavefront, TPR tiles per
+// workgroup round, CT tiles per chunk (four rounds, kChunkValues values).
+template <int TL>
+struct Tiling {
+  static_assert(TL == 64 || TL == 128 || TL == 256, "tile length");
+  static constexpr int LPT = TL / 8;
+  static constexpr int TPW = 64 / LPT;
+  static constexpr int TPR = 4 * TPW;
+  static constexpr int CT = kChunkValues / TL;
+  static_assert(CT == 4 * TPR, "four rounds per chunk");
+};
+
 // ---------------------------------------------------------------------------------------------
 // Front half shared by the rate, encode and codes kernels: sign, FWHT, tile energy and scale.
 // Returns the scale bits; y holds the transformed values (zeroed when the energy is not finite).
-template <int DT>
+template <int DT, int TL>
 __device__ __forceinline__ uint32_t transform_octet(const void* x, uint64_t t, bool valid, int o,
                                                      uint32_t sgn, float* y, bool* finite) {
+  constexpr int LPT = Tiling<TL>::LPT;
   if (valid) {
-    load_octet<DT>(x, t, o, y);
+    load_octet<DT, TL>(x, t, o, y);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
@@ -133,15 +146,15 @@ __device__ __forceinline__ uint32_t transform_octet(const void* x, uint64_t t, b
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = ((sgn >> i) & 1u) ? -y[i] : y[i];
   fwht_lane(y);
-  fwht_cross(y, o);
-  float S = tile_sumsq(y);
+  fwht_cross<LPT>(y, o);
+  float S = tile_sumsq<LPT>(y);
   *finite = isfinite(S);
   if (!*finite) {
     S = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
   }
-  return tile_scale_bits(S);
+  return tile_scale_bits<TL>(S);
 }
 
 // Per-tile multiplier m = 1 / (s * step) (0 when s = 0), with the lane's sign folded in.  A2's
@@ -230,7 +243,7 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
 //    2.05 - target octaves; pass B (4 candidates, h = 18: 1/16 octave) refines.  With a fixed step
 //    and automatic k one pass (8192 tiles) with the single candidate picks k.
 // Bits of candidate j over the Rice window (lane j of the solving wavefront computes its own).
-template <int LAT>
+template <int LAT, int TL>
 __device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t centre, int j, int nc, int half_log2,
                                                int fixed_k, uint32_t N, int64_t* b_out, double* R_out, int* k_out) {
   const int64_t b = nc == 1 ? centre
@@ -241,7 +254,7 @@ __device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t cen
   double rb = 0.0;
   for (int w = 0; w < kRcKwin; ++w) {
     const int k = fixed_k >= 0 ? fixed_k : kb + w;
-    const double per_tile = (double)(tile_fixed_bits<LAT>(k) - 16u) + 128.0;
+    const double per_tile = (double)(tile_fixed_bits<LAT, TL>(k) - 16u) + (double)TL;
     const double bits = per_tile * (double)N + (double)sumq[j * kRcKwin + w];
     if (w == 0 || bits < rb) {
       rb = bits;
@@ -256,9 +269,9 @@ __device__ __forceinline__ void rate_candidate(const uint64_t* sumq, int64_t cen
 // Bracket, interpolate and round: the next centre (or the final step bits) and the k of the
 // candidate nearest to it (one lane; b, R, kc per candidate).
 __device__ void rate_solve(const int64_t* b, const double* R, const int* kc, int nc, float target, uint32_t N,
-                           int64_t* xb_out, int* k_out) {
-  const double Tb = (double)target * (double)((uint64_t)N * kTile);
-  const double nominal = (double)((uint64_t)N * kTile) / 8388608.0;
+                           int tl, int64_t* xb_out, int* k_out) {
+  const double Tb = (double)target * (double)((uint64_t)N * (uint64_t)tl);
+  const double nominal = (double)((uint64_t)N * (uint64_t)tl) / 8388608.0;
   double xv;
   int64_t lo, hi;
   int jf = -1;
@@ -320,7 +333,7 @@ struct SolveLds {
 // Solve a rate pass around `centre` with the first lanes of a workgroup (every lane of the
 // workgroup calls it: it holds two barriers).  The counter sets are added in a fixed order; every
 // lane gets the result, and the workspace's step, k and centre are set to it.
-template <int LAT>
+template <int LAT, int TL>
 __device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, SolveLds* L, int64_t* xb, int* k) {
   const int tid = threadIdx.x;
   if (tid < kRcCounters) {
@@ -334,14 +347,14 @@ __device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, So
     int64_t b;
     double R;
     int kk;
-    rate_candidate<LAT>(L->sumq, centre, tid, pd.nc, pd.half_log2, pd.fixed_k, pd.N, &b, &R, &kk);
+    rate_candidate<LAT, TL>(L->sumq, centre, tid, pd.nc, pd.half_log2, pd.fixed_k, pd.N, &b, &R, &kk);
     L->b[tid] = b;
     L->R[tid] = R;
     L->k[tid] = kk;
   }
   __syncthreads();
   if (tid == 0) {
-    rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, &L->xb, &L->kres);
+    rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, TL, &L->xb, &L->kres);
     ws->rc_centre = L->xb;
     ws->step_bits = (uint32_t)L->xb;
     ws->rice_k = L->kres;
@@ -374,38 +387,39 @@ __device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// A wavefront takes 4 sample tiles and cpw of the pass's candidates; the cw = ceil(nc / cpw)
-// wavefronts that share a group of 4 tiles sit in the same workgroup, which therefore holds 4 / cw
+// A wavefront takes TPW sample tiles and cpw of the pass's candidates; the cw = ceil(nc / cpw)
+// wavefronts that share a group of TPW tiles sit in the same workgroup, which therefore holds 4 / cw
 // tile groups (cw is 1, 2 or 4).  Splitting the candidates over wavefronts keeps each wavefront's
 // chain short and the pass latency low; every wavefront repeats its tiles' transform.
 // With solve_prev, workgroup 0 first solves the previous pass (prev) for this pass's centre and
 // publishes it in Workspace::sync_centre; the other workgroups transform their tiles meanwhile and
 // then wait for it.
-template <int LAT, bool DITHER, int DT>
+template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
                                                       Workspace* ws, RateAcc* racc, uint64_t seed, int nc,
                                                       int half_log2, int fixed_k, float target, int cpw,
                                                       int solve_prev, PassDesc prev) {
+  constexpr int LPT = Tiling<TL>::LPT, TPW = Tiling<TL>::TPW;
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
   __shared__ SolveLds s_solve;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   int64_t centre_solved = 0;
   if (solve_prev && blockIdx.x == 0) {
     int kk;
-    solve_pass<LAT>(prev, ws->rc_centre, ws, &s_solve, &centre_solved, &kk);
+    solve_pass<LAT, TL>(prev, ws->rc_centre, ws, &s_solve, &centre_solved, &kk);
     if (tid == 0)
       __hip_atomic_store(&ws->sync_centre, (1ull << 63) | (uint64_t)(uint32_t)centre_solved, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
   const int cw = (nc + cpw - 1) / cpw;
   const int jlo = (wave % cw) * cpw, jhi = jlo + cpw;
-  const uint64_t i = ((uint64_t)blockIdx.x * (4 / cw) + wave / cw) * 4 + tw;
+  const uint64_t i = ((uint64_t)blockIdx.x * (4 / cw) + wave / cw) * TPW + tw;
   const bool valid = i < N;
   const uint64_t t = valid ? sample_tile(i, T, N) : 0;
   const uint32_t sgn = octet_sign_bits(seed, o);
   float y[8];
   bool finite;
-  const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
+  const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
   if (valid && !finite && o == 0 && jlo == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
@@ -418,26 +432,33 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
     const uint64_t w = wait_published(&ws->sync_centre, &ws->status);
     centre = (w >> 63) ? (int64_t)(uint32_t)w : ws->rc_centre;
   }
-  // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots);
-  // the group shares them by broadcast
+  // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots, or,
+  // with 8 lanes per tile, every lane both); the group shares them by broadcast
   const int jm = nc == 1 ? 0 : (o & 7);
   const int64_t bm = nc == 1 ? centre
                              : clamp_i64(centre + (int64_t)(2 * jm - (nc - 1)) * ((int64_t)1 << half_log2), kStepBitsMin,
                                          kStepBitsMax);
   const float stepm = __uint_as_float((uint32_t)bm);
-  const uint32_t m_mine = __float_as_uint((LAT == kLatA2 && o >= 8) ? tile_multiplier<true>(sb, stepm, 0u)
-                                                                     : tile_multiplier<false>(sb, stepm, 0u));
-  const bool lane_neg = lane_sign_bit(o) != 0u;
+  const bool odd_lane = LAT == kLatA2 && LPT >= 16 && o >= 8;
+  const uint32_t m_mine = __float_as_uint(odd_lane ? tile_multiplier<true>(sb, stepm, 0u)
+                                                   : tile_multiplier<false>(sb, stepm, 0u));
+  const bool lane_neg = lane_sign_bit<LPT>(o) != 0u;
   float mj[kRcCand], mo[kRcCand];
-  mj[0] = __uint_as_float(group_bcast<0>(m_mine)); mj[1] = __uint_as_float(group_bcast<1>(m_mine));
-  mj[2] = __uint_as_float(group_bcast<2>(m_mine)); mj[3] = __uint_as_float(group_bcast<3>(m_mine));
-  mj[4] = __uint_as_float(group_bcast<4>(m_mine)); mj[5] = __uint_as_float(group_bcast<5>(m_mine));
-  mj[6] = __uint_as_float(group_bcast<6>(m_mine)); mj[7] = __uint_as_float(group_bcast<7>(m_mine));
-  if (LAT == kLatA2) {
-    mo[0] = __uint_as_float(group_bcast<8>(m_mine)); mo[1] = __uint_as_float(group_bcast<9>(m_mine));
-    mo[2] = __uint_as_float(group_bcast<10>(m_mine)); mo[3] = __uint_as_float(group_bcast<11>(m_mine));
-    mo[4] = __uint_as_float(group_bcast<12>(m_mine)); mo[5] = __uint_as_float(group_bcast<13>(m_mine));
-    mo[6] = __uint_as_float(group_bcast<14>(m_mine)); mo[7] = __uint_as_float(group_bcast<15>(m_mine));
+  mj[0] = __uint_as_float(group_bcast<0, LPT>(m_mine)); mj[1] = __uint_as_float(group_bcast<1, LPT>(m_mine));
+  mj[2] = __uint_as_float(group_bcast<2, LPT>(m_mine)); mj[3] = __uint_as_float(group_bcast<3, LPT>(m_mine));
+  mj[4] = __uint_as_float(group_bcast<4, LPT>(m_mine)); mj[5] = __uint_as_float(group_bcast<5, LPT>(m_mine));
+  mj[6] = __uint_as_float(group_bcast<6, LPT>(m_mine)); mj[7] = __uint_as_float(group_bcast<7, LPT>(m_mine));
+  if constexpr (LAT == kLatA2 && LPT >= 16) {
+    mo[0] = __uint_as_float(group_bcast<8, LPT>(m_mine)); mo[1] = __uint_as_float(group_bcast<9, LPT>(m_mine));
+    mo[2] = __uint_as_float(group_bcast<10, LPT>(m_mine)); mo[3] = __uint_as_float(group_bcast<11, LPT>(m_mine));
+    mo[4] = __uint_as_float(group_bcast<12, LPT>(m_mine)); mo[5] = __uint_as_float(group_bcast<13, LPT>(m_mine));
+    mo[6] = __uint_as_float(group_bcast<14, LPT>(m_mine)); mo[7] = __uint_as_float(group_bcast<15, LPT>(m_mine));
+  } else if constexpr (LAT == kLatA2) {
+    const uint32_t m_odd = __float_as_uint(tile_multiplier<true>(sb, stepm, 0u));
+    mo[0] = __uint_as_float(group_bcast<0, LPT>(m_odd)); mo[1] = __uint_as_float(group_bcast<1, LPT>(m_odd));
+    mo[2] = __uint_as_float(group_bcast<2, LPT>(m_odd)); mo[3] = __uint_as_float(group_bcast<3, LPT>(m_odd));
+    mo[4] = __uint_as_float(group_bcast<4, LPT>(m_odd)); mo[5] = __uint_as_float(group_bcast<5, LPT>(m_odd));
+    mo[6] = __uint_as_float(group_bcast<6, LPT>(m_odd)); mo[7] = __uint_as_float(group_bcast<7, LPT>(m_odd));
   } else {
 #pragma unroll
     for (int j = 0; j < kRcCand; ++j) mo[j] = mj[j];
@@ -485,12 +506,12 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
 }
 
 // One workgroup: add up the counter sets of a rate pass, evaluate the candidates, solve.
-template <int LAT>
+template <int LAT, int TL>
 __global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, PassDesc pd) {
   __shared__ SolveLds s_solve;
   int64_t xb;
   int k;
-  solve_pass<LAT>(pd, ws->rc_centre, ws, &s_solve, &xb, &k);
+  solve_pass<LAT, TL>(pd, ws->rc_centre, ws, &s_solve, &xb, &k);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -499,30 +520,31 @@ __global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, PassDesc 
 // FWHT, tile scale, multiplier, dither, lattice).  Used only for octets whose unary code is longer
 // than one word and for segments larger than the staging window; every lane of the wavefront must
 // call it together (the FWHT and the tile energy exchange values between lanes).
-template <int LAT, bool DITHER, int DT>
+template <int LAT, bool DITHER, int DT, int TL>
 __device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_t seed, uint32_t c, int r,
                                               int wave, int tw, int o, uint32_t sgn, uint32_t lane_neg, float step,
                                               uint32_t* sym) {
-  const uint64_t t = (uint64_t)c * kChunkTiles + 16u * r + 4u * wave + tw;
+  using TI = Tiling<TL>;
+  const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
   uint32_t smask[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
   float y[8];
   if (t < T) {
-    load_octet_signed<DT>(x, t, o, smask, y);
+    load_octet_signed<DT, TL>(x, t, o, smask, y);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
   }
   fwht_lane(y);
-  fwht_cross(y, o);
-  const float S = tile_sumsq(y);
+  fwht_cross<TI::LPT>(y, o);
+  const float S = tile_sumsq<TI::LPT>(y);
   const bool fin = isfinite(S);
   if (!fin) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
   }
-  const uint32_t sb = tile_scale_bits(fin ? S : 0.0f);
+  const uint32_t sb = tile_scale_bits<TL>(fin ? S : 0.0f);
   const float m = tile_multiplier<false>(sb, step, lane_neg);
   const float m1 = LAT == kLatA2 ? tile_multiplier<true>(sb, step, lane_neg) : m;
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -534,12 +556,12 @@ __device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_
 __device__ void write_header(uint8_t* out, uint64_t cap, int lattice, int dither, int k, uint32_t step_bits,
                              uint64_t seed, uint64_t n, uint64_t T, uint32_t chunks, uint32_t F,
                              uint64_t fixed_off, uint64_t unary_off, uint64_t words, uint64_t ubits,
-                             uint64_t payload, uint64_t total) {
+                             uint64_t payload, uint64_t total, uint32_t tile, uint32_t log2_ct) {
   if (cap < (uint64_t)kHeaderBytes) return;
   uint32_t h[32];
   h[0] = kMagic;
   h[1] = kVersion | ((uint32_t)lattice << 16) | ((uint32_t)(dither ? 1 : 0) << 24);
-  h[2] = (uint32_t)kTile | ((uint32_t)k << 16) | (6u << 24);
+  h[2] = tile | ((uint32_t)k << 16) | (log2_ct << 24);
   h[3] = step_bits;
   h[4] = (uint32_t)seed; h[5] = (uint32_t)(seed >> 32);
   h[6] = (uint32_t)n; h[7] = (uint32_t)(n >> 32);
@@ -620,8 +642,10 @@ struct EncParams {
   uint64_t* flags;
 };
 
-template <int LAT, bool DITHER, int DT>
+template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
+  using TI = Tiling<TL>;
+  constexpr int LPT = TI::LPT;
   __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
   __shared__ uint4 s_unary4[kUnaryWinWords / 4];
   __shared__ uint4 s_wtot4[4];  // per round, the four wavefronts' Rice-length totals
@@ -629,18 +653,19 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
   uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   Workspace* ws = P.ws;
   const uint32_t c = blockIdx.x;
   const uint32_t step_bits = ws->step_bits;
   const int k = ws->rice_k;
   const float step = __uint_as_float(step_bits);
-  const uint32_t F = tile_fixed_bits<LAT>(k);
+  const uint32_t F = tile_fixed_bits<LAT, TL>(k);
   const int RW = octet_rem_bits<LAT>(k);
-  const int hdr = tile_hdr_bits<LAT>();
-  const uint32_t fixed_words = 2u * F;
+  const int hdr = tile_hdr_bits<LAT, TL>();
+  const uint32_t fixed_words = (uint32_t)TI::CT * F / 32u;  // a chunk's record, 16-byte multiple
+  const uint64_t chunk_bytes = 4ull * fixed_words;
   const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (P.chunks + 1));
-  const uint64_t unary_off = align256(fixed_off + (uint64_t)P.chunks * 8ull * F);
+  const uint64_t unary_off = align256(fixed_off + (uint64_t)P.chunks * chunk_bytes);
   const uint4 z4 = make_uint4(0, 0, 0, 0);
   for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) s_fixed4[i] = z4;
   for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
@@ -649,7 +674,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   // alignment padding of the stream (after the index, after the fixed plane) is zero bytes
   if (c == 0) {
     const uint64_t pads[2][2] = {{kHeaderBytes + 4ull * (P.chunks + 1), fixed_off},
-                                 {fixed_off + (uint64_t)P.chunks * 8ull * F, unary_off}};
+                                 {fixed_off + (uint64_t)P.chunks * chunk_bytes, unary_off}};
     for (int pz = 0; pz < 2; ++pz)
       for (uint64_t b = pads[pz][0] + 4ull * tid; b < pads[pz][1]; b += 4ull * kBlock)
         if (b + 4 <= P.cap) *reinterpret_cast<uint32_t*>(P.out + b) = 0u;
@@ -659,7 +684,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     if (P.chunks == 0 && tid == 0) {
       const uint64_t total = unary_off;
       write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, 0, F, fixed_off, unary_off, 0, 0,
-                   0, total);
+                   0, total, TL, __builtin_ctz(TI::CT));
       if (P.cap >= kHeaderBytes + 4) reinterpret_cast<uint32_t*>(P.out)[kHeaderBytes / 4] = 0;
       if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
       ws->res_total_bytes = total;
@@ -676,23 +701,23 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   uint32_t smask[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
-  const uint32_t lane_neg = lane_sign_bit(o);
+  const uint32_t lane_neg = lane_sign_bit<LPT>(o);
 
   // phase 1: every round's transform and tile energy
   float y[4][8];
   float S[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint64_t t = (uint64_t)c * kChunkTiles + 16u * r + 4u * wave + tw;
+    const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
     if (t < P.T) {
-      load_octet_signed<DT>(P.x, t, o, smask, y[r]);
+      load_octet_signed<DT, TL>(P.x, t, o, smask, y[r]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
     }
     fwht_lane(y[r]);
-    fwht_cross(y[r], o);
-    S[r] = tile_sumsq(y[r]);
+    fwht_cross<LPT>(y[r], o);
+    S[r] = tile_sumsq<LPT>(y[r]);
   }
   // one scale and one division per lane (round o mod 4; A2: lanes with bit 2 of o set divide for
   // the odd slots), broadcast inside the tile's lane group
@@ -702,25 +727,25 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const int rr = o & 3;
     const float Sr = rr == 0 ? S[0] : rr == 1 ? S[1] : rr == 2 ? S[2] : S[3];
     const bool fin = isfinite(Sr);
-    const uint64_t t = (uint64_t)c * kChunkTiles + 16u * rr + 4u * wave + tw;
+    const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * rr + (uint32_t)TI::TPW * wave + tw;
     if (!fin && t < P.T && o < 4) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
-    sb_mine = tile_scale_bits(fin ? Sr : 0.0f);
+    sb_mine = tile_scale_bits<TL>(fin ? Sr : 0.0f);
     m_mine = (LAT == kLatA2 && (o & 4)) ? tile_multiplier<true>(sb_mine, step, 0u)
                                         : tile_multiplier<false>(sb_mine, step, 0u);
   }
   uint32_t sbr[4];
   float mr[4], mr1[4];
-  sbr[0] = group_bcast<0>(sb_mine); sbr[1] = group_bcast<1>(sb_mine);
-  sbr[2] = group_bcast<2>(sb_mine); sbr[3] = group_bcast<3>(sb_mine);
-  mr[0] = __uint_as_float(group_bcast<0>(__float_as_uint(m_mine)));
-  mr[1] = __uint_as_float(group_bcast<1>(__float_as_uint(m_mine)));
-  mr[2] = __uint_as_float(group_bcast<2>(__float_as_uint(m_mine)));
-  mr[3] = __uint_as_float(group_bcast<3>(__float_as_uint(m_mine)));
+  sbr[0] = group_bcast<0, LPT>(sb_mine); sbr[1] = group_bcast<1, LPT>(sb_mine);
+  sbr[2] = group_bcast<2, LPT>(sb_mine); sbr[3] = group_bcast<3, LPT>(sb_mine);
+  mr[0] = __uint_as_float(group_bcast<0, LPT>(__float_as_uint(m_mine)));
+  mr[1] = __uint_as_float(group_bcast<1, LPT>(__float_as_uint(m_mine)));
+  mr[2] = __uint_as_float(group_bcast<2, LPT>(__float_as_uint(m_mine)));
+  mr[3] = __uint_as_float(group_bcast<3, LPT>(__float_as_uint(m_mine)));
   if (LAT == kLatA2) {
-    mr1[0] = __uint_as_float(group_bcast<4>(__float_as_uint(m_mine)));
-    mr1[1] = __uint_as_float(group_bcast<5>(__float_as_uint(m_mine)));
-    mr1[2] = __uint_as_float(group_bcast<6>(__float_as_uint(m_mine)));
-    mr1[3] = __uint_as_float(group_bcast<7>(__float_as_uint(m_mine)));
+    mr1[0] = __uint_as_float(group_bcast<4, LPT>(__float_as_uint(m_mine)));
+    mr1[1] = __uint_as_float(group_bcast<5, LPT>(__float_as_uint(m_mine)));
+    mr1[2] = __uint_as_float(group_bcast<6, LPT>(__float_as_uint(m_mine)));
+    mr1[3] = __uint_as_float(group_bcast<7, LPT>(__float_as_uint(m_mine)));
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) mr1[r] = mr[r];
@@ -731,8 +756,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   uint32_t L[4], pat[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint32_t tc = 16u * r + 4u * wave + tw;
-    const uint64_t t = (uint64_t)c * kChunkTiles + tc;
+    const uint32_t tc = (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
+    const uint64_t t = (uint64_t)c * TI::CT + tc;
     const bool valid = t < P.T;
     if (__ballot(!isfinite(S[r]))) {  // uniform test: the common case skips the block entirely
       if (!isfinite(S[r])) {
@@ -750,7 +775,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       const uint32_t rec = tc * F;
       if (o == 0) {
         lds_put_bits(s_fixed, rec, sbr[r], 16);
-        if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (16 * tw)) & 0xFFFFu, 16);
+        if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (LPT * tw)) & low_mask(LPT), LPT);
       }
       // A2: the octet's four pair cosets, bits 4 o .. 4 o + 3 after the scale (never across a word)
       if (LAT == kLatA2) lds_put_bits(s_fixed, rec + 16 + 4u * (uint32_t)o, cos, 4);
@@ -821,8 +846,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
 
   // fixed record of the chunk
   {
-    const uint64_t fbase = fixed_off + (uint64_t)c * 8ull * F;
-    if (fbase + 8ull * F <= P.cap) {
+    const uint64_t fbase = fixed_off + (uint64_t)c * chunk_bytes;
+    if (fbase + chunk_bytes <= P.cap) {
       uint4* dst = reinterpret_cast<uint4*>(P.out + fbase);
       for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) dst[i] = s_fixed4[i];
     } else if (tid == 0) {
@@ -871,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       const uint32_t Lr = r == 0 ? L[0] : r == 1 ? L[1] : r == 2 ? L[2] : L[3];
       const uint32_t offr = r == 0 ? off[0] : r == 1 ? off[1] : r == 2 ? off[2] : off[3];
       uint32_t sy[8];
-      round_symbols<LAT, DITHER, DT>(P.x, P.T, P.seed, c, r, wave, tw, o, sgn, lane_neg, step, sy);
+      round_symbols<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, c, r, wave, tw, o, sgn, lane_neg, step, sy);
       if (multi ? Lr != 0u : Lr > 32u) {
         uint32_t p = offr;
 #pragma unroll
@@ -899,7 +924,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const uint64_t ubits = 64ull * words - (prefix_pad + (64ull * W - B));
     const uint64_t payload = P.T * (uint64_t)(F - 16u) + ubits;
     write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, P.chunks, F, fixed_off, unary_off,
-                 words, ubits, payload, total);
+                 words, ubits, payload, total, TL, __builtin_ctz(TI::CT));
     if (kHeaderBytes + 4ull * P.chunks + 4 <= P.cap)
       reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[P.chunks] = (uint32_t)words;
     if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
@@ -914,24 +939,25 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
 
 // ---------------------------------------------------------------------------------------------
 // Diagnostic codes kernel: front half at a fixed step, integer codes and scale bits out.
-template <int LAT, bool DITHER, int DT>
+template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ x, uint64_t T, uint64_t seed,
                                                        uint32_t step_bits, int32_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales, Workspace* ws) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
-  const uint64_t t = (uint64_t)blockIdx.x * 16 + wave * 4 + tw;
+  using TI = Tiling<TL>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
+  const uint64_t t = (uint64_t)blockIdx.x * TI::TPR + wave * TI::TPW + tw;
   const bool valid = t < T;
   const uint32_t sgn = octet_sign_bits(seed, o);
   float y[8];
   bool finite;
-  const uint32_t sb = transform_octet<DT>(x, t, valid, o, sgn, y, &finite);
+  const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
   if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, u);
   int32_t code[8];
-  quantize_octet<LAT, DITHER>(y, sb, __uint_as_float(step_bits), u, code, lane_sign_bit(o));
+  quantize_octet<LAT, DITHER>(y, sb, __uint_as_float(step_bits), u, code, lane_sign_bit<TI::LPT>(o));
   if (valid) {
-    int4* dst = reinterpret_cast<int4*>(codes + t * kTile + 8 * o);
+    int4* dst = reinterpret_cast<int4*>(codes + t * TL + 8 * o);
     dst[0] = make_int4(code[0], code[1], code[2], code[3]);
     dst[1] = make_int4(code[4], code[5], code[6], code[7]);
     if (o == 0) scales[t] = (uint16_t)sb;
@@ -940,7 +966,9 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
 
 // ---------------------------------------------------------------------------------------------
 // Decoder.
-__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws) {
+// cols: the row length of a matrix product (a whole number of the stream's tiles), 0 for a plain decode.
+__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, uint64_t cols,
+                                    Workspace* ws) {
   __shared__ uint32_t s_h[32];
   __shared__ uint32_t s_idx[2];
   const int tid = threadIdx.x;
@@ -949,12 +977,16 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
   __syncthreads();
   const uint32_t* h = s_h;
   const uint64_t hn = ((uint64_t)h[7] << 32) | h[6];
-  const uint64_t T = n / kTile;
-  const uint32_t chunks = (uint32_t)((T + kChunkTiles - 1) / kChunkTiles);
+  const uint32_t htile = h[2] & 0xFFFFu;
+  const bool tile_ok = htile == 64u || htile == 128u || htile == 256u;
+  const uint32_t tile = tile_ok ? htile : 128u;
+  const uint32_t ct = (uint32_t)kChunkValues / tile;  // tiles per chunk
+  const uint64_t T = n / tile;
+  const uint32_t chunks = (uint32_t)((T + ct - 1) / ct);
   const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
-  bool ok = have && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags <= 1 &&
-            (h[2] & 0xFFFFu) == (uint32_t)kTile && k <= 15 && (h[2] >> 24) == 6u && h[3] >= kStepBitsMin &&
-            h[3] <= kStepBitsMax && hn == n && (n % kTile) == 0;
+  bool ok = have && tile_ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags <= 1 &&
+            k <= 15 && (h[2] >> 24) == (uint32_t)__builtin_ctz(ct) && h[3] >= kStepBitsMin &&
+            h[3] <= kStepBitsMax && hn == n && (n % tile) == 0 && (cols % tile) == 0;
   uint32_t F = 0;
   if (ok) {
     const int kh = k > 0 ? k - 1 : 0;
@@ -962,10 +994,11 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
                     : lattice == kLatD4 ? 6 * k + 2 * kh
                     : lattice == kLatA2 ? 4 * k + 4 * kh
                                         : 8 * k;
-    F = (uint32_t)((lattice == kLatE8 ? 32 : lattice == kLatA2 ? 80 : 16) + 16 * rem);
+    const uint32_t oct = tile / 8u;
+    F = 16u + (lattice == kLatE8 ? oct : lattice == kLatA2 ? 4u * oct : 0u) + oct * (uint32_t)rem;
   }
   const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (chunks + 1));
-  const uint64_t unary_off = align256(fixed_off + (uint64_t)chunks * 8ull * F);
+  const uint64_t unary_off = align256(fixed_off + (uint64_t)chunks * ct * F / 8ull);
   const uint64_t words = ((uint64_t)h[17] << 32) | h[16];
   const uint64_t total = ((uint64_t)h[23] << 32) | h[22];
   ok = ok && (((uint64_t)h[9] << 32) | h[8]) == T && h[10] == chunks && h[11] == F &&
@@ -981,6 +1014,7 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
     return;
   }
   ws->status = 0;
+  ws->dec_tile = tile;
   ws->dec_lattice = (uint32_t)lattice;
   ws->dec_dither = (uint32_t)flags;
   ws->dec_k = k;
@@ -995,7 +1029,7 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
   ws->dec_valid = 1;
 }
 
-constexpr int kMaxSymsPerChunk = kChunkTiles * kTile;
+constexpr int kMaxSymsPerChunk = kChunkValues;
 
 // One slot's remainder from an octet field held in (lo, hi) (at most 64 bits); off and w are the
 // same in every lane.
@@ -1024,48 +1058,57 @@ __device__ __forceinline__ int32_t twice_unzz(uint32_t s) {
 // Decode of one chunk's tiles once the terminator positions of its unary segment are in s_pos.
 // Each lane rebuilds one octet per round: Rice symbols (unary part from consecutive terminator
 // positions, remainders from the fixed record read in place), lattice codes, rescale (and dither
-// removal), inverse FWHT, sign and 2^-7, store.  The fixed-record words of round r + 1 are loaded
+// removal), inverse FWHT, sign and 1/TL, store.  The fixed-record words of round r + 1 are loaded
 // while round r is computed.  Every read of the record stays inside the stream: a chunk's record
-// has room for 64 tiles, and at most two words past its end lie in the unary plane, which holds at
-// least one word per symbol's chunk once the chunk's terminator count has been checked.
+// has room for all its 8192 / TL tiles, and at most two words past its end lie in the unary plane,
+// which holds at least one word per symbol's chunk once the chunk's terminator count has been
+// checked.
 // Extra arguments of the fused decode + matrix-vector product: the rotated activation (one
-// 128-value tile per column tile of the matrix), the number of column tiles, and the per-tile
-// partial products.
+// TL-value tile per column tile of the matrix), the matrix's columns, and the per-tile partial
+// products.
 struct GemvArgs {
   const float* xt;
-  uint32_t ctiles;
+  uint64_t cols;  // the matrix's columns: cols / TL column tiles
   float* tp;
 };
 
-template <int LAT, int DT_OUT, bool GEMV>
+template <int LAT, int DT_OUT, bool GEMV, int TL>
 __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
                                              uint32_t c, uint32_t tiles_c, const uint32_t* s_pos, bool check_q,
                                              GemvArgs g) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
+  using TI = Tiling<TL>;
+  constexpr int LPT = TI::LPT;
+  constexpr float kInvTile = 1.0f / (float)TL;  // exact power of two
+  // the E8 coset bit of a tile of 256 lies beyond the 32-bit window that holds the scale
+  constexpr bool kCosetWord = LAT == kLatA2 || (LAT == kLatE8 && LPT > 16);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   const int k = ws->dec_k;
   const uint32_t F = ws->dec_F;
   const bool dither = ws->dec_dither != 0;
   const uint64_t seed = ws->dec_seed;
   const float step = __uint_as_float(ws->dec_step_bits);
   const int RW = octet_rem_bits<LAT>(k);
-  const uint32_t hdr = (uint32_t)tile_hdr_bits<LAT>();
-  const uint32_t* __restrict__ fw = reinterpret_cast<const uint32_t*>(in + ws->dec_fixed_off + (uint64_t)c * 8ull * F);
-  // output factor per coordinate: +-2^-7 with the sign of D and of the lane's butterfly sign; the
+  const uint32_t hdr = (uint32_t)tile_hdr_bits<LAT, TL>();
+  const uint32_t* __restrict__ fw =
+      reinterpret_cast<const uint32_t*>(in + ws->dec_fixed_off + (uint64_t)c * ((uint64_t)TI::CT * F / 8ull));
+  // output factor per coordinate: +-1/TL with the sign of D and of the lane's butterfly sign; the
   // fused multiply-add with +0 below is exact and turns an exact zero into +0
-  const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit(o) ? 0xFFu : 0u);
+  const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit<LPT>(o) ? 0xFFu : 0u);
   float cmul[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -0.0078125f : 0.0078125f;
+  for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -kInvTile : kInvTile;
   bool bad = false;
-  // record words of a round: the tile header (scale, then E8 coset bits), A2's word with the
-  // octet's four coset bits, and the octet's field
+  // record words of a round: the tile header (scale, then E8 coset bits), the word with the octet's
+  // coset bits when they are not in that window (A2's four; E8 at 32 lanes per tile), and the
+  // octet's field
+  const uint32_t cbit = LAT == kLatA2 ? 4u * (uint32_t)o : (uint32_t)o;  // coset bits after the scale
   uint32_t hA, hB, hC, f0, f1, f2;
   auto issue = [&](int r) {
-    const uint32_t rec = (16u * r + 4u * wave + tw) * F;
+    const uint32_t rec = ((uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw) * F;
     const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
     hA = fw[rec >> 5];
     hB = fw[(rec >> 5) + 1];
-    hC = LAT == kLatA2 ? fw[(rec + 16u + 4u * (uint32_t)o) >> 5] : 0u;
+    hC = kCosetWord ? fw[(rec + 16u + cbit) >> 5] : 0u;
     f0 = fw[P >> 5];
     f1 = fw[(P >> 5) + 1];
     f2 = RW > 32 ? fw[(P >> 5) + 2] : 0u;
@@ -1073,27 +1116,27 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
   issue(0);
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
-    const uint32_t tc = 16u * r + 4u * wave + tw;
+    const uint32_t tc = (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
     const bool valid = tc < tiles_c;
-    const uint64_t t = (uint64_t)c * kChunkTiles + tc;
+    const uint64_t t = (uint64_t)c * TI::CT + tc;
     const uint32_t rec = tc * F;
     const uint32_t P = rec + hdr + (uint32_t)o * (uint32_t)RW;
     const uint32_t a0 = hA, a1 = hB, a2w = hC, x0 = f0, x1 = f1, x2 = f2;
     if (r < 3) issue(r + 1);
     float yv[8];
     if (valid) {
-      // rec is a multiple of 16: the 32 bits at rec are the scale (low half) and, for E8, the
-      // coset bits of the tile's 16 octets (high half)
+      // the 32 bits at rec are the scale (low half) and, for E8 with at most 16 octets, the
+      // coset bits of the tile's octets (high half)
       const uint32_t th = __builtin_amdgcn_alignbit(a1, a0, rec & 31u);
       const uint32_t sb = th & 0xFFFFu;
-      const uint32_t coset = LAT == kLatE8   ? (th >> (16 + o)) & 1u
-                             : LAT == kLatA2 ? (a2w >> ((rec + 16u + 4u * (uint32_t)o) & 31u)) & 0xFu
+      const uint32_t coset = kCosetWord      ? (a2w >> ((rec + 16u + cbit) & 31u)) & (LAT == kLatA2 ? 0xFu : 1u)
+                             : LAT == kLatE8 ? (th >> (16 + o)) & 1u
                                              : 0u;
       const uint32_t sh = P & 31u;
       const uint32_t lo = __builtin_amdgcn_alignbit(x1, x0, sh), hi = __builtin_amdgcn_alignbit(x2, x1, sh);
       // unary parts: q = p - p_prev - 1 = (p_prev ^ ~0) + p; the symbol before the chunk's first
       // sits at -1
-      const uint32_t g0 = (16u * tc + (uint32_t)o) * 8u;
+      const uint32_t g0 = ((uint32_t)LPT * tc + (uint32_t)o) * 8u;  // symbol index of slot 0: tc TL + 8 o
       const uint32_t pv = s_pos[g0 ? g0 - 1 : 0];
       uint32_t pprev = g0 ? pv : 0xFFFFFFFFu;
       const uint4 pa = *reinterpret_cast<const uint4*>(s_pos + g0);
@@ -1187,11 +1230,11 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       for (int i = 0; i < 8; ++i) yv[i] = 0.0f;
     }
     if constexpr (GEMV) {
-      // the tile's share of its row: 2^-7 <yhat, x~_j> (the lane's butterfly sign plays no part:
+      // the tile's share of its row: <yhat, x~_j> / TL (the lane's butterfly sign plays no part:
       // yhat is not transformed here); the octet partial is a fixed-order chain, the tile sum a
       // fixed xor tree
-      const uint32_t j = (uint32_t)(t % g.ctiles);
-      const float4* xp = reinterpret_cast<const float4*>(g.xt + (uint64_t)j * kTile + 8 * o);
+      const uint32_t j = (uint32_t)(t % (g.cols / TL));
+      const float4* xp = reinterpret_cast<const float4*>(g.xt + (uint64_t)j * TL + 8 * o);
       const float4 a = valid ? xp[0] : make_float4(0, 0, 0, 0), b = valid ? xp[1] : make_float4(0, 0, 0, 0);
       float part = yv[0] * a.x;
       part = __builtin_fmaf(yv[1], a.y, part);
@@ -1204,12 +1247,13 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       part = part + lane_xor<1>(part);
       part = part + lane_xor<2>(part);
       part = part + lane_xor<4>(part);
-      part = part + lane_xor<8>(part);
-      if (valid && o == 0) g.tp[t] = part * 0.0078125f;
+      if (LPT >= 16) part = part + lane_xor<8>(part);
+      if (LPT >= 32) part = part + lane_xor<16>(part);
+      if (valid && o == 0) g.tp[t] = part * kInvTile;
       continue;
     }
     fwht_lane(yv);
-    fwht_cross(yv, o);
+    fwht_cross<LPT>(yv, o);
     if (valid) {
       float xo[8];
 #pragma unroll
@@ -1223,9 +1267,9 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         st.y = __builtin_bit_cast(uint32_t, pk[1]);
         st.z = __builtin_bit_cast(uint32_t, pk[2]);
         st.w = __builtin_bit_cast(uint32_t, pk[3]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * kTile + 8 * o) = st;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * TL + 8 * o) = st;
       } else {
-        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * kTile + 8 * o);
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * TL + 8 * o);
         dst[0] = make_float4(xo[0], xo[1], xo[2], xo[3]);
         dst[1] = make_float4(xo[4], xo[5], xo[6], xo[7]);
       }
@@ -1250,8 +1294,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   const uint32_t chunks = ws->dec_chunks;
   if (c >= chunks) return;
   const uint64_t T = ws->dec_tiles;
-  const uint32_t tiles_c = (uint32_t)min((uint64_t)kChunkTiles, T - (uint64_t)c * kChunkTiles);
-  const uint32_t nsym = tiles_c * kTile;
+  const uint32_t tile = ws->dec_tile;
+  const uint32_t ct = (uint32_t)kChunkValues / tile;
+  const uint32_t tiles_c = (uint32_t)min((uint64_t)ct, T - (uint64_t)c * ct);
+  const uint32_t nsym = tiles_c * tile;
   const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
   const uint32_t w0 = idx[c], w1 = idx[c + 1];
   if (w1 < w0 || (uint64_t)w1 > ws->dec_words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
@@ -1310,58 +1356,82 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   __syncthreads();
   // q of a corrupt segment can exceed what q << w holds only when the segment is that long
   const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
-  switch (ws->dec_lattice) {
-    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
-    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
-    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
-    default: decode_chunk<kLatZ, DT_OUT, GEMV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;
+  // uniform dispatch on the stream's lattice and tile length
+#define HQ_DEC_LAT(TLV)                                                                                      \
+  switch (ws->dec_lattice) {                                                                                 \
+    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
+    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
+    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
+    default: decode_chunk<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;      \
   }
+  if (tile == 64u) {
+    HQ_DEC_LAT(64)
+  } else if (tile == 256u) {
+    HQ_DEC_LAT(256)
+  } else {
+    HQ_DEC_LAT(128)
+  }
+#undef HQ_DEC_LAT
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fused decode + matrix-vector product.  For a stream of a [rows][cols] matrix (tiles of 128 along
-// cols), tile (r, j) decodes to D H yhat / 128, so its dot product with the activation's tile x_j
-// is <yhat, H D x_j> / 128 (H is symmetric, D diagonal): rotate each activation tile once, then
+// Fused decode + matrix-vector product.  For a stream of a [rows][cols] matrix (tiles of TL values
+// along cols), tile (r, j) decodes to D H yhat / TL, so its dot product with the activation's tile
+// x_j is <yhat, H D x_j> / TL (H is symmetric, D diagonal): rotate each activation tile once, then
 // every matrix tile needs only its lattice values, no inverse transform.
 
 // x~_j = H D x_j for every column tile, binary32 in the encoder's butterfly order, stored with the
 // lanes' butterfly signs removed (an exact negation).  Runs after the header check (the seed of D
-// comes from the stream).
-template <int DT>
-__global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const void* __restrict__ x, uint32_t ctiles,
-                                                             const Workspace* ws, float* __restrict__ xt) {
-  if (!ws->dec_valid) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane & 15, tw = lane >> 4;
-  const uint64_t t = (uint64_t)blockIdx.x * 16 + 4 * wave + tw;
-  const bool valid = t < ctiles;
+// and the tile length come from the stream).  A workgroup covers 2048 columns at every tile length.
+template <int DT, int TL>
+__device__ __forceinline__ void gemv_rotate_tiles(const void* __restrict__ x, uint64_t cols, const Workspace* ws,
+                                                  float* __restrict__ xt) {
+  using TI = Tiling<TL>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
+  const uint64_t t = (uint64_t)blockIdx.x * TI::TPR + TI::TPW * wave + tw;
+  const bool valid = t < cols / TL;
   const uint32_t sgn = octet_sign_bits(ws->dec_seed, o);
   uint32_t smask[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
   float y[8];
   if (valid) {
-    load_octet_signed<DT>(x, t, o, smask, y);
+    load_octet_signed<DT, TL>(x, t, o, smask, y);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.0f;
   }
   fwht_lane(y);
-  fwht_cross(y, o);
+  fwht_cross<TI::LPT>(y, o);
   if (!valid) return;
-  const uint32_t neg = lane_sign_bit(o) << 31;
-  float4* dst = reinterpret_cast<float4*>(xt + t * kTile + 8 * o);
+  const uint32_t neg = lane_sign_bit<TI::LPT>(o) << 31;
+  float4* dst = reinterpret_cast<float4*>(xt + t * TL + 8 * o);
   dst[0] = make_float4(__uint_as_float(__float_as_uint(y[0]) ^ neg), __uint_as_float(__float_as_uint(y[1]) ^ neg),
                        __uint_as_float(__float_as_uint(y[2]) ^ neg), __uint_as_float(__float_as_uint(y[3]) ^ neg));
   dst[1] = make_float4(__uint_as_float(__float_as_uint(y[4]) ^ neg), __uint_as_float(__float_as_uint(y[5]) ^ neg),
                        __uint_as_float(__float_as_uint(y[6]) ^ neg), __uint_as_float(__float_as_uint(y[7]) ^ neg));
 }
 
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const void* __restrict__ x, uint64_t cols,
+                                                             const Workspace* ws, float* __restrict__ xt) {
+  if (!ws->dec_valid) return;
+  const uint32_t tile = ws->dec_tile;
+  if (tile == 64u)
+    gemv_rotate_tiles<DT, 64>(x, cols, ws, xt);
+  else if (tile == 256u)
+    gemv_rotate_tiles<DT, 256>(x, cols, ws, xt);
+  else
+    gemv_rotate_tiles<DT, 128>(x, cols, ws, xt);
+}
+
 // y_r = sum over the row's column tiles of the tile partials, in column order (one lane per row).
 __global__ __launch_bounds__(kBlock) void gemv_rows_kernel(const float* __restrict__ tp, uint64_t rows,
-                                                           uint32_t ctiles, const Workspace* ws, float* __restrict__ y) {
+                                                           uint64_t cols, const Workspace* ws, float* __restrict__ y) {
   if (!ws->dec_valid) return;
   const uint64_t r = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
   if (r >= rows) return;
+  const uint32_t ctiles = (uint32_t)(cols / ws->dec_tile);
   const float* p = tp + r * ctiles;
   float acc = 0.0f;
   for (uint32_t j = 0; j < ctiles; ++j) acc += p[j];
@@ -1371,21 +1441,29 @@ __global__ __launch_bounds__(kBlock) void gemv_rows_kernel(const float* __restri
 // ---------------------------------------------------------------------------------------------
 // Launchers.
 
-#define HQ_DISPATCH(LATV, DITHV, DTV, CALL)                                   \
-  do {                                                                        \
-    if ((LATV) == kLatE8) {                                                   \
-      if (DITHV) { if ((DTV) == 1) CALL(kLatE8, true, 1); else CALL(kLatE8, true, 0); }   \
-      else { if ((DTV) == 1) CALL(kLatE8, false, 1); else CALL(kLatE8, false, 0); }       \
-    } else if ((LATV) == kLatA2) {                                            \
-      if (DITHV) { if ((DTV) == 1) CALL(kLatA2, true, 1); else CALL(kLatA2, true, 0); }   \
-      else { if ((DTV) == 1) CALL(kLatA2, false, 1); else CALL(kLatA2, false, 0); }       \
-    } else if ((LATV) == kLatD4) {                                            \
-      if (DITHV) { if ((DTV) == 1) CALL(kLatD4, true, 1); else CALL(kLatD4, true, 0); }   \
-      else { if ((DTV) == 1) CALL(kLatD4, false, 1); else CALL(kLatD4, false, 0); }       \
-    } else {                                                                  \
-      if (DITHV) { if ((DTV) == 1) CALL(kLatZ, true, 1); else CALL(kLatZ, true, 0); }     \
-      else { if ((DTV) == 1) CALL(kLatZ, false, 1); else CALL(kLatZ, false, 0); }         \
-    }                                                                         \
+// Compile-time variants: lattice x dither x input type x tile length.
+#define HQ_DISPATCH_TL(L, D, T, TLV, CALL) \
+  do {                                     \
+    if ((TLV) == 64) CALL(L, D, T, 64);    \
+    else if ((TLV) == 256) CALL(L, D, T, 256); \
+    else CALL(L, D, T, 128);               \
+  } while (0)
+#define HQ_DISPATCH_DT(L, D, DTV, TLV, CALL)                       \
+  do {                                                             \
+    if ((DTV) == 1) HQ_DISPATCH_TL(L, D, 1, TLV, CALL);            \
+    else HQ_DISPATCH_TL(L, D, 0, TLV, CALL);                       \
+  } while (0)
+#define HQ_DISPATCH_D(L, DITHV, DTV, TLV, CALL)                    \
+  do {                                                             \
+    if (DITHV) HQ_DISPATCH_DT(L, true, DTV, TLV, CALL);            \
+    else HQ_DISPATCH_DT(L, false, DTV, TLV, CALL);                 \
+  } while (0)
+#define HQ_DISPATCH(LATV, DITHV, DTV, TLV, CALL)                                      \
+  do {                                                                                \
+    if ((LATV) == kLatE8) HQ_DISPATCH_D(kLatE8, DITHV, DTV, TLV, CALL);               \
+    else if ((LATV) == kLatA2) HQ_DISPATCH_D(kLatA2, DITHV, DTV, TLV, CALL);          \
+    else if ((LATV) == kLatD4) HQ_DISPATCH_D(kLatD4, DITHV, DTV, TLV, CALL);          \
+    else HQ_DISPATCH_D(kLatZ, DITHV, DTV, TLV, CALL);                                 \
   } while (0)
 
 hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
@@ -1425,31 +1503,27 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
   // pass A (8 candidates, a small sample): two candidates per wavefront, so that the pass is not
   // one long chain per wavefront; otherwise every wavefront takes all candidates of its tiles
   const int cpw = nc == kRcCand ? 2 : nc;
-  const int cw = (nc + cpw - 1) / cpw;  // 1, 2 or 4 wavefronts per group of 4 tiles
+  const int cw = (nc + cpw - 1) / cpw;  // 1, 2 or 4 wavefronts per group of a wavefront's tiles
   if (cw != 1 && cw != 2 && cw != 4) return hipErrorInvalidValue;  // nc is 1, 2, 4 or 8
-  const uint32_t tiles_per_block = 4u * (uint32_t)(4 / cw);
+  const uint32_t tpw = 64u / ((uint32_t)a.tile / 8u);  // tiles per wavefront
+  const uint32_t tiles_per_block = tpw * (uint32_t)(4 / cw);
   const uint32_t blocks = (N + tiles_per_block - 1) / tiles_per_block;
   if (blocks == 0) return hipSuccess;
   const int solve_prev = pass > 0 ? 1 : 0;
   const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1) : PassDesc{};
-#define HQ_RATE(L, D, T)                                                                              \
-  hipLaunchKernelGGL((rate_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
+#define HQ_RATE(L, D, T, TL)                                                                           \
+  hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
                      rate_acc(a.ws, pass), a.seed, nc, half_log2, a.rice_k, a.target, cpw, solve_prev, prev)
-  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_RATE);
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_RATE);
 #undef HQ_RATE
   return hipGetLastError();
 }
 
 hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
   const PassDesc pd = pass_desc(a, nc, half_log2, N, pass);
-  if (a.lattice == kLatE8)
-    hipLaunchKernelGGL((rate_solve_kernel<kLatE8>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
-  else if (a.lattice == kLatA2)
-    hipLaunchKernelGGL((rate_solve_kernel<kLatA2>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
-  else if (a.lattice == kLatD4)
-    hipLaunchKernelGGL((rate_solve_kernel<kLatD4>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
-  else
-    hipLaunchKernelGGL((rate_solve_kernel<kLatZ>), dim3(1), dim3(64), 0, a.stream, a.ws, pd);
+#define HQ_SOLVE(L, D, T, TL) hipLaunchKernelGGL((rate_solve_kernel<L, TL>), dim3(1), dim3(64), 0, a.stream, a.ws, pd)
+  HQ_DISPATCH(a.lattice, false, 0, a.tile, HQ_SOLVE);
+#undef HQ_SOLVE
   return hipGetLastError();
 }
 
@@ -1465,32 +1539,35 @@ hipError_t launch_encode(const EncodeArgs& a) {
   P.ws = a.ws;
   P.flags = lookback_flags(a.ws);
   const uint32_t blocks = a.chunks ? a.chunks : 1u;
-#define HQ_ENC(L, D, T) hipLaunchKernelGGL((encode_kernel<L, D, T>), dim3(blocks), dim3(kBlock), 0, a.stream, P)
-  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_ENC);
+#define HQ_ENC(L, D, T, TL) \
+  hipLaunchKernelGGL((encode_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, P)
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_ENC);
 #undef HQ_ENC
   return hipGetLastError();
 }
 
 hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales) {
-  const uint64_t blocks = (a.tiles + 15) / 16;
+  const uint64_t tpr = 4u * (64u / ((uint32_t)a.tile / 8u));  // tiles per workgroup
+  const uint64_t blocks = (a.tiles + tpr - 1) / tpr;
   if (blocks == 0) return hipSuccess;
-#define HQ_CODES(L, D, T)                                                                             \
-  hipLaunchKernelGGL((codes_kernel<L, D, T>), dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, \
+#define HQ_CODES(L, D, T, TL)                                                                          \
+  hipLaunchKernelGGL((codes_kernel<L, D, T, TL>), dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, \
                      a.seed, a.fixed_step_bits, codes, scales, a.ws)
-  HQ_DISPATCH(a.lattice, a.dither, a.dtype, HQ_CODES);
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_CODES);
 #undef HQ_CODES
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
                          Workspace* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, (uint64_t)0, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint64_t T = n / kTile;
-  const uint64_t chunks = (T + kChunkTiles - 1) / kChunkTiles;
+  // a chunk holds kChunkValues values at every tile length (the header check rejects an n that
+  // is not a whole number of the stream's tiles)
+  const uint64_t chunks = (n + kChunkValues - 1) / kChunkValues;
   if (chunks == 0) return hipSuccess;
-  const GemvArgs none{nullptr, 1u, nullptr};
+  const GemvArgs none{nullptr, 128u, nullptr};
   if (out_dtype == 1)
     hipLaunchKernelGGL((decode_kernel<1, false>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws, none);
   else
@@ -1501,26 +1578,24 @@ hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int ou
 hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
                        float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream) {
   const uint64_t n = rows * cols;
-  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, cols, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t ctiles = (uint32_t)(cols / kTile);
-  const uint64_t T = n / kTile;
-  const uint64_t chunks = (T + kChunkTiles - 1) / kChunkTiles;
+  const uint64_t chunks = (n + kChunkValues - 1) / kChunkValues;
   if (chunks == 0) return hipSuccess;
-  const uint32_t rblocks = (ctiles + 15) / 16;
+  const uint32_t rblocks = (uint32_t)((cols + 2047) / 2048);  // 2048 columns per workgroup at every tile length
   if (x_dtype == 1)
-    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, x, ctiles, ws, xt);
+    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, x, cols, ws, xt);
   else
-    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, x, ctiles, ws, xt);
+    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, x, cols, ws, xt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const GemvArgs g{xt, ctiles, tp};
+  const GemvArgs g{xt, cols, tp};
   hipLaunchKernelGGL((decode_kernel<1, true>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, nullptr, ws, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemv_rows_kernel, dim3((uint32_t)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, tp,
-                     rows, ctiles, ws, y);
+                     rows, cols, ws, y);
   return hipGetLastError();
 }
 

@@ -32,11 +32,16 @@ def test_strerror_codes():
 
 
 def test_sizes_match_oracle_layout(orc):
-    for n in (0, 128, 128 * 65, 128 * 458752):
-        for lat in ("z", "d4", "e8", "a2"):
-            for k in (0, 1, 3, 15):
-                fo, uo, F = orc.layout(n, orc.LATTICES[lat], k)
-                assert hq.hq_stream_fixed_bytes(n, lat, k) == uo
+    for tile in (64, 128, 256):
+        for n in (0, 256, 256 * 33, 128 * 65 * 2, 128 * 458752):
+            for lat in ("z", "d4", "e8", "a2"):
+                for k in (0, 1, 3, 15):
+                    fo, uo, F = orc.layout(n, orc.LATTICES[lat], k, tile)
+                    assert hq.hq_stream_fixed_bytes(n, lat, k, tile) == uo
+    L = hq.lib()
+    out = ctypes.c_uint64(0)
+    assert L.hq_stream_fixed_bytes(256, 2, 4, 32, ctypes.byref(out)) == hq.HQ_ERR_UNSUPPORTED
+    assert L.hq_stream_fixed_bytes(64, 2, 4, 128, ctypes.byref(out)) == hq.HQ_ERR_INVALID_ARG  # n % tile
     rate = 2 * 16 * 32 * 4  # two rate passes, 16 sets of 32 counters each
     assert hq.hq_workspace_size(0) == 4096 + rate + 256
     assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + rate + ((8 * 101 + 255) // 256) * 256
@@ -50,7 +55,8 @@ def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(tile=64), hq.HQ_ERR_UNSUPPORTED),
+    (dict(tile=32), hq.HQ_ERR_UNSUPPORTED),
+    (dict(tile=512), hq.HQ_ERR_UNSUPPORTED),
     (dict(lattice=4), hq.HQ_ERR_INVALID_ARG),
     (dict(rice_k=16), hq.HQ_ERR_INVALID_ARG),
     (dict(step=-2.0), hq.HQ_ERR_INVALID_ARG),          # -1 alone is a valid sentinel
@@ -73,6 +79,8 @@ def test_encode_rejects_bad_params_on_host(kw, code):
 def test_encode_rejects_bad_buffers_on_host():
     p = hq.make_params("e8", 4.0)
     assert _encode_rc(p, n=100) == hq.HQ_ERR_INVALID_ARG           # n % 128
+    assert _encode_rc(p, n=64) == hq.HQ_ERR_INVALID_ARG            # n % 128 (tile 128)
+    assert _encode_rc(hq.make_params("e8", 4.0, tile=256), n=128) == hq.HQ_ERR_INVALID_ARG  # n % 256
     assert _encode_rc(p, ws_bytes=16) == hq.HQ_ERR_INVALID_ARG       # workspace too small
     assert _encode_rc(p, ws=0) == hq.HQ_ERR_INVALID_ARG              # null workspace
     assert _encode_rc(p, x=0) == hq.HQ_ERR_INVALID_ARG               # null input
@@ -125,10 +133,10 @@ def test_product_package_does_not_import_oracle():
 def test_gemv_rejects_bad_args_on_host():
     L = hq.lib()
     sz = ctypes.c_size_t(0)
-    assert L.hq_gemv_workspace_size(4, 100, ctypes.byref(sz)) == hq.HQ_ERR_INVALID_ARG   # cols % 128
+    assert L.hq_gemv_workspace_size(4, 100, ctypes.byref(sz)) == hq.HQ_ERR_INVALID_ARG   # cols % 64
     assert L.hq_gemv_workspace_size(4, 1024, None) == hq.HQ_ERR_INVALID_ARG
     assert L.hq_gemv_workspace_size(4, 1024, ctypes.byref(sz)) == hq.HQ_OK
-    assert sz.value == 4096 + 4096 + 256  # header, 1024 rotated values, 32 tile partials (aligned)
+    assert sz.value == 4096 + 4096 + 256  # header, 1024 rotated values, 64 partials of 64-value tiles
     ws, big = ctypes.c_void_p(1 << 21), 1 << 20
     args = dict(s=ctypes.c_void_p(1 << 20), rows=4, cols=1024, x=ctypes.c_void_p(1 << 22), dt=0,
                 y=ctypes.c_void_p(1 << 23), ws=ws, wsb=big)
