@@ -31,9 +31,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", choices=["weight", "kv", "sweep", "model", "kv_all", "gemv", "kv_haar", "srft"],
+    ap.add_argument("--config", choices=["weight", "kv", "sweep", "tiles", "model", "kv_all", "gemv", "kv_haar",
+                                         "srft"],
                     default="weight",
                     help="weight / kv: one tensor, the headline line; sweep: Z, A2, D4 and E8 on the weight; "
+                         "tiles: E8 on the weight with tiles of 64, 128 and 256 values; "
                          "model: the 224 linear weights of an 8B-shaped decoder, one at a time; kv_all: "
                          "the 64 (layer, K|V) calls of the KV cache; gemv: fused decode + matrix-vector "
                          "product on the weight's stream; kv_haar: one KV call with the full per-layer "
@@ -111,13 +113,13 @@ def profiled_traffic(profile_stem: str, kernel_prefix: str, sources=CODEC_SOURCE
     return None
 
 
-def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=None, ws_dec=None, y=None):
+def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=None, ws_dec=None, y=None, tile=128):
     """Events around encode (with rate control) and decode of one device tensor (steps timed,
     warmup untimed).  Returns per-step means (ms), the stream header and the decoded tensor."""
     dev = x.device
     n = x.numel()
     if out is None:
-        s_ref, _ = hq.hq_encode(x, lat, tb, seed=seed, dither=dither)
+        s_ref, _ = hq.hq_encode(x, lat, tb, seed=seed, dither=dither, tile=tile)
         out = torch.empty(int(s_ref.numel() * 1.05) + 65536, dtype=torch.uint8, device=dev)
         del s_ref
     ws = hq.workspace(n, dev) if ws is None else ws
@@ -126,7 +128,7 @@ def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=N
     stream = torch.cuda.current_stream()
 
     def one():
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False, tile=tile)
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(stream)
         hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
@@ -138,7 +140,7 @@ def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=N
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps):
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False, tile=tile)
         hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -175,6 +177,15 @@ def series(args):
         for lat in ("z", "a2", "d4", "e8"):
             items.append((lat, lambda: xw, lat, tb, 0, False))
         workload = f"lattice sweep on the mlp weight 14336x4096 bf16 at {tb:g} bps: Z, A2, D4, E8, no dither"
+        steps, warmup = args.steps, args.warmup
+    elif args.config == "tiles":
+        import synth
+        xw = torch.from_numpy(synth.weight().reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+        tb = 4.0 if args.bps is None else args.bps
+        for tl in (64, 128, 256):
+            items.append((f"tile{tl}", lambda: xw, "e8", tb, 0, False, tl))
+        workload = (f"tile-length sweep on the mlp weight 14336x4096 bf16, E8 {tb:g} bps, no dither: tiles of "
+                    f"64, 128 and 256 values")
         steps, warmup = args.steps, args.warmup
     elif args.config == "model":
         import synth
@@ -219,17 +230,18 @@ def series(args):
     per = {}
     worst_rate_err = 0.0
     enc_alg = 0
-    for name, make, lat, tb, seed, dither in items:
+    for name, make, lat, tb, seed, dither, *rest in items:
+        tile = rest[0] if rest else 128
         x = make()
         n = x.numel()
-        r, hdr, y = time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup)
+        r, hdr, y = time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, tile=tile)
         for k in tot:
             tot[k] += r[k]
         total_in += 2 * n
         enc_alg += 2 * n + hdr["total_bytes"]
         rate_err = abs(hdr["payload_bits"] / n - tb)
         worst_rate_err = max(worst_rate_err, rate_err)
-        if args.config == "sweep":
+        if args.config in ("sweep", "tiles"):
             xf = x.float()
             nmse = float(((y.float() - xf) ** 2).sum() / (xf ** 2).sum())
             per[name] = {"payload_bps": round(hdr["payload_bits"] / n, 5),
@@ -248,7 +260,7 @@ def series(args):
                      "frac": round(enc_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "rate passes + encode_kernel",
                      "alg_bytes_per_launch": enc_alg // len(items), "launch_ms": round(tot["encode_ms"] / len(items), 5)},
         "extra": {**{k: round(v, 4) for k, v in tot.items()}, "worst_payload_rate_error_bps": round(worst_rate_err, 5),
-                  **({"per_lattice": per} if per else {})},
+                  **({("per_tile" if args.config == "tiles" else "per_lattice"): per} if per else {})},
     }
     print(json.dumps(result), flush=True)
 
@@ -523,7 +535,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
         return
-    if args.config in ("sweep", "model", "kv_all"):
+    if args.config in ("sweep", "tiles", "model", "kv_all"):
         series(args)
         return
     if args.config == "gemv":
