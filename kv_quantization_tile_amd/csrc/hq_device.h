@@ -36,12 +36,14 @@ struct U4 {
   uint32_t x, y, z, w;
 };
 
+// Each round's two 32 x 32 -> 64-bit products are written as 64-bit multiplies of zero-extended
+// words, which gfx950 computes with one v_mad_u64_u32 each instead of a mul_lo / mul_hi pair.
 __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = c.x * 0xD2511F53u, hi0 = __umulhi(c.x, 0xD2511F53u);
-    const uint32_t lo1 = c.z * 0xCD9E8D57u, hi1 = __umulhi(c.z, 0xCD9E8D57u);
-    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
+    c = U4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
