@@ -51,6 +51,8 @@ def lib():
         P = ctypes.c_void_p
         u64, u32, i32, f32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float
         L.hqo_philox4x32_10.argtypes = [P, P, P]
+        L.hqo_philox4x32_r.argtypes = [P, P, i32, P]
+        L.hqo_philox4x32_span.argtypes = [P, P, i32, i32, P]
         L.hqo_signs.argtypes = [u64, P]
         L.hqo_signs_n.argtypes = [u64, i32, P]
         L.hqo_fwht128.argtypes = [P]
@@ -66,6 +68,7 @@ def lib():
         L.hqo_nearest_octet.argtypes = [i32, P, P]
         L.hqo_nearest_batch.argtypes = [i32, P, u64, P]
         L.hqo_dither_octet.argtypes = [u64, u64, i32, i32, P]
+        L.hqo_dither_octet_flags.argtypes = [u64, u64, i32, i32, i32, P]
         L.hqo_strip_octet.argtypes = [i32, P, P, P]
         L.hqo_unstrip_octet.argtypes = [i32, P, i32, P]
         L.hqo_tile_fixed_bits.argtypes = [i32, i32]
@@ -127,6 +130,15 @@ def philox4x32_10(counter, key) -> np.ndarray:
     return out
 
 
+def philox4x32_span(counter, key, r0: int, r1: int) -> np.ndarray:
+    """Rounds r0 .. r1-1 of Philox4x32 (the key first bumped r0 times); (0, R) is Philox4x32-R."""
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().hqo_philox4x32_span(_p(c), _p(k), r0, r1, _p(out))
+    return out
+
+
 TILES = (64, 128, 256)
 
 
@@ -178,10 +190,23 @@ def nearest(lattice: int, v) -> np.ndarray:
     return out
 
 
-def dither_octet(seed: int, tile: int, octet: int, lattice: int) -> np.ndarray:
+def dither_octet(seed: int, tile: int, octet: int, lattice: int, flags: int = 1) -> np.ndarray:
+    """U of octet `octet` of tile `tile`; flags as in dither_flags (1: 16-bit draw, 10 rounds)."""
     u = np.zeros(8, dtype=np.float32)
-    lib().hqo_dither_octet(seed, tile, octet, lattice, _p(u))
+    if flags == 1:
+        lib().hqo_dither_octet(seed, tile, octet, lattice, _p(u))
+    else:
+        lib().hqo_dither_octet_flags(seed, tile, octet, lattice, flags, _p(u))
     return u
+
+
+# Dither flags: bit 0 on; bit 1 the dither's Philox calls take 7 rounds instead of 10; bit 2 a
+# 24-bit draw instead of 16.  True / False mean 1 / 0.
+DITHER_PHILOX7, DITHER_24BIT = 2, 4
+
+
+def dither_flags(dither) -> int:
+    return int(dither) if not isinstance(dither, bool) else (1 if dither else 0)
 
 
 def strip_octet(lattice: int, code):
@@ -230,7 +255,7 @@ def quantize(x: np.ndarray, lattice: int, step: float, seed: int = 0, dither: bo
     n = x.size
     codes = np.zeros(n, dtype=np.int32)
     scales = np.zeros(max(n // tile, 1), dtype=np.uint16)
-    _check(lib().hqo_quantize(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
+    _check(lib().hqo_quantize(_p(x), _dtype_code(x), n, lattice, dither_flags(dither), seed,
                               ctypes.c_float(step), _p(codes), _p(scales), tile), "quantize")
     return codes, scales[: n // tile]
 
@@ -240,7 +265,7 @@ def lattice_inputs(x, lattice: int, step: float, seed: int = 0, dither: bool = F
     """The binary32 values fed to the nearest-point step (y * m, plus U with dither)."""
     x = np.ascontiguousarray(x).reshape(-1)
     v = np.zeros(x.size, dtype=np.float32)
-    _check(lib().hqo_lattice_inputs(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
+    _check(lib().hqo_lattice_inputs(_p(x), _dtype_code(x), x.size, lattice, dither_flags(dither), seed,
                                     ctypes.c_float(step), _p(v), tile), "lattice_inputs")
     return v
 
@@ -249,7 +274,7 @@ def dequantize(codes, scales, lattice: int, step: float, seed: int = 0, dither: 
     codes = np.ascontiguousarray(codes, dtype=np.int32)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     out = np.zeros(codes.size, dtype=np.float32)
-    _check(lib().hqo_dequantize(_p(codes), _p(scales), codes.size, lattice, int(bool(dither)), seed,
+    _check(lib().hqo_dequantize(_p(codes), _p(scales), codes.size, lattice, dither_flags(dither), seed,
                                 ctypes.c_float(step), _p(out), tile), "dequantize")
     return out
 
@@ -260,7 +285,7 @@ def rate(x, lattice: int, target_bps: float, seed: int = 0, dither: bool = False
     x = np.ascontiguousarray(x).reshape(-1)
     sb = ctypes.c_uint32(0)
     k = ctypes.c_int(0)
-    _check(lib().hqo_rate(_p(x), _dtype_code(x), x.size, lattice, int(bool(dither)), seed,
+    _check(lib().hqo_rate(_p(x), _dtype_code(x), x.size, lattice, dither_flags(dither), seed,
                           ctypes.c_float(target_bps), ctypes.c_float(step), rice_k,
                           ctypes.byref(sb), ctypes.byref(k), tile), "rate")
     step_f = np.array([sb.value], dtype=np.uint32).view(np.float32)[0]
@@ -285,7 +310,7 @@ def encode(x, lattice: int, target_bps: float = 4.0, seed: int = 0, dither: bool
     nbytes = ctypes.c_uint64(0)
     while True:
         out = np.zeros(capacity, dtype=np.uint8)
-        rc = lib().hqo_encode(_p(x), _dtype_code(x), n, lattice, int(bool(dither)), seed,
+        rc = lib().hqo_encode(_p(x), _dtype_code(x), n, lattice, dither_flags(dither), seed,
                               ctypes.c_float(target_bps), ctypes.c_float(step), rice_k, _p(out),
                               capacity, ctypes.byref(nbytes), _p(info), tile)
         if rc == ERR_CAPACITY and nbytes.value > capacity:

@@ -66,15 +66,22 @@ static float f32_from_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
 static uint32_t bits_from_f32(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Philox4x32-10, as defined by Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as     */
-/* easy as 1, 2, 3" (SC'11): ten rounds; each round multiplies counter words 0 and 2 by the two */
-/* round multipliers, xors the high halves with the other counter words and the key, and the    */
-/* key is bumped by the two Weyl constants between rounds.                                      */
+/* Philox4x32-R, as defined by Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy */
+/* as 1, 2, 3" (SC'11): R rounds (10 is the generator's recommended count, 7 the fewest its      */
+/* authors report as passing their statistical batteries); each round multiplies counter words  */
+/* 0 and 2 by the two round multipliers, xors the high halves with the other counter words and  */
+/* the key, and the key is bumped by the two Weyl constants between rounds.  hqo_philox4x32_span */
+/* applies rounds r0 .. r1-1 only (the key first bumped r0 times), so a count of R rounds is the */
+/* first R rounds of the same function.                                                         */
 /* ------------------------------------------------------------------------------------------ */
-void hqo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+void hqo_philox4x32_span(const uint32_t ctr_in[4], const uint32_t key_in[2], int r0, int r1, uint32_t out[4]) {
   uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
   uint32_t k0 = key_in[0], k1 = key_in[1];
-  for (int round = 0; round < 10; ++round) {
+  for (int round = 0; round < r0; ++round) {
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  for (int round = r0; round < r1; ++round) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
     uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
@@ -88,6 +95,12 @@ void hqo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint3
     k1 += 0xBB67AE85u;
   }
   out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+void hqo_philox4x32_r(const uint32_t ctr_in[4], const uint32_t key_in[2], int rounds, uint32_t out[4]) {
+  hqo_philox4x32_span(ctr_in, key_in, 0, rounds, out);
+}
+void hqo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  hqo_philox4x32_r(ctr_in, key_in, 10, out);
 }
 
 /* Sign diagonal D of the RHT (HyperQuant summary, Methodology component 1: "D is a random sign
@@ -302,26 +315,43 @@ static float code_to_coord(int lattice, int32_t c) {
 }
 
 /* Subtractive dither (HyperQuant summary, Methodology component 4: add a fresh U ~ Unif(V(L))
- * before quantising and subtract it after).  Reading: for tile t and octet o, one Philox call
- * with counter (o, t low word, t high word, 1) and the call's key gives four 32-bit words; their
- * eight 16-bit halves (low half first) h_i give b_i = 2 h_i / 65536 in [0, 2).  [0,2)^8 is a
- * fundamental domain of 2Z^8, a sublattice of E8, D4 x D4, Z^8 and (in stretched coordinates)
- * A2^4, so b is (to 16-bit resolution) uniform on a union of whole cells and U = b - Q(b) is
- * uniform on the Voronoi cell V(L) (for A2 in stretched coordinates, i.e. U_1 sqrt 3 is the data-
- * space offset).  Every operation here is exact in binary32. */
-void hqo_dither_octet(uint64_t seed, uint64_t tile, int octet, int lattice, float u[8]) {
+ * before quantising and subtract it after).  Reading: for tile t and octet o, Philox calls with
+ * the call's key and counter (o, t low word, t high word, 1) give four 32-bit words w; their eight
+ * 16-bit halves (low half first) h_i give b_i = 2 h_i / 2^16 in [0, 2).  [0,2)^8 is a fundamental
+ * domain of 2Z^8, a sublattice of E8, D4 x D4, Z^8 and (in stretched coordinates) A2^4, so b is
+ * (to the draw's resolution) uniform on a union of whole cells and U = b - Q(b) is uniform on the
+ * Voronoi cell V(L) (for A2 in stretched coordinates, i.e. U_1 sqrt 3 is the data-space offset).
+ * Every operation here is exact in binary32.
+ * The pages fix neither the generator's round count nor the draw's resolution; both are format
+ * options in the dither flags (bit 0: dither on; bit 1: the dither's Philox calls take 7 rounds
+ * instead of 10; bit 2: 24-bit resolution, from a second call with counter word 3 = 2: b_i =
+ * 2 (w_i >> 8) / 2^24 with w_0..w_3 from the first call and w_4..w_7 from the second). */
+void hqo_dither_octet_flags(uint64_t seed, uint64_t tile, int octet, int lattice, int flags, float u[8]) {
+  const int rounds = (flags & 2) ? 7 : 10;
   uint32_t ctr[4] = {(uint32_t)octet, (uint32_t)tile, (uint32_t)(tile >> 32), 1u};
-  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[4];
-  hqo_philox4x32_10(ctr, key, w);
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, w[8];
+  hqo_philox4x32_r(ctr, key, rounds, w);
   float b[8];
   int32_t q[8];
-  for (int i = 0; i < 8; ++i) {
-    uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-    b[i] = (float)h * (1.0f / 32768.0f);
+  if (flags & 4) {
+    ctr[3] = 2u;
+    hqo_philox4x32_r(ctr, key, rounds, w + 4);
+    for (int i = 0; i < 8; ++i) b[i] = (float)(w[i] >> 8) * (1.0f / 8388608.0f);
+  } else {
+    for (int i = 0; i < 8; ++i) {
+      uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      b[i] = (float)h * (1.0f / 32768.0f);
+    }
   }
   hqo_nearest_octet(lattice, b, q);
   for (int i = 0; i < 8; ++i) u[i] = b[i] - code_to_coord(lattice, q[i]);
 }
+void hqo_dither_octet(uint64_t seed, uint64_t tile, int octet, int lattice, float u[8]) {
+  hqo_dither_octet_flags(seed, tile, octet, lattice, 1, u);
+}
+
+/* Valid dither flags: 0 (off), or bit 0 set with any of bits 1 and 2. */
+static int valid_dither(int d) { return d == 0 || (d >= 1 && d <= 7 && (d & 1)); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* Per-layer Haar-uniform rotation for KV caches (HyperQuant summary, Methodology component 4: the
@@ -531,7 +561,7 @@ static int quantize_tile(const qctx *q, uint64_t t, const float *x, float step, 
     for (int i = 0; i < 8; ++i) v[i] = y[8 * o + i] * m[i & 1];
     if (q->dither) {
       float u[8];
-      hqo_dither_octet(q->seed, t, o, q->lattice, u);
+      hqo_dither_octet_flags(q->seed, t, o, q->lattice, q->dither, u);
       for (int i = 0; i < 8; ++i) v[i] = v[i] + u[i];
     }
     hqo_nearest_octet(q->lattice, v, code + 8 * o);
@@ -552,7 +582,7 @@ static void dequantize_tile(const qctx *q, uint64_t t, const int32_t *code, uint
   float y[TILE_MAX];
   for (int o = 0; o < q->tl / 8; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
+    if (q->dither) hqo_dither_octet_flags(q->seed, t, o, q->lattice, q->dither, u);
     for (int i = 0; i < 8; ++i) {
       float c = code_to_coord(q->lattice, code[8 * o + i]);
       float cu = q->dither ? c - u[i] : c;
@@ -580,7 +610,7 @@ static void load_tile(const void *x, int dtype, uint64_t t, int tl, float *out) 
  * encoder's front half; the GPU exposes the same thing for code-level parity). */
 int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
                  float step, int32_t *codes, uint16_t *scales, int tl) {
-  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
+  if (!valid_tile(tl) || n % (uint64_t)tl || !valid_dither(dither)) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   qctx q;
   qctx_init(&q, lattice, dither, seed, tl);
@@ -598,7 +628,7 @@ int hqo_quantize(const void *x, int dtype, uint64_t n, int lattice, int dither, 
  * relative to the Voronoi boundary in the tests). */
 int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
                        float step, float *v_out, int tl) {
-  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
+  if (!valid_tile(tl) || n % (uint64_t)tl || !valid_dither(dither)) return ERR_INVALID_ARG;
   qctx q;
   qctx_init(&q, lattice, dither, seed, tl);
   for (uint64_t t = 0; t < n / (uint64_t)tl; ++t) {
@@ -613,7 +643,7 @@ int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int di
     tile_factors(lattice, s, step, m, tf);
     for (int o = 0; o < tl / 8; ++o) {
       float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (dither) hqo_dither_octet(seed, t, o, lattice, u);
+      if (dither) hqo_dither_octet_flags(seed, t, o, lattice, dither, u);
       for (int i = 0; i < 8; ++i) {
         float v = y[8 * o + i] * m[i & 1];
         v_out[t * (uint64_t)tl + 8 * o + i] = dither ? v + u[i] : v;
@@ -625,7 +655,7 @@ int hqo_lattice_inputs(const void *x, int dtype, uint64_t n, int lattice, int di
 
 int hqo_dequantize(const int32_t *codes, const uint16_t *scales, uint64_t n, int lattice,
                    int dither, uint64_t seed, float step, float *out, int tl) {
-  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
+  if (!valid_tile(tl) || n % (uint64_t)tl || !valid_dither(dither)) return ERR_INVALID_ARG;
   qctx q;
   qctx_init(&q, lattice, dither, seed, tl);
   for (uint64_t t = 0; t < n / (uint64_t)tl; ++t)
@@ -765,7 +795,7 @@ static double rc_bits(int lattice, uint64_t N, int k, uint64_t sumq, int tl) {
 /* Output: chosen step bits, Rice k, and the sample payload estimate (bits/value) by interpolation. */
 int hqo_rate(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
              float target_bps, float step, int rice_k, uint32_t *step_bits_out, int *k_out, int tl) {
-  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
+  if (!valid_tile(tl) || n % (uint64_t)tl || !valid_dither(dither)) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   if (rice_k < -1 || rice_k > 15) return ERR_INVALID_ARG;
   qctx q;
@@ -939,7 +969,7 @@ int hqo_encode_layout(uint64_t n, int lattice, int k, uint64_t *fixed_off, uint6
 int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, uint64_t seed,
                float target_bps, float step, int rice_k, uint8_t *out, uint64_t cap,
                uint64_t *out_bytes, uint64_t info[4], int tl) {
-  if (!valid_tile(tl) || n % (uint64_t)tl) return ERR_INVALID_ARG;
+  if (!valid_tile(tl) || n % (uint64_t)tl || !valid_dither(dither)) return ERR_INVALID_ARG;
   if (lattice < LAT_Z || lattice > LAT_A2) return ERR_INVALID_ARG;
   uint32_t sbits;
   int k;
@@ -978,7 +1008,7 @@ int hqo_encode(const void *x, int dtype, uint64_t n, int lattice, int dither, ui
   put_u32(out + 0, MAGIC);
   put_u16(out + 4, VERSION);
   out[6] = (uint8_t)lattice;
-  out[7] = (uint8_t)(dither ? 1 : 0);
+  out[7] = (uint8_t)dither;  /* the dither flags */
   put_u16(out + 8, (uint16_t)tl);
   out[10] = (uint8_t)k;
   out[11] = (uint8_t)log2_int(L.ctiles);
@@ -1039,8 +1069,8 @@ typedef void (*tile_sink)(void *ctx, const qctx *q, uint64_t t, const int32_t *c
 static int read_stream(const uint8_t *s, uint64_t bytes, uint64_t n, tile_sink sink, void *ctx) {
   if (bytes < HEADER_BYTES) return ERR_CORRUPT;
   if (get_u32(s) != MAGIC || get_u16(s + 4) != VERSION) return ERR_CORRUPT;
-  int lattice = s[6], dither = s[7] & 1, k = s[10], tl = get_u16(s + 8);
-  if (lattice > LAT_A2 || (s[7] & ~1u) || !valid_tile(tl) || k > 15) return ERR_CORRUPT;
+  int lattice = s[6], dither = s[7], k = s[10], tl = get_u16(s + 8);
+  if (lattice > LAT_A2 || !valid_dither(dither) || !valid_tile(tl) || k > 15) return ERR_CORRUPT;
   if (s[11] != log2_int(CHUNK_VALUES / (uint64_t)tl)) return ERR_CORRUPT;
   if (get_u64(s + 24) != n || n % (uint64_t)tl) return ERR_CORRUPT;
   uint32_t sbits = get_u32(s + 12);
@@ -1129,7 +1159,7 @@ static void coords_sink(void *ctx, const qctx *q, uint64_t t, const int32_t *cod
   tile_factors(q->lattice, bf16_to_f32(sb), step, m, tf);
   for (int o = 0; o < q->tl / 8; ++o) {
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (q->dither) hqo_dither_octet(q->seed, t, o, q->lattice, u);
+    if (q->dither) hqo_dither_octet_flags(q->seed, t, o, q->lattice, q->dither, u);
     for (int i = 0; i < 8; ++i) {
       const double c = (double)code_to_coord(q->lattice, code[8 * o + i]);
       out[8 * o + i] = (c - (double)u[i]) * (double)tf[i & 1];

@@ -25,6 +25,8 @@ CASES = [
     ("weight16x4096_e8_3bps", "weight16", "e8", 3.0, 0, False),
     ("tiny_e8_4bps_tile64", "tiny", "e8", 4.0, 0, False, 64),
     ("tiny_e8_3bps_dither_tile256", "tiny", "e8", 3.0, 5, True, 256),
+    # dither flags 7: 24-bit draw from 7-round Philox calls
+    ("tiny_e8_2bps_dither_flags7", "tiny", "e8", 2.0, 5, 7),
 ]
 
 

@@ -104,3 +104,13 @@ def test_dither_halfwords_uniform(orc):
     assert abs(vals.mean()) < 5 * np.sqrt(1 / 12 / vals.size)
     assert abs(vals.var() - 1 / 12) < 0.02 * (1 / 12)
     assert vals.min() >= -0.5 and vals.max() <= 0.5
+
+
+@pytest.mark.parametrize("ctr,key,want", KAT)
+def test_round_count_is_a_prefix_of_the_pinned_rounds(orc, ctr, key, want):
+    """Philox4x32-R with R = 7 (a dither format option) is the first 7 rounds of the function the
+    known answers pin: running rounds 7..9 on its output gives the 10-round answer."""
+    r7 = orc.philox4x32_span(ctr, key, 0, 7)
+    assert tuple(int(v) for v in orc.philox4x32_span(r7, key, 7, 10)) == want
+    assert tuple(int(v) for v in orc.philox4x32_span(ctr, key, 0, 10)) == want
+    assert tuple(int(v) for v in r7) != want
