@@ -42,6 +42,8 @@ def parse():
                          "Haar rotation before encode and after decode; srft: the SRFT fixed-rate codec "
                          "(int4, or int8 with --bps 8) on the KV call")
     ap.add_argument("--bps", type=float, default=None)
+    ap.add_argument("--dither-flags", type=int, default=1, choices=[1, 3, 5, 7],
+                    help="kv: dither options (+2: 7-round Philox draw, +4: 24-bit draw)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -66,7 +68,7 @@ def copy_calibration(steps: int):
                                            "launches": steps}}), flush=True)
 
 
-def workload(cfg: str, bps):
+def workload(cfg: str, bps, dither_flags: int = 1):
     import synth
     if cfg == "weight":
         x = synth.weight()
@@ -76,9 +78,11 @@ def workload(cfg: str, bps):
                        profile=f"weight_14336x4096_e8_{tb:g}bps"), 0
     x = synth.kv(0, 0)
     tb = 2.0 if bps is None else bps
-    return x, dict(workload=f"kv cache layer 0 K [8][32768][128] bf16, E8 + dither {tb:g} bps",
-                   shape=[8, 32768, 128], lattice="e8", target_bps=tb, dither=True,
-                   seed=synth.kv_seed(0, 0), profile=f"kv_8x32768x128_e8_dither_{tb:g}bps"), synth.kv_seed(0, 0)
+    opts = {1: "", 3: " (7-round Philox draw)", 5: " (24-bit draw)", 7: " (24-bit draw, 7-round Philox)"}
+    suffix = "" if dither_flags == 1 else f"_flags{dither_flags}"
+    return x, dict(workload=f"kv cache layer 0 K [8][32768][128] bf16, E8 + dither{opts[dither_flags]} {tb:g} bps",
+                   shape=[8, 32768, 128], lattice="e8", target_bps=tb, dither=dither_flags,
+                   seed=synth.kv_seed(0, 0), profile=f"kv_8x32768x128_e8_dither_{tb:g}bps{suffix}"), synth.kv_seed(0, 0)
 
 
 CODEC_SOURCES = ("csrc/hq_kernels.hip", "csrc/hq_device.h", "csrc/hq_internal.h")
@@ -551,7 +555,7 @@ def main():
 
     import kv_quantization_tile_amd as hq
 
-    x_host, cfg, seed = workload(args.config, args.bps)
+    x_host, cfg, seed = workload(args.config, args.bps, args.dither_flags)
     profile_stem = cfg.pop("profile")
     n = x_host.size
     dev = torch.device("cuda:0")

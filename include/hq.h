@@ -26,7 +26,7 @@
  *    recorded in the workspace; blocking calls return them, hq_status() reads them otherwise.
  *
  * Bitstream (format version 1, little-endian; the pages give no format, this is the codec's own):
- *   header, 128 bytes: u32 magic 'HQ01' | u16 version | u8 lattice | u8 flags (bit0 dither) |
+ *   header, 128 bytes: u32 magic 'HQ01' | u16 version | u8 lattice | u8 dither flags |
  *     u16 tile TL | u8 rice k | u8 log2 tiles per chunk (log2(8192 / TL)) | u32 step (binary32 bits) |
  *     u64 seed | u64 n | u64 tiles | u32 chunks | u32 F (fixed bits per tile) | u64 fixed_off |
  *     u64 unary_off | u64 unary_words | u64 unary_bits | u64 payload_bits | u64 total_bytes | 32 B 0
@@ -49,6 +49,13 @@
  *   A2 is the hexagonal lattice with minimal distance 1; each pair (v0, v1) is quantised as
  *     (v0, v1 / sqrt 3) onto Z^2 u (Z+1/2)^2 under the distance dw0^2 + 3 dw1^2: its odd slots use
  *     the multiplier 1 / ((s step) R) and reconstruct with (s step) R, R = binary32 sqrt 3.
+ *   Dither flags (0: no dither): bit 0 dither on; bit 1 the dither's Philox4x32 calls take 7 rounds
+ *     instead of 10; bit 2 a 24-bit draw instead of 16 bits (valid: 0, 1, 3, 5, 7).  Octet o of
+ *     tile t draws b in [0, 2)^8 from Philox with key = seed and counter (o, t lo, t hi, 1): the
+ *     eight 16-bit halves (low first) / 2^15; with 24 bits, words w0..w3 of that call and w4..w7
+ *     of counter (o, t lo, t hi, 2) give (w_i >> 8) / 2^23.  U = b - Q(b), Q the lattice's
+ *     nearest point: uniform on the Voronoi cell to the draw's resolution.  The pages fix neither
+ *     the round count nor the resolution; 10 rounds and 16 bits are the defaults.
  */
 #ifndef HQ_H_
 #define HQ_H_
@@ -82,7 +89,8 @@ typedef struct {
   int32_t lattice;     /* hq_lattice                                                                */
   float target_bps;    /* payload bits per value (coset + Rice bits / n); used when step == 0       */
   uint64_t seed;       /* Philox key of the sign diagonal D and of the dither                        */
-  uint32_t dither;     /* 0 = off, 1 = subtractive dither (component 4)                              */
+  uint32_t dither;     /* dither flags: 0 off; 1 subtractive dither (component 4); + 2: 7-round     */
+                       /* Philox for the draw; + 4: 24-bit draw (3, 5, 7; see the format above)     */
   float step;          /* 0 = choose by rate control; > 0 = fixed lattice step (KV append, tests);
                           -1 (hq_encode only) = the step and k that the preceding hq_rate on the
                           same workspace and stream left there                                     */

@@ -93,10 +93,19 @@ def _check(rc: int, what: str):
         raise HqError(rc, what)
 
 
+# Dither flags: bit 0 on; bit 1 the dither's Philox calls take 7 rounds instead of 10; bit 2 a
+# 24-bit draw instead of 16.  True / False mean 1 / 0.
+HQ_DITHER, HQ_DITHER_PHILOX7, HQ_DITHER_24BIT = 1, 2, 4
+
+
+def dither_flags(dither) -> int:
+    return (1 if dither else 0) if isinstance(dither, bool) else int(dither)
+
+
 def make_params(lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, rice_k=-1, tile=128) -> HqParams:
     lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
     return HqParams(tile=tile, lattice=lat, target_bps=float(target_bps), seed=int(seed),
-                    dither=1 if dither else 0, step=float(step), rice_k=int(rice_k))
+                    dither=dither_flags(dither), step=float(step), rice_k=int(rice_k))
 
 
 def hq_workspace_size(n: int, params: HqParams | None = None) -> int:
@@ -338,7 +347,7 @@ def header_fields(stream_bytes_host) -> dict:
     seed, n, T = struct.unpack_from("<QQQ", b, 16)
     chunks, F = struct.unpack_from("<II", b, 40)
     fixed_off, unary_off, words, ubits, payload, total = struct.unpack_from("<QQQQQQ", b, 48)
-    return dict(magic=magic, version=ver, lattice=lat, dither=flags & 1, tile=tile, k=k, chunk_log2=clog,
+    return dict(magic=magic, version=ver, lattice=lat, dither=flags, tile=tile, k=k, chunk_log2=clog,
                 step_bits=step_bits, seed=seed, n=n, tiles=T, chunks=chunks, F=F, fixed_off=fixed_off,
                 unary_off=unary_off, unary_words=words, unary_bits=ubits, payload_bits=payload,
                 total_bytes=total)

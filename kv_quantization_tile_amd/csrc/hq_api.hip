@@ -47,7 +47,7 @@ int check_params(const hq_params* p, uint64_t n) {
   if (p->lattice < HQ_Z || p->lattice > HQ_A2) return HQ_ERR_INVALID_ARG;
   if (n % p->tile) return HQ_ERR_INVALID_ARG;
   if (n > (1ull << 35)) return HQ_ERR_INVALID_ARG;  // the encoder's look-back packs 28-bit padding sums
-  if (p->dither > 1) return HQ_ERR_INVALID_ARG;
+  if (p->dither > 7 || (p->dither > 1 && !(p->dither & 1))) return HQ_ERR_INVALID_ARG;  // dither flags
   if (p->rice_k < -1 || p->rice_k > 15) return HQ_ERR_INVALID_ARG;
   if (p->step == -1.0f) return HQ_OK;  // operating point left in the workspace by hq_rate
   if (!(p->step >= 0.0f)) return HQ_ERR_INVALID_ARG;  // also rejects NaN

@@ -36,17 +36,29 @@ struct U4 {
   uint32_t x, y, z, w;
 };
 
-// Each round's two 32 x 32 -> 64-bit products are written as 64-bit multiplies of zero-extended
-// words, which gfx950 computes with one v_mad_u64_u32 each instead of a mul_lo / mul_hi pair.
-__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+// Rounds R0 .. R1-1 (the key already bumped R0 times).  Each round's two 32 x 32 -> 64-bit
+// products are written as 64-bit multiplies of zero-extended words, which gfx950 computes with one
+// v_mad_u64_u32 each instead of a mul_lo / mul_hi pair.
+template <int R0, int R1>
+__device__ __forceinline__ U4 philox_rounds(U4 c, uint32_t& k0, uint32_t& k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
+  for (int r = R0; r < R1; ++r) {
     const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
     c = U4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
+  return c;
+}
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+  return philox_rounds<0, 10>(c, k0, k1);
+}
+// Philox4x32 with 7 rounds when `seven` (the same for every lane), else 10: the 7-round function
+// is the first 7 rounds of the 10-round one.
+__device__ __forceinline__ U4 philox4x32_7_or_10(U4 c, uint32_t k0, uint32_t k1, bool seven) {
+  c = philox_rounds<0, 7>(c, k0, k1);
+  if (!seven) c = philox_rounds<7, 10>(c, k0, k1);
   return c;
 }
 
@@ -342,19 +354,33 @@ __device__ __forceinline__ float code_coord(int32_t c) {
   return (LAT == kLatE8 || LAT == kLatA2) ? (float)c * 0.5f : (float)c;
 }
 
-// Subtractive dither of octet o of tile t: one Philox call, counter (o, t lo, t hi, 1); the eight
-// 16-bit halves h (low half first) give b = h / 32768 in [0, 2), and U = b - Q(b) is uniform on the
-// Voronoi cell (to 16-bit resolution).  Exact in binary32.
+// Dither flags (the stream header's flags byte): bit 0 dither on; bit 1 the dither's Philox calls
+// take 7 rounds instead of 10; bit 2 a 24-bit draw instead of 16-bit halves.
+constexpr uint32_t kDitherOn = 1u, kDitherPhilox7 = 2u, kDither24 = 4u;
+
+// Subtractive dither of octet o of tile t: a Philox call with counter (o, t lo, t hi, 1); its eight
+// 16-bit halves h (low half first) give b = h / 32768 in [0, 2).  With the 24-bit draw a second
+// call (counter word 3 = 2) adds four more words and b_i = (w_i >> 8) / 2^23.  U = b - Q(b) is
+// uniform on the Voronoi cell to the draw's resolution.  Exact in binary32.  df is the same in
+// every lane, so both branches are uniform.
 template <int LAT>
-__device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, float* u) {
-  const U4 w = philox4x32_10(U4{(uint32_t)o, (uint32_t)t, (uint32_t)(t >> 32), 1u}, (uint32_t)seed,
-                             (uint32_t)(seed >> 32));
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, uint32_t df, float* u) {
+  const bool seven = (df & kDitherPhilox7) != 0u;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const U4 w = philox4x32_7_or_10(U4{(uint32_t)o, (uint32_t)t, (uint32_t)(t >> 32), 1u}, k0, k1, seven);
   float b[8];
+  if (df & kDither24) {
+    const U4 v = philox4x32_7_or_10(U4{(uint32_t)o, (uint32_t)t, (uint32_t)(t >> 32), 2u}, k0, k1, seven);
+    const uint32_t ww[8] = {w.x, w.y, w.z, w.w, v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t h = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
-    b[i] = (float)h * (1.0f / 32768.0f);
+    for (int i = 0; i < 8; ++i) b[i] = (float)(ww[i] >> 8) * (1.0f / 8388608.0f);
+  } else {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
+      b[i] = (float)h * (1.0f / 32768.0f);
+    }
   }
   int32_t q[8];
   nearest_octet<LAT>(b, q);

@@ -396,8 +396,8 @@ __device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
 // then wait for it.
 template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
-                                                      Workspace* ws, RateAcc* racc, uint64_t seed, int nc,
-                                                      int half_log2, int fixed_k, float target, int cpw,
+                                                      Workspace* ws, RateAcc* racc, uint64_t seed, uint32_t df,
+                                                      int nc, int half_log2, int fixed_k, float target, int cpw,
                                                       int solve_prev, PassDesc prev) {
   constexpr int LPT = Tiling<TL>::LPT, TPW = Tiling<TL>::TPW;
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
   if (valid && !finite && o == 0 && jlo == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  if (DITHER) dither_octet<LAT>(seed, t, o, df, u);
   int64_t centre;
   if (!solve_prev) {
     centre = ws->rc_centre;  // stored by init_kernel
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, PassDesc 
 // than one word and for segments larger than the staging window; every lane of the wavefront must
 // call it together (the FWHT and the tile energy exchange values between lanes).
 template <int LAT, bool DITHER, int DT, int TL>
-__device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_t seed, uint32_t c, int r,
+__device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_t seed, uint32_t df, uint32_t c, int r,
                                               int wave, int tw, int o, uint32_t sgn, uint32_t lane_neg, float step,
                                               uint32_t* sym) {
   using TI = Tiling<TL>;
@@ -548,19 +548,19 @@ __device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_
   const float m = tile_multiplier<false>(sb, step, lane_neg);
   const float m1 = LAT == kLatA2 ? tile_multiplier<true>(sb, step, lane_neg) : m;
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  if (DITHER) dither_octet<LAT>(seed, t, o, df, u);
   uint32_t cos;
   octet_symbols<LAT, DITHER>(y, m, m1, u, sym, &cos);
 }
 
-__device__ void write_header(uint8_t* out, uint64_t cap, int lattice, int dither, int k, uint32_t step_bits,
+__device__ void write_header(uint8_t* out, uint64_t cap, int lattice, uint32_t dflags, int k, uint32_t step_bits,
                              uint64_t seed, uint64_t n, uint64_t T, uint32_t chunks, uint32_t F,
                              uint64_t fixed_off, uint64_t unary_off, uint64_t words, uint64_t ubits,
                              uint64_t payload, uint64_t total, uint32_t tile, uint32_t log2_ct) {
   if (cap < (uint64_t)kHeaderBytes) return;
   uint32_t h[32];
   h[0] = kMagic;
-  h[1] = kVersion | ((uint32_t)lattice << 16) | ((uint32_t)(dither ? 1 : 0) << 24);
+  h[1] = kVersion | ((uint32_t)lattice << 16) | ((dflags & 0xFFu) << 24);
   h[2] = tile | ((uint32_t)k << 16) | (log2_ct << 24);
   h[3] = step_bits;
   h[4] = (uint32_t)seed; h[5] = (uint32_t)(seed >> 32);
@@ -636,6 +636,7 @@ struct EncParams {
   uint64_t n, T;
   uint32_t chunks;
   uint64_t seed;
+  uint32_t dflags;  // dither flags (0 without dither)
   uint8_t* out;
   uint64_t cap;
   Workspace* ws;
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   if (c >= P.chunks) {  // empty tensor: one workgroup writes the header and the index
     if (P.chunks == 0 && tid == 0) {
       const uint64_t total = unary_off;
-      write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, 0, F, fixed_off, unary_off, 0, 0,
+      write_header(P.out, P.cap, LAT, P.dflags, k, step_bits, P.seed, P.n, P.T, 0, F, fixed_off, unary_off, 0, 0,
                    0, total, TL, __builtin_ctz(TI::CT));
       if (P.cap >= kHeaderBytes + 4) reinterpret_cast<uint32_t*>(P.out)[kHeaderBytes / 4] = 0;
       if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
@@ -766,7 +767,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       }
     }
     float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (DITHER) dither_octet<LAT>(P.seed, t, o, u);
+    if (DITHER) dither_octet<LAT>(P.seed, t, o, P.dflags, u);
     uint32_t cos;
     octet_symbols<LAT, DITHER>(y[r], lane_neg ? -mr[r] : mr[r], lane_neg ? -mr1[r] : mr1[r], u, sym[r], &cos);
     const uint64_t bal = __ballot(valid && cos != 0u);
@@ -896,7 +897,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       const uint32_t Lr = r == 0 ? L[0] : r == 1 ? L[1] : r == 2 ? L[2] : L[3];
       const uint32_t offr = r == 0 ? off[0] : r == 1 ? off[1] : r == 2 ? off[2] : off[3];
       uint32_t sy[8];
-      round_symbols<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, c, r, wave, tw, o, sgn, lane_neg, step, sy);
+      round_symbols<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, P.dflags, c, r, wave, tw, o, sgn, lane_neg, step, sy);
       if (multi ? Lr != 0u : Lr > 32u) {
         uint32_t p = offr;
 #pragma unroll
@@ -923,7 +924,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     const uint64_t total = unary_off + 8ull * words;
     const uint64_t ubits = 64ull * words - (prefix_pad + (64ull * W - B));
     const uint64_t payload = P.T * (uint64_t)(F - 16u) + ubits;
-    write_header(P.out, P.cap, LAT, DITHER, k, step_bits, P.seed, P.n, P.T, P.chunks, F, fixed_off, unary_off,
+    write_header(P.out, P.cap, LAT, P.dflags, k, step_bits, P.seed, P.n, P.T, P.chunks, F, fixed_off, unary_off,
                  words, ubits, payload, total, TL, __builtin_ctz(TI::CT));
     if (kHeaderBytes + 4ull * P.chunks + 4 <= P.cap)
       reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[P.chunks] = (uint32_t)words;
@@ -941,7 +942,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
 // Diagnostic codes kernel: front half at a fixed step, integer codes and scale bits out.
 template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ x, uint64_t T, uint64_t seed,
-                                                       uint32_t step_bits, int32_t* __restrict__ codes,
+                                                       uint32_t df, uint32_t step_bits, int32_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales, Workspace* ws) {
   using TI = Tiling<TL>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
@@ -953,7 +954,7 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
   const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
   if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (DITHER) dither_octet<LAT>(seed, t, o, u);
+  if (DITHER) dither_octet<LAT>(seed, t, o, df, u);
   int32_t code[8];
   quantize_octet<LAT, DITHER>(y, sb, __uint_as_float(step_bits), u, code, lane_sign_bit<TI::LPT>(o));
   if (valid) {
@@ -984,7 +985,8 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
   const uint64_t T = n / tile;
   const uint32_t chunks = (uint32_t)((T + ct - 1) / ct);
   const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
-  bool ok = have && tile_ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags <= 1 &&
+  const bool flags_ok = flags == 0 || (flags <= 7 && (flags & 1));  // dither flags
+  bool ok = have && tile_ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags_ok &&
             k <= 15 && (h[2] >> 24) == (uint32_t)__builtin_ctz(ct) && h[3] >= kStepBitsMin &&
             h[3] <= kStepBitsMax && hn == n && (n % tile) == 0 && (cols % tile) == 0;
   uint32_t F = 0;
@@ -1084,7 +1086,8 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   const int k = ws->dec_k;
   const uint32_t F = ws->dec_F;
-  const bool dither = ws->dec_dither != 0;
+  const uint32_t df = ws->dec_dither;  // dither flags of the stream
+  const bool dither = df != 0u;
   const uint64_t seed = ws->dec_seed;
   const float step = __uint_as_float(ws->dec_step_bits);
   const int RW = octet_rem_bits<LAT>(k);
@@ -1191,7 +1194,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         z[7] = 2 * twice_unzz(sym[7]) + (int32_t)((xz & 2u) | coset);
         if (dither) {
           float u[8];
-          dither_octet<LAT>(seed, t, o, u);
+          dither_octet<LAT>(seed, t, o, df, u);
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] = ((float)z[i] * 0.5f - u[i]) * tsc;
         } else {
@@ -1206,7 +1209,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         unstrip_octet<LAT>(sym, coset, code);
         const float tsc1 = tsc * __uint_as_float(kA2R3Bits);
         float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (dither) dither_octet<LAT>(seed, t, o, u);
+        if (dither) dither_octet<LAT>(seed, t, o, df, u);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float cc = code_coord<LAT>(code[i]);
@@ -1217,7 +1220,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         unstrip_octet<LAT>(sym, coset, code);
         if (dither) {
           float u[8];
-          dither_octet<LAT>(seed, t, o, u);
+          dither_octet<LAT>(seed, t, o, df, u);
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] = (code_coord<LAT>(code[i]) - u[i]) * tsc;
         } else {
@@ -1513,7 +1516,8 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
   const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1) : PassDesc{};
 #define HQ_RATE(L, D, T, TL)                                                                           \
   hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
-                     rate_acc(a.ws, pass), a.seed, nc, half_log2, a.rice_k, a.target, cpw, solve_prev, prev)
+                     rate_acc(a.ws, pass), a.seed, (uint32_t)a.dither, nc, half_log2, a.rice_k, a.target, cpw,      \
+                     solve_prev, prev)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_RATE);
 #undef HQ_RATE
   return hipGetLastError();
@@ -1534,6 +1538,7 @@ hipError_t launch_encode(const EncodeArgs& a) {
   P.T = a.tiles;
   P.chunks = a.chunks;
   P.seed = a.seed;
+  P.dflags = (uint32_t)a.dither;
   P.out = a.out;
   P.cap = a.cap;
   P.ws = a.ws;
@@ -1552,7 +1557,7 @@ hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales) {
   if (blocks == 0) return hipSuccess;
 #define HQ_CODES(L, D, T, TL)                                                                          \
   hipLaunchKernelGGL((codes_kernel<L, D, T, TL>), dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, \
-                     a.seed, a.fixed_step_bits, codes, scales, a.ws)
+                     a.seed, (uint32_t)a.dither, a.fixed_step_bits, codes, scales, a.ws)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_CODES);
 #undef HQ_CODES
   return hipGetLastError();

@@ -67,6 +67,10 @@ def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 
     (dict(lattice="a2", target_bps=1.4), hq.HQ_ERR_RATE),  # below A2's floor of 1.5 (coset bits)
     (dict(target_bps=13.0), hq.HQ_ERR_RATE),
     (dict(dither=True, lattice="z", target_bps=0.5), hq.HQ_ERR_RATE),
+    (dict(dither=2), hq.HQ_ERR_INVALID_ARG),            # dither option bits without the dither
+    (dict(dither=4), hq.HQ_ERR_INVALID_ARG),
+    (dict(dither=6), hq.HQ_ERR_INVALID_ARG),
+    (dict(dither=8), hq.HQ_ERR_INVALID_ARG),
 ])
 def test_encode_rejects_bad_params_on_host(kw, code):
     base = dict(lattice="e8", target_bps=4.0)

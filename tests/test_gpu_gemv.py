@@ -43,7 +43,7 @@ def check_rows(orc, s_gpu, rows, cols, x_host, x_dev, seed):
 
 
 @pytest.mark.parametrize("lattice,dither,target", [("e8", False, 4.0), ("e8", True, 2.0), ("d4", False, 4.0),
-                                                    ("a2", True, 3.0),
+                                                    ("a2", True, 3.0), ("e8", 7, 2.0),
                                                     ("z", False, 3.0)])
 def test_gemv_small_matrix(orc, lattice, dither, target):
     say(f"case: gemv 96x1024 {lattice} dither={dither} {target} bps")

@@ -348,3 +348,60 @@ def test_overflowing_energy_is_nonfinite(orc):
     with pytest.raises(hq.HqError) as e:
         hq.hq_encode(dev(x), "e8", 0.0, step=0.3, rice_k=2)
     assert e.value.code == hq.HQ_ERR_NONFINITE
+
+
+# ---- dither format options (flags: + 2 Philox with 7 rounds, + 4 a 24-bit draw) -------------------
+
+@pytest.mark.parametrize("flags", [3, 5, 7])
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
+def test_dither_options_fixed_point(orc, flags, lattice):
+    say(f"case: dither flags {flags} fixed point {lattice}")
+    for T in (1, 65, 300):
+        x = _scaled_gaussian_tiles(T, seed=T + flags)
+        for step, k in ((0.3, 2), (1.1, 0)):
+            s_orc, _ = orc.encode(x, LAT[lattice], 0.0, seed=9, dither=flags, step=step, rice_k=k)
+            s_gpu, _ = hq.hq_encode(dev(x), lattice, 0.0, seed=9, dither=flags, step=step, rice_k=k)
+            assert_same_stream(host_bytes(s_gpu), s_orc, f"T {T} step {step} k {k}")
+            assert hq.header_fields(host_bytes(s_gpu))["dither"] == flags
+            y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.decode(s_orc, x.size).view(np.uint32))
+
+
+@pytest.mark.parametrize("flags", [3, 5, 7])
+def test_dither_options_codes_and_rate(orc, flags):
+    say(f"case: dither flags {flags} codes and rate control")
+    w = synth.weight(rows=256)
+    c_orc, s_orc = orc.quantize(w, orc.LAT_E8, 0.27, seed=3, dither=flags)
+    c_gpu, s_gpu = hq.hq_codes(dev(w), 0.27, "e8", seed=3, dither=flags)
+    assert np.array_equal(s_gpu.cpu().numpy().view(np.uint16), s_orc)
+    boundary_check(orc, w, "e8", 0.27, 3, flags, c_gpu.cpu().numpy(), c_orc)
+    x = synth.kv(1, 0, heads=2, tokens=8192)
+    st, sb, k = orc.rate(x, orc.LAT_E8, 2.0, seed=synth.kv_seed(1, 0), dither=flags)
+    info = hq.hq_rate(dev(x), "e8", 2.0, seed=synth.kv_seed(1, 0), dither=flags)
+    assert int(np.array([info["step"]], dtype=np.float32).view(np.uint32)[0]) == sb and info["rice_k"] == k
+
+
+@pytest.mark.parametrize("flags", [3, 7])
+def test_dither_options_kv_call_full_size(orc, flags):
+    """One (layer, K|V) call of the KV workload, [8][32768][128] bf16, E8 at 3 bps with the option."""
+    say(f"case: kv layer 5 K 3 bps dither flags {flags}")
+    x = synth.kv(5, 0)
+    seed = synth.kv_seed(5, 0)
+    s_orc, info_orc = orc.encode(x, orc.LAT_E8, 3.0, seed=seed, dither=flags)
+    s_gpu, info = hq.hq_encode(dev(x), "e8", 3.0, seed=seed, dither=flags)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    assert abs(info["payload_bps"] - 3.0) <= 0.01
+    y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(y), orc.decode(s_orc, x.size, out_dtype="bf16"))
+
+
+def test_corrupt_dither_flags_reported():
+    say("case: corrupt dither flags")
+    x = synth.tiny(tiles=8)
+    s_gpu, _ = hq.hq_encode(dev(x), "e8", 3.0, dither=True)
+    for bad in (2, 4, 6, 8):
+        s = s_gpu.clone()
+        s[7] = bad
+        with pytest.raises(hq.HqError) as e:
+            hq.hq_decode(s, x.size, out_dtype=torch.float32)
+        assert e.value.code == hq.HQ_ERR_CORRUPT
