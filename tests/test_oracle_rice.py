@@ -105,3 +105,29 @@ def test_stream_roundtrip_other_tiles(orc, tile, lattice):
         bad[8] ^= 0xC0
         with pytest.raises(orc.OracleError):
             orc.decode(bad, x.size)
+
+
+@pytest.mark.parametrize("case", ["weight_4bps", "kv_dither_2bps"])
+def test_per_tile_rice_k_would_not_pay(orc, case):
+    """Why the Rice parameter is one per stream, not one per tile: after the per-tile RMS scale,
+    every tile's symbols follow nearly the same law, so the per-tile best k saves far less than
+    the 4 bits per tile (1/32 bit per value) it would cost to store.  Measured on the oracle's own
+    stripped symbols at the rate-controlled operating point."""
+    if case == "weight_4bps":
+        x, tb, seed, dither = synth.weight(rows=64), 4.0, 0, False
+    else:
+        x, tb, seed, dither = synth.kv(1, 0, heads=1, tokens=2048), 2.0, synth.kv_seed(1, 0), True
+    step, _, k_glob = orc.rate(x, orc.LAT_E8, tb, seed=seed, dither=dither)
+    codes, _ = orc.quantize(x, orc.LAT_E8, step, seed=seed, dither=dither)
+    tiles = codes.reshape(-1, 128)
+    ks = np.arange(0, 12)
+    bits = np.zeros((tiles.shape[0], ks.size), dtype=np.int64)
+    for t in range(tiles.shape[0]):
+        syms = np.stack([orc.strip_octet(orc.LAT_E8, tiles[t, 8 * o:8 * o + 8])[0] for o in range(16)])
+        for j, k in enumerate(ks):
+            w = np.array([k] * 7 + [max(k - 1, 0)], dtype=np.int64)
+            bits[t, j] = ((syms.astype(np.int64) >> w) + 1 + w).sum()
+    glob = bits.sum(axis=0)
+    assert int(np.argmin(glob)) == k_glob
+    saving_per_value = (glob.min() - bits.min(axis=1).sum()) / codes.size
+    assert saving_per_value < 0.25 * (4.0 / 128.0), saving_per_value
