@@ -113,3 +113,17 @@ def gaussian(n: int, seed: int = 0, std: float = 1.0) -> np.ndarray:
     if std != 1.0:
         x *= np.float32(std)
     return x
+
+
+def device_normal_bf16(n: int, seed: int, std: float = 0.02, device: str = "cuda"):
+    """n bf16 values N(0, std^2) drawn on the GPU with torch's seeded generator (for tensors too
+    large to draw on the host in reasonable time); returns the torch tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.empty(n, dtype=torch.bfloat16, device=device)
+    step = 1 << 28
+    for i in range(0, n, step):
+        m = min(step, n - i)
+        x[i:i + m] = (torch.randn(m, generator=g, device=device) * std).to(torch.bfloat16)
+    return x

@@ -405,3 +405,37 @@ def test_corrupt_dither_flags_reported():
         with pytest.raises(hq.HqError) as e:
             hq.hq_decode(s, x.size, out_dtype=torch.float32)
         assert e.value.code == hq.HQ_ERR_CORRUPT
+
+
+def test_tensor_beyond_4_gib(orc):
+    """n = 2^31 + 3 * 8192 + 5 * 128 bf16 values (4.3 GB of input, byte offsets past 2^32 in the
+    input, the decoded output and the stream's planes), E8 at 4 bps with rate control.  The oracle
+    checks the rate-control point on the whole tensor (it reads only the sampled tiles), then each
+    sampled chunk's fixed record, unary segment and decoded values against its own encoding of
+    those chunks at the same point (without dither a chunk's bytes depend only on its tiles)."""
+    n = (1 << 31) + 3 * 8192 + 5 * 128
+    say(f"case: {n} values, E8 4 bps")
+    x = synth.device_normal_bf16(n, seed=77)
+    x_host = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    st, sb, k = orc.rate(x_host, orc.LAT_E8, 4.0)
+    s_gpu, info = hq.hq_encode(x, "e8", 4.0)
+    assert int(np.array([info["step"]], dtype=np.float32).view(np.uint32)[0]) == sb and info["rice_k"] == k
+    assert abs(info["payload_bps"] - 4.0) <= 0.01
+    y = hq.hq_decode(s_gpu, n, out_dtype=torch.bfloat16)
+    s = host_bytes(s_gpu)
+    h = hq.header_fields(s)
+    chunks = h["chunks"]
+    assert chunks == (n + 8191) // 8192 and h["tiles"] == n // 128
+    idx = s[128:128 + 4 * (chunks + 1)].view(np.uint32).astype(np.int64)
+    rec = 64 * h["F"] // 8
+    for c in (0, 1, (1 << 31) // 8192 - 1, (1 << 31) // 8192, chunks // 3, chunks - 2, chunks - 1):
+        lo, hi = 8192 * c, min(8192 * (c + 1), n)
+        sub, _ = orc.encode(x_host[lo:hi], orc.LAT_E8, 0.0, step=st, rice_k=k)
+        hs = hq.header_fields(sub)
+        assert hs["F"] == h["F"]
+        f_gpu = s[h["fixed_off"] + c * rec: h["fixed_off"] + (c + 1) * rec]
+        assert np.array_equal(f_gpu, sub[hs["fixed_off"]: hs["fixed_off"] + rec]), c
+        u_gpu = s[h["unary_off"] + 8 * idx[c]: h["unary_off"] + 8 * idx[c + 1]]
+        assert np.array_equal(u_gpu, sub[hs["unary_off"]: hs["unary_off"] + 8 * hs["unary_words"]]), c
+        yb = bf16_host(y[lo:hi])
+        assert np.array_equal(yb, orc.decode(sub, hi - lo, out_dtype="bf16")), c
