@@ -439,3 +439,48 @@ def test_tensor_beyond_4_gib(orc):
         assert np.array_equal(u_gpu, sub[hs["unary_off"]: hs["unary_off"] + 8 * hs["unary_words"]]), c
         yb = bf16_host(y[lo:hi])
         assert np.array_equal(yb, orc.decode(sub, hi - lo, out_dtype="bf16")), c
+
+
+@pytest.mark.parametrize("lattice", ["e8", "d4", "a2", "z"])
+def test_fixed_step_automatic_k_and_fixed_k_rate_control(orc, lattice):
+    """The two mixed operating modes: a fixed step with the Rice parameter chosen by one sample pass,
+    and rate control on the step with the Rice parameter fixed."""
+    say(f"case: fixed step / auto k and rate control / fixed k, {lattice}")
+    w = synth.weight(rows=512)
+    for dither in (False, True):
+        s_orc, info_orc = orc.encode(w, LAT[lattice], 0.0, seed=4, dither=dither, step=0.3, rice_k=-1)
+        s_gpu, info = hq.hq_encode(dev(w), lattice, 0.0, seed=4, dither=dither, step=0.3, rice_k=-1)
+        assert info["rice_k"] == info_orc["k"]
+        assert_same_stream(host_bytes(s_gpu), s_orc, f"fixed step, dither={dither}")
+        s_orc, info_orc = orc.encode(w, LAT[lattice], 3.0, seed=4, dither=dither, rice_k=1)
+        s_gpu, info = hq.hq_encode(dev(w), lattice, 3.0, seed=4, dither=dither, rice_k=1)
+        assert info["rice_k"] == 1 and info["step"] == info_orc["step"]
+        assert_same_stream(host_bytes(s_gpu), s_orc, f"fixed k, dither={dither}")
+
+
+def test_concurrent_calls_on_separate_streams(orc):
+    """Calls in flight together on three streams, each with its own workspaces and buffers (the
+    streamed series of the benchmark): every stream and decode equals the oracle's."""
+    say("case: concurrent calls on three streams")
+    xs = [synth.weight(rows=rows, seed=s) for rows, s in ((256, 3), (512, 4), (128, 5))]
+    streams = [torch.cuda.Stream() for _ in xs]
+    outs = []
+    for x, st in zip(xs, streams):
+        n = x.size
+        xd = dev(x)
+        cap = hq.capacity_estimate(n, "e8", 4.0)
+        out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+        y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        ws, wsd = hq.workspace(n), hq.workspace(0)
+        torch.cuda.synchronize()
+        outs.append((xd, out, y, ws, wsd, st))
+    for _ in range(3):   # several rounds of the three calls in flight together
+        for (xd, out, y, ws, wsd, st), x in zip(outs, xs):
+            hq.hq_encode(xd, "e8", 4.0, out=out, ws=ws, blocking=False, stream=st)
+            hq.hq_decode(out, x.size, out=y, ws=wsd, check=False, stream=st)
+    torch.cuda.synchronize()
+    for (xd, out, y, ws, wsd, st), x in zip(outs, xs):
+        assert hq.hq_status(ws, st) == 0 and hq.hq_status(wsd, st) == 0
+        s_orc, _ = orc.encode(x, orc.LAT_E8, 4.0)
+        assert_same_stream(host_bytes(out)[: s_orc.size], s_orc)
+        assert np.array_equal(bf16_host(y), orc.decode(s_orc, x.size, out_dtype="bf16"))
