@@ -1145,16 +1145,25 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       const uint4 pa = *reinterpret_cast<const uint4*>(s_pos + g0);
       const uint4 pb = *reinterpret_cast<const uint4*>(s_pos + g0 + 4);
       const uint32_t pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      uint32_t q[8];
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        q[sl] = (pprev ^ 0xFFFFFFFFu) + pp[sl];
+        pprev = pp[sl];
+      }
+      // q << w can only lose bits in a segment that long (uniform, and rare: the branch is skipped)
+      if (__builtin_expect(check_q, 0)) {
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl)
+          if (q[sl] > (0xFFFFFFFFu >> slot_width<LAT>(sl, k))) bad = true;
+      }
       uint32_t sym[8];
       if (RW <= 32) {  // uniform: every slot is one bit-field extract of lo
         int off = 0;
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int w = slot_width<LAT>(sl, k);
-          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
-          pprev = pp[sl];
-          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
-          sym[sl] = (q << w) | __builtin_amdgcn_ubfe(lo, (uint32_t)off, (uint32_t)w);
+          sym[sl] = (q[sl] << w) | __builtin_amdgcn_ubfe(lo, (uint32_t)off, (uint32_t)w);
           off += w;
         }
       } else if (k <= 8) {
@@ -1162,10 +1171,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int w = slot_width<LAT>(sl, k);
-          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
-          pprev = pp[sl];
-          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
-          sym[sl] = (q << w) | field_slot(lo, hi, off, w);
+          sym[sl] = (q[sl] << w) | field_slot(lo, hi, off, w);
           off += w;
         }
       } else {
@@ -1173,10 +1179,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int w = slot_width<LAT>(sl, k);
-          const uint32_t q = (pprev ^ 0xFFFFFFFFu) + pp[sl];
-          pprev = pp[sl];
-          if (check_q && q > (0xFFFFFFFFu >> w)) bad = true;
-          sym[sl] = (q << w) | plane_bits(fw, pos, w);
+          sym[sl] = (q[sl] << w) | plane_bits(fw, pos, w);
           pos += (uint32_t)w;
         }
       }
