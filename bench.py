@@ -779,17 +779,23 @@ def main():
         import oracle
         if not os.path.exists(os.path.join(ROOT, "oracle", "libhq_oracle.so")):
             oracle.build()
-        t1 = time.perf_counter()
-        s_orc, info_orc = oracle.encode(x_host, oracle.LATTICES[lat], tb, seed=seed, dither=dither)
-        t2 = time.perf_counter()
-        y_orc = oracle.decode(s_orc, n, out_dtype="bf16")
-        t3 = time.perf_counter()
-        cpu_gbs = input_bytes / (t3 - t1) / 1e9
+        # the whole workload, repeated until about 10 s of host time have been spent (at most 8 times)
+        reps, t_enc, t_dec = 0, 0.0, 0.0
+        while True:
+            t1 = time.perf_counter()
+            s_orc, info_orc = oracle.encode(x_host, oracle.LATTICES[lat], tb, seed=seed, dither=dither)
+            t2 = time.perf_counter()
+            y_orc = oracle.decode(s_orc, n, out_dtype="bf16")
+            t3 = time.perf_counter()
+            reps, t_enc, t_dec = reps + 1, t_enc + (t2 - t1), t_dec + (t3 - t2)
+            if args.no_cpu_baseline or t_enc + t_dec >= 10.0 or reps >= 8:
+                break
+        cpu_gbs = reps * input_bytes / (t_enc + t_dec) / 1e9
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                                      "sample": f"the whole workload ({n} values), one encode (with rate "
-                                                f"control) + one bf16 decode, single host thread: "
-                                                f"encode {t2 - t1:.2f} s, decode {t3 - t2:.2f} s"}
+                                      "sample": f"the whole workload ({n} values), {reps} times one encode (with "
+                                                f"rate control) + one bf16 decode, single host thread: encode "
+                                                f"{t_enc / reps:.2f} s, decode {t_dec / reps:.2f} s each"}
         if not args.no_parity:
             g = out[:total_bytes].cpu().numpy()
             same_stream = bool(g.size == s_orc.size and np.array_equal(g, s_orc))
