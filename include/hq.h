@@ -217,8 +217,10 @@ int hq_srft_decode(const void *codes, const void *scales, uint64_t n, uint64_t s
 
 /* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
  * E8 and A2 codes are twice the lattice point (A2 in stretched coordinates), D4 and Z codes are the
- * point) and per-tile bf16 scale bits
- * (uint16).  Asynchronous; non-finite tiles are reported through hq_status. */
+ * point) and per-tile bf16 scale bits (uint16).  codes: n values, scales: n / params->tile
+ * values, both device buffers, 16-byte aligned.  params->step must be positive (a fixed step);
+ * the dither flags apply as for hq_encode.  Asynchronous; non-finite tiles are reported through
+ * hq_status. */
 int hq_codes(const void *x, int32_t dtype, uint64_t n, const hq_params *params, int32_t *codes,
              uint16_t *scales, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 

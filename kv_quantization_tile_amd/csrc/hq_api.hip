@@ -325,6 +325,9 @@ int hq_codes(const void* x, int32_t dtype, uint64_t n, const hq_params* params, 
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < workspace_bytes_for(0) || (n && (!x || !codes || !scales)))
     return HQ_ERR_INVALID_ARG;
+  // the kernel reads x and writes codes with 16-byte vector accesses
+  if (((uintptr_t)x & 15u) || ((uintptr_t)codes & 15u) || ((uintptr_t)scales & 1u) || ((uintptr_t)workspace & 255u))
+    return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
   a.chunks = 0;  // no look-back flags are needed
   if (launch_init(a, (int64_t)a.fixed_step_bits) != hipSuccess) return HQ_ERR_HIP;

@@ -177,3 +177,15 @@ def test_srft_rejects_bad_args_on_host():
     assert L.hq_srft_decode(ok, None, 128, 0, None, 4, ok, 1, None) == E
     assert L.hq_srft_decode(ok, ok, 128, 0, lam_bad, 4, ok, 1, None) == E
     assert L.hq_srft_decode(None, None, 0, 0, None, 4, None, 1, None) == hq.HQ_OK
+
+
+def test_codes_rejects_misaligned_buffers_on_host():
+    L = hq.lib()
+    p = hq.make_params("e8", step=0.3)
+    ok, ws = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    for x, codes, scales in (((1 << 20) + 8, 1 << 20, 1 << 20), (1 << 20, (1 << 20) + 4, 1 << 20),
+                             (1 << 20, 1 << 20, (1 << 20) + 1)):
+        assert L.hq_codes(ctypes.c_void_p(x), 1, 128, ctypes.byref(p), ctypes.c_void_p(codes),
+                          ctypes.c_void_p(scales), ws, 8192, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_codes(ok, 1, 128, ctypes.byref(p), ok, ok, ctypes.c_void_p((1 << 21) + 64), 8192,
+                      None) == hq.HQ_ERR_INVALID_ARG
