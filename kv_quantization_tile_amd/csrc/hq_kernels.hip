@@ -775,8 +775,16 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     if (valid) {
       const uint32_t rec = tc * F;
       if (o == 0) {
-        lds_put_bits(s_fixed, rec, sbr[r], 16);
-        if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (LPT * tw)) & low_mask(LPT), LPT);
+        if (LAT == kLatE8 && LPT <= 16) {
+          // the scale and the tile's coset bits as one field of 16 + LPT <= 32 bits
+          const uint32_t v = sbr[r] | (((uint32_t)(bal >> (LPT * tw)) & low_mask(LPT)) << 16);
+          const uint32_t sh = rec & 31u;
+          atomicOr(&s_fixed[rec >> 5], v << sh);
+          if (sh + 16u + (uint32_t)LPT > 32u) atomicOr(&s_fixed[(rec >> 5) + 1], __builtin_amdgcn_alignbit(0u, v, 32u - sh));
+        } else {
+          lds_put_bits(s_fixed, rec, sbr[r], 16);
+          if (LAT == kLatE8) lds_put_bits(s_fixed, rec + 16, (uint32_t)(bal >> (LPT * tw)) & low_mask(LPT), LPT);
+        }
       }
       // A2: the octet's four pair cosets, bits 4 o .. 4 o + 3 after the scale (never across a word)
       if (LAT == kLatA2) lds_put_bits(s_fixed, rec + 16 + 4u * (uint32_t)o, cos, 4);
@@ -967,9 +975,18 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
 
 // ---------------------------------------------------------------------------------------------
 // Decoder.
-// cols: the row length of a matrix product (a whole number of the stream's tiles), 0 for a plain decode.
-__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, uint64_t cols,
-                                    Workspace* ws) {
+// The stream header's validity and the fields the decoder needs.
+struct HeaderCheck {
+  uint32_t ok, tile;
+  uint64_t seed;
+};
+
+// Header validation by one workgroup (every lane calls it: it holds two barriers).  cols: the row
+// length of a matrix product (a whole number of the stream's tiles), 0 for a plain decode.  With
+// `publish`, lane 0 records the result in the workspace (status, and the decoder's fields when the
+// stream is valid); every lane receives the result in *res (LDS).
+__device__ void check_header(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, uint64_t cols,
+                             Workspace* ws, bool publish, HeaderCheck* res) {
   __shared__ uint32_t s_h[32];
   __shared__ uint32_t s_idx[2];
   const int tid = threadIdx.x;
@@ -1008,27 +1025,37 @@ __global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_
        total <= in_bytes && words <= (1ull << 32) && unary_off + 8ull * words == total;
   if (ok && tid < 2) s_idx[tid] = reinterpret_cast<const uint32_t*>(in + kHeaderBytes)[tid == 0 ? 0 : chunks];
   __syncthreads();
-  if (tid != 0) return;
-  ok = ok && s_idx[0] == 0u && (uint64_t)s_idx[1] == words;
-  ws->dec_valid = 0;
-  if (!ok) {
-    ws->status = kErrCorrupt;
-    return;
+  if (tid == 0) {
+    ok = ok && s_idx[0] == 0u && (uint64_t)s_idx[1] == words;
+    res->ok = ok ? 1u : 0u;
+    res->tile = tile;
+    res->seed = ((uint64_t)h[5] << 32) | h[4];
+    if (publish) {
+      ws->dec_valid = 0;
+      ws->status = ok ? 0u : (uint32_t)kErrCorrupt;
+      if (ok) {
+        ws->dec_tile = tile;
+        ws->dec_lattice = (uint32_t)lattice;
+        ws->dec_dither = (uint32_t)flags;
+        ws->dec_k = k;
+        ws->dec_step_bits = h[3];
+        ws->dec_F = F;
+        ws->dec_chunks = chunks;
+        ws->dec_seed = res->seed;
+        ws->dec_tiles = T;
+        ws->dec_fixed_off = fixed_off;
+        ws->dec_unary_off = unary_off;
+        ws->dec_words = words;
+        ws->dec_valid = 1;
+      }
+    }
   }
-  ws->status = 0;
-  ws->dec_tile = tile;
-  ws->dec_lattice = (uint32_t)lattice;
-  ws->dec_dither = (uint32_t)flags;
-  ws->dec_k = k;
-  ws->dec_step_bits = h[3];
-  ws->dec_F = F;
-  ws->dec_chunks = chunks;
-  ws->dec_seed = ((uint64_t)h[5] << 32) | h[4];
-  ws->dec_tiles = T;
-  ws->dec_fixed_off = fixed_off;
-  ws->dec_unary_off = unary_off;
-  ws->dec_words = words;
-  ws->dec_valid = 1;
+  __syncthreads();
+}
+
+__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws) {
+  __shared__ HeaderCheck s_res;
+  check_header(in, in_bytes, n, 0, ws, true, &s_res);
 }
 
 constexpr int kMaxSymsPerChunk = kChunkValues;
@@ -1387,16 +1414,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
 // every matrix tile needs only its lattice values, no inverse transform.
 
 // x~_j = H D x_j for every column tile, binary32 in the encoder's butterfly order, stored with the
-// lanes' butterfly signs removed (an exact negation).  Runs after the header check (the seed of D
-// and the tile length come from the stream).  A workgroup covers 2048 columns at every tile length.
+// lanes' butterfly signs removed (an exact negation).  Every workgroup checks the stream header
+// itself (the seed of D and the tile length come from it), and workgroup 0 also publishes the
+// check for the decode that follows, so no separate check launch is needed.  A workgroup covers
+// 2048 columns at every tile length.
 template <int DT, int TL>
-__device__ __forceinline__ void gemv_rotate_tiles(const void* __restrict__ x, uint64_t cols, const Workspace* ws,
+__device__ __forceinline__ void gemv_rotate_tiles(const void* __restrict__ x, uint64_t cols, uint64_t seed,
                                                   float* __restrict__ xt) {
   using TI = Tiling<TL>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
   const uint64_t t = (uint64_t)blockIdx.x * TI::TPR + TI::TPW * wave + tw;
   const bool valid = t < cols / TL;
-  const uint32_t sgn = octet_sign_bits(ws->dec_seed, o);
+  const uint32_t sgn = octet_sign_bits(seed, o);
   uint32_t smask[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
@@ -1419,16 +1448,19 @@ __device__ __forceinline__ void gemv_rotate_tiles(const void* __restrict__ x, ui
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const void* __restrict__ x, uint64_t cols,
-                                                             const Workspace* ws, float* __restrict__ xt) {
-  if (!ws->dec_valid) return;
-  const uint32_t tile = ws->dec_tile;
+__global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+                                                             uint64_t n, const void* __restrict__ x, uint64_t cols,
+                                                             Workspace* ws, float* __restrict__ xt) {
+  __shared__ HeaderCheck s_res;
+  check_header(in, in_bytes, n, cols, ws, blockIdx.x == 0, &s_res);
+  if (!s_res.ok) return;
+  const uint32_t tile = s_res.tile;
   if (tile == 64u)
-    gemv_rotate_tiles<DT, 64>(x, cols, ws, xt);
+    gemv_rotate_tiles<DT, 64>(x, cols, s_res.seed, xt);
   else if (tile == 256u)
-    gemv_rotate_tiles<DT, 256>(x, cols, ws, xt);
+    gemv_rotate_tiles<DT, 256>(x, cols, s_res.seed, xt);
   else
-    gemv_rotate_tiles<DT, 128>(x, cols, ws, xt);
+    gemv_rotate_tiles<DT, 128>(x, cols, s_res.seed, xt);
 }
 
 // y_r = sum over the row's column tiles of the tile partials, in column order (one lane per row).
@@ -1568,7 +1600,7 @@ hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales) {
 
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
                          Workspace* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, (uint64_t)0, ws);
+  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // a chunk holds kChunkValues values at every tile length (the header check rejects an n that
@@ -1586,18 +1618,20 @@ hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int ou
 hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
                        float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream) {
   const uint64_t n = rows * cols;
-  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, cols, ws);
+  if (n == 0) {  // nothing to multiply (x may then be null): check the stream only
+    hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+    return hipGetLastError();
+  }
+  // the rotation kernel also checks the header (its workgroup 0 publishes the check)
+  const uint32_t rblocks = (uint32_t)((cols + 2047) / 2048);
+  if (x_dtype == 1)
+    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt);
+  else
+    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunks = (n + kChunkValues - 1) / kChunkValues;
   if (chunks == 0) return hipSuccess;
-  const uint32_t rblocks = (uint32_t)((cols + 2047) / 2048);  // 2048 columns per workgroup at every tile length
-  if (x_dtype == 1)
-    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, x, cols, ws, xt);
-  else
-    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, x, cols, ws, xt);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const GemvArgs g{xt, cols, tp};
   hipLaunchKernelGGL((decode_kernel<1, true>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, nullptr, ws, g);
   e = hipGetLastError();
