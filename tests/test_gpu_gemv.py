@@ -95,3 +95,16 @@ def test_gemv_rejects_mismatched_shape():
     with pytest.raises(hq.HqError) as e:
         hq.hq_gemv(s_gpu, 16, 1024, x)
     assert e.value.code == hq.HQ_ERR_CORRUPT
+
+
+def test_gemv_empty_matrix():
+    """rows = 0: only the stream is checked (the activation may then be empty)."""
+    say("case: gemv on an empty matrix")
+    s_gpu, _ = hq.hq_encode(torch.zeros(0, device="cuda"), "e8", 4.0)
+    y = hq.hq_gemv(s_gpu, 0, 1024, torch.zeros(1024, device="cuda"))
+    assert y.numel() == 0
+    bad = s_gpu.clone()
+    bad[0] ^= 1
+    with pytest.raises(hq.HqError) as e:
+        hq.hq_gemv(bad, 0, 1024, torch.zeros(1024, device="cuda"))
+    assert e.value.code == hq.HQ_ERR_CORRUPT
