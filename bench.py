@@ -71,6 +71,36 @@ def copy_calibration(steps: int):
                                            "launches": steps}}), flush=True)
 
 
+def measured_copy_gbs(torch, reps: int = 20) -> float:
+    """Device-to-device copy of 1 GiB (read + written bytes over event time): the HBM bandwidth a
+    plain streaming kernel reaches here, the second denominator beside the 8 TB/s spec."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def workload(cfg: str, bps, dither_flags: int = 1):
     import synth
     if cfg == "weight":
@@ -781,6 +811,10 @@ def main():
                   "host_wall_ms_per_step": round(wall / K * 1e3, 5)},
     }
 
+    copy_gbs = measured_copy_gbs(torch)
+    result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
+    result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
+
     if not args.no_cpu_baseline or not args.no_parity:
         import oracle
         if not os.path.exists(os.path.join(ROOT, "oracle", "libhq_oracle.so")):
@@ -801,7 +835,8 @@ def main():
             result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                       "sample": f"the whole workload ({n} values), {reps} times one encode (with "
                                                 f"rate control) + one bf16 decode, single host thread: encode "
-                                                f"{t_enc / reps:.2f} s, decode {t_dec / reps:.2f} s each"}
+                                                f"{t_enc / reps:.2f} s, decode {t_dec / reps:.2f} s each",
+                                      "cpu": cpu_model(), "host_cpus": os.cpu_count()}
         if not args.no_parity:
             g = out[:total_bytes].cpu().numpy()
             same_stream = bool(g.size == s_orc.size and np.array_equal(g, s_orc))
