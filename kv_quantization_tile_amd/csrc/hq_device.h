@@ -271,6 +271,7 @@ __device__ __forceinline__ void e8_nearest(const float* v, int32_t* z) {
 // 2^22, so every step is exact), and zigzag is |2u + 1/2| truncated: 2u for u >= 0, -2u - 1 below.
 // 1 - 2 a_max and 2 + 2 a_min are formed by a fused multiply-add: the product by 2 is exact, so
 // the single rounding equals that of the separate multiply and add.
+template <bool MASK_FIX = false>
 __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32_t* coset) {
   float e[8], rf[8];
 #pragma unroll
@@ -301,17 +302,39 @@ __device__ __forceinline__ void e8_symbols(const float* v, uint32_t* sym, uint32
   const float t = keep_a ? amax : amin;
   bool found = keep_a ? (pa == 0u) : (pb == 0u);  // no fix needed: nothing to find
   float u[8];
+  if (MASK_FIX) {
+    // u_i = rf_i + D_i.  D8 candidate: D = +-1 (toward e) on the fixed coordinate, else 0.  D8 + 1/2:
+    // u = floor(v) = rf - [e < 0], moved by 1 against e on the fixed coordinate, so D = -([e < 0]
+    // xor hit).  The conditions stay lane masks (scalar work); per coordinate only the compares and
+    // two selects of c = 2 D + 1/2 are vector work, and 2 u + 1/2 = fma(2, rf, c) exactly.  Fewer
+    // vector instructions and registers, more scalar ones: the choice for kernels whose scalar
+    // unit has room.
+    float c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float base = keep_a ? rf[i] : floorf(v[i]);
-    const bool hit = !found && (fabsf(e[i]) == t);
-    found = found || hit;
-    // +-1 with the sign of e (D8) or against it (D8 + 1/2): sign bit of e ^ kb on 1.0
-    const float step1 = __uint_as_float(((__float_as_uint(e[i]) ^ kb) & 0x80000000u) | 0x3F800000u);
-    u[i] = base + (hit ? step1 : 0.0f);
+    for (int i = 0; i < 8; ++i) {
+      const bool hit = !found && (fabsf(e[i]) == t);
+      found = found || hit;
+      const bool neg = e[i] < 0.0f;  // e is never -0: it is v - rint(v) in round to nearest
+      const bool up = keep_a && hit && !neg;                   // D = +1
+      const bool down = keep_a ? (hit && neg) : (neg != hit);  // D = -1
+      c[i] = down ? -1.5f : (up ? 2.5f : 0.5f);
+    }
+    u[7] = rf[7] + (c[7] - 0.5f) * 0.5f;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) sym[i] = (uint32_t)fabsf(__builtin_fmaf(2.0f, rf[i], c[i]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float base = keep_a ? rf[i] : floorf(v[i]);
+      const bool hit = !found && (fabsf(e[i]) == t);
+      found = found || hit;
+      // +-1 with the sign of e (D8) or against it (D8 + 1/2): sign bit of e ^ kb on 1.0
+      const float step1 = __uint_as_float(((__float_as_uint(e[i]) ^ kb) & 0x80000000u) | 0x3F800000u);
+      u[i] = base + (hit ? step1 : 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < 7; ++i) sym[i] = (uint32_t)fabsf(__builtin_fmaf(2.0f, u[i], 0.5f));
   }
-#pragma unroll
-  for (int i = 0; i < 7; ++i) sym[i] = (uint32_t)fabsf(__builtin_fmaf(2.0f, u[i], 0.5f));
   const uint32_t x = xor3(xor3(sym[0], sym[1], sym[2]), xor3(sym[3], sym[4], sym[5]), sym[6]);
   // parity of u_0 + .. + u_6: u and zz(u) satisfy [u odd] = bit 1 ^ bit 0 of zz(u)
   const int32_t par = (int32_t)(((x >> 1) ^ x) & 1u);
