@@ -92,8 +92,8 @@ typedef struct {
   uint32_t dither;     /* dither flags: 0 off; 1 subtractive dither (component 4); + 2: 7-round     */
                        /* Philox for the draw; + 4: 24-bit draw (3, 5, 7; see the format above)     */
   float step;          /* 0 = choose by rate control; > 0 = fixed lattice step (KV append, tests);
-                          -1 (hq_encode only) = the step and k that the preceding hq_rate on the
-                          same workspace and stream left there                                     */
+                          -1 (hq_encode only) = the step and k the workspace holds: those that a
+                          preceding hq_rate or hq_encode on the same workspace chose            */
   int32_t rice_k;      /* -1 = automatic; 0..15 = fixed Rice parameter                              */
 } hq_params;
 
@@ -107,54 +107,104 @@ typedef struct {
   double total_bps;     /* 8 bytes / n                                                              */
 } hq_info;
 
-/* Library and format version: returns (major << 16) | format_version. */
+/* Library and format version: returns (major << 16) | format_version.
+ * Defined by this codec (the pages give no format); the format is the one described above. */
 uint32_t hq_version(void);
 
-/* Human-readable text of a status code (static storage). */
+/* Human-readable text of a status code (static storage).  Host only; no device call. */
 const char *hq_strerror(int code);
 
 /* Bytes of device workspace that hq_encode / hq_rate / hq_decode / hq_codes need for n values
- * (host only; no device call).  The workspace needs no initialisation. */
+ * (host only; no device call).  The workspace needs no initialisation.
+ * The workspace holds the state of components 1-3 of "Methodology: the HyperQuant pipeline"
+ * across the kernels of one call: the operating point that rate targeting (component 3) picks, its
+ * sample counters, and the encoder's per-chunk offset flags.  HQ_ERR_INVALID_ARG: bytes == NULL or
+ * n not a multiple of 64. */
 int hq_workspace_size(uint64_t n, const hq_params *params, size_t *bytes);
 
 /* Stream size for n values at a fixed step, Rice k and tile length, without the unary plane (host
  * only): the header, index and fixed plane.  The unary plane adds (symbol >> width) + 1 bits per value,
- * which depends on the data; hq_encode reports the exact size needed when a buffer is too small. */
+ * which depends on the data (hq_encode_bound bounds it).  Component 3 of "Methodology: the
+ * HyperQuant pipeline" (Rice codes: a fixed-width remainder per symbol).  HQ_ERR_INVALID_ARG for a
+ * bad lattice or k, or n % tile != 0; HQ_ERR_UNSUPPORTED for another tile length. */
 int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint32_t tile, uint64_t *bytes);
 
-/* Rate control alone (component 3's rate targeting): chooses the lattice step and Rice parameter
- * for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles meets
- * params->target_bps (a coarse pass on min(T, 2048) tiles first).  With info != NULL the call blocks and fills info (payload_bps is the target);
- * with info == NULL it only enqueues work, and a following hq_encode with params->step == -1 on the
- * same workspace and stream encodes at the chosen point (the pair then does exactly what one
- * hq_encode with rate control does).  x must be 16-byte aligned and the workspace 256-byte aligned
- * (HQ_ERR_INVALID_ARG otherwise), as for hq_encode. */
+/* Worst-case stream size in bytes for n values encoded with `params` (host only; no device call),
+ * so that a caller can size the output of an asynchronous hq_encode, or of a KV-cache append at a
+ * fixed operating point, before the data exist.  Component 3 of "Methodology: the HyperQuant
+ * pipeline" codes lattice symbols with Rice codes and no overload region (the codebook is
+ * unbounded), so the size is bounded only through the energy normalisation of component 2: each
+ * tile's scale s (the bf16 RMS of its transformed values, 16 bits) makes the lattice inputs w of a
+ * tile satisfy sum w^2 <= TL K^2 / step^2, K = 1 + 2^-7 (the bf16 rounding of s and the binary32
+ * roundings).  By Cauchy-Schwarz, sum |w| <= TL K / step; a lattice point lies within the covering
+ * radius of its input (and the dither of component 4 within the Voronoi cell), and a Rice unary
+ * part of a symbol of magnitude u with parameter k is at most u / 2^k + 1 bits.  Summed per tile:
+ *   unary bits <= TL + (A TL K / step + (TL / 8) B) / 2^k,
+ * A = 2 (E8, D4, Z) or sqrt(14/3) (A2), B per octet: E8 2 sqrt 8 d + 12, D4 8 d + 8, Z 8 d,
+ * A2 (4 sqrt 28 / 3) d + 12, where d = 1 without dither and 2 with it; then the stream layout
+ * (header, index, fixed plane, 64-bit padding per chunk).  params->step > 0 is used as given;
+ * step == 0 or -1 (the step is chosen later) takes the smallest step of the range, 2^-12;
+ * params->rice_k == -1 takes the largest bound over k = 0..15.  target_bps and seed play no part.
+ * The bound holds for every input whose tiles are each all zero or hold a value of magnitude at
+ * least 2^-60 (it then covers the binary32 rounding of the tile energy; a tile whose values all lie
+ * below 2^-60 in magnitude can round its energy down and exceed it).  An encode whose stream would
+ * exceed the buffer is never written past it: hq_encode then reports HQ_ERR_CAPACITY.
+ * HQ_ERR_INVALID_ARG for a null pointer, a bad lattice, dither flags or k, n % tile != 0,
+ * n > 2^35 or a step outside [2^-12, 2^12]; HQ_ERR_UNSUPPORTED for another tile length. */
+int hq_encode_bound(uint64_t n, const hq_params *params, uint64_t *max_bytes);
+
+/* Rate control alone: component 3 of "Methodology: the HyperQuant pipeline" (rate targeting, the
+ * realised rate within ~0.01 bits per value of the target).  Chooses the lattice step and Rice
+ * parameter for x so that the payload rate of a jittered stratified sample of min(T, 8192) tiles
+ * meets params->target_bps (a coarse pass on min(T, 2048) tiles first).  With info != NULL the call
+ * blocks and fills info (payload_bps is the target); with info == NULL it only enqueues work, and a
+ * following hq_encode with params->step == -1 on the same workspace and stream encodes at the chosen
+ * point (the pair then does exactly what one hq_encode with rate control does).  x must be 16-byte
+ * aligned and the workspace 256-byte aligned (HQ_ERR_INVALID_ARG otherwise), as for hq_encode.
+ * Errors: HQ_ERR_INVALID_ARG (null or misaligned pointers, bad params, step == -1, a workspace
+ * smaller than hq_workspace_size), HQ_ERR_RATE (target outside the lattice's range),
+ * HQ_ERR_UNSUPPORTED (tile length); device-side HQ_ERR_NONFINITE / HQ_ERR_TIMEOUT when blocking. */
 int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, hq_info *info,
             void *workspace, size_t workspace_bytes, hq_stream_t stream);
 
-/* Encode x (n values, dtype hq_dtype) into `out` (device, out_capacity bytes).
+/* Encode x (n values, dtype hq_dtype) into `out` (device, out_capacity bytes): components 1-4 of
+ * "Methodology: the HyperQuant pipeline" (per-tile RHT H D x; nearest point of the scaled lattice;
+ * stripping of the bits lattice membership fixes and Rice coding; the subtractive dither of the KV
+ * path when params->dither is set).
  * With out_bytes != NULL the call blocks, stores the stream size in *out_bytes (also when the
  * result is HQ_ERR_CAPACITY: the size needed) and fills *info (may be NULL).  With out_bytes == NULL
  * the call only enqueues work on `stream`; the size is in the stream header (total_bytes) and
  * device-side errors are returned later by hq_status(workspace).  Rate control runs when
- * params->step == 0; step > 0 fixes the step; step == -1 takes the point a preceding asynchronous
- * hq_rate left in the workspace. */
+ * params->step == 0; step > 0 fixes the step; step == -1 takes the operating point that the
+ * workspace holds: the one a preceding hq_rate, or a preceding hq_encode with step >= 0, chose on
+ * it (repeated step == -1 calls, e.g. appends to a KV cache at one operating point, keep using
+ * it).  Every call resets the workspace's status, results and offset flags first; an encode with
+ * step == -1 on a workspace that holds no operating point reports HQ_ERR_INVALID_ARG (blocking) or
+ * through hq_status.  x, out: 16-byte aligned; workspace: 256-byte aligned, at least
+ * hq_workspace_size(n) bytes.  Errors: as hq_rate, plus HQ_ERR_CAPACITY (out too small; nothing
+ * is written past out_capacity) and HQ_ERR_UNSUPPORTED (a unary plane of 2^32 words or more). */
 int hq_encode(const void *x, int32_t dtype, uint64_t n, const hq_params *params, void *out,
               uint64_t out_capacity, uint64_t *out_bytes, hq_info *info, void *workspace,
               size_t workspace_bytes, hq_stream_t stream);
 
 /* Decode a stream of `stream_bytes` bytes into out (n values of out_dtype; bf16 is round to nearest
- * even of the fp32 reconstruction).  Asynchronous: header and per-chunk validation happen on the
- * device; call hq_status(workspace) to learn of HQ_ERR_CORRUPT.  On a corrupt stream the output
- * contents are unspecified, but no access leaves the given buffers. */
+ * even of the fp32 reconstruction): the exact inverse of components 1-4 of "Methodology: the
+ * HyperQuant pipeline" (Rice and unstrip are lossless; yhat = (c - U) s step; x = D H yhat / TL,
+ * the transform being orthogonal up to the factor TL).  Asynchronous: header and per-chunk
+ * validation happen on the device; call hq_status(workspace) to learn of HQ_ERR_CORRUPT.  On a
+ * corrupt stream the output contents are unspecified, but no access leaves the given buffers.
+ * out: n values, 16-byte aligned; stream_data 16-byte aligned; workspace 256-byte aligned, at least
+ * hq_workspace_size(0) bytes.  HQ_ERR_INVALID_ARG on the host for bad pointers, dtype or n. */
 int hq_decode(const void *stream_data, uint64_t stream_bytes, void *out, int32_t out_dtype,
               uint64_t n, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 
 /* Waits for `stream` and returns the first device-side error recorded in `workspace` since the last
- * hq_encode / hq_decode / hq_rate that used it (HQ_OK when none). */
+ * hq_encode / hq_decode / hq_rate / hq_codes / hq_gemv that used it (HQ_OK when none).  Reports
+ * the device-side outcome of the calls above (no step of the method of its own). */
 int hq_status(void *workspace, hq_stream_t stream);
 
-/* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only; enough for any tile length). */
+/* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only; enough for any tile length).
+ * Holds the rotated activation and the per-tile partial products of the fused product below. */
 int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 
 /* Fused decode + matrix-vector product y = W_hat x, where the stream encodes a row-major
@@ -175,8 +225,8 @@ int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 int hq_gemv(const void *stream_data, uint64_t stream_bytes, uint64_t rows, uint64_t cols, const void *x,
             int32_t x_dtype, float *y, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 
-/* The per-layer Haar-uniform rotation of a seed (component 4: the full-matrix alternative to the
- * +-1 sign diagonal), written to q (HOST pointer, 128 * 128 floats, q[128 i + j] = Q[i][j]).
+/* The per-layer Haar-uniform rotation of a seed (component 4 of "Methodology: the HyperQuant
+ * pipeline": the full-matrix alternative to the +-1 sign diagonal), written to q (HOST pointer, 128 * 128 floats, q[128 i + j] = Q[i][j]).
  * Construction (the pages give none; the textbook one): G with independent N(0,1) entries, entry
  * e = 128 i + j from Philox4x32-10 with key = seed and counter (e / 4, 0, 0, 2), two Box-Muller
  * pairs per call (u(w) = (w + 1/2) 2^-32; r = sqrt(-2 ln u(w0)); (r cos 2pi u(w1), r sin 2pi u(w1)),
@@ -188,7 +238,9 @@ int hq_haar_matrix(uint64_t seed, float *q);
  * hq_decode) for every 128-value vector v of x.  x, y: DEVICE, n bf16 values each (n % 128 == 0),
  * 16-byte aligned, may not overlap; q: DEVICE, 128 * 128 binary32 as from hq_haar_matrix.
  * On MFMA (bf16 inputs, Q split into two bf16 parts, binary32 accumulation); y is rounded to bf16
- * (nearest even).  Asynchronous on `stream`. */
+ * (nearest even).  Asynchronous on `stream`.  Component 4 of "Methodology: the HyperQuant
+ * pipeline" (the per-layer rotation of the KV path, applied before the codec and undone after).
+ * HQ_ERR_INVALID_ARG for null or misaligned pointers or n % 128 != 0. */
 int hq_rotate(const void *x, uint64_t n, const float *q, int32_t transpose, void *y, hq_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
@@ -215,12 +267,14 @@ int hq_srft_encode(const void *x, int32_t dtype, uint64_t n, uint64_t seed, cons
 int hq_srft_decode(const void *codes, const void *scales, uint64_t n, uint64_t seed, const float *lambda,
                    int32_t bits, void *out, int32_t out_dtype, hq_stream_t stream);
 
-/* Diagnostic front half of the encoder at a fixed step: per-value integer lattice codes (int32;
+/* Diagnostic front half of the encoder at a fixed step (components 1 and 2 of "Methodology: the
+ * HyperQuant pipeline", with component 4's dither when params->dither is set; the integer codes
+ * before component 3's stripping): per-value integer lattice codes (int32;
  * E8 and A2 codes are twice the lattice point (A2 in stretched coordinates), D4 and Z codes are the
  * point) and per-tile bf16 scale bits (uint16).  codes: n values, scales: n / params->tile
  * values, both device buffers, 16-byte aligned.  params->step must be positive (a fixed step);
  * the dither flags apply as for hq_encode.  Asynchronous; non-finite tiles are reported through
- * hq_status. */
+ * hq_status.  HQ_ERR_INVALID_ARG for step <= 0, bad params or misaligned pointers. */
 int hq_codes(const void *x, int32_t dtype, uint64_t n, const hq_params *params, int32_t *codes,
              uint16_t *scales, void *workspace, size_t workspace_bytes, hq_stream_t stream);
 

@@ -5,7 +5,8 @@ declared in ``include/hq.h``.  PyTorch provides device memory and the stream.  T
 fallback: if the library is missing the calls raise.
 
 Entry points mirror the C ABI: ``hq_encode``, ``hq_decode``, ``hq_rate``, ``hq_codes``,
-``hq_status``, ``hq_workspace_size``, ``hq_stream_fixed_bytes``, ``hq_version``, ``hq_strerror``.
+``hq_status``, ``hq_workspace_size``, ``hq_stream_fixed_bytes``, ``hq_encode_bound``,
+``hq_version``, ``hq_strerror``.
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ HQ_Z, HQ_D4, HQ_E8, HQ_A2 = 0, 1, 2, 3
 HQ_F32, HQ_BF16 = 0, 1
 LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8, "a2": HQ_A2}
 
-EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_rate",
+EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_encode_bound", "hq_rate",
            "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
            "hq_haar_matrix", "hq_rotate", "hq_srft_encode", "hq_srft_decode")
 
@@ -63,6 +64,7 @@ def lib():
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_workspace_size.argtypes = [u64, P, ctypes.POINTER(sz)]
         L.hq_stream_fixed_bytes.argtypes = [u64, i32, i32, ctypes.c_uint32, ctypes.POINTER(u64)]
+        L.hq_encode_bound.argtypes = [u64, P, ctypes.POINTER(u64)]
         L.hq_rate.argtypes = [P, i32, u64, P, P, P, sz, P]
         L.hq_encode.argtypes = [P, i32, u64, P, P, u64, P, P, P, sz, P]
         L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
@@ -122,6 +124,14 @@ def hq_stream_fixed_bytes(n: int, lattice, rice_k: int, tile: int = 128) -> int:
     return out.value
 
 
+def hq_encode_bound(n: int, lattice="e8", step=0.0, rice_k=-1, dither=False, tile=128) -> int:
+    """Worst-case stream bytes of an encode of n values (host only; see include/hq.h)."""
+    out = ctypes.c_uint64(0)
+    p = make_params(lattice, 4.0, 0, dither, step, rice_k, tile)
+    _check(lib().hq_encode_bound(n, ctypes.byref(p), ctypes.byref(out)), "hq_encode_bound")
+    return out.value
+
+
 # ---- torch-side helpers (device memory and streams only) ------------------------------------------
 
 def _torch():
@@ -167,17 +177,31 @@ def hq_encode(x, lattice="e8", target_bps=4.0, seed=0, dither=False, step=0.0, r
     or 256).
 
     Returns (stream bytes as a uint8 CUDA tensor, info dict).  With blocking=False the call only
-    enqueues work and returns (out, None); the size is then in the stream header."""
+    enqueues work and returns (out, None); the size is then in the stream header.  Without `out`,
+    the asynchronous call sizes the buffer with hq_encode_bound: at the given step (step > 0), or,
+    with rate control (step == 0), at the operating point of a blocking hq_rate on the workspace,
+    which the asynchronous encode then uses (step == -1)."""
     torch = _torch()
     assert x.is_cuda and x.is_contiguous()
     n = x.numel()
     p = make_params(lattice, target_bps, seed, dither, step, rice_k, tile)
     if ws is None:
         ws = workspace(n, x.device)
+    sh = _stream_handle(stream)
+    if out is None and not blocking:
+        if step > 0:
+            cap = hq_encode_bound(n, p.lattice, step, rice_k, p.dither, tile)
+        elif step == 0:
+            point = hq_rate(x, lattice, target_bps, seed, dither, 0.0, rice_k, ws=ws, stream=stream, tile=tile)
+            cap = hq_encode_bound(n, p.lattice, point["step"], point["rice_k"], p.dither, tile)
+            p = make_params(lattice, target_bps, seed, dither, -1.0, rice_k, tile)
+        else:
+            raise ValueError("an asynchronous encode at the workspace's operating point (step=-1) needs `out`")
+        out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty(capacity_estimate(n, p.lattice, target_bps, rice_k, step, tile), dtype=torch.uint8,
                           device=x.device)
-    sh = _stream_handle(stream)
+    assert out.is_cuda and out.is_contiguous() and out.dtype == torch.uint8
     if not blocking:
         _check(lib().hq_encode(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ctypes.byref(p),
                                ctypes.c_void_p(out.data_ptr()), out.numel(), None, None,
@@ -201,8 +225,12 @@ def hq_decode(stream_bytes, n: int, out_dtype=None, out=None, ws=None, stream=No
     """Decode a uint8 CUDA tensor holding a stream into n values (bf16 by default)."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
+    assert stream_bytes.is_cuda and stream_bytes.is_contiguous() and stream_bytes.dtype == torch.uint8
     if out is None:
         out = torch.empty(n, dtype=out_dtype, device=stream_bytes.device)
+    # the kernels write n values of out's type: a shorter or strided tensor would be written past
+    assert out.is_cuda and out.is_contiguous() and out.numel() >= n, "out must be a contiguous CUDA tensor of n values"
+    assert out.dtype in (torch.float32, torch.bfloat16), "out must be float32 or bfloat16"
     if ws is None:
         ws = workspace(0, stream_bytes.device)
     sh = _stream_handle(stream)
@@ -225,8 +253,12 @@ def hq_gemv(stream_bytes, rows: int, cols: int, x, y=None, ws=None, stream=None,
     (float32 output)."""
     torch = _torch()
     assert x.is_cuda and x.is_contiguous() and x.numel() == cols
+    assert stream_bytes.is_cuda and stream_bytes.is_contiguous() and stream_bytes.dtype == torch.uint8
     if y is None:
         y = torch.empty(rows, dtype=torch.float32, device=x.device)
+    # the kernels write `rows` binary32 values
+    assert y.is_cuda and y.is_contiguous() and y.dtype == torch.float32 and y.numel() >= rows, \
+        "y must be a contiguous float32 CUDA tensor of `rows` values"
     if ws is None:
         ws = torch.empty(hq_gemv_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
     sh = _stream_handle(stream)
@@ -253,6 +285,7 @@ def hq_rotate(x, q, transpose: bool = False, out=None, stream=None):
     assert q.is_cuda and q.is_contiguous() and q.dtype == torch.float32 and q.numel() == 128 * 128
     if out is None:
         out = torch.empty_like(x)
+    assert out.is_cuda and out.is_contiguous() and out.dtype == torch.bfloat16 and out.numel() >= x.numel()
     _check(lib().hq_rotate(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(q.data_ptr()),
                            1 if transpose else 0, ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
            "hq_rotate")
@@ -280,6 +313,8 @@ def hq_srft_encode(x, seed: int = 0, bits: int = 4, lam=None, codes=None, scales
         codes = torch.empty((nv, 64 if bits == 4 else 128), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((nv, 16), dtype=torch.int16, device=x.device)
+    assert codes.is_cuda and codes.is_contiguous() and codes.numel() * codes.element_size() >= nv * (64 if bits == 4 else 128)
+    assert scales.is_cuda and scales.is_contiguous() and scales.numel() * scales.element_size() >= nv * 32
     keep, lp = _host_lambda(lam)
     _check(lib().hq_srft_encode(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, int(seed), lp, int(bits),
                                 ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
@@ -294,6 +329,7 @@ def hq_srft_decode(codes, scales, n: int, seed: int = 0, bits: int = 4, lam=None
     assert codes.is_cuda and scales.is_cuda and codes.is_contiguous() and scales.is_contiguous()
     if out is None:
         out = torch.empty(n, dtype=out_dtype or torch.bfloat16, device=codes.device)
+    assert out.is_cuda and out.is_contiguous() and out.numel() >= n and out.dtype in (torch.float32, torch.bfloat16)
     keep, lp = _host_lambda(lam)
     _check(lib().hq_srft_decode(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), n,
                                 int(seed), lp, int(bits), ctypes.c_void_p(out.data_ptr()), _dtype_code(out),

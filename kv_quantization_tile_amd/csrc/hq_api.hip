@@ -61,6 +61,7 @@ int check_params(const hq_params* p, uint64_t n) {
 }
 
 int status_from_flags(uint32_t f) {
+  if (f & kErrNoPoint) return HQ_ERR_INVALID_ARG;  // the root cause of whatever else that call saw
   if (f & kErrCorrupt) return HQ_ERR_CORRUPT;
   if (f & kErrNonfinite) return HQ_ERR_NONFINITE;
   if (f & kErrCapacity) return HQ_ERR_CAPACITY;
@@ -115,9 +116,10 @@ int run_rate_control(const EncodeArgs& a, LastPass* last) {
   hipError_t e;
   *last = LastPass{};
   if (a.fixed_step_bits) {
-    e = launch_init(a, (int64_t)a.fixed_step_bits);
+    const bool pass_follows = a.rice_k < 0 && N > 0;
+    e = launch_init(a, (int64_t)a.fixed_step_bits, pass_follows ? kInitProvisional : kInitFinal);
     if (e != hipSuccess) return HQ_ERR_HIP;
-    if (a.rice_k < 0 && N > 0) {
+    if (pass_follows) {
       e = launch_rate_pass(a, 1, 0, N, 0);
       if (e != hipSuccess) return HQ_ERR_HIP;
       last->pass = 0;
@@ -126,7 +128,7 @@ int run_rate_control(const EncodeArgs& a, LastPass* last) {
     }
     return HQ_OK;
   }
-  e = launch_init(a, initial_centre(a.target));
+  e = launch_init(a, initial_centre(a.target), N == 0 ? kInitFinal : kInitProvisional);
   if (e != hipSuccess) return HQ_ERR_HIP;
   if (N == 0) return HQ_OK;
   e = launch_rate_pass(a, kRcCand, 21, NA, 0);
@@ -172,6 +174,47 @@ void fill_info(hq_info* info, uint64_t n, uint32_t step_bits, int k, uint64_t by
   info->side_bps = info->total_bps - info->payload_bps;
 }
 
+// Worst-case stream bytes for n values at step `step` and Rice parameter k (see hq_encode_bound in
+// hq.h for the derivation).  Per tile of TL values the encoder's lattice inputs w satisfy
+// sum |w_i| <= TL K / step (Cauchy-Schwarz on the energy the tile scale normalises, K = 1 + 2^-7
+// covering the bf16 rounding of the scale and the binary32 roundings), and each slot's unary part
+// is at most (a_i |w_i| + b_i) / 2^k.  Summed with Cauchy-Schwarz over the tile:
+//   sum of unary parts <= (A TL K / step + (TL / 8) B) / 2^k
+// with A = 2 (E8, D4, Z) or sqrt(14 / 3) (A2: slopes 2 and 4 / sqrt 3 on its even and stretched
+// odd slots), and B per octet = the lattice's covering-radius term (doubled with dither, U lies in
+// the same cell) plus the zigzag and halved-slot constants.
+double unary_per_tile_bound(int lattice, uint32_t tile, double step, int k, bool dither) {
+  const double K = 1.0 + 1.0 / 128.0;
+  const double d = dither ? 2.0 : 1.0;
+  double A = 2.0, B = 0.0;
+  switch (lattice) {
+    case HQ_E8: B = 2.0 * sqrt(8.0) * 1.0 * d + 12.0; break;          // covering radius 1 per octet
+    case HQ_D4: B = 2.0 * sqrt(8.0) * sqrt(2.0) * d + 8.0; break;     // radius 1 per 4-block
+    case HQ_Z: B = 2.0 * sqrt(8.0) * (sqrt(8.0) / 2.0) * d; break;    // 1/2 per coordinate
+    default:                                                          // A2: 1/sqrt 3 per pair
+      A = sqrt(14.0 / 3.0);
+      B = 4.0 * (sqrt(28.0) / 3.0) * d + 12.0;
+      break;
+  }
+  const double q = (A * (double)tile * K / step + ((double)tile / 8.0) * B) / ldexp(1.0, k);
+  return floor(q * (1.0 + 1e-12)) + (double)tile;  // plus one terminator bit per value
+}
+
+uint64_t encode_bound_at(uint64_t n, int lattice, uint32_t tile, double step, int k, bool dither) {
+  const uint64_t chunks = chunks_of(n);
+  const uint64_t ct = 8192ull / tile;
+  const uint64_t fixed_off = align256h(128 + 4 * (chunks + 1));
+  const uint64_t unary_off = align256h(fixed_off + chunks * ct * tile_fixed_bits_h(lattice, k, tile) / 8ull);
+  if (chunks == 0) return unary_off;
+  const double per_tile = unary_per_tile_bound(lattice, tile, step, k, dither);
+  const uint64_t T = n / tile;
+  const uint64_t last_tiles = T - (chunks - 1) * ct;
+  const double full_words = ceil((double)ct * per_tile / 64.0);
+  const double last_words = ceil((double)last_tiles * per_tile / 64.0);
+  const double bytes = (double)unary_off + 8.0 * ((double)(chunks - 1) * full_words + last_words);
+  return bytes >= 1.8e19 ? UINT64_MAX : (uint64_t)bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +250,33 @@ int hq_stream_fixed_bytes(uint64_t n, int32_t lattice, int32_t rice_k, uint32_t 
   const uint64_t chunks = chunks_of(n);
   const uint64_t fixed_off = align256h(128 + 4 * (chunks + 1));
   *bytes = align256h(fixed_off + chunks * (8192ull / tile) * tile_fixed_bits_h(lattice, rice_k, tile) / 8ull);
+  return HQ_OK;
+}
+
+int hq_encode_bound(uint64_t n, const hq_params* params, uint64_t* max_bytes) {
+  if (!max_bytes || !params) return HQ_ERR_INVALID_ARG;
+  if (!valid_tile(params->tile)) return HQ_ERR_UNSUPPORTED;
+  if (params->lattice < HQ_Z || params->lattice > HQ_A2 || n % params->tile || n > (1ull << 35))
+    return HQ_ERR_INVALID_ARG;
+  if (params->dither > 7 || (params->dither > 1 && !(params->dither & 1))) return HQ_ERR_INVALID_ARG;
+  if (params->rice_k < -1 || params->rice_k > 15) return HQ_ERR_INVALID_ARG;
+  double step;
+  if (params->step > 0.0f) {
+    const uint32_t b = f32_bits(params->step);
+    if (b < kStepMin || b > kStepMax) return HQ_ERR_INVALID_ARG;
+    step = (double)params->step;
+  } else if (params->step == 0.0f || params->step == -1.0f) {
+    step = ldexp(1.0, -12);  // rate control may pick any step of the range: the smallest is the worst
+  } else {
+    return HQ_ERR_INVALID_ARG;
+  }
+  uint64_t worst = 0;
+  for (int k = 0; k <= 15; ++k) {
+    if (params->rice_k >= 0 && k != params->rice_k) continue;
+    const uint64_t b = encode_bound_at(n, params->lattice, params->tile, step, k, params->dither != 0);
+    if (b > worst) worst = b;
+  }
+  *max_bytes = worst;
   return HQ_OK;
 }
 
@@ -255,6 +325,9 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
     if (rc) return rc;
     if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
       return HQ_ERR_HIP;
+  } else if (launch_init(a, 0, kInitKeep) != hipSuccess) {
+    // the workspace's operating point is kept; status, results, tickets and look-back flags reset
+    return HQ_ERR_HIP;
   }
   if (launch_encode(a) != hipSuccess) return HQ_ERR_HIP;
   if (!out_bytes) return HQ_OK;
@@ -330,7 +403,7 @@ int hq_codes(const void* x, int32_t dtype, uint64_t n, const hq_params* params, 
     return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
   a.chunks = 0;  // no look-back flags are needed
-  if (launch_init(a, (int64_t)a.fixed_step_bits) != hipSuccess) return HQ_ERR_HIP;
+  if (launch_init(a, (int64_t)a.fixed_step_bits, kInitFinal) != hipSuccess) return HQ_ERR_HIP;
   if (launch_codes(a, codes, scales) != hipSuccess) return HQ_ERR_HIP;
   return HQ_OK;
 }

@@ -6,8 +6,15 @@
 
 namespace hq {
 
-// Device-side error flags recorded in Workspace::status.
-enum { kErrNonfinite = 1u, kErrCapacity = 2u, kErrCorrupt = 4u, kErrTimeout = 8u, kErrRange = 16u };
+// Device-side error flags recorded in Workspace::status.  kErrNoPoint: an encode at the operating
+// point left in the workspace (step == -1) found none there.
+enum { kErrNonfinite = 1u, kErrCapacity = 2u, kErrCorrupt = 4u, kErrTimeout = 8u, kErrRange = 16u,
+       kErrNoPoint = 32u };
+
+// Workspace::point_tag holds this value while step_bits and rice_k are a complete operating point
+// (the end of rate control, or a fixed step and Rice parameter); any other value means there is
+// none.
+constexpr uint32_t kPointTag = 0x54505148u;  // 'H' 'Q' 'P' 'T'
 
 // Rate control (the pages ask for a realised rate within ~0.01 bits per value and give no
 // algorithm; see hq_kernels.hip for the search).
@@ -47,10 +54,17 @@ struct alignas(256) Workspace {
   uint64_t dec_fixed_off;
   uint64_t dec_unary_off;
   uint64_t dec_words;
-  // pass B's centre, which its workgroup 0 solves from pass A and publishes to the rest of the
-  // launch (bit 63 set = published, the centre in the low 32 bits; relaxed agent-scope atomics,
-  // the value travels in the word itself).  init_kernel clears it.
+  // pass B's centre, which the workgroup holding pass B's ticket 0 solves from pass A and publishes
+  // to the rest of the launch (bit 63 set = published, the centre in the low 32 bits; relaxed
+  // agent-scope atomics, the value travels in the word itself).  init_kernel clears it.
   uint64_t sync_centre;
+  // kPointTag while step_bits / rice_k hold a complete operating point
+  uint32_t point_tag;
+  // Work tickets, taken with one atomic add per workgroup and reset by init_kernel: the encoder's
+  // chunk index (chunk c is processed by the c-th workgroup to start, so every predecessor of a
+  // chunk is running or done) and pass B's solver election (ticket 0 solves pass A).
+  uint32_t enc_ticket;
+  uint32_t rate_ticket;
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
@@ -92,8 +106,11 @@ struct EncodeArgs {
   hipStream_t stream;
 };
 
-hipError_t launch_init(const EncodeArgs& a, int64_t centre);
-// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its workgroup 0, with pass 0's
+// Modes of the call's first kernel (see init_kernel): the operating point is provisional (rate
+// passes follow), final, or kept from the workspace (an encode with step == -1).
+enum { kInitProvisional = 0, kInitFinal = 1, kInitKeep = 2 };
+hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode);
+// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its first workgroup, with pass 0's
 // candidates (nc0, half_spacing_log2_0, sample0); pass 0 reads the centre init_kernel stored.
 hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass,
                             int nc0 = 0, int half_spacing_log2_0 = 0, uint32_t sample0 = 0);

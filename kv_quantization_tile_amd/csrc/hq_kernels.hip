@@ -208,14 +208,33 @@ __device__ __forceinline__ void octet_symbols(const float* y, float m, float m1,
 }
 
 // ---------------------------------------------------------------------------------------------
+// Resets a call's workspace: status, results, tickets, the look-back flags and the rate counters.
+// mode kInitProvisional / kInitFinal: the operating point becomes (step_bits, k), and the point tag
+// says whether it is complete (kInitFinal) or awaits rate passes (their last solve sets the tag).
+// mode kInitKeep (an encode with step == -1): the operating point already in the workspace is
+// kept; without a valid tag, or with a step or k out of range, the call records kErrNoPoint and
+// the encoder runs at a harmless point (step 1, k 0) so that every access stays in bounds.
 __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uint32_t* acc, uint32_t nacc,
-                            int64_t centre, uint32_t step_bits, int32_t k) {
+                            int64_t centre, uint32_t step_bits, int32_t k, int mode) {
   const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid == 0) {
-    ws->status = 0;
+    uint32_t status = 0;
+    if (mode == kInitKeep) {
+      step_bits = ws->step_bits;
+      k = ws->rice_k;
+      if (ws->point_tag != kPointTag || step_bits < kStepBitsMin || step_bits > kStepBitsMax || k < 0 || k > 15) {
+        status = kErrNoPoint;
+        step_bits = 127u << 23;
+        k = 0;
+        ws->point_tag = 0;
+      }
+    } else {
+      ws->point_tag = mode == kInitFinal ? kPointTag : 0u;
+      ws->rc_centre = centre;
+    }
+    ws->status = status;
     ws->step_bits = step_bits;
     ws->rice_k = k;
-    ws->rc_centre = centre;
     ws->res_total_bytes = 0;
     ws->res_payload_bits = 0;
     ws->res_unary_bits = 0;
@@ -223,6 +242,8 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
     ws->res_step_bits = step_bits;
     ws->res_k = k;
     ws->sync_centre = 0;
+    ws->enc_ticket = 0;
+    ws->rate_ticket = 0;
   }
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
   for (uint64_t i = gid; i < nacc; i += (uint64_t)gridDim.x * blockDim.x) acc[i] = 0;
@@ -319,6 +340,7 @@ struct PassDesc {
   int nc, half_log2, fixed_k;
   float target;
   uint32_t N;
+  int final;  // this solve gives the call's operating point (it sets the point tag)
 };
 
 struct SolveLds {
@@ -358,15 +380,17 @@ __device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, So
     ws->rc_centre = L->xb;
     ws->step_bits = (uint32_t)L->xb;
     ws->rice_k = L->kres;
+    ws->point_tag = pd.final ? kPointTag : 0u;
   }
   __syncthreads();
   *xb = L->xb;
   *k = L->kres;
 }
 
-// Waits (one lane per wavefront, bounded) until workgroup 0 of this launch has published `word`
-// (bit 63 set) and returns it, wave-uniform; 0 after the bound, with kErrTimeout recorded.
-// Workgroup 0 is dispatched first and publishes without waiting on anyone, so the wait ends.
+// Waits (one lane per wavefront, bounded) until the launch's solver workgroup has published `word`
+// (bit 63 set) and returns it, wave-uniform; 0 after the bound, with kErrTimeout recorded.  The
+// solver is the workgroup that took ticket 0, so it is running before anyone can wait for it, and
+// it publishes without waiting on anyone: the wait ends whatever order workgroups start in.
 __device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
   uint64_t v = 0;
   if ((threadIdx.x & 63) == 0) {
@@ -391,9 +415,9 @@ __device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
 // wavefronts that share a group of TPW tiles sit in the same workgroup, which therefore holds 4 / cw
 // tile groups (cw is 1, 2 or 4).  Splitting the candidates over wavefronts keeps each wavefront's
 // chain short and the pass latency low; every wavefront repeats its tiles' transform.
-// With solve_prev, workgroup 0 first solves the previous pass (prev) for this pass's centre and
-// publishes it in Workspace::sync_centre; the other workgroups transform their tiles meanwhile and
-// then wait for it.
+// With solve_prev, the workgroup that takes ticket 0 first solves the previous pass (prev) for this
+// pass's centre and publishes it in Workspace::sync_centre; the other workgroups transform their
+// tiles meanwhile and then wait for it.
 template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
                                                       Workspace* ws, RateAcc* racc, uint64_t seed, uint32_t df,
@@ -402,9 +426,18 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   constexpr int LPT = Tiling<TL>::LPT, TPW = Tiling<TL>::TPW;
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
   __shared__ SolveLds s_solve;
+  __shared__ uint32_t s_ticket;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   int64_t centre_solved = 0;
-  if (solve_prev && blockIdx.x == 0) {
+  // the solver is the first workgroup of the launch to start (ticket 0), whatever the dispatch order
+  bool solver = false;
+  if (solve_prev) {
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(&ws->rate_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    solver = s_ticket == 0u;
+  }
+  if (solver) {
     int kk;
     solve_pass<LAT, TL>(prev, ws->rc_centre, ws, &s_solve, &centre_solved, &kk);
     if (tid == 0)
@@ -426,7 +459,7 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   int64_t centre;
   if (!solve_prev) {
     centre = ws->rc_centre;  // stored by init_kernel
-  } else if (blockIdx.x == 0) {
+  } else if (solver) {
     centre = centre_solved;
   } else {
     const uint64_t w = wait_published(&ws->sync_centre, &ws->status);
@@ -582,9 +615,9 @@ __device__ void write_header(uint8_t* out, uint64_t cap, int lattice, uint32_t d
 // Decoupled look-back (Merrill & Garland, "Single-pass parallel prefix scan with decoupled
 // look-back", 2016) over chunks, run by one wavefront: each round reads the flags of 64
 // predecessors at once, sums the aggregates up to the nearest inclusive prefix, and retries the
-// window while a predecessor there has not published.  Chunk c is workgroup c; workgroups start in
-// index order on each XCD (workgroup i runs on XCD i mod 8), so every predecessor of a running
-// chunk is running or done, and it publishes its aggregate without waiting: every wait ends.  The
+// window while a predecessor there has not published.  Chunk c belongs to the workgroup that took
+// the launch's c-th chunk ticket, so every predecessor of a chunk is running or done, and each
+// publishes its aggregate without waiting on anyone: every wait ends, in any dispatch order.  The
 // wait is still bounded (kSpinLimit rounds); on expiry the status records kErrTimeout.
 // Each flag word carries its own value (flag in bits 62-63; the 64-bit word count in bits 0-33
 // and the padding-bit count in bits 34-61, summed field-wise), so relaxed agent-scope atomics
@@ -654,9 +687,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
   uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
 
+  __shared__ uint32_t s_chunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   Workspace* ws = P.ws;
-  const uint32_t c = blockIdx.x;
+  // chunk ticket: the c-th workgroup to start takes chunk c, so every predecessor of a chunk has
+  // started when the chunk looks back (whatever order the hardware dispatches workgroups in)
+  if (tid == 0) s_chunk = __hip_atomic_fetch_add(&ws->enc_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t step_bits = ws->step_bits;
   const int k = ws->rice_k;
   const float step = __uint_as_float(step_bits);
@@ -671,6 +707,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) s_fixed4[i] = z4;
   for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
   __syncthreads();
+  const uint32_t c = s_chunk;
 
   // alignment padding of the stream (after the index, after the fixed plane) is zero bytes
   if (c == 0) {
@@ -1507,15 +1544,17 @@ __global__ __launch_bounds__(kBlock) void gemv_rows_kernel(const float* __restri
     else HQ_DISPATCH_D(kLatZ, DITHV, DTV, TLV, CALL);                                 \
   } while (0)
 
-hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
+hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode) {
   const uint64_t nflags = (uint64_t)a.chunks + 1;
   const uint32_t nacc = (uint32_t)(kWsRate / sizeof(uint32_t));
   const uint64_t work = nflags > nacc ? nflags : nacc;
   uint64_t blocks = (work + kBlock - 1) / kBlock;
   if (blocks > 1024) blocks = 1024;
-  uint32_t step_bits;
-  int32_t k;
-  if (a.fixed_step_bits) {
+  uint32_t step_bits = 0;
+  int32_t k = 0;
+  if (mode == kInitKeep) {
+    // the kernel takes the workspace's point
+  } else if (a.fixed_step_bits) {
     step_bits = a.fixed_step_bits;
     k = a.rice_k >= 0 ? a.rice_k : kwin_base(a.fixed_step_bits) + 1;
   } else {
@@ -1524,11 +1563,11 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre) {
     k = a.rice_k >= 0 ? a.rice_k : kwin_base(centre) + 1;
   }
   hipLaunchKernelGGL(init_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.ws, lookback_flags(a.ws),
-                     nflags, reinterpret_cast<uint32_t*>(rate_acc(a.ws, 0)), nacc, centre, step_bits, k);
+                     nflags, reinterpret_cast<uint32_t*>(rate_acc(a.ws, 0)), nacc, centre, step_bits, k, mode);
   return hipGetLastError();
 }
 
-static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
+static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass, int final) {
   PassDesc d;
   d.racc = rate_acc(a.ws, pass);
   d.nc = nc;
@@ -1536,6 +1575,7 @@ static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N
   d.fixed_k = a.rice_k;
   d.target = a.target;
   d.N = N;
+  d.final = final;
   return d;
 }
 
@@ -1551,7 +1591,7 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
   const uint32_t blocks = (N + tiles_per_block - 1) / tiles_per_block;
   if (blocks == 0) return hipSuccess;
   const int solve_prev = pass > 0 ? 1 : 0;
-  const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1) : PassDesc{};
+  const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1, 0) : PassDesc{};
 #define HQ_RATE(L, D, T, TL)                                                                           \
   hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
                      rate_acc(a.ws, pass), a.seed, (uint32_t)a.dither, nc, half_log2, a.rice_k, a.target, cpw,      \
@@ -1562,7 +1602,7 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
 }
 
 hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
-  const PassDesc pd = pass_desc(a, nc, half_log2, N, pass);
+  const PassDesc pd = pass_desc(a, nc, half_log2, N, pass, 1);
 #define HQ_SOLVE(L, D, T, TL) hipLaunchKernelGGL((rate_solve_kernel<L, TL>), dim3(1), dim3(64), 0, a.stream, a.ws, pd)
   HQ_DISPATCH(a.lattice, false, 0, a.tile, HQ_SOLVE);
 #undef HQ_SOLVE

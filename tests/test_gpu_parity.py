@@ -328,6 +328,93 @@ def test_async_rate_then_encode_equals_one_call(orc):
     assert_same_stream(host_bytes(b), s_orc)
 
 
+def test_async_rate_then_encode_with_capacity_retry(orc):
+    """An encode at the workspace's operating point (step=-1) into too small a buffer reports
+    CAPACITY with the size needed; the retry at the same point, on the same workspace, succeeds
+    (every encode call resets the workspace's status and offset flags first)."""
+    say("case: rate then encode(step=-1) with a capacity retry")
+    import ctypes
+    w = synth.weight(rows=256)
+    xd = dev(w)
+    s_orc, _ = orc.encode(w, orc.LAT_E8, 3.0)
+    ws = hq.workspace(w.size)
+    hq.hq_rate(xd, "e8", 3.0, ws=ws, blocking=False)
+    small = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    p = hq.make_params("e8", 3.0, step=-1.0)
+    nb = ctypes.c_uint64(0)
+    assert xd.dtype == torch.bfloat16 and xd.numel() == w.size
+    rc = hq.lib().hq_encode(ctypes.c_void_p(xd.data_ptr()), hq.HQ_BF16, w.size, ctypes.byref(p),
+                            ctypes.c_void_p(small.data_ptr()), small.numel(), ctypes.byref(nb), None,
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert rc == hq.HQ_ERR_CAPACITY and nb.value == s_orc.size
+    s_gpu, _ = hq.hq_encode(xd, "e8", 3.0, step=-1.0, ws=ws, out=small)  # the binding retries
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+
+
+def test_repeated_encodes_at_the_workspace_point(orc):
+    """KV-append pattern: the operating point is chosen once (rate control on the first block), then
+    further blocks of different data and sizes are encoded at that point with step=-1 on the same
+    workspace; each stream equals the oracle's at that fixed point."""
+    say("case: repeated step=-1 encodes on one workspace")
+    blocks = [synth.kv(3, 0, heads=1, tokens=t) for t in (4096, 1000, 2500)]
+    seed = synth.kv_seed(3, 0)
+    ws = hq.workspace(max(b.size for b in blocks))
+    first, info = hq.hq_encode(dev(blocks[0]), "e8", 2.0, seed=seed, dither=True, ws=ws)
+    s_orc, info_orc = orc.encode(blocks[0], orc.LAT_E8, 2.0, seed=seed, dither=True)
+    assert_same_stream(host_bytes(first), s_orc)
+    for b in blocks[1:] + blocks[:1]:
+        s_gpu, inf = hq.hq_encode(dev(b), "e8", 2.0, seed=seed, dither=True, step=-1.0, ws=ws)
+        assert inf["step"] == info["step"] and inf["rice_k"] == info["rice_k"]
+        s_o, _ = orc.encode(b, orc.LAT_E8, 0.0, seed=seed, dither=True, step=info["step"], rice_k=info["rice_k"])
+        assert_same_stream(host_bytes(s_gpu), s_o, f"block of {b.size} values")
+
+
+def test_encode_at_workspace_point_without_one_is_rejected():
+    say("case: step=-1 on a workspace with no operating point")
+    x = synth.tiny()
+    ws = torch.zeros(hq.hq_workspace_size(x.size), dtype=torch.uint8, device="cuda")
+    with pytest.raises(hq.HqError) as e:
+        hq.hq_encode(dev(x), "e8", 4.0, step=-1.0, ws=ws)
+    assert e.value.code == hq.HQ_ERR_INVALID_ARG
+    # a decode on that workspace sets no operating point either
+    ok, _ = hq.hq_encode(dev(x), "e8", 4.0)
+    hq.hq_decode(ok, x.size, ws=ws)
+    with pytest.raises(hq.HqError) as e:
+        hq.hq_encode(dev(x), "e8", 4.0, step=-1.0, ws=ws)
+    assert e.value.code == hq.HQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("lattice,dither,step,k", [("e8", False, 0.27, 2), ("e8", True, 1.3, 0),
+                                                   ("d4", True, 0.4, 1), ("a2", False, 0.2, 3),
+                                                   ("z", False, 2.0 ** -6, 6)])
+def test_async_encode_into_exactly_the_bound(orc, lattice, dither, step, k):
+    """An asynchronous encode at a fixed point into a buffer of exactly hq_encode_bound bytes
+    succeeds, and its stream equals the oracle's."""
+    say(f"case: async encode into the bound {lattice} dither={dither}")
+    w = synth.weight(rows=128)
+    cap = hq.hq_encode_bound(w.size, lattice, step, k, dither)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    ws = hq.workspace(w.size)
+    hq.hq_encode(dev(w), lattice, 0.0, seed=2, dither=dither, step=step, rice_k=k, out=out, ws=ws, blocking=False)
+    assert hq.hq_status(ws) == hq.HQ_OK
+    size = hq.header_fields(host_bytes(out[:128]))["total_bytes"]
+    s_orc, _ = orc.encode(w, LAT[lattice], 0.0, seed=2, dither=dither, step=step, rice_k=k)
+    assert size == s_orc.size <= cap
+    assert_same_stream(host_bytes(out[:size]), s_orc)
+
+
+def test_async_encode_sized_by_the_binding(orc):
+    """The binding's asynchronous encode with rate control and no buffer: a blocking rate pass,
+    a buffer of the bound at that point, then the asynchronous encode at the workspace's point."""
+    say("case: async encode sized by the binding")
+    w = synth.weight(rows=300)
+    out, _ = hq.hq_encode(dev(w), "e8", 4.0, blocking=False)
+    torch.cuda.synchronize()
+    size = hq.header_fields(host_bytes(out[:128]))["total_bytes"]
+    s_orc, _ = orc.encode(w, orc.LAT_E8, 4.0)
+    assert_same_stream(host_bytes(out[:size]), s_orc)
+
+
 def test_deterministic_repeat():
     say("case: determinism")
     w = synth.weight(rows=1024)
