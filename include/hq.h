@@ -78,7 +78,8 @@ typedef enum {
   HQ_ERR_CORRUPT = -5,     /* stream fails validation (header, index, segment, terminator count)   */
   HQ_ERR_RATE = -6,        /* target outside [1.125 (E8), 1.5 (A2) or 1.0 (D4, Z), 12] bits / value */
   HQ_ERR_HIP = -7,         /* a HIP runtime call failed                                             */
-  HQ_ERR_TIMEOUT = -8      /* the encoder's cross-workgroup wait exceeded its bound (never expected) */
+  HQ_ERR_TIMEOUT = -8,     /* the encoder's cross-workgroup wait exceeded its bound (never expected) */
+  HQ_ERR_SCRATCH = -9      /* hq_encode_noalloc: n above its static workspace's maximum (2^30 values) */
 } hq_status_code;
 
 typedef enum { HQ_Z = 0, HQ_D4 = 1, HQ_E8 = 2, HQ_A2 = 3 } hq_lattice;
@@ -186,6 +187,21 @@ int hq_rate(const void *x, int32_t dtype, uint64_t n, const hq_params *params, h
 int hq_encode(const void *x, int32_t dtype, uint64_t n, const hq_params *params, void *out,
               uint64_t out_capacity, uint64_t *out_bytes, hq_info *info, void *workspace,
               size_t workspace_bytes, hq_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): hq_encode without a workspace argument.  The workspace
+ * is a static device array of the library, 1,057,024 bytes on each GPU the library runs on, held
+ * until the process ends; it serves n up to 2^30 values (HQ_ERR_SCRATCH above that).  The call
+ * allocates nothing.  Arguments, results and errors are those of hq_encode with the same params
+ * (the same kernels, the same stream bytes); step == -1 takes the operating point of the previous
+ * hq_encode_noalloc on this GPU.  Every call on a GPU shares that GPU's array: each call resets its
+ * status, results and offset flags first, and calls that overlap on one GPU (other streams, other
+ * host threads) race and may corrupt each other's streams.  With out_bytes == NULL the call only
+ * enqueues work; its device-side errors then have no workspace to be read from (the stream
+ * header's total_bytes still gives the size, and a stream is complete when that is at most
+ * out_capacity), so callers that must learn of non-finite input use the blocking form. */
+int hq_encode_noalloc(const void *x, int32_t dtype, uint64_t n, const hq_params *params, void *out,
+                      uint64_t out_capacity, uint64_t *out_bytes, hq_info *info, hq_stream_t stream);
 
 /* Decode a stream of `stream_bytes` bytes into out (n values of out_dtype; bf16 is round to nearest
  * even of the fp32 reconstruction): the exact inverse of components 1-4 of "Methodology: the

@@ -17,13 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhq.so")
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_NONFINITE = 0, -1, -2, -3
-HQ_ERR_CAPACITY, HQ_ERR_CORRUPT, HQ_ERR_RATE, HQ_ERR_HIP, HQ_ERR_TIMEOUT = -4, -5, -6, -7, -8
+HQ_ERR_CAPACITY, HQ_ERR_CORRUPT, HQ_ERR_RATE, HQ_ERR_HIP, HQ_ERR_TIMEOUT, HQ_ERR_SCRATCH = -4, -5, -6, -7, -8, -9
 HQ_Z, HQ_D4, HQ_E8, HQ_A2 = 0, 1, 2, 3
 HQ_F32, HQ_BF16 = 0, 1
 LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8, "a2": HQ_A2}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_encode_bound", "hq_rate",
-           "hq_encode", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
+           "hq_encode", "hq_encode_noalloc", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
            "hq_haar_matrix", "hq_rotate", "hq_srft_encode", "hq_srft_decode")
 
 
@@ -67,6 +67,7 @@ def lib():
         L.hq_encode_bound.argtypes = [u64, P, ctypes.POINTER(u64)]
         L.hq_rate.argtypes = [P, i32, u64, P, P, P, sz, P]
         L.hq_encode.argtypes = [P, i32, u64, P, P, u64, P, P, P, sz, P]
+        L.hq_encode_noalloc.argtypes = [P, i32, u64, P, P, u64, P, P, P]
         L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
         L.hq_status.argtypes = [P, P]
         L.hq_codes.argtypes = [P, i32, u64, P, P, P, P, sz, P]

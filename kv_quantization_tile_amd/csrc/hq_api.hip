@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hq.h"
 #include "hq_internal.h"
 
@@ -215,6 +217,37 @@ uint64_t encode_bound_at(uint64_t n, int lattice, uint32_t tile, double step, in
   return bytes >= 1.8e19 ? UINT64_MAX : (uint64_t)bytes;
 }
 
+// ---- the allocation-free encode: its workspace is a static device array ------------------------
+// Largest n of hq_encode_noalloc, and the array sized for it: the workspace of an encode of that
+// many values (4 KiB of state, 4 KiB of rate counters, one 8-byte offset flag per 8192-value chunk
+// plus one): 1,057,024 bytes per GPU, held until the process ends.
+constexpr uint64_t kNoAllocMaxValues = 1ull << 30;
+constexpr size_t kScratchBytes =
+    kWsHeader + kWsRate + ((8ull * ((kNoAllocMaxValues + 8191) / 8192 + 1) + 255) & ~(uint64_t)255);
+
+// In host code `scratch` names a host-side stand-in, not device memory: kernels and copies take the
+// device address that hipGetSymbolAddress returns for the current device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+int scratch_address(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_address[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return HQ_ERR_HIP;
+    g_scratch_address[dev] = a;
+  }
+  *p = g_scratch_address[dev];
+  return HQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,6 +265,7 @@ const char* hq_strerror(int code) {
     case HQ_ERR_RATE: return "target rate out of range";
     case HQ_ERR_HIP: return "HIP runtime error";
     case HQ_ERR_TIMEOUT: return "cross-workgroup wait exceeded its bound";
+    case HQ_ERR_SCRATCH: return "n exceeds the allocation-free encode's maximum (2^30 values)";
   }
   return "unknown status";
 }
@@ -337,6 +371,16 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
   *out_bytes = r.total_bytes;
   fill_info(info, n, r.step_bits, r.k, r.total_bytes, r.payload_bits);
   return status_from_flags(r.status);
+}
+
+int hq_encode_noalloc(const void* x, int32_t dtype, uint64_t n, const hq_params* params, void* out,
+                      uint64_t out_capacity, uint64_t* out_bytes, hq_info* info, hq_stream_t stream) {
+  const int rc = check_params(params, n);
+  if (rc) return rc;
+  if (n > kNoAllocMaxValues) return HQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != HQ_OK) return HQ_ERR_HIP;
+  return hq_encode(x, dtype, n, params, out, out_capacity, out_bytes, info, ws, kScratchBytes, stream);
 }
 
 int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t out_dtype, uint64_t n,

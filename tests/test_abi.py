@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_codes():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert hq.strerror(code) != "unknown status"
     assert hq.strerror(-99) == "unknown status"
 
@@ -189,3 +189,16 @@ def test_codes_rejects_misaligned_buffers_on_host():
                           ctypes.c_void_p(scales), ws, 8192, None) == hq.HQ_ERR_INVALID_ARG
     assert L.hq_codes(ok, 1, 128, ctypes.byref(p), ok, ok, ctypes.c_void_p((1 << 21) + 64), 8192,
                       None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_sizes_beyond_its_static_workspace_on_host():
+    """hq_encode_noalloc checks n against its static workspace's maximum before any device call."""
+    p = hq.make_params("e8", 4.0)
+    nb = ctypes.c_uint64(0)
+    rc = hq.lib().hq_encode_noalloc(ctypes.c_void_p(1 << 20), hq.HQ_BF16, (1 << 30) + 128, ctypes.byref(p),
+                                    ctypes.c_void_p(1 << 21), 1 << 20, ctypes.byref(nb), None, None)
+    assert rc == hq.HQ_ERR_SCRATCH
+    bad = hq.make_params("e8", 4.0, tile=32)
+    rc = hq.lib().hq_encode_noalloc(ctypes.c_void_p(1 << 20), hq.HQ_BF16, 1024, ctypes.byref(bad),
+                                    ctypes.c_void_p(1 << 21), 1 << 20, ctypes.byref(nb), None, None)
+    assert rc == hq.HQ_ERR_UNSUPPORTED
