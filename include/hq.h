@@ -78,7 +78,7 @@ typedef enum {
   HQ_ERR_CORRUPT = -5,     /* stream fails validation (header, index, segment, terminator count)   */
   HQ_ERR_RATE = -6,        /* target outside [1.125 (E8), 1.5 (A2) or 1.0 (D4, Z), 12] bits / value */
   HQ_ERR_HIP = -7,         /* a HIP runtime call failed                                             */
-  HQ_ERR_TIMEOUT = -8,     /* the encoder's cross-workgroup wait exceeded its bound (never expected) */
+  HQ_ERR_TIMEOUT = -8,     /* reserved: no longer produced (every cross-workgroup wait now ends)   */
   HQ_ERR_SCRATCH = -9      /* hq_encode_noalloc: n above its static workspace's maximum (2^30 values) */
 } hq_status_code;
 

@@ -3,6 +3,7 @@
 // Host side only: argument validation, the order of kernel launches on the caller's stream and
 // the read-back of results.  Every step of the method runs in the kernels of hq_kernels.hip.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -74,6 +75,13 @@ int status_from_flags(uint32_t f) {
 
 size_t workspace_bytes_for(uint64_t n) { return kWsHeader + kWsRate + align256h(8ull * (chunks_of(n) + 1)); }
 
+uint32_t spin_budget() {
+  const char* e = getenv("HQ_SPIN_BUDGET");
+  if (!e || !*e) return kSpinBudget;
+  const unsigned long v = strtoul(e, nullptr, 10);
+  return v > 0xFFFFFFFFul ? 0xFFFFFFFFu : (uint32_t)v;
+}
+
 EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, void* out, uint64_t cap,
                      void* ws, hq_stream_t s) {
   EncodeArgs a;
@@ -93,6 +101,7 @@ EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, v
   a.cap = cap;
   a.ws = static_cast<Workspace*>(ws);
   a.stream = static_cast<hipStream_t>(s);
+  a.spin_budget = spin_budget();
   return a;
 }
 
@@ -135,7 +144,7 @@ int run_rate_control(const EncodeArgs& a, LastPass* last) {
   if (N == 0) return HQ_OK;
   e = launch_rate_pass(a, kRcCand, 21, NA, 0);
   if (e != hipSuccess) return HQ_ERR_HIP;
-  e = launch_rate_pass(a, kRcCandB, 18, N, 1, kRcCand, 21, NA);
+  e = launch_rate_pass(a, kRcCandB, 18, N, 1, kRcCand, 21, NA, initial_centre(a.target));
   if (e != hipSuccess) return HQ_ERR_HIP;
   last->pass = 1;
   last->nc = kRcCandB;
@@ -360,7 +369,7 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
     if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
       return HQ_ERR_HIP;
   } else if (launch_init(a, 0, kInitKeep) != hipSuccess) {
-    // the workspace's operating point is kept; status, results, tickets and look-back flags reset
+    // the workspace's operating point is kept; status, results and look-back flags reset
     return HQ_ERR_HIP;
   }
   if (launch_encode(a) != hipSuccess) return HQ_ERR_HIP;

@@ -54,17 +54,12 @@ struct alignas(256) Workspace {
   uint64_t dec_fixed_off;
   uint64_t dec_unary_off;
   uint64_t dec_words;
-  // pass B's centre, which the workgroup holding pass B's ticket 0 solves from pass A and publishes
-  // to the rest of the launch (bit 63 set = published, the centre in the low 32 bits; relaxed
-  // agent-scope atomics, the value travels in the word itself).  init_kernel clears it.
+  // pass B's centre, which pass B's workgroup 0 solves from pass A and publishes to the rest of the
+  // launch (bit 63 set = published, the centre in the low 32 bits; relaxed agent-scope atomics, the
+  // value travels in the word itself).  init_kernel clears it.
   uint64_t sync_centre;
   // kPointTag while step_bits / rice_k hold a complete operating point
   uint32_t point_tag;
-  // Work tickets, taken with one atomic add per workgroup and reset by init_kernel: the encoder's
-  // chunk index (chunk c is processed by the c-th workgroup to start, so every predecessor of a
-  // chunk is running or done) and pass B's solver election (ticket 0 solves pass A).
-  uint32_t enc_ticket;
-  uint32_t rate_ticket;
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
@@ -88,6 +83,13 @@ inline uint64_t* lookback_flags(void* ws) {
   return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + kWsHeader + kWsRate);
 }
 
+// Spin rounds a cross-workgroup wait makes before the waiting wavefront computes the awaited value
+// itself (a look-back predecessor's aggregate from its input; pass A's solve from its counters).
+// Far above any wait in normal operation; the environment variable HQ_SPIN_BUDGET overrides it (0
+// makes every wait that finds its value missing compute it at once: the tests use that to run the
+// fallback paths).
+constexpr uint32_t kSpinBudget = 256;
+
 struct EncodeArgs {
   const void* x;
   int dtype;
@@ -104,16 +106,18 @@ struct EncodeArgs {
   uint64_t cap;
   Workspace* ws;
   hipStream_t stream;
+  uint32_t spin_budget;
 };
 
 // Modes of the call's first kernel (see init_kernel): the operating point is provisional (rate
 // passes follow), final, or kept from the workspace (an encode with step == -1).
 enum { kInitProvisional = 0, kInitFinal = 1, kInitKeep = 2 };
 hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode);
-// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its first workgroup, with pass 0's
-// candidates (nc0, half_spacing_log2_0, sample0); pass 0 reads the centre init_kernel stored.
+// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its workgroup 0, with pass 0's
+// candidates (nc0, half_spacing_log2_0, sample0) around pass 0's centre centre0; pass 0 reads the
+// centre init_kernel stored.
 hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass,
-                            int nc0 = 0, int half_spacing_log2_0 = 0, uint32_t sample0 = 0);
+                            int nc0 = 0, int half_spacing_log2_0 = 0, uint32_t sample0 = 0, int64_t centre0 = 0);
 // One-workgroup solve of a rate pass into the workspace's step and k (hq_rate's last launch).
 hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass);
 // The encoder, at the operating point the workspace holds.

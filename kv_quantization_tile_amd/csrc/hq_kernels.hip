@@ -22,7 +22,6 @@ constexpr int kFixedWordsMax = 3904;      // 2 F u32 words per chunk; F <= 1952 
 constexpr int kUnaryWinWords = 1024;      // 4 KiB unary staging window = 32768 bits
 constexpr uint32_t kUnaryWinBits = kUnaryWinWords * 32u;
 constexpr uint64_t kFlagAgg = 1ull << 62, kFlagPrefix = 2ull << 62, kValMask = (1ull << 62) - 1;
-constexpr uint32_t kSpinLimit = 1u << 20;
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
 
@@ -208,7 +207,7 @@ __device__ __forceinline__ void octet_symbols(const float* y, float m, float m1,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Resets a call's workspace: status, results, tickets, the look-back flags and the rate counters.
+// Resets a call's workspace: status, results, the look-back flags and the rate counters.
 // mode kInitProvisional / kInitFinal: the operating point becomes (step_bits, k), and the point tag
 // says whether it is complete (kInitFinal) or awaits rate passes (their last solve sets the tag).
 // mode kInitKeep (an encode with step == -1): the operating point already in the workspace is
@@ -242,8 +241,6 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
     ws->res_step_bits = step_bits;
     ws->res_k = k;
     ws->sync_centre = 0;
-    ws->enc_ticket = 0;
-    ws->rate_ticket = 0;
   }
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
   for (uint64_t i = gid; i < nacc; i += (uint64_t)gridDim.x * blockDim.x) acc[i] = 0;
@@ -387,59 +384,88 @@ __device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, So
   *k = L->kres;
 }
 
-// Waits (one lane per wavefront, bounded) until the launch's solver workgroup has published `word`
-// (bit 63 set) and returns it, wave-uniform; 0 after the bound, with kErrTimeout recorded.  The
-// solver is the workgroup that took ticket 0, so it is running before anyone can wait for it, and
-// it publishes without waiting on anyone: the wait ends whatever order workgroups start in.
-__device__ uint64_t wait_published(const uint64_t* word, uint32_t* status) {
-  uint64_t v = 0;
+// One wavefront's own solve of a rate pass (no barriers; the result is the same as solve_pass's:
+// the same counter sums and the same arithmetic), into L, which only this wavefront uses.
+template <int LAT, int TL>
+__device__ int64_t solve_pass_wave(const PassDesc& pd, int64_t centre, SolveLds* L) {
+  const int lane = threadIdx.x & 63;
+  if (lane < kRcCounters) {
+    uint64_t t = 0;
+#pragma unroll
+    for (int sl = 0; sl < kRcAccSlots; ++sl) t += __hip_atomic_load(&pd.racc->cnt[sl][lane], __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT);
+    L->sumq[lane] = t;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < pd.nc) {
+    int64_t b;
+    double R;
+    int kk;
+    rate_candidate<LAT, TL>(L->sumq, centre, lane, pd.nc, pd.half_log2, pd.fixed_k, pd.N, &b, &R, &kk);
+    L->b[lane] = b;
+    L->R[lane] = R;
+    L->k[lane] = kk;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int64_t xb = 0;
+  int kres;
+  if (lane == 0) rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, TL, &xb, &kres);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)xb);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)xb >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The centre that workgroup 0 of this launch solves from the previous pass and publishes in `word`
+// (bit 63 set, the centre in the low 32 bits).  One lane per wavefront polls; after `budget` spin
+// rounds without it, the wavefront solves the previous pass itself (solve_pass_wave: the same
+// value), so the wait ends whatever order workgroups are started in.  Wave-uniform result.
+template <int LAT, int TL>
+__device__ int64_t wait_centre(const uint64_t* word, uint32_t budget, const PassDesc& prev, int64_t centre0,
+                               SolveLds* L) {
+  uint32_t got = 0, val = 0;
   if ((threadIdx.x & 63) == 0) {
-    uint32_t spins = 0;
-    while (true) {
-      v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (v >> 63) break;
-      if (++spins > kSpinLimit) {
-        atomicOr(status, (uint32_t)kErrTimeout);
-        v = 0;
+    for (uint32_t spins = 0;; ++spins) {
+      const uint64_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v >> 63) {
+        got = 1;
+        val = (uint32_t)v;
         break;
       }
+      if (spins >= budget) break;
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
+  if (__builtin_amdgcn_readfirstlane(got)) return (int64_t)__builtin_amdgcn_readfirstlane(val);
+  return solve_pass_wave<LAT, TL>(prev, centre0, L);
 }
 
 // A wavefront takes TPW sample tiles and cpw of the pass's candidates; the cw = ceil(nc / cpw)
 // wavefronts that share a group of TPW tiles sit in the same workgroup, which therefore holds 4 / cw
 // tile groups (cw is 1, 2 or 4).  Splitting the candidates over wavefronts keeps each wavefront's
 // chain short and the pass latency low; every wavefront repeats its tiles' transform.
-// With solve_prev, the workgroup that takes ticket 0 first solves the previous pass (prev) for this
-// pass's centre and publishes it in Workspace::sync_centre; the other workgroups transform their
-// tiles meanwhile and then wait for it.
+// With solve_prev, workgroup 0 first solves the previous pass (prev, centre0) for this pass's
+// centre and publishes it in Workspace::sync_centre; the other workgroups transform their tiles
+// meanwhile and then wait for it (or, after spin_budget rounds, solve it themselves).
 template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
                                                       Workspace* ws, RateAcc* racc, uint64_t seed, uint32_t df,
                                                       int nc, int half_log2, int fixed_k, float target, int cpw,
-                                                      int solve_prev, PassDesc prev) {
+                                                      int solve_prev, PassDesc prev, int64_t centre0,
+                                                      uint32_t spin_budget) {
   constexpr int LPT = Tiling<TL>::LPT, TPW = Tiling<TL>::TPW;
   __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
   __shared__ SolveLds s_solve;
-  __shared__ uint32_t s_ticket;
+  __shared__ SolveLds s_fallback[kBlock / 64];  // one per wavefront, for wait_centre's own solve
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   int64_t centre_solved = 0;
-  // the solver is the first workgroup of the launch to start (ticket 0), whatever the dispatch order
-  bool solver = false;
-  if (solve_prev) {
-    if (tid == 0)
-      s_ticket = __hip_atomic_fetch_add(&ws->rate_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    solver = s_ticket == 0u;
-  }
+  const bool solver = solve_prev && blockIdx.x == 0;
   if (solver) {
     int kk;
-    solve_pass<LAT, TL>(prev, ws->rc_centre, ws, &s_solve, &centre_solved, &kk);
+    solve_pass<LAT, TL>(prev, centre0, ws, &s_solve, &centre_solved, &kk);
     if (tid == 0)
       __hip_atomic_store(&ws->sync_centre, (1ull << 63) | (uint64_t)(uint32_t)centre_solved, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -462,8 +488,7 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x
   } else if (solver) {
     centre = centre_solved;
   } else {
-    const uint64_t w = wait_published(&ws->sync_centre, &ws->status);
-    centre = (w >> 63) ? (int64_t)(uint32_t)w : ws->rc_centre;
+    centre = wait_centre<LAT, TL>(&ws->sync_centre, spin_budget, prev, centre0, &s_fallback[wave]);
   }
   // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots, or,
   // with 8 lanes per tile, every lane both); the group shares them by broadcast
@@ -559,6 +584,9 @@ __device__ __forceinline__ void round_symbols(const void* x, uint64_t T, uint64_
                                               uint32_t* sym) {
   using TI = Tiling<TL>;
   const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
+  // the sign masks are rebuilt here (the asm hides that they equal the caller's), so that callers
+  // do not keep their own eight masks alive for this rarely taken path
+  __asm__ volatile("" : "+v"(sgn));
   uint32_t smask[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
@@ -615,14 +643,16 @@ __device__ void write_header(uint8_t* out, uint64_t cap, int lattice, uint32_t d
 // Decoupled look-back (Merrill & Garland, "Single-pass parallel prefix scan with decoupled
 // look-back", 2016) over chunks, run by one wavefront: each round reads the flags of 64
 // predecessors at once, sums the aggregates up to the nearest inclusive prefix, and retries the
-// window while a predecessor there has not published.  Chunk c belongs to the workgroup that took
-// the launch's c-th chunk ticket, so every predecessor of a chunk is running or done, and each
-// publishes its aggregate without waiting on anyone: every wait ends, in any dispatch order.  The
-// wait is still bounded (kSpinLimit rounds); on expiry the status records kErrTimeout.
-// Each flag word carries its own value (flag in bits 62-63; the 64-bit word count in bits 0-33
-// and the padding-bit count in bits 34-61, summed field-wise), so relaxed agent-scope atomics
-// suffice and no cache write-back or invalidation is needed.
-__device__ uint64_t lookback_wave(uint64_t* flags, uint32_t c, uint64_t agg, uint32_t* status) {
+// window while a predecessor there has not published.  Chunk c is workgroup c.  A predecessor that
+// has not published after `budget` spin rounds has its aggregate computed here from its input
+// (agg_of, the whole wavefront: the same value its own workgroup will publish), so every wait ends
+// whether or not the hardware has started that workgroup: forward progress does not depend on
+// the order workgroups are dispatched in.  Each flag word carries its own value (flag in bits
+// 62-63; the 64-bit word count in bits 0-33 and the padding-bit count in bits 34-61, summed
+// field-wise), so relaxed agent-scope atomics suffice and no cache write-back or invalidation is
+// needed.
+template <class AggOf>
+__device__ uint64_t lookback_wave(uint64_t* flags, uint32_t c, uint64_t agg, uint32_t budget, AggOf agg_of) {
   const int lane = threadIdx.x & 63;
   if (c == 0) {
     if (lane == 0) __hip_atomic_store(&flags[0], kFlagPrefix | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -634,20 +664,27 @@ __device__ uint64_t lookback_wave(uint64_t* flags, uint32_t c, uint64_t agg, uin
   uint32_t spins = 0;
   while (true) {
     const int64_t j = base - lane;
-    const uint64_t sv = j >= 0 ? __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : kFlagPrefix;
+    uint64_t sv = j >= 0 ? __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : kFlagPrefix;
     const uint64_t f = sv & ~kValMask;
     const uint64_t pmask = __ballot(f == kFlagPrefix);
     const uint64_t zmask = __ballot(f == 0);
     const int first_p = pmask ? __ffsll((unsigned long long)pmask) - 1 : 64;
     const uint64_t need = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
-    if (zmask & need) {
-      if (++spins > kSpinLimit) {
-        if (lane == 0) atomicOr(status, (uint32_t)kErrTimeout);
-        break;
+    uint64_t miss = zmask & need;
+    if (miss) {
+      if (spins++ < budget) {
+        __builtin_amdgcn_s_sleep(1);
+        continue;
       }
-      __builtin_amdgcn_s_sleep(1);
-      continue;
+      // fallback: the missing aggregates of this window, computed from the predecessors' input
+      while (miss) {
+        const int l = __ffsll((unsigned long long)miss) - 1;
+        miss &= miss - 1;
+        const uint64_t a = agg_of((uint32_t)(base - l));
+        if (lane == l) sv = kFlagAgg | a;
+      }
+      spins = 0;
     }
     uint64_t v = lane <= first_p ? (sv & kValMask) : 0ull;
 #pragma unroll
@@ -664,6 +701,34 @@ __device__ uint64_t lookback_wave(uint64_t* flags, uint32_t c, uint64_t agg, uin
 constexpr int kPadShift = 34;
 constexpr uint64_t kWordsMask = (1ull << kPadShift) - 1;
 
+// Look-back aggregate of chunk p (64-bit words of its unary segment, and its padding bits) computed
+// by one wavefront from the chunk's input: the unary bits of its 4 x 4 (wavefront, round) tile
+// groups, each recomputed by round_symbols.  Every lane of the wavefront calls it together.
+template <int LAT, bool DITHER, int DT, int TL>
+__device__ __forceinline__ uint64_t chunk_aggregate(const void* x, uint64_t T, uint64_t seed, uint32_t df,
+                                                                uint32_t p, int k, uint32_t step_bits, uint32_t sgn,
+                                                                uint32_t lane_neg) {
+  using TI = Tiling<TL>;
+  const int lane = threadIdx.x & 63, o = lane % TI::LPT, tw = lane / TI::LPT;
+  const float step = __uint_as_float(step_bits);
+  uint32_t bits = 0;
+#pragma unroll 1
+  for (int g = 0; g < 16; ++g) {
+    const int gw = g >> 2, gr = g & 3;
+    uint32_t sy[8];
+    round_symbols<LAT, DITHER, DT, TL>(x, T, seed, df, p, gr, gw, tw, o, sgn, lane_neg, step, sy);
+    const uint64_t t = (uint64_t)p * TI::CT + (uint32_t)TI::TPR * gr + (uint32_t)TI::TPW * gw + tw;
+    if (t < T) {
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) bits += (sy[sl] >> slot_width<LAT>(sl, k)) + 1u;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) bits += __shfl_xor(bits, m, 64);
+  const uint64_t w = (bits + 63u) / 64u;
+  return w | ((64ull * w - bits) << kPadShift);
+}
+
 struct EncParams {
   const void* x;
   uint64_t n, T;
@@ -674,25 +739,27 @@ struct EncParams {
   uint64_t cap;
   Workspace* ws;
   uint64_t* flags;
+  uint32_t spin_budget;
 };
 
+// Occupancy: six waves per SIMD without dither, four with it (the register budgets the hot path
+// fits in); the look-back's rare fallback must fit the same budget.
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ? 4 : 6))) void encode_kernel(
+    EncParams P) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
   __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
   __shared__ uint4 s_unary4[kUnaryWinWords / 4];
   __shared__ uint4 s_wtot4[4];  // per round, the four wavefronts' Rice-length totals
+  __shared__ uint32_t s_off[4][kBlock];  // unary offsets of rounds written terminator by terminator
   __shared__ uint64_t s_prefix;
   uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
   uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
 
-  __shared__ uint32_t s_chunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   Workspace* ws = P.ws;
-  // chunk ticket: the c-th workgroup to start takes chunk c, so every predecessor of a chunk has
-  // started when the chunk looks back (whatever order the hardware dispatches workgroups in)
-  if (tid == 0) s_chunk = __hip_atomic_fetch_add(&ws->enc_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t c = blockIdx.x;
   const uint32_t step_bits = ws->step_bits;
   const int k = ws->rice_k;
   const float step = __uint_as_float(step_bits);
@@ -707,7 +774,6 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
   for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) s_fixed4[i] = z4;
   for (uint32_t i = tid; i < kUnaryWinWords / 4; i += kBlock) s_unary4[i] = z4;
   __syncthreads();
-  const uint32_t c = s_chunk;
 
   // alignment padding of the stream (after the index, after the fixed plane) is zero bytes
   if (c == 0) {
@@ -884,9 +950,39 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
     B += (t4.x + t4.y) + (t4.z + t4.w);
   }
   const uint64_t W = (B + 63u) / 64u;
+
+  // unary segment, staged through LDS in windows of kUnaryWinBits.  Common case: the segment fits
+  // one window and each octet's code (at most 32 bits) is ORed in as one pattern, now: its position
+  // inside the chunk does not depend on the chunk's prefix.  Otherwise the symbols of the rounds
+  // concerned are computed again after the look-back and written terminator by terminator; those
+  // rounds' offsets wait in LDS (nothing of a round stays in registers across the look-back).
+  const bool multi = B > kUnaryWinBits;
+  if (!multi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t p0 = off[r];
+      if (L[r] != 0u && L[r] <= 32u) {
+        const uint32_t sh = p0 & 31u;
+        atomicOr(&s_unary[p0 >> 5], pat[r] << sh);
+        if (sh + L[r] > 32u) atomicOr(&s_unary[(p0 >> 5) + 1], __builtin_amdgcn_alignbit(0u, pat[r], 32u - sh));
+      }
+    }
+  }
+  uint32_t slow = 0;  // rounds (bit r) in which some lane of this wavefront writes terminators
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (__ballot(multi ? L[r] != 0u : L[r] > 32u)) {
+      slow |= 1u << r;
+      s_off[r][tid] = off[r];
+    }
+
   if (wave == 0) {
     const uint64_t agg = W | ((64ull * W - B) << kPadShift);
-    const uint64_t ex = lookback_wave(P.flags, c, agg, &ws->status);
+    // the look-back's fallback: a predecessor's aggregate computed by this wavefront
+    auto agg_of = [&](uint32_t p) -> uint64_t {
+      return chunk_aggregate<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, P.dflags, p, k, step_bits, sgn, lane_neg);
+    };
+    const uint64_t ex = lookback_wave(P.flags, c, agg, P.spin_budget, agg_of);
     if (lane == 0) s_prefix = ex;
   }
   __syncthreads();
@@ -911,28 +1007,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
       atomicOr(&ws->status, (uint32_t)kErrCapacity);
   }
 
-  // unary segment, staged through LDS in windows of kUnaryWinBits.  Common case: the segment fits
-  // one window and each octet's code (at most 32 bits) is ORed in as one pattern.  Otherwise the
-  // symbols of the rounds concerned are computed again and written terminator by terminator.
   const uint64_t ubase = unary_off + 8ull * prefix;
   const bool fits = ubase + 8ull * W <= P.cap;
   const uint32_t seg_words = (uint32_t)(2u * W);
-  const bool multi = B > kUnaryWinBits;
-  if (!multi) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t p0 = off[r];
-      if (L[r] != 0u && L[r] <= 32u) {
-        const uint32_t sh = p0 & 31u;
-        atomicOr(&s_unary[p0 >> 5], pat[r] << sh);
-        if (sh + L[r] > 32u) atomicOr(&s_unary[(p0 >> 5) + 1], __builtin_amdgcn_alignbit(0u, pat[r], 32u - sh));
-      }
-    }
-  }
-  uint32_t slow = 0;  // rounds (bit r) in which some lane of this wavefront writes terminators
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (__ballot(multi ? L[r] != 0u : L[r] > 32u)) slow |= 1u << r;
   for (uint32_t wb = 0; wb < B; wb += kUnaryWinBits) {
     if (wb) {
       __syncthreads();
@@ -942,10 +1019,14 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncParams P) {
 #pragma unroll 1
     for (int r = 0; r < 4; ++r) {
       if (!((slow >> r) & 1u)) continue;  // uniform in the wavefront
-      const uint32_t Lr = r == 0 ? L[0] : r == 1 ? L[1] : r == 2 ? L[2] : L[3];
-      const uint32_t offr = r == 0 ? off[0] : r == 1 ? off[1] : r == 2 ? off[2] : off[3];
+      const uint32_t offr = s_off[r][tid];
       uint32_t sy[8];
       round_symbols<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, P.dflags, c, r, wave, tw, o, sgn, lane_neg, step, sy);
+      // the octet's unary length again, from the recomputed symbols (0 past the last tile)
+      uint32_t Lr = 0;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) Lr += (sy[sl] >> slot_width<LAT>(sl, k)) + 1u;
+      if ((uint64_t)c * TI::CT + (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw >= P.T) Lr = 0;
       if (multi ? Lr != 0u : Lr > 32u) {
         uint32_t p = offr;
 #pragma unroll
@@ -1580,7 +1661,7 @@ static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N
 }
 
 hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass, int nc0,
-                            int half_log2_0, uint32_t N0) {
+                            int half_log2_0, uint32_t N0, int64_t centre0) {
   // pass A (8 candidates, a small sample): two candidates per wavefront, so that the pass is not
   // one long chain per wavefront; otherwise every wavefront takes all candidates of its tiles
   const int cpw = nc == kRcCand ? 2 : nc;
@@ -1595,7 +1676,7 @@ hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t
 #define HQ_RATE(L, D, T, TL)                                                                           \
   hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
                      rate_acc(a.ws, pass), a.seed, (uint32_t)a.dither, nc, half_log2, a.rice_k, a.target, cpw,      \
-                     solve_prev, prev)
+                     solve_prev, prev, centre0, a.spin_budget)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_RATE);
 #undef HQ_RATE
   return hipGetLastError();
@@ -1621,6 +1702,7 @@ hipError_t launch_encode(const EncodeArgs& a) {
   P.cap = a.cap;
   P.ws = a.ws;
   P.flags = lookback_flags(a.ws);
+  P.spin_budget = a.spin_budget;
   const uint32_t blocks = a.chunks ? a.chunks : 1u;
 #define HQ_ENC(L, D, T, TL) \
   hipLaunchKernelGGL((encode_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, P)

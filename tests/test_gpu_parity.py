@@ -415,6 +415,32 @@ def test_async_encode_sized_by_the_binding(orc):
     assert_same_stream(host_bytes(out[:size]), s_orc)
 
 
+@pytest.mark.parametrize("case", ["weight_full", "kv_dither", "tiles64", "tiles256"])
+def test_wait_fallbacks_give_the_same_streams(orc, monkeypatch, case):
+    """Forward progress does not rest on the order workgroups start in: a look-back wait that
+    outlasts its spin budget computes the missing predecessor's aggregate from its input, and a
+    pass-B wavefront that does not see pass A's solve published solves it itself.  A budget of 0
+    (set from the host) makes every wait that finds its value missing take that path at once; the
+    streams must be unchanged."""
+    say(f"case: wait fallbacks forced ({case})")
+    monkeypatch.setenv("HQ_SPIN_BUDGET", "0")
+    if case == "weight_full":
+        x, lat, tb, seed, dither, tile = synth.weight(), "e8", 4.0, 0, False, 128
+    elif case == "kv_dither":
+        x, lat, tb, seed, dither, tile = synth.kv(2, 1, heads=2), "e8", 2.0, synth.kv_seed(2, 1), True, 128
+    elif case == "tiles64":
+        x, lat, tb, seed, dither, tile = synth.weight(rows=700), "d4", 3.0, 1, True, 64
+    else:
+        x, lat, tb, seed, dither, tile = synth.weight(rows=700), "a2", 3.0, 1, False, 256
+    s_gpu, info = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile)
+    s_orc, info_orc = orc.encode(x, LAT[lat], tb, seed=seed, dither=dither, tile=tile)
+    assert info["step"] == info_orc["step"] and info["rice_k"] == info_orc["k"]
+    assert_same_stream(host_bytes(s_gpu), s_orc, case)
+    monkeypatch.delenv("HQ_SPIN_BUDGET")
+    s_again, _ = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile)
+    assert torch.equal(s_again, s_gpu)
+
+
 def test_deterministic_repeat():
     say("case: determinism")
     w = synth.weight(rows=1024)
