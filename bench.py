@@ -3,11 +3,13 @@
 A step is one pass of the whole path over the workload: rate control (two sample passes), encode
 (RHT, lattice, strip, Rice, look-back scan, packing) and decode (unpack, inverse RHT, bf16 store).
 The default workload is the 14336 x 4096 bf16 MLP-weight tensor, E8 at 4 bits per value, no dither;
---config kv times one (layer, K) call of the KV cache, [8][32768][128] bf16, E8 + dither at 2 bps.
+the default run also times one (layer, K) call of the KV cache, [8][32768][128] bf16, E8 + dither at
+2 bps, reported under extra.kv (--config kv makes that call the headline).
 
 Printed: one JSON line.  value = bf16 input bytes / (encode + decode time), GB/s; roofline: the
 dominant kernel's algorithmic bytes per launch over its event-timed duration, against MI355X's
-8 TB/s HBM peak; cpu_baseline: the CPU oracle on the same tensor, one host thread.
+8 TB/s HBM peak; cpu_baseline: the CPU oracle on the same tensor on all host threads (and on one);
+extra.parity: the run's stream, decode and integer codes against the oracle's.
 """
 from __future__ import annotations
 
@@ -48,6 +50,8 @@ def parse():
     ap.add_argument("--streams", type=int, default=3,
                     help="model / kv_all: streams the resident tensors are issued on, round-robin")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv", action="store_true",
+                    help="default run: skip the second workload (one KV call) timed beside the weight")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 256 MiB (known traffic), for scaling "
@@ -647,6 +651,239 @@ def srft_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def measure(hq, torch, x_host, cfg, seed, K, W):
+    """Times K steps (after W warm-up steps) of one workload and breaks the step down.  Returns the
+    parts of the JSON line: value, ms_per_step, config additions, roofline and extra, plus the
+    device buffers the parity report reads."""
+    profile_stem = cfg.pop("profile")
+    n = x_host.size
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(x_host.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
+    lat, tb, dither = cfg["lattice"], cfg["target_bps"], cfg["dither"]
+
+    # one blocking encode gives the operating point; the output buffer is the worst-case bound there
+    s_ref, info = hq.hq_encode(x, lat, tb, seed=seed, dither=dither)
+    cap = hq.hq_encode_bound(n, lat, info["step"], info["rice_k"], dither)
+    del s_ref
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    ws = hq.workspace(n, dev)
+    ws_dec = hq.workspace(0, dev)
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # one step = hq_encode with rate control (init, two sample passes, the solve, the encode kernel)
+    # and hq_decode (header check, decode kernel)
+    def encode():
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
+
+    def decode():
+        hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
+
+    # the encode kernel alone, for its roofline: an asynchronous hq_rate leaves the operating point
+    # in the workspace, and hq_encode at that point (step=-1) launches the reset and the encode kernel
+    def rate():
+        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
+
+    def encode_at_point():
+        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
+
+    for _ in range(W):
+        encode(); decode()
+        rate(); encode_at_point()
+    torch.cuda.synchronize()
+
+    # the timed region: K steps back to back, events only at its two ends (an event recorded
+    # between two kernels delays the second by several microseconds)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(K):
+        encode()
+        decode()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = t_start.elapsed_time(t_end) / K
+    st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
+    assert st == 0 and st2 == 0, (st, st2)
+    g_step = out[:128].clone()
+
+    # breakdown (separate loops): encode with rate control, decode; rate control, the encode kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        encode()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    enc_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    dec_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    ek = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ek[i][0].record(stream)
+        rate()
+        ek[i][1].record(stream)
+        encode_at_point()
+        ek[i][2].record(stream)
+    torch.cuda.synchronize()
+    assert hq.hq_status(ws) == 0
+    rate_ms = float(np.mean([ek[i][0].elapsed_time(ek[i][1]) for i in range(K)]))
+    enc_kernel_ms = float(np.mean([ek[i][1].elapsed_time(ek[i][2]) for i in range(K)]))
+    assert torch.equal(out[:128], g_step), "hq_rate + hq_encode(step=-1) differs from hq_encode"
+
+    hdr = hq.header_fields(out[:128].cpu().numpy())
+    total_bytes = hdr["total_bytes"]
+    input_bytes = 2 * n
+    value = input_bytes / (step_ms * 1e-3) / 1e9
+    # algorithmic bytes: encode reads the input and writes the stream; decode reads the stream and
+    # writes bf16 values
+    alg_step = 2 * (input_bytes + total_bytes)
+    # dominant kernel: encode_kernel (timed with its one-lane reset launch) or decode_kernel (timed
+    # with its one-lane header check launch); both figures are therefore slightly conservative
+    dec_alg = total_bytes + input_bytes
+    enc_alg = input_bytes + total_bytes
+    if dec_ms >= enc_kernel_ms:
+        dom, dom_ms, dom_bytes = "decode_kernel", dec_ms, dec_alg
+    else:
+        dom, dom_ms, dom_bytes = "encode_kernel", enc_kernel_ms, enc_alg
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = profiled_traffic(profile_stem, dom)
+    # the kernel's binding resource is the vector ALU: its measured VALU instructions (64 lanes
+    # each) over the same launch time, against 256 CUs x 64 lanes x 2.4 GHz
+    valu = profiled_valu(profile_stem, dom)
+    valu_issue = None
+    if valu is not None:
+        tops = valu * 64 / (dom_ms * 1e-3) / 1e12
+        valu_issue = {"achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-ops/s",
+                      "frac": round(tops / VALU_PEAK_TOPS, 4), "lane_ops_per_value": round(valu * 64 / n, 2),
+                      "source": "SQ_INSTS_VALU per dispatch x 64, from the committed counter summary"}
+    r = {
+        "value": value, "ms_per_step": step_ms,
+        "config": {**cfg, "n_values": n, "stream_bytes": total_bytes,
+                   "payload_bps": round(hdr["payload_bits"] / n, 5),
+                   "side_bps": round((8 * total_bytes - hdr["payload_bits"]) / n, 5),
+                   "total_bps": round(8 * total_bytes / n, 5),
+                   "step": float(np.array([hdr["step_bits"]], dtype=np.uint32).view(np.float32)[0]),
+                   "rice_k": hdr["k"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                     "alg_bytes_per_launch": dom_bytes, "launch_ms": round(dom_ms, 5), "valu_issue": valu_issue},
+        "extra": {"encode_with_rate_control_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5),
+                  "encode_kernel_ms": round(enc_kernel_ms, 5), "hq_rate_alone_ms": round(rate_ms, 5),
+                  "encode_kernel_gbs": round(enc_alg / (enc_kernel_ms * 1e-3) / 1e9, 1),
+                  "decode_kernel_gbs": round(dec_alg / (dec_ms * 1e-3) / 1e9, 1),
+                  "step_alg_bytes": alg_step,
+                  "step_hbm_gbs": round(alg_step / (step_ms * 1e-3) / 1e9, 1),
+                  "step_hbm_frac": round(alg_step / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "host_wall_ms_per_step": round(wall / K * 1e3, 5)},
+        "_dev": dict(x=x, out=out, y=y, total_bytes=total_bytes, step=float(info["step"]), k=int(info["rice_k"])),
+    }
+    return r
+
+
+def parity_report(hq, torch, oracle, x_host, cfg, seed, dev_bufs):
+    """The GPU results of the timed run against the oracle on the same tensor: stream bytes, decoded
+    bf16 values, integer lattice codes (mismatching octets, and how many of them lie within 1e-5 of
+    a Voronoi boundary), and the largest per-tile relative error of the fp32 decode,
+    max_i |x_gpu - x_oracle| / max_i |x_oracle|.  Returns the report and the oracle's timings."""
+    lat, tb, dither = cfg["lattice"], cfg["target_bps"], cfg["dither"]
+    n = x_host.size
+    L = oracle.LATTICES[lat]
+    t1 = time.perf_counter()
+    s_orc, info_orc = oracle.encode(x_host, L, tb, seed=seed, dither=dither)
+    t2 = time.perf_counter()
+    y_orc_b = oracle.decode(s_orc, n, out_dtype="bf16")
+    t3 = time.perf_counter()
+    g = dev_bufs["out"][:dev_bufs["total_bytes"]].cpu().numpy()
+    rep = {"stream_bytes_equal": bool(g.size == s_orc.size and np.array_equal(g, s_orc)),
+           "decoded_bf16_equal": bool(np.array_equal(
+               dev_bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16), y_orc_b)),
+           "step_and_k_equal": bool(info_orc["step"] == dev_bufs["step"] and info_orc["k"] == dev_bufs["k"])}
+    # integer codes at the operating point
+    step = dev_bufs["step"]
+    c_orc, sc_orc = oracle.quantize(x_host, L, step, seed=seed, dither=dither)
+    c_gpu, sc_gpu = hq.hq_codes(dev_bufs["x"], step, lat, seed=seed, dither=dither)
+    c_gpu = c_gpu.cpu().numpy()
+    bad = np.nonzero((c_gpu.reshape(-1, 8) != c_orc.reshape(-1, 8)).any(axis=1))[0]
+    attributed = 0
+    if bad.size:
+        v = oracle.lattice_inputs(x_host, L, step, seed, dither).reshape(-1, 8).astype(np.float64)
+        half = 0.5 if lat in ("e8", "a2") else 1.0
+        wm = np.tile([1.0, 3.0], 4) if lat == "a2" else np.ones(8)
+        for i in bad[:100000]:
+            cg, co = c_gpu.reshape(-1, 8)[i] * half, c_orc.reshape(-1, 8)[i] * half
+            dist = abs((wm * (v[i] - cg) ** 2).sum() - (wm * (v[i] - co) ** 2).sum()) / (
+                2 * np.sqrt((wm * (cg - co) ** 2).sum()))
+            attributed += int(dist <= 1e-5)
+    rep["octets"] = int(n // 8)
+    rep["code_mismatch_octets"] = int(bad.size)
+    rep["code_mismatch_boundary_attributed"] = attributed
+    rep["scales_equal"] = bool(np.array_equal(sc_gpu.cpu().numpy().view(np.uint16), sc_orc))
+    # fp32 decode, per-tile relative error
+    y32 = hq.hq_decode(dev_bufs["out"][:dev_bufs["total_bytes"]], n, out_dtype=torch.float32).cpu().numpy()
+    y_orc = oracle.decode(s_orc, n).reshape(-1, 128)
+    err = np.abs(y32.reshape(-1, 128).astype(np.float64) - y_orc).max(axis=1)
+    mag = np.abs(y_orc).max(axis=1).astype(np.float64)
+    rel = np.where(mag > 0, err / np.where(mag > 0, mag, 1.0), np.where(err > 0, np.inf, 0.0))
+    rep["max_tile_rel_decode_err_f32"] = float(rel.max())
+    rep["payload_bps_error"] = round(abs(info_orc["payload_bps"] - tb), 5)
+    return rep, {"encode_s": t2 - t1, "decode_s": t3 - t2, "stream": s_orc, "info": info_orc}
+
+
+def host_threads() -> int:
+    """The host CPUs this process may use (its affinity mask), at most 16: the CPU share of one GPU
+    on the machines this runs on."""
+    try:
+        c = len(os.sched_getaffinity(0))
+    except AttributeError:
+        c = os.cpu_count() or 1
+    return max(1, min(c, 16))
+
+
+def cpu_baseline_all_cores(oracle, x_host, cfg, seed, orc_times, threads):
+    """The oracle, unchanged and single-threaded per call, on all host threads: rate control once on
+    the whole tensor, then the tensor split into `threads` slices of whole 8192-value chunks, each
+    encoded (at the operating point rate control chose) and decoded to bf16 by one thread (ctypes
+    releases the interpreter lock during the oracle's C calls, and the oracle holds no global
+    state).  Repeated until about 2 s of wall time (at most 8 times)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lat, tb, dither = cfg["lattice"], cfg["target_bps"], cfg["dither"]
+    L = oracle.LATTICES[lat]
+    flat = x_host.reshape(-1)
+    n = flat.size
+    chunks = (n + 8191) // 8192
+    bounds = [min(n, (chunks * i // threads) * 8192) for i in range(threads + 1)]
+    slices = [flat[bounds[i]:bounds[i + 1]] for i in range(threads) if bounds[i + 1] > bounds[i]]
+
+    def work(part, step, k):
+        s, _ = oracle.encode(part, L, 0.0, seed=seed, dither=dither, step=step, rice_k=k)
+        oracle.decode(s, part.size, out_dtype="bf16")
+        return part.size
+
+    reps, wall = 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        while True:
+            t0 = time.perf_counter()
+            step, _, k = oracle.rate(x_host, L, tb, seed=seed, dither=dither)
+            done = sum(pool.map(lambda p: work(p, step, k), slices))
+            wall += time.perf_counter() - t0
+            reps += 1
+            assert done == n
+            if wall >= 2.0 or reps >= 8:
+                break
+    one = 2 * n / (orc_times["encode_s"] + orc_times["decode_s"]) / 1e9
+    return {"value": round(reps * 2 * n / wall / 1e9, 4), "unit": "GB/s", "cores": len(slices), "kind": "oracle",
+            "sample": f"the whole workload ({n} values), {reps} times: the oracle's rate control on one thread, "
+                      f"then {len(slices)} slices of whole 8192-value chunks encoded at that operating point and "
+                      f"decoded to bf16, one slice per host thread; mean wall {wall / reps:.3f} s per pass",
+            "one_thread_gbs": round(one, 4),
+            "one_thread_sample": f"one encode with rate control ({orc_times['encode_s']:.2f} s) and one bf16 decode "
+                                 f"({orc_times['decode_s']:.2f} s) of the whole workload on one thread",
+            "cpu": cpu_model(), "host_cpus_visible": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -672,177 +909,59 @@ def main():
 
     import kv_quantization_tile_amd as hq
 
+    # the headline workload (the weight by default), and, in the default run, one KV call beside it
     x_host, cfg, seed = workload(args.config, args.bps, args.dither_flags)
-    profile_stem = cfg.pop("profile")
-    n = x_host.size
-    dev = torch.device("cuda:0")
-    x = torch.from_numpy(x_host.reshape(-1).view(np.int16)).view(torch.bfloat16).to(dev)
-    lat, tb, dither = cfg["lattice"], cfg["target_bps"], cfg["dither"]
-
-    # one blocking encode sizes the buffers and gives the operating point
-    s_ref, info = hq.hq_encode(x, lat, tb, seed=seed, dither=dither)
-    cap = int(s_ref.numel() * 1.05) + 65536
-    out = torch.empty(cap, dtype=torch.uint8, device=dev)
-    ws = hq.workspace(n, dev)
-    ws_dec = hq.workspace(0, dev)
-    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-
-    # one step = hq_encode with rate control (two sample passes, then the encode kernel, whose
-    # workgroup 0 solves the second pass) and hq_decode
-    def encode():
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, out=out, ws=ws, blocking=False)
-
-    def decode():
-        hq.hq_decode(out, n, out=y, ws=ws_dec, check=False)
-
-    # the encode kernel alone, for its roofline: an asynchronous hq_rate leaves the operating point
-    # (its passes and a one-workgroup solve), and hq_encode at that point launches only the kernel
-    def rate():
-        hq.hq_rate(x, lat, tb, seed=seed, dither=dither, ws=ws, blocking=False)
-
-    def encode_at_point():
-        hq.hq_encode(x, lat, tb, seed=seed, dither=dither, step=-1.0, out=out, ws=ws, blocking=False)
-
-    for _ in range(args.warmup):
-        encode(); decode()
-        rate(); encode_at_point()
-    torch.cuda.synchronize()
-
-    # the timed region: K steps back to back, events only at its two ends (an event recorded
-    # between two kernels delays the second by several microseconds)
     K = args.steps
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(K):
-        encode()
-        decode()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = t_start.elapsed_time(t_end) / K
-    st = hq.hq_status(ws)
-    st2 = hq.hq_status(ws_dec)
-    assert st == 0 and st2 == 0, (st, st2)
-    g_step = out[:128].clone()
-
-    # breakdown (separate loops): encode with rate control, decode, the encode kernel alone
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record(stream)
-        encode()
-        ev[i][1].record(stream)
-        decode()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    enc_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
-    dec_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
-
-    ek = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        ek[i][0].record(stream)
-        rate()
-        ek[i][1].record(stream)
-        encode_at_point()
-        ek[i][2].record(stream)
-    torch.cuda.synchronize()
-    assert hq.hq_status(ws) == 0
-    rate_ms = float(np.mean([ek[i][0].elapsed_time(ek[i][1]) for i in range(K)]))
-    enc_kernel_ms = float(np.mean([ek[i][1].elapsed_time(ek[i][2]) for i in range(K)]))
-    assert torch.equal(out[:128], g_step), "hq_rate + hq_encode(step=-1) differs from hq_encode"
-
-    hdr = hq.header_fields(out[:128].cpu().numpy())
-    total_bytes = hdr["total_bytes"]
-    input_bytes = 2 * n
-    value = input_bytes / (step_ms * 1e-3) / 1e9
-    # algorithmic bytes: encode reads the input and writes the stream; decode reads the stream and
-    # writes bf16 values
-    alg_step = 2 * (input_bytes + total_bytes)
-    # dominant kernel: encode_kernel (timed alone) or decode_kernel (timed with its 1-lane header
-    # check launch, which makes the decode figure slightly conservative)
-    dec_alg = total_bytes + input_bytes
-    enc_alg = input_bytes + total_bytes
-    if dec_ms >= enc_kernel_ms:
-        dom, dom_ms, dom_bytes = "decode_kernel", dec_ms, dec_alg
-    else:
-        dom, dom_ms, dom_bytes = "encode_kernel", enc_kernel_ms, enc_alg
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = profiled_traffic(profile_stem, dom)
-    # the kernel's binding resource is the vector ALU: its measured VALU instructions (64 lanes
-    # each) over the same launch time, against 256 CUs x 64 lanes x 2.4 GHz
-    valu = profiled_valu(profile_stem, dom)
-    valu_issue = None
-    if valu is not None:
-        tops = valu * 64 / (dom_ms * 1e-3) / 1e12
-        valu_issue = {"achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-ops/s",
-                      "frac": round(tops / VALU_PEAK_TOPS, 4),
-                      "source": "SQ_INSTS_VALU per dispatch x 64, from the committed counter summary"}
+    r = measure(hq, torch, x_host, cfg, seed, K, args.warmup)
+    second = None
+    if args.config == "weight" and args.bps is None and not args.no_kv:
+        xk, cfgk, seedk = workload("kv", None, 1)
+        second = (xk, cfgk, seedk, measure(hq, torch, xk, cfgk, seedk, K, args.warmup))
 
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(r["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {**cfg, "n_values": n, "stream_bytes": total_bytes,
-                   "payload_bps": round(hdr["payload_bits"] / n, 5),
-                   "total_bps": round(8 * total_bytes / n, 5),
-                   "step": float(np.array([hdr["step_bits"]], dtype=np.uint32).view(np.float32)[0]),
-                   "rice_k": hdr["k"]},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                     "alg_bytes_per_launch": dom_bytes, "launch_ms": round(dom_ms, 5), "valu_issue": valu_issue},
-        "extra": {"encode_with_rate_control_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5),
-                  "encode_kernel_ms": round(enc_kernel_ms, 5), "hq_rate_alone_ms": round(rate_ms, 5),
-                  "encode_kernel_gbs": round(enc_alg / (enc_kernel_ms * 1e-3) / 1e9, 1),
-                  "decode_kernel_gbs": round(dec_alg / (dec_ms * 1e-3) / 1e9, 1),
-                  "step_alg_bytes": alg_step,
-                  "step_hbm_gbs": round(alg_step / (step_ms * 1e-3) / 1e9, 1),
-                  "step_hbm_frac": round(alg_step / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "host_wall_ms_per_step": round(wall / K * 1e3, 5)},
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "extra": r["extra"],
     }
-
     copy_gbs = measured_copy_gbs(torch)
     result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
-    result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
+    result["roofline"]["frac_of_measured_copy"] = round(r["roofline"]["achieved"] / copy_gbs, 4)
+    if second is not None:
+        xk, cfgk, seedk, rk = second
+        result["extra"]["kv"] = {"workload": rk["config"]["workload"], "value_gbs": round(rk["value"], 2),
+                                 "ms_per_step": round(rk["ms_per_step"], 5), "config": rk["config"],
+                                 "roofline": {**rk["roofline"], "measured_copy_gbs": round(copy_gbs, 1)},
+                                 **rk["extra"]}
 
     if not args.no_cpu_baseline or not args.no_parity:
         import oracle
         if not os.path.exists(os.path.join(ROOT, "oracle", "libhq_oracle.so")):
             oracle.build()
-        # the whole workload, repeated until about 10 s of host time have been spent (at most 8 times)
-        reps, t_enc, t_dec = 0, 0.0, 0.0
-        while True:
-            t1 = time.perf_counter()
-            s_orc, info_orc = oracle.encode(x_host, oracle.LATTICES[lat], tb, seed=seed, dither=dither)
-            t2 = time.perf_counter()
-            y_orc = oracle.decode(s_orc, n, out_dtype="bf16")
-            t3 = time.perf_counter()
-            reps, t_enc, t_dec = reps + 1, t_enc + (t2 - t1), t_dec + (t3 - t2)
-            if args.no_cpu_baseline or t_enc + t_dec >= 10.0 or reps >= 8:
-                break
-        cpu_gbs = reps * input_bytes / (t_enc + t_dec) / 1e9
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                                      "sample": f"the whole workload ({n} values), {reps} times one encode (with "
-                                                f"rate control) + one bf16 decode, single host thread: encode "
-                                                f"{t_enc / reps:.2f} s, decode {t_dec / reps:.2f} s each",
-                                      "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+        rep, times = parity_report(hq, torch, oracle, x_host, r["config"], seed, r["_dev"])
         if not args.no_parity:
-            g = out[:total_bytes].cpu().numpy()
-            same_stream = bool(g.size == s_orc.size and np.array_equal(g, s_orc))
-            same_out = bool(np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), y_orc))
-            result["extra"]["parity_stream_bytes_equal"] = same_stream
-            result["extra"]["parity_decoded_equal"] = same_out
+            result["extra"]["parity"] = rep
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline_all_cores(oracle, x_host, r["config"], seed, times,
+                                                            host_threads())
+        if second is not None:
+            xk, cfgk, seedk, rk = second
+            repk, tk = parity_report(hq, torch, oracle, xk, rk["config"], seedk, rk["_dev"])
+            if not args.no_parity:
+                result["extra"]["kv"]["parity"] = repk
+            result["extra"]["kv"]["cpu_oracle_one_thread_gbs"] = round(
+                2 * xk.size / (tk["encode_s"] + tk["decode_s"]) / 1e9, 4)
     print(json.dumps(result), flush=True)
 
 
