@@ -377,6 +377,47 @@ __device__ __forceinline__ float code_coord(int32_t c) {
   return (LAT == kLatE8 || LAT == kLatA2) ? (float)c * 0.5f : (float)c;
 }
 
+// U = b - Q(b) for E8, straight from the nearest-point decision (the rule and arithmetic of
+// e8_nearest, evaluated as in e8_symbols): with r = rint b and e = b - r, the chosen point differs
+// from r by D, and U = e - D.  D8 candidate: D = 0, or +-1 with the sign of e on the coordinate the
+// parity fix moves.  D8 + 1/2 candidate: D = +-1/2 with the sign of e, against it on the coordinate
+// that candidate's fix turns.  Every step is exact (e and U lie on the draw's grid).
+__device__ __forceinline__ void e8_dither_u(const float* b, float* u) {
+  float e[8], rf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    rf[i] = rintf(b[i]);
+    e[i] = b[i] - rf[i];
+  }
+  const float rsum = ((rf[0] + rf[1]) + (rf[2] + rf[3])) + ((rf[4] + rf[5]) + (rf[6] + rf[7]));
+  const uint32_t xe =
+      xor3(xor3(__float_as_uint(e[0]), __float_as_uint(e[1]), __float_as_uint(e[2])),
+           xor3(__float_as_uint(e[3]), __float_as_uint(e[4]), __float_as_uint(e[5])),
+           __float_as_uint(e[6]) ^ __float_as_uint(e[7]));
+  const uint32_t pa = (uint32_t)(int32_t)rsum & 1u, pb = pa ^ (xe >> 31);
+  const float amax = fmaxf(fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))),
+                           fmaxf(fmaxf(fabsf(e[4]), fabsf(e[5])), fmaxf(fabsf(e[6]), fabsf(e[7]))));
+  const float amin = fminf(fminf(fminf(fabsf(e[0]), fabsf(e[1])), fminf(fabsf(e[2]), fabsf(e[3]))),
+                           fminf(fminf(fabsf(e[4]), fabsf(e[5])), fminf(fabsf(e[6]), fabsf(e[7]))));
+  const float d = ((fabsf(e[0]) + fabsf(e[1])) + (fabsf(e[2]) + fabsf(e[3]))) +
+                  ((fabsf(e[4]) + fabsf(e[5])) + (fabsf(e[6]) + fabsf(e[7])));
+  const float lhs = d + (pa ? __builtin_fmaf(-2.0f, amax, 1.0f) : 0.0f);
+  const float rhs = pb ? __builtin_fmaf(2.0f, amin, 2.0f) : 2.0f;
+  const bool keep_a = lhs <= rhs;
+  const float t = keep_a ? amax : amin;
+  bool found = keep_a ? (pa == 0u) : (pb == 0u);  // no fix needed: nothing to find
+  // D relative to the sign of e: on the moved coordinate (hit) and elsewhere
+  const float dh = keep_a ? 1.0f : -0.5f, dn = keep_a ? 0.0f : 0.5f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool hit = !found && (fabsf(e[i]) == t);
+    found = found || hit;
+    const float dm = hit ? dh : dn;
+    const float D = __uint_as_float(__float_as_uint(dm) ^ (__float_as_uint(e[i]) & 0x80000000u));
+    u[i] = e[i] - D;
+  }
+}
+
 // Dither flags (the stream header's flags byte): bit 0 dither on; bit 1 the dither's Philox calls
 // take 7 rounds instead of 10; bit 2 a 24-bit draw instead of 16-bit halves.
 constexpr uint32_t kDitherOn = 1u, kDitherPhilox7 = 2u, kDither24 = 4u;
@@ -398,12 +439,19 @@ __device__ __forceinline__ void dither_octet(uint64_t seed, uint64_t t, int o, u
 #pragma unroll
     for (int i = 0; i < 8; ++i) b[i] = (float)(ww[i] >> 8) * (1.0f / 8388608.0f);
   } else {
+    // h / 2^15 for a 16-bit half h: the binary32 with exponent 2^8 and h in the low mantissa bits is
+    // 256 + h 2^-15, so one subtraction of 256 leaves h 2^-15 exactly
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t h = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
-      b[i] = (float)h * (1.0f / 32768.0f);
+      const uint32_t bits = (i & 1) ? __builtin_amdgcn_alignbit(0x4380u, ww[i >> 1], 16u)
+                                    : ((ww[i >> 1] & 0xFFFFu) | 0x43800000u);
+      b[i] = __uint_as_float(bits) - 256.0f;
     }
+  }
+  if (LAT == kLatE8) {
+    e8_dither_u(b, u);
+    return;
   }
   int32_t q[8];
   nearest_octet<LAT>(b, q);

@@ -745,7 +745,7 @@ struct EncParams {
 // Occupancy: six waves per SIMD without dither, four with it (the register budgets the hot path
 // fits in); the look-back's rare fallback must fit the same budget.
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ? 4 : 6))) void encode_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 6))) void encode_kernel(
     EncParams P) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
