@@ -119,6 +119,32 @@ __device__ __forceinline__ void fwht_cross(float a[8], int o) {
   if (LPT >= 32) fwht_stage<16>(a, o);
 }
 
+// The same stages with the per-lane factors of the stages (+-1.0 for lane bits 1, 2, 4, 8, 16)
+// given by the caller, which computes them once per kernel instead of once per call.
+template <int M>
+__device__ __forceinline__ void fwht_stage_s(float a[8], float sgn) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(lane_xor<M>(a[i]), sgn, a[i]);
+}
+template <int LPT = 16>
+__device__ __forceinline__ void fwht_cross_s(float a[8], const float* sg) {
+  fwht_stage_s<1>(a, sg[0]);
+  fwht_stage_s<2>(a, sg[1]);
+  fwht_stage_s<4>(a, sg[2]);
+  if (LPT >= 16) fwht_stage_s<8>(a, sg[3]);
+  if (LPT >= 32) fwht_stage_s<16>(a, sg[4]);
+}
+// Per-lane factors for fwht_cross_s.  The asm keeps them in registers: left visible, the compiler
+// recomputes them at every use (three instructions each) to save the registers.
+template <int LPT = 16>
+__device__ __forceinline__ void fwht_lane_signs(int o, float* sg) {
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    sg[j] = (o & (1 << j)) ? -1.0f : 1.0f;
+    if ((1 << j) < LPT) __asm__ volatile("" : "+v"(sg[j]));
+  }
+}
+
 template <int LPT = 16>
 __device__ __forceinline__ uint32_t lane_sign_bit(int o) { return (uint32_t)__popc(o & (LPT - 1)) & 1u; }
 
@@ -575,6 +601,35 @@ __device__ __forceinline__ void load_octet_signed(const void* x, uint64_t t, int
     const float vv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(vv[i]) ^ smask[i]);
+  }
+}
+
+// Buffer resource over bytes [base, base + bytes) of global memory (raw, no stride): loads past
+// the end return zeros, so a ragged last chunk needs no per-tile branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// load_octet_signed through a buffer resource: the lane's octet at byte offset `off` (zeros past
+// the resource's end).
+template <int DT>
+__device__ __forceinline__ void load_octet_signed_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint32_t* smask,
+                                                      float* v) {
+  if (DT == 1) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float((w[i] << 16) + smask[2 * i]);
+      v[2 * i + 1] = __uint_as_float((w[i] & 0xFFFF0000u) ^ smask[2 * i + 1]);
+    }
+  } else {
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i] ^ smask[i]);
+      v[4 + i] = __uint_as_float(b[i] ^ smask[4 + i]);
+    }
   }
 }
 

@@ -807,21 +807,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ?
   for (int i = 0; i < 8; ++i) smask[i] = ((sgn >> i) & 1u) << 31;
   const uint32_t lane_neg = lane_sign_bit<LPT>(o);
 
-  // phase 1: every round's transform and tile energy
+  // phase 1: every round's transform and tile energy.  The chunk's input is read through a buffer
+  // resource over its valid tiles, so tiles past the end load as zeros without per-tile branches.
   float y[4][8];
   float S[4];
+  {
+    constexpr uint32_t kEsz = DT == 1 ? 2u : 4u;
+    const uint64_t t0 = (uint64_t)c * TI::CT;
+    const uint64_t left = P.T - t0;
+    const uint32_t vbytes = (uint32_t)(left < (uint64_t)TI::CT ? left : (uint64_t)TI::CT) * (uint32_t)TL * kEsz;
+    const __amdgpu_buffer_rsrc_t rin =
+        byte_range(reinterpret_cast<const uint8_t*>(P.x) + t0 * (uint64_t)TL * kEsz, vbytes);
+    float sg[5];
+    fwht_lane_signs<LPT>(o, sg);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
-    if (t < P.T) {
-      load_octet_signed<DT, TL>(P.x, t, o, smask, y[r]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t tc = (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
+      load_octet_signed_buf<DT>(rin, (tc * (uint32_t)TL + 8u * (uint32_t)o) * kEsz, smask, y[r]);
+      fwht_lane(y[r]);
+      fwht_cross_s<LPT>(y[r], sg);
+      S[r] = tile_sumsq<LPT>(y[r]);
     }
-    fwht_lane(y[r]);
-    fwht_cross<LPT>(y[r], o);
-    S[r] = tile_sumsq<LPT>(y[r]);
   }
   // one scale and one division per lane (round o mod 4; A2: lanes with bit 2 of o set divide for
   // the odd slots), broadcast inside the tile's lane group
