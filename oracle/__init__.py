@@ -22,6 +22,12 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = [os.path.join(_HERE, "hq_oracle.c"), os.path.join(_HERE, "srft_oracle.c")]
 _LIB = os.path.join(_HERE, "libhq_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same sources (host code only).  lib()
+# loads it when HQO_SANITIZE is set; the process must then have libasan preloaded (the Python
+# interpreter itself is not instrumented), e.g.
+#   LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 HQO_SANITIZE=1 \
+#     python -m pytest tests -m "not gpu"
+_LIB_SAN = os.path.join(_HERE, "libhq_oracle_san.so")
 
 LAT_Z, LAT_D4, LAT_E8, LAT_A2 = 0, 1, 2, 3
 LATTICES = {"z": LAT_Z, "d4": LAT_D4, "e8": LAT_E8, "a2": LAT_A2}
@@ -29,14 +35,18 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NONFINITE, ERR_CAPACITY, ERR_CORRUPT, 
     0, -1, -2, -3, -4, -5, -6)
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle into ``oracle/libhq_oracle.so`` with gcc."""
-    if force or not os.path.exists(_LIB):
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle into ``oracle/libhq_oracle.so`` with gcc (``libhq_oracle_san.so`` with
+    AddressSanitizer and UndefinedBehaviorSanitizer when ``sanitize``; any report aborts)."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out):
+        san = (["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+               if sanitize else [])
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", _LIB + ".tmp", *_SRC, "-lm"]
+               "-Wall", "-Wextra", *san, "-o", out + ".tmp", *_SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+        os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
@@ -45,9 +55,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = ctypes.CDLL(_LIB)
+        sanitize = bool(os.environ.get("HQO_SANITIZE"))
+        path = _LIB_SAN if sanitize else _LIB
+        if not os.path.exists(path):
+            build(sanitize=sanitize)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         u64, u32, i32, f32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float
         L.hqo_philox4x32_10.argtypes = [P, P, P]
