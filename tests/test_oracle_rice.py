@@ -107,27 +107,82 @@ def test_stream_roundtrip_other_tiles(orc, tile, lattice):
             orc.decode(bad, x.size)
 
 
-@pytest.mark.parametrize("case", ["weight_4bps", "kv_dither_2bps"])
-def test_per_tile_rice_k_would_not_pay(orc, case):
+def _zigzag(a):
+    a = a.astype(np.int64)
+    return ((a << 1) ^ (a >> 63)) & 0xFFFFFFFF
+
+
+def _strip_all(codes, lattice):
+    """The stripped symbols of every octet at once ([octets, 8]); pinned to orc.strip_octet below."""
+    z = codes.reshape(-1, 8).astype(np.int64)
+    if lattice == "e8":
+        u = (z - (z[:, :1] & 1)) >> 1
+        r = u[:, :7].sum(axis=1, keepdims=True) & 1
+        return np.concatenate([_zigzag(u[:, :7]), _zigzag((u[:, 7:] - r) >> 1)], axis=1)
+    if lattice == "d4":
+        parts = []
+        for b in (0, 4):
+            h = z[:, b:b + 4]
+            r = h[:, :3].sum(axis=1, keepdims=True) & 1
+            parts += [_zigzag(h[:, :3]), _zigzag((h[:, 3:] - r) >> 1)]
+        return np.concatenate(parts, axis=1)
+    if lattice == "a2":
+        return _zigzag((z - np.repeat(z[:, 0::2] & 1, 2, axis=1)) >> 1)
+    return _zigzag(z)
+
+
+def _remainder_widths(lattice, k):
+    kh = max(k - 1, 0)
+    return np.array({"e8": [k] * 7 + [kh], "d4": [k, k, k, kh] * 2, "a2": [k, kh] * 4, "z": [k] * 8}[lattice])
+
+
+LATTICES = {"z": 0, "d4": 1, "e8": 2, "a2": 3}
+
+
+@pytest.mark.parametrize("lattice", list(LATTICES))
+def test_vectorised_strip_matches_the_oracle(orc, lattice):
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((8, 128)) * 3).astype(np.float32)
+    codes, _ = orc.quantize(x, LATTICES[lattice], 0.15)
+    s = _strip_all(codes, lattice)
+    for o in range(codes.size // 8):
+        ref = np.asarray(orc.strip_octet(LATTICES[lattice], codes[8 * o:8 * o + 8])[0], dtype=np.int64)
+        assert np.array_equal(s[o], ref), (lattice, o)
+    for k in range(6):
+        lengths = ((s >> _remainder_widths(lattice, k)) + 1 + _remainder_widths(lattice, k)).sum()
+        # the payload is the Rice codes plus the coset bits (one per E8 octet, one per A2 pair)
+        coset = (x.size // 128) * {"e8": 16, "a2": 64, "z": 0, "d4": 0}[lattice]
+        assert lengths == orc.encode(x, LATTICES[lattice], 0.0, step=0.15, rice_k=k)[1]["payload_bits"] - coset
+
+
+PER_TILE_CASES = [
+    ("weight", "e8", 4.0, 128), ("weight", "e8", 3.0, 128), ("weight", "e8", 5.0, 128),
+    ("weight", "d4", 4.0, 128), ("weight", "a2", 4.0, 128), ("weight", "z", 4.0, 128),
+    ("weight", "e8", 4.0, 64), ("weight", "e8", 4.0, 256),
+    ("kv_k", "e8", 2.0, 128), ("kv_v", "e8", 2.0, 128), ("kv_k", "e8", 3.0, 128),
+]
+
+
+@pytest.mark.parametrize("source,lattice,bps,tile", PER_TILE_CASES)
+def test_per_tile_rice_k_would_not_pay(orc, source, lattice, bps, tile):
     """Why the Rice parameter is one per stream, not one per tile: after the per-tile RMS scale,
-    every tile's symbols follow nearly the same law, so the per-tile best k saves far less than
-    the 4 bits per tile (1/32 bit per value) it would cost to store.  Measured on the oracle's own
-    stripped symbols at the rate-controlled operating point."""
-    if case == "weight_4bps":
-        x, tb, seed, dither = synth.weight(rows=64), 4.0, 0, False
+    every tile's lattice input has the same energy, so every tile's symbols follow nearly the same
+    law and the per-tile best k saves far less than the 4 bits per tile (4/tile bits per value) it
+    would cost to store.  Measured on the oracle's stripped symbols at the rate-controlled
+    operating point, for every lattice, tile length and both sources."""
+    if source == "weight":
+        x, seed, dither = synth.weight(rows=64), 0, False
     else:
-        x, tb, seed, dither = synth.kv(1, 0, heads=1, tokens=2048), 2.0, synth.kv_seed(1, 0), True
-    step, _, k_glob = orc.rate(x, orc.LAT_E8, tb, seed=seed, dither=dither)
-    codes, _ = orc.quantize(x, orc.LAT_E8, step, seed=seed, dither=dither)
-    tiles = codes.reshape(-1, 128)
-    ks = np.arange(0, 12)
-    bits = np.zeros((tiles.shape[0], ks.size), dtype=np.int64)
-    for t in range(tiles.shape[0]):
-        syms = np.stack([orc.strip_octet(orc.LAT_E8, tiles[t, 8 * o:8 * o + 8])[0] for o in range(16)])
-        for j, k in enumerate(ks):
-            w = np.array([k] * 7 + [max(k - 1, 0)], dtype=np.int64)
-            bits[t, j] = ((syms.astype(np.int64) >> w) + 1 + w).sum()
+        v = int(source == "kv_v")
+        x, seed, dither = synth.kv(1, v, heads=1, tokens=2048), synth.kv_seed(1, v), True
+    L = LATTICES[lattice]
+    step, _, k_glob = orc.rate(x, L, bps, seed=seed, dither=dither, tile=tile)
+    codes, _ = orc.quantize(x, L, step, seed=seed, dither=dither, tile=tile)
+    syms = _strip_all(codes, lattice)
+    T = codes.size // tile
+    bits = np.stack([((syms >> _remainder_widths(lattice, k)) + 1 + _remainder_widths(lattice, k))
+                     .sum(axis=1).reshape(T, tile // 8).sum(axis=1) for k in range(16)], axis=1)
     glob = bits.sum(axis=0)
     assert int(np.argmin(glob)) == k_glob
     saving_per_value = (glob.min() - bits.min(axis=1).sum()) / codes.size
-    assert saving_per_value < 0.25 * (4.0 / 128.0), saving_per_value
+    assert saving_per_value < 0.25 * (4.0 / tile), saving_per_value
