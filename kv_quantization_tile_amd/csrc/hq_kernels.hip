@@ -1204,6 +1204,7 @@ __device__ __forceinline__ uint32_t plane_bits(const uint32_t* __restrict__ pl, 
 }
 
 typedef float hq_f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t hq_u4 __attribute__((ext_vector_type(4)));
 typedef __bf16 hq_b2 __attribute__((ext_vector_type(2)));
 
 // Twice the un-zigzagged value of a symbol: 2 unzz(s) = s ^ -(s & 1) (s for even s, -s - 1 for odd).
@@ -1211,14 +1212,16 @@ __device__ __forceinline__ int32_t twice_unzz(uint32_t s) {
   return (int32_t)(s ^ (uint32_t)__builtin_amdgcn_sbfe((int32_t)s, 0u, 1u));
 }
 
-// Decode of one chunk's tiles once the terminator positions of its unary segment are in s_pos.
+// Decode of one chunk's tiles: the first round's record words are requested, the terminator
+// positions of the chunk's unary segment are found (unary_positions), then the rounds run.
 // Each lane rebuilds one octet per round: Rice symbols (unary part from consecutive terminator
 // positions, remainders from the fixed record read in place), lattice codes, rescale (and dither
 // removal), inverse FWHT, sign and 1/TL, store.  The fixed-record words of round r + 1 are loaded
 // while round r is computed.  Every read of the record stays inside the stream: a chunk's record
 // has room for all its 8192 / TL tiles, and at most two words past its end lie in the unary plane,
 // which holds at least one word per symbol's chunk once the chunk's terminator count has been
-// checked.
+// checked.  The first round, requested before that check, reads only the first quarter of the
+// chunk's records.
 // Extra arguments of the fused decode + matrix-vector product: the rotated activation (one
 // TL-value tile per column tile of the matrix), the matrix's columns, and the per-tile partial
 // products.
@@ -1228,18 +1231,87 @@ struct GemvArgs {
   float* tp;
 };
 
-template <int LAT, int DT_OUT, bool GEMV, int TL>
+// Terminator positions of a chunk's unary segment (nW32 words at seg) into s_pos.  Thread i takes
+// words [i m, i m + m) (m = ceil(nW32 / 256)), counts their set bits, a workgroup scan gives each
+// thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
+// count nsym (so every write below stays inside s_pos), it writes the position of each set bit.
+// Returns false (for the whole workgroup) on a count mismatch, after flagging the stream corrupt.
+__device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t nsym,
+                                                uint32_t* s_pos, Workspace* ws) {
+  uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t m = (nW32 + kBlock - 1) / kBlock;
+  const uint32_t j0 = min((uint32_t)tid * m, nW32), j1 = min(j0 + m, nW32);
+  // segments of up to 1024 words (4 bits per symbol): the run is loaded once, all words at once,
+  // and kept in registers for the scatter
+  const bool small = m <= 4u;
+  uint32_t wd[4] = {0u, 0u, 0u, 0u};
+  uint32_t cnt = 0;
+  if (small) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (j0 + (uint32_t)i < j1) wd[i] = seg[j0 + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt += (uint32_t)__popc(wd[i]);
+  } else {
+    for (uint32_t j = j0; j < j1; ++j) cnt += (uint32_t)__popc(seg[j]);
+  }
+  const uint32_t incl = wave_incl_scan(cnt);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  const uint32_t t0 = s_wsum[0], t1 = s_wsum[1], t2 = s_wsum[2], t3 = s_wsum[3];
+  const uint32_t total = (t0 + t1) + (t2 + t3);
+  __syncthreads();  // every lane has the totals before s_pos is overwritten
+  if (total != nsym) {  // uniform: the whole workgroup leaves
+    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+    return false;
+  }
+  uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
+  if (small) {
+    // two set bits per pass (the second write only where that bit exists): half the passes of a
+    // one-bit loop for one more compare
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t bits = wd[i];
+      const uint32_t bitbase = (j0 + (uint32_t)i) * 32u;
+      const uint32_t gnext = g + (uint32_t)__popc(bits);
+      while (bits) {
+        const uint32_t b1 = bits & (bits - 1u);
+        s_pos[g] = bitbase + (uint32_t)__builtin_ctz(bits);
+        if (b1) s_pos[g + 1] = bitbase + (uint32_t)__builtin_ctz(b1);
+        g += 2;
+        bits = b1 & (b1 - 1u);
+      }
+      g = gnext;
+    }
+  } else {
+    for (uint32_t j = j0; j < j1; ++j) {
+      uint32_t bits = seg[j];
+      const uint32_t bitbase = j * 32u;
+      while (bits) {
+        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
+        bits &= bits - 1u;
+      }
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+template <int LAT, int DT_OUT, bool GEMV, int TL, int KC = -1>
 __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
-                                             uint32_t c, uint32_t tiles_c, const uint32_t* s_pos, bool check_q,
-                                             GemvArgs g) {
+                                             uint32_t c, uint32_t tiles_c, const uint32_t* __restrict__ seg,
+                                             uint32_t nW32, uint32_t* s_pos, GemvArgs g) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
   constexpr float kInvTile = 1.0f / (float)TL;  // exact power of two
   // the E8 coset bit of a tile of 256 lies beyond the 32-bit window that holds the scale
   constexpr bool kCosetWord = LAT == kLatA2 || (LAT == kLatE8 && LPT > 16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
-  const int k = ws->dec_k;
-  const uint32_t F = ws->dec_F;
+  // KC >= 0: the stream's Rice parameter as a compile-time constant (the header check has
+  // verified that the record length matches it)
+  const int k = KC >= 0 ? KC : ws->dec_k;
+  const uint32_t F = KC >= 0 ? tile_fixed_bits<LAT, TL>(KC) : ws->dec_F;
   const uint32_t df = ws->dec_dither;  // dither flags of the stream
   const bool dither = df != 0u;
   const uint64_t seed = ws->dec_seed;
@@ -1270,8 +1342,12 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
     f1 = fw[(P >> 5) + 1];
     f2 = RW > 32 ? fw[(P >> 5) + 2] : 0u;
   };
+  // the first round's record words are in flight while the positions are found
   issue(0);
-#pragma unroll 1
+  if (!unary_positions(seg, nW32, tiles_c * (uint32_t)TL, s_pos, ws)) return;
+  // q of a corrupt segment can exceed what q << w holds only when the segment is that long
+  const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
+#pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t tc = (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
     const bool valid = tc < tiles_c;
@@ -1281,7 +1357,10 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
     const uint32_t a0 = hA, a1 = hB, a2w = hC, x0 = f0, x1 = f1, x2 = f2;
     if (r < 3) issue(r + 1);
     float yv[8];
-    if (valid) {
+    // a tile past the chunk's end is decoded like the others from what lies in its record's place
+    // (inside the stream: every chunk has room for all its tiles) and dropped at the store; the
+    // matrix-vector product needs its zeros
+    if (!GEMV || valid) {
       // the 32 bits at rec are the scale (low half) and, for E8 with at most 16 octets, the
       // coset bits of the tile's octets (high half)
       const uint32_t th = __builtin_amdgcn_alignbit(a1, a0, rec & 31u);
@@ -1296,8 +1375,10 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       const uint32_t g0 = ((uint32_t)LPT * tc + (uint32_t)o) * 8u;  // symbol index of slot 0: tc TL + 8 o
       const uint32_t pv = s_pos[g0 ? g0 - 1 : 0];
       uint32_t pprev = g0 ? pv : 0xFFFFFFFFu;
-      const uint4 pa = *reinterpret_cast<const uint4*>(s_pos + g0);
-      const uint4 pb = *reinterpret_cast<const uint4*>(s_pos + g0 + 4);
+      hq_u4 pa = *reinterpret_cast<const hq_u4*>(s_pos + g0);
+      hq_u4 pb = *reinterpret_cast<const hq_u4*>(s_pos + g0 + 4);
+      // keeps the two reads 16 bytes wide: split into narrower pieces they conflict in more banks
+      __asm__ volatile("" : "+v"(pa), "+v"(pb));
       const uint32_t pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
       uint32_t q[8];
 #pragma unroll
@@ -1306,7 +1387,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         pprev = pp[sl];
       }
       // q << w can only lose bits in a segment that long (uniform, and rare: the branch is skipped)
-      if (__builtin_expect(check_q, 0)) {
+      if (__builtin_expect(check_q, 0) && valid) {
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl)
           if (q[sl] > (0xFFFFFFFFu >> slot_width<LAT>(sl, k))) bad = true;
@@ -1438,18 +1519,15 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
   if (bad) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
 }
 
-// One workgroup per chunk.  Terminator positions: thread i takes words [i m, i m + m) of the
-// chunk's unary segment (m = ceil(words / 256)), counts their set bits, a workgroup scan gives each
-// thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
-// count (so every write below stays inside s_pos), it writes the position of each set bit.
+// One workgroup per chunk: the chunk's index entries are checked, then decode_chunk of the stream's
+// lattice and tile length finds the terminator positions (unary_positions) and decodes the tiles.
 template <int DT_OUT, bool GEMV>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) void decode_kernel(
     const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, GemvArgs gv) {
   __shared__ uint4 s_pos4[kMaxSymsPerChunk / 4];  // exactly 32 KiB: five workgroups fit one CU's LDS
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
-  uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
   if (!ws->dec_valid) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const uint32_t c = blockIdx.x;
   const uint32_t chunks = ws->dec_chunks;
   if (c >= chunks) return;
@@ -1457,7 +1535,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   const uint32_t tile = ws->dec_tile;
   const uint32_t ct = (uint32_t)kChunkValues / tile;
   const uint32_t tiles_c = (uint32_t)min((uint64_t)ct, T - (uint64_t)c * ct);
-  const uint32_t nsym = tiles_c * tile;
   const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
   const uint32_t w0 = idx[c], w1 = idx[c + 1];
   if (w1 < w0 || (uint64_t)w1 > ws->dec_words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
@@ -1466,65 +1543,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   }
   const uint32_t* __restrict__ seg = reinterpret_cast<const uint32_t*>(in + ws->dec_unary_off + 8ull * w0);
   const uint32_t nW32 = 2u * (w1 - w0);
-  const uint32_t m = (nW32 + kBlock - 1) / kBlock;
-  const uint32_t j0 = min((uint32_t)tid * m, nW32), j1 = min(j0 + m, nW32);
-  // segments of up to 1024 words (4 bits per symbol): the run is loaded once, all words at once,
-  // and kept in registers for the scatter
-  const bool small = m <= 4u;
-  uint32_t wd[4] = {0u, 0u, 0u, 0u};
-  uint32_t cnt = 0;
-  if (small) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (j0 + (uint32_t)i < j1) wd[i] = seg[j0 + i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cnt += (uint32_t)__popc(wd[i]);
-  } else {
-    for (uint32_t j = j0; j < j1; ++j) cnt += (uint32_t)__popc(seg[j]);
-  }
-  const uint32_t incl = wave_incl_scan(cnt);
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  const uint32_t t0 = s_wsum[0], t1 = s_wsum[1], t2 = s_wsum[2], t3 = s_wsum[3];
-  const uint32_t total = (t0 + t1) + (t2 + t3);
-  __syncthreads();  // every lane has the totals before s_pos is overwritten
-  if (total != nsym) {  // uniform: the whole workgroup leaves
-    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
-    return;
-  }
-  uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
-  if (small) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t bits = wd[i];
-      const uint32_t bitbase = (j0 + (uint32_t)i) * 32u;
-      while (bits) {
-        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
-        bits &= bits - 1u;
-      }
-    }
-  } else {
-    for (uint32_t j = j0; j < j1; ++j) {
-      uint32_t bits = seg[j];
-      const uint32_t bitbase = j * 32u;
-      while (bits) {
-        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
-        bits &= bits - 1u;
-      }
-    }
-  }
-  __syncthreads();
-  // q of a corrupt segment can exceed what q << w holds only when the segment is that long
-  const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
   // uniform dispatch on the stream's lattice and tile length
 #define HQ_DEC_LAT(TLV)                                                                                      \
   switch (ws->dec_lattice) {                                                                                 \
-    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
-    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
-    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break; \
-    default: decode_chunk<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, s_pos, check_q, gv); break;      \
+    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
+    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
+    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
+    default: decode_chunk<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;      \
   }
-  if (tile == 64u) {
+  if (tile == 128u && ws->dec_lattice == kLatE8 && ws->dec_k <= 3) {
+    switch (ws->dec_k) {
+      case 0: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 0>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
+      case 1: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 1>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
+      case 2: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 2>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
+      default: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 3>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
+    }
+  } else if (tile == 64u) {
     HQ_DEC_LAT(64)
   } else if (tile == 256u) {
     HQ_DEC_LAT(256)
