@@ -742,18 +742,26 @@ struct EncParams {
   uint32_t spin_budget;
 };
 
-// Occupancy: six waves per SIMD without dither, four with it (the register budgets the hot path
-// fits in); the look-back's rare fallback must fit the same budget.
+// The encoder's LDS: the chunk's fixed record, the unary staging window, per-round wavefront totals,
+// the offsets of rounds written terminator by terminator, and the chunk's prefix.
+struct EncLds {
+  uint4 fixed4[kFixedWordsMax / 4];
+  uint4 unary4[kUnaryWinWords / 4];
+  uint4 wtot4[4];
+  uint32_t off[4][kBlock];
+  uint64_t prefix;
+};
+
+// One chunk of the encode (the body of encode_kernel; the LDS is the kernel's).
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 6))) void encode_kernel(
-    EncParams P) {
+__device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
-  __shared__ uint4 s_fixed4[kFixedWordsMax / 4];
-  __shared__ uint4 s_unary4[kUnaryWinWords / 4];
-  __shared__ uint4 s_wtot4[4];  // per round, the four wavefronts' Rice-length totals
-  __shared__ uint32_t s_off[4][kBlock];  // unary offsets of rounds written terminator by terminator
-  __shared__ uint64_t s_prefix;
+  uint4* s_fixed4 = lds.fixed4;
+  uint4* s_unary4 = lds.unary4;
+  uint4* s_wtot4 = lds.wtot4;
+  auto& s_off = lds.off;
+  uint64_t& s_prefix = lds.prefix;
   uint32_t* s_fixed = reinterpret_cast<uint32_t*>(s_fixed4);
   uint32_t* s_unary = reinterpret_cast<uint32_t*>(s_unary4);
 
@@ -1071,6 +1079,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ?
     ws->res_step_bits = step_bits;
     ws->res_k = k;
   }
+}
+
+// Occupancy: six waves per SIMD without dither, five with it (the register budgets the hot path
+// fits in); the look-back's rare fallback must fit the same budget.
+template <int LAT, bool DITHER, int DT, int TL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 6))) void encode_kernel(
+    EncParams P) {
+  __shared__ EncLds lds;
+  encode_chunk<LAT, DITHER, DT, TL>(P, lds);
 }
 
 // ---------------------------------------------------------------------------------------------
