@@ -29,6 +29,11 @@ enum { kLatZ = 0, kLatD4 = 1, kLatE8 = 2, kLatA2 = 3 };
 constexpr uint32_t kA2R3Bits = 0x3FDDB3D7u;
 
 
+// Three-input XOR in one v_bitop3 (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): the counter-based generator behind the sign
 // diagonal D and the dither.
@@ -38,14 +43,19 @@ struct U4 {
 
 // Rounds R0 .. R1-1 (the key already bumped R0 times).  Each round's two 32 x 32 -> 64-bit
 // products are written as 64-bit multiplies of zero-extended words, which gfx950 computes with one
-// v_mad_u64_u32 each instead of a mul_lo / mul_hi pair.
-template <int R0, int R1>
+// v_mad_u64_u32 each instead of a mul_lo / mul_hi pair.  VXOR: each three-way XOR as one
+// v_bitop3, for counters that differ in every lane (the dither); otherwise plain XORs, which the
+// compiler keeps on the scalar unit where the counter is uniform (the sign diagonal).
+template <int R0, int R1, bool VXOR = false>
 __device__ __forceinline__ U4 philox_rounds(U4 c, uint32_t& k0, uint32_t& k1) {
 #pragma unroll
   for (int r = R0; r < R1; ++r) {
     const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
-    c = U4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
+    if (VXOR)
+      c = U4{xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0};
+    else
+      c = U4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -55,10 +65,10 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
   return philox_rounds<0, 10>(c, k0, k1);
 }
 // Philox4x32 with 7 rounds when `seven` (the same for every lane), else 10: the 7-round function
-// is the first 7 rounds of the 10-round one.
+// is the first 7 rounds of the 10-round one.  Per-lane counters (the dither's draws).
 __device__ __forceinline__ U4 philox4x32_7_or_10(U4 c, uint32_t k0, uint32_t k1, bool seven) {
-  c = philox_rounds<0, 7>(c, k0, k1);
-  if (!seven) c = philox_rounds<7, 10>(c, k0, k1);
+  c = philox_rounds<0, 7, true>(c, k0, k1);
+  if (!seven) c = philox_rounds<7, 10, true>(c, k0, k1);
   return c;
 }
 
@@ -201,10 +211,6 @@ __device__ __forceinline__ uint32_t tile_scale_bits(float S) {
   return (uint32_t)((int32_t)c - adj * 128);
 }
 
-// Three-input XOR in one v_bitop3 (truth table 0x96).
-__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
-  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
-}
 
 __device__ __forceinline__ uint32_t zigzag(int32_t a) { return ((uint32_t)a << 1) ^ (uint32_t)(a >> 31); }
 __device__ __forceinline__ int32_t unzigzag(uint32_t u) { return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u); }
@@ -407,7 +413,8 @@ __device__ __forceinline__ float code_coord(int32_t c) {
 // e8_nearest, evaluated as in e8_symbols): with r = rint b and e = b - r, the chosen point differs
 // from r by D, and U = e - D.  D8 candidate: D = 0, or +-1 with the sign of e on the coordinate the
 // parity fix moves.  D8 + 1/2 candidate: D = +-1/2 with the sign of e, against it on the coordinate
-// that candidate's fix turns.  Every step is exact (e and U lie on the draw's grid).
+// that candidate's fix turns.  Every step is exact (e and U lie on the draw's grid).  Requires b
+// in [0, 2)^8, which every dither draw is.
 __device__ __forceinline__ void e8_dither_u(const float* b, float* u) {
   float e[8], rf[8];
 #pragma unroll
@@ -415,12 +422,17 @@ __device__ __forceinline__ void e8_dither_u(const float* b, float* u) {
     rf[i] = rintf(b[i]);
     e[i] = b[i] - rf[i];
   }
-  const float rsum = ((rf[0] + rf[1]) + (rf[2] + rf[3])) + ((rf[4] + rf[5]) + (rf[6] + rf[7]));
+  // b lies in [0, 2), so each rint is 0.0, 1.0 or 2.0 and only 1.0 has bit 23 (the exponent's low
+  // bit) set: the parity of the sum is bit 23 of the XOR of the eight patterns
+  const uint32_t xr =
+      xor3(xor3(__float_as_uint(rf[0]), __float_as_uint(rf[1]), __float_as_uint(rf[2])),
+           xor3(__float_as_uint(rf[3]), __float_as_uint(rf[4]), __float_as_uint(rf[5])),
+           __float_as_uint(rf[6]) ^ __float_as_uint(rf[7]));
   const uint32_t xe =
       xor3(xor3(__float_as_uint(e[0]), __float_as_uint(e[1]), __float_as_uint(e[2])),
            xor3(__float_as_uint(e[3]), __float_as_uint(e[4]), __float_as_uint(e[5])),
            __float_as_uint(e[6]) ^ __float_as_uint(e[7]));
-  const uint32_t pa = (uint32_t)(int32_t)rsum & 1u, pb = pa ^ (xe >> 31);
+  const uint32_t pa = (xr >> 23) & 1u, pb = pa ^ (xe >> 31);
   const float amax = fmaxf(fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))),
                            fmaxf(fmaxf(fabsf(e[4]), fabsf(e[5])), fmaxf(fabsf(e[6]), fabsf(e[7]))));
   const float amin = fminf(fminf(fminf(fabsf(e[0]), fabsf(e[1])), fminf(fabsf(e[2]), fabsf(e[3]))),

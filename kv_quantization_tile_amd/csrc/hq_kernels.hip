@@ -1451,7 +1451,8 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
           float u[8];
           dither_octet<LAT>(seed, t, o, df, u);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) yv[i] = ((float)z[i] * 0.5f - u[i]) * tsc;
+          // z / 2 is exact, so the fused form rounds the difference once, as z / 2 - u does
+          for (int i = 0; i < 8; ++i) yv[i] = __builtin_fmaf((float)z[i], 0.5f, -u[i]) * tsc;
         } else {
           // (z / 2) * tsc equals z * (tsc / 2): both are the same real product rounded once
           const float f = tsc * 0.5f;
