@@ -1248,20 +1248,28 @@ struct GemvArgs {
   float* tp;
 };
 
-// Terminator positions of a chunk's unary segment (nW32 words at seg) into s_pos.  Thread i takes
-// words [i m, i m + m) (m = ceil(nW32 / 256)), counts their set bits, a workgroup scan gives each
-// thread the index of its first symbol, and, once the total is checked to equal the chunk's symbol
-// count nsym (so every write below stays inside s_pos), it writes the position of each set bit.
+// Terminator positions of a chunk's unary segment (nW32 words at seg) into the workgroup's table,
+// which holds kMaxSymsPerChunk 16-bit entries or half as many 32-bit ones.  Thread i takes words
+// [i m, i m + m) (m = ceil(nW32 / 256)), counts their set bits, a workgroup scan gives each thread
+// the index of its first symbol, and, once the total is checked to equal the chunk's symbol count
+// nsym (so every write below stays inside the table), it writes the position of each set bit:
+//   MODE 0 (nW32 <= kPos16Words, so every position fits 16 bits): every terminator, 16-bit;
+//   MODE 1 / 2: the terminators of symbols [0, 4096) / [4096, 8192) as 32-bit entries at index
+//   g - 4096 (MODE - 1); MODE 2 also puts terminator 4095's position into *s_boundary.
 // Returns false (for the whole workgroup) on a count mismatch, after flagging the stream corrupt.
+constexpr uint32_t kPos16Words = 2048;       // 65536 bits
+constexpr uint32_t kPosHalf = kMaxSymsPerChunk / 2;
+template <int MODE>
 __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t nsym,
-                                                uint32_t* s_pos, Workspace* ws) {
+                                                uint32_t* s_pos, uint32_t* s_boundary, Workspace* ws) {
   uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(s_pos);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t m = (nW32 + kBlock - 1) / kBlock;
   const uint32_t j0 = min((uint32_t)tid * m, nW32), j1 = min(j0 + m, nW32);
   // segments of up to 1024 words (4 bits per symbol): the run is loaded once, all words at once,
   // and kept in registers for the scatter
-  const bool small = m <= 4u;
+  const bool small = MODE == 0 && m <= 4u;
   uint32_t wd[4] = {0u, 0u, 0u, 0u};
   uint32_t cnt = 0;
   if (small) {
@@ -1278,9 +1286,9 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
   __syncthreads();
   const uint32_t t0 = s_wsum[0], t1 = s_wsum[1], t2 = s_wsum[2], t3 = s_wsum[3];
   const uint32_t total = (t0 + t1) + (t2 + t3);
-  __syncthreads();  // every lane has the totals before s_pos is overwritten
+  __syncthreads();  // every lane has the totals before the table is overwritten
   if (total != nsym) {  // uniform: the whole workgroup leaves
-    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+    if (tid == 0 && MODE != 2) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
     return false;
   }
   uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
@@ -1294,8 +1302,8 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
       const uint32_t gnext = g + (uint32_t)__popc(bits);
       while (bits) {
         const uint32_t b1 = bits & (bits - 1u);
-        s_pos[g] = bitbase + (uint32_t)__builtin_ctz(bits);
-        if (b1) s_pos[g + 1] = bitbase + (uint32_t)__builtin_ctz(b1);
+        t16[g] = (uint16_t)(bitbase + (uint32_t)__builtin_ctz(bits));
+        if (b1) t16[g + 1] = (uint16_t)(bitbase + (uint32_t)__builtin_ctz(b1));
         g += 2;
         bits = b1 & (b1 - 1u);
       }
@@ -1306,7 +1314,15 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
       uint32_t bits = seg[j];
       const uint32_t bitbase = j * 32u;
       while (bits) {
-        s_pos[g++] = bitbase + (uint32_t)__builtin_ctz(bits);
+        const uint32_t pos = bitbase + (uint32_t)__builtin_ctz(bits);
+        if (MODE == 0) {
+          t16[g] = (uint16_t)pos;
+        } else {
+          const uint32_t gl = g - (MODE == 2 ? kPosHalf : 0u);  // wraps above the half when below it
+          if (gl < kPosHalf) s_pos[gl] = pos;
+          if (MODE == 2 && g == kPosHalf - 1u) *s_boundary = pos;
+        }
+        ++g;
         bits &= bits - 1u;
       }
     }
@@ -1316,9 +1332,10 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
 }
 
 template <int LAT, int DT_OUT, bool GEMV, int TL, int KC = -1>
-__device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws,
-                                             uint32_t c, uint32_t tiles_c, const uint32_t* __restrict__ seg,
-                                             uint32_t nW32, uint32_t* s_pos, GemvArgs g) {
+__device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in, void* __restrict__ out,
+                                                  Workspace* ws, uint32_t c, uint32_t tiles_c,
+                                                  const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t* s_pos,
+                                                  uint32_t* s_boundary, GemvArgs g) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
   constexpr float kInvTile = 1.0f / (float)TL;  // exact power of two
@@ -1359,13 +1376,12 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
     f1 = fw[(P >> 5) + 1];
     f2 = RW > 32 ? fw[(P >> 5) + 2] : 0u;
   };
-  // the first round's record words are in flight while the positions are found
-  issue(0);
-  if (!unary_positions(seg, nW32, tiles_c * (uint32_t)TL, s_pos, ws)) return;
   // q of a corrupt segment can exceed what q << w holds only when the segment is that long
   const bool check_q = nW32 > (0xFFFFFFFFu >> 15) / 32u;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  // segments longer than kPos16Words words (q beyond 16-bit positions: a tiny step at a small k,
+  // or a corrupt stream): the table holds 32-bit positions of half the chunk's symbols at a time
+  const bool wide = nW32 > kPos16Words;  // uniform
+  auto do_round = [&](int r) {
     const uint32_t tc = (uint32_t)TI::TPR * r + (uint32_t)TI::TPW * wave + tw;
     const bool valid = tc < tiles_c;
     const uint64_t t = (uint64_t)c * TI::CT + tc;
@@ -1390,13 +1406,29 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       // unary parts: q = p - p_prev - 1 = (p_prev ^ ~0) + p; the symbol before the chunk's first
       // sits at -1
       const uint32_t g0 = ((uint32_t)LPT * tc + (uint32_t)o) * 8u;  // symbol index of slot 0: tc TL + 8 o
-      const uint32_t pv = s_pos[g0 ? g0 - 1 : 0];
-      uint32_t pprev = g0 ? pv : 0xFFFFFFFFu;
-      hq_u4 pa = *reinterpret_cast<const hq_u4*>(s_pos + g0);
-      hq_u4 pb = *reinterpret_cast<const hq_u4*>(s_pos + g0 + 4);
-      // keeps the two reads 16 bytes wide: split into narrower pieces they conflict in more banks
-      __asm__ volatile("" : "+v"(pa), "+v"(pb));
-      const uint32_t pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      uint32_t pprev, pp[8];
+      if (!wide) {
+        // the octet's eight 16-bit positions in one 16-byte read (the asm keeps it whole: split into
+        // narrower pieces the reads conflict in more banks)
+        const uint16_t* t16 = reinterpret_cast<const uint16_t*>(s_pos);
+        const uint32_t pv = t16[g0 ? g0 - 1 : 0];
+        pprev = g0 ? pv : 0xFFFFFFFFu;
+        hq_u4 pw = *reinterpret_cast<const hq_u4*>(t16 + g0);
+        __asm__ volatile("" : "+v"(pw));
+        pp[0] = pw.x & 0xFFFFu; pp[1] = pw.x >> 16; pp[2] = pw.y & 0xFFFFu; pp[3] = pw.y >> 16;
+        pp[4] = pw.z & 0xFFFFu; pp[5] = pw.z >> 16; pp[6] = pw.w & 0xFFFFu; pp[7] = pw.w >> 16;
+      } else {
+        // 32-bit entries of the current half of the chunk's symbols (rounds 0-1: [0, 4096), 2-3:
+        // [4096, 8192)); the terminator before the second half is in *s_boundary
+        const uint32_t gl = g0 - (r >= 2 ? kPosHalf : 0u);
+        const uint32_t pv = gl ? s_pos[gl - 1] : *s_boundary;
+        pprev = g0 ? pv : 0xFFFFFFFFu;
+        hq_u4 pa = *reinterpret_cast<const hq_u4*>(s_pos + gl);
+        hq_u4 pb = *reinterpret_cast<const hq_u4*>(s_pos + gl + 4);
+        __asm__ volatile("" : "+v"(pa), "+v"(pb));
+        pp[0] = pa.x; pp[1] = pa.y; pp[2] = pa.z; pp[3] = pa.w;
+        pp[4] = pb.x; pp[5] = pb.y; pp[6] = pb.z; pp[7] = pb.w;
+      }
       uint32_t q[8];
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) {
@@ -1509,7 +1541,7 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
       if (LPT >= 16) part = part + lane_xor<8>(part);
       if (LPT >= 32) part = part + lane_xor<16>(part);
       if (valid && o == 0) g.tp[t] = part * kInvTile;
-      continue;
+      return;
     }
     fwht_lane(yv);
     fwht_cross<LPT>(yv, o);
@@ -1533,16 +1565,33 @@ __device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ in, voi
         dst[1] = make_float4(xo[4], xo[5], xo[6], xo[7]);
       }
     }
+    };
+  // the first round's record words are in flight while the positions are found
+  issue(0);
+  const uint32_t nsym = tiles_c * (uint32_t)TL;
+  if (!(wide ? unary_positions<1>(seg, nW32, nsym, s_pos, s_boundary, ws)
+              : unary_positions<0>(seg, nW32, nsym, s_pos, s_boundary, ws)))
+    return;
+  do_round(0);
+  do_round(1);
+  if (wide) {
+    __syncthreads();  // every read of the first half is done before the table is rewritten
+    if (!unary_positions<2>(seg, nW32, nsym, s_pos, s_boundary, ws)) return;
   }
+  do_round(2);
+  do_round(3);
   if (bad) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
 }
 
 // One workgroup per chunk: the chunk's index entries are checked, then decode_chunk of the stream's
 // lattice and tile length finds the terminator positions (unary_positions) and decodes the tiles.
 template <int DT_OUT, bool GEMV>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) void decode_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_kernel(
     const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, GemvArgs gv) {
-  __shared__ uint4 s_pos4[kMaxSymsPerChunk / 4];  // exactly 32 KiB: five workgroups fit one CU's LDS
+  // 16 KiB of terminator positions (8192 16-bit or 4096 32-bit entries) and the boundary word: the
+  // register budget of six waves per SIMD, not LDS, sets the occupancy
+  __shared__ uint4 s_pos4[kMaxSymsPerChunk / 8];
+  __shared__ uint32_t s_boundary;
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
   if (!ws->dec_valid) return;
   const int tid = threadIdx.x;
@@ -1564,17 +1613,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5, 8))) 
   // uniform dispatch on the stream's lattice and tile length
 #define HQ_DEC_LAT(TLV)                                                                                      \
   switch (ws->dec_lattice) {                                                                                 \
-    case kLatE8: decode_chunk<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
-    case kLatA2: decode_chunk<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
-    case kLatD4: decode_chunk<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break; \
-    default: decode_chunk<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;      \
+    case kLatE8: decode_chunk_body<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
+    case kLatA2: decode_chunk_body<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
+    case kLatD4: decode_chunk_body<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
+    default: decode_chunk_body<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;      \
   }
   if (tile == 128u && ws->dec_lattice == kLatE8 && ws->dec_k <= 3) {
     switch (ws->dec_k) {
-      case 0: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 0>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
-      case 1: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 1>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
-      case 2: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 2>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
-      default: decode_chunk<kLatE8, DT_OUT, GEMV, 128, 3>(in, out, ws, c, tiles_c, seg, nW32, s_pos, gv); break;
+      case 0: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 0>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
+      case 1: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 1>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
+      case 2: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 2>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
+      default: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 3>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
     }
   } else if (tile == 64u) {
     HQ_DEC_LAT(64)

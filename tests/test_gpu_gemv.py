@@ -55,6 +55,22 @@ def test_gemv_small_matrix(orc, lattice, dither, target):
     check_rows(orc, s_gpu, rows, cols, x, dev(x), seed=5)
 
 
+def test_gemv_long_segments(orc):
+    """The decoder's long-segment path (k = 0 at a small step: every chunk's unary segment above
+    2048 words) under the fused product."""
+    say("case: gemv 64x1024 e8 long segments")
+    rows, cols = 64, 1024
+    g = np.random.Generator(np.random.PCG64(23))
+    w = synth.bf16_bits(0.02 * g.standard_normal((rows, cols)).astype(np.float32))
+    x = g.standard_normal(cols).astype(np.float32)
+    s_gpu, _ = hq.hq_encode(dev(w), "e8", 0.0, seed=5, step=0.03, rice_k=0)
+    s_host = s_gpu.cpu().numpy()
+    h = s_host[:128].view(np.uint32)
+    idx = s_host[128:128 + 4 * (int(h[10]) + 1)].view(np.uint32).astype(np.int64)
+    assert (2 * np.diff(idx) > 2048).all()
+    check_rows(orc, s_gpu, rows, cols, x, dev(x), seed=5)
+
+
 def test_gemv_bf16_activation_and_ragged_chunk(orc):
     """bf16 activation; 3 x 1024 is 24 tiles, one partly filled chunk."""
     say("case: gemv 3x1024 bf16 x")

@@ -254,7 +254,9 @@ def test_zero_tiles_and_tiny_values(orc):
 
 def test_long_unary_segments(orc):
     """k = 0 at a small step: ~35 unary bits per value, so a chunk's unary segment spans several
-    staging windows of the encoder."""
+    staging windows of the encoder, and the decoder takes its long-segment path (positions beyond
+    16 bits: the table holds half the chunk's at a time); the last chunk is short (1024 values)
+    and takes the common path."""
     say("case: long unary segments")
     x = synth.gaussian(128 * 200, seed=4).reshape(200, 128)
     s_orc, info_orc = orc.encode(x, orc.LAT_Z, 0.0, step=0.05, rice_k=0)
@@ -263,6 +265,54 @@ def test_long_unary_segments(orc):
     assert_same_stream(host_bytes(s_gpu), s_orc)
     y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
     assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+
+
+def _segment_words(s: np.ndarray):
+    h = s[:128].view(np.uint32)
+    chunks = int(h[10])
+    idx = s[128:128 + 4 * (chunks + 1)].view(np.uint32).astype(np.int64)
+    return 2 * np.diff(idx)  # 32-bit words per chunk
+
+
+@pytest.mark.parametrize("lattice,tile,dither,step,tiles", [
+    ("e8", 128, 1, 0.03, 148),    # E8 at k = 0 (the compile-time k path), dither; last chunk 2560 values
+    ("e8", 256, 0, 0.02, 70),     # tiles of 256; last chunk 1536 values
+    ("a2", 64, 0, 0.03, 300),     # tiles of 64; last chunk 2816 values
+    ("d4", 128, 1, 0.05, 128),    # whole chunks only
+])
+def test_long_segments_every_lattice(orc, lattice, tile, dither, step, tiles):
+    """The decoder's long-segment path (a chunk's unary segment above 2048 words) on every lattice,
+    tile length and both outputs, including a short last chunk whose second half has no valid tile,
+    against the oracle bit for bit."""
+    say(f"case: long segments {lattice} tile {tile} dither {dither} step {step} tiles {tiles}")
+    x = synth.gaussian(tile * tiles, seed=11).reshape(tiles, tile)
+    s_orc, _ = orc.encode(x, LAT[lattice], 0.0, seed=9, dither=dither, step=step, rice_k=0, tile=tile)
+    words = _segment_words(s_orc)
+    assert (words > 2048).all(), words  # every chunk, the last one too, takes the long path
+    s_gpu, _ = hq.hq_encode(dev(x), lattice, 0.0, seed=9, dither=dither, step=step, rice_k=0, tile=tile)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    y = hq.hq_decode(s_gpu, x.size, out_dtype=torch.float32)
+    assert np.array_equal(y.cpu().numpy(), orc.decode(s_orc, x.size))
+    yb = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(yb), orc.decode(s_orc, x.size, out_dtype="bf16"))
+
+
+def test_mixed_segment_lengths(orc):
+    """Chunks of both kinds in one stream: all-zero chunks (every symbol 0: short segments, 16-bit
+    positions) alternate with noise chunks at a small step (long segments)."""
+    say("case: mixed segment lengths")
+    g = np.random.Generator(np.random.PCG64(31))
+    T = 64 * 6 + 40
+    x = g.standard_normal((T, 128)).astype(np.float32)
+    for c in range(0, 7, 2):
+        x[64 * c: 64 * c + 64] = 0.0
+    s_orc, _ = orc.encode(x, orc.LAT_E8, 0.0, step=0.03, rice_k=1)
+    words = _segment_words(s_orc)
+    assert (words > 2048).any() and (words <= 2048).any(), words
+    s_gpu, _ = hq.hq_encode(dev(x), "e8", 0.0, step=0.03, rice_k=1)
+    assert_same_stream(host_bytes(s_gpu), s_orc)
+    yb = hq.hq_decode(s_gpu, x.size, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_host(yb), orc.decode(s_orc, x.size, out_dtype="bf16"))
 
 
 def test_nonfinite_reported():
