@@ -111,46 +111,39 @@ int64_t initial_centre(float target) {
   return (int64_t)(127u << 23) + (int64_t)floor((2.05 - (double)target) * 8388608.0 + 0.5);
 }
 
-// The rate pass whose solve is still to be done after run_rate_control (pass < 0: none; the
-// workspace holds the operating point).
-struct LastPass {
-  int pass = -1, nc = 0, half_log2 = 0;
-  uint32_t N = 0;
-};
-
-// init + rate passes (when needed).  Pass B solves pass A inside its own launch; the caller solves
-// the last pass with one more launch (launch_rate_solve).
-int run_rate_control(const EncodeArgs& a, LastPass* last) {
+// The rate control of a call (see RatePlan): for rate control proper (step == 0) two passes around
+// the Gaussian guess; for a fixed step with automatic k one pass at that step; none otherwise (or
+// for an empty tensor).  Pass A samples min(T, 2048) tiles, pass B min(T, 8192).
+RatePlan plan_rate(const EncodeArgs& a) {
+  RatePlan rp{};
   const uint64_t T = a.tiles;
   const uint32_t N = (uint32_t)(T < kRcSampleTiles ? T : kRcSampleTiles);
   const uint32_t NA = (uint32_t)(T < kRcSampleTilesA ? T : kRcSampleTilesA);
-  hipError_t e;
-  *last = LastPass{};
+  const uint32_t tpw = 64u / ((uint32_t)a.tile / 8u);  // sample tiles per wavefront
   if (a.fixed_step_bits) {
-    const bool pass_follows = a.rice_k < 0 && N > 0;
-    e = launch_init(a, (int64_t)a.fixed_step_bits, pass_follows ? kInitProvisional : kInitFinal);
-    if (e != hipSuccess) return HQ_ERR_HIP;
-    if (pass_follows) {
-      e = launch_rate_pass(a, 1, 0, N, 0);
-      if (e != hipSuccess) return HQ_ERR_HIP;
-      last->pass = 0;
-      last->nc = 1;
-      last->N = N;
-    }
-    return HQ_OK;
+    rp.needed = a.rice_k < 0 && N > 0;
+    rp.two_pass = 0;
+    rp.centre0 = (int64_t)a.fixed_step_bits;
+  } else {
+    rp.needed = N > 0;
+    rp.two_pass = 1;
+    rp.centre0 = initial_centre(a.target);
   }
-  e = launch_init(a, initial_centre(a.target), N == 0 ? kInitFinal : kInitProvisional);
-  if (e != hipSuccess) return HQ_ERR_HIP;
-  if (N == 0) return HQ_OK;
-  e = launch_rate_pass(a, kRcCand, 21, NA, 0);
-  if (e != hipSuccess) return HQ_ERR_HIP;
-  e = launch_rate_pass(a, kRcCandB, 18, N, 1, kRcCand, 21, NA, initial_centre(a.target));
-  if (e != hipSuccess) return HQ_ERR_HIP;
-  last->pass = 1;
-  last->nc = kRcCandB;
-  last->half_log2 = 18;
-  last->N = N;
-  return HQ_OK;
+  if (!rp.needed) return rp;
+  rp.NB = N;
+  rp.blkB = (N + 4u * tpw - 1u) / (4u * tpw);
+  if (rp.two_pass) {
+    rp.NA = NA;
+    rp.blkA = (NA + tpw - 1u) / tpw;
+  }
+  return rp;
+}
+
+// The call's first kernel: it resets the workspace, with the operating point final (no rate
+// control follows) or provisional (the rate workgroups of rp will set it).
+int start_call(const EncodeArgs& a, const RatePlan& rp) {
+  const int64_t centre = a.fixed_step_bits ? (int64_t)a.fixed_step_bits : initial_centre(a.target);
+  return launch_init(a, centre, rp.needed ? kInitProvisional : kInitFinal) == hipSuccess ? HQ_OK : HQ_ERR_HIP;
 }
 
 struct Results {
@@ -228,8 +221,8 @@ uint64_t encode_bound_at(uint64_t n, int lattice, uint32_t tile, double step, in
 
 // ---- the allocation-free encode: its workspace is a static device array ------------------------
 // Largest n of hq_encode_noalloc, and the array sized for it: the workspace of an encode of that
-// many values (4 KiB of state, 4 KiB of rate counters, one 8-byte offset flag per 8192-value chunk
-// plus one): 1,057,024 bytes per GPU, held until the process ends.
+// many values (4 KiB of state, 12 KiB of rate counters and published words, one 8-byte offset flag
+// per 8192-value chunk plus one): 1,065,216 bytes per GPU, held until the process ends.
 constexpr uint64_t kNoAllocMaxValues = 1ull << 30;
 constexpr size_t kScratchBytes =
     kWsHeader + kWsRate + ((8ull * ((kNoAllocMaxValues + 8191) / 8192 + 1) + 255) & ~(uint64_t)255);
@@ -332,11 +325,10 @@ int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, h
   if (((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   if (params->step == -1.0f) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, nullptr, 0, workspace, stream);
-  LastPass last;
-  rc = run_rate_control(a, &last);
+  const RatePlan rp = plan_rate(a);
+  rc = start_call(a, rp);
   if (rc) return rc;
-  if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
-    return HQ_ERR_HIP;
+  if (launch_rate(a, rp) != hipSuccess) return HQ_ERR_HIP;
   if (!info) return HQ_OK;  // asynchronous: the operating point stays in the workspace
   Workspace h;
   if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
@@ -363,11 +355,10 @@ int hq_encode(const void* x, int32_t dtype, uint64_t n, const hq_params* params,
   if (((uintptr_t)out & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)workspace & 255u)) return HQ_ERR_INVALID_ARG;
   EncodeArgs a = make_args(x, dtype, n, params, out, out_capacity, workspace, stream);
   if (params->step != -1.0f) {
-    LastPass last;
-    rc = run_rate_control(a, &last);
+    const RatePlan rp = plan_rate(a);
+    rc = start_call(a, rp);
     if (rc) return rc;
-    if (last.pass >= 0 && launch_rate_solve(a, last.nc, last.half_log2, last.N, last.pass) != hipSuccess)
-      return HQ_ERR_HIP;
+    if (launch_rate(a, rp) != hipSuccess) return HQ_ERR_HIP;
   } else if (launch_init(a, 0, kInitKeep) != hipSuccess) {
     // the workspace's operating point is kept; status, results and look-back flags reset
     return HQ_ERR_HIP;

@@ -54,29 +54,40 @@ struct alignas(256) Workspace {
   uint64_t dec_fixed_off;
   uint64_t dec_unary_off;
   uint64_t dec_words;
-  // pass B's centre, which pass B's workgroup 0 solves from pass A and publishes to the rest of the
-  // launch (bit 63 set = published, the centre in the low 32 bits; relaxed agent-scope atomics, the
-  // value travels in the word itself).  init_kernel clears it.
-  uint64_t sync_centre;
   // kPointTag while step_bits / rice_k hold a complete operating point
   uint32_t point_tag;
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
 // Counters of the two rate passes.  A workgroup of a pass adds its sums into one of kRcAccSlots
-// counter sets (workgroup index mod kRcAccSlots, so that few workgroups share an address); the
-// one-workgroup solve kernel that follows adds the sets up.  The init kernel of every call zeroes
-// both passes' counters.
+// counter sets (workgroup index mod kRcAccSlots, so that few workgroups share an address).  Each
+// 64-bit word holds the sum of the contributions in bits 0-39 and their number in bits 40-63, so
+// that the solver can tell from the word alone that every workgroup of the pass has added into it
+// (relaxed agent-scope atomics suffice: no ordering between words is needed).  The init kernel of
+// every call zeroes both passes' counters and the published words below.
 constexpr int kRcAccSlots = 16;
 constexpr int kRcCounters = kRcCand * kRcKwin;
+constexpr int kCntShift = 40;
 struct RateAcc {
-  uint32_t cnt[kRcAccSlots][kRcCounters];
+  uint64_t cnt[kRcAccSlots][kRcCounters];
 };
-constexpr size_t kWsRate = 2 * sizeof(RateAcc);  // pass A, pass B
+// Word in which rate workgroup 0 publishes pass A's solve, the centre of pass B, to the other rate
+// workgroups of the launch (bit 63 set = published, the centre in the low 32 bits).  kPubCopies
+// copies, kPubStride words (256 bytes) apart, so that the waiting workgroups spread their polls
+// over several addresses.
+constexpr int kPubCopies = 16;
+constexpr int kPubStride = 32;
+struct RatePub {
+  uint64_t centre[kPubCopies * kPubStride];
+};
+constexpr size_t kWsRate = 2 * sizeof(RateAcc) + sizeof(RatePub);  // pass A, pass B, published centre
 static_assert(kWsRate % 256 == 0, "rate counters keep the flags 256-byte aligned");
 
 inline RateAcc* rate_acc(void* ws, int pass) {
   return reinterpret_cast<RateAcc*>(reinterpret_cast<char*>(ws) + kWsHeader) + pass;
+}
+inline RatePub* rate_pub(void* ws) {
+  return reinterpret_cast<RatePub*>(reinterpret_cast<char*>(ws) + kWsHeader + 2 * sizeof(RateAcc));
 }
 // the encoder's look-back flags follow the rate counters
 inline uint64_t* lookback_flags(void* ws) {
@@ -110,16 +121,23 @@ struct EncodeArgs {
 };
 
 // Modes of the call's first kernel (see init_kernel): the operating point is provisional (rate
-// passes follow), final, or kept from the workspace (an encode with step == -1).
+// workgroups follow), final, or kept from the workspace (an encode with step == -1).
 enum { kInitProvisional = 0, kInitFinal = 1, kInitKeep = 2 };
 hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode);
-// One rate pass.  Pass 1 (pass B) solves pass 0 first, inside its workgroup 0, with pass 0's
-// candidates (nc0, half_spacing_log2_0, sample0) around pass 0's centre centre0; pass 0 reads the
-// centre init_kernel stored.
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass,
-                            int nc0 = 0, int half_spacing_log2_0 = 0, uint32_t sample0 = 0, int64_t centre0 = 0);
-// One-workgroup solve of a rate pass into the workspace's step and k (hq_rate's last launch).
-hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_spacing_log2, uint32_t sample, int pass);
+
+// Rate control of one call (see rate_workgroup in hq_kernels.hip): two passes (pass A: 8
+// candidates around centre0 on NA sample tiles; pass B: 4 candidates around pass A's solve on NB
+// tiles), or, for a fixed step with automatic k, one pass of the single candidate centre0 on NB
+// tiles.  blkA / blkB workgroups run the passes (the first max(blkA, blkB) workgroups of a launch).
+struct RatePlan {
+  int needed;
+  int two_pass;
+  int64_t centre0;
+  uint32_t NA, NB, blkA, blkB;
+};
+// Rate control: one launch of the rate workgroups, whose workgroup 0 leaves the operating point in
+// the workspace (nothing when rp.needed is 0).
+hipError_t launch_rate(const EncodeArgs& a, const RatePlan& rp);
 // The encoder, at the operating point the workspace holds.
 hipError_t launch_encode(const EncodeArgs& a);
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,

@@ -5,10 +5,11 @@
 // coding with rate targeting, KV dither).  The byte format is described in include/hq.h.
 //
 // Kernels of one encode call, all on the caller's stream, with no host round trip in between:
-//   init_kernel     clears the workspace flags and seeds the rate search;
-//   rate_kernel x2  evaluates 8 candidate steps on a sample of tiles into per-pass counters, each
-//                   followed by rate_solve_kernel, which solves for the next centre (pass A:
-//                   half-octave spacing, pass B: 1/32 octave);
+//   init_kernel     clears the workspace flags and counters and seeds the rate search;
+//   rate_kernel     the rate search in one launch: its workgroups evaluate candidate steps on
+//                   samples of tiles into per-pass counters, and its workgroup 0 solves pass A
+//                   (8 candidates, quarter octaves) for pass B's centre, publishes it to the
+//                   others, and solves pass B (4 candidates, 1/16 octave) for the operating point;
 //   encode_kernel   one workgroup per 64-tile chunk: load, sign, FWHT, scale, lattice, strip, Rice
 //                   lengths, workgroup scan, decoupled look-back over chunks for the unary offsets,
 //                   and coalesced stores of the chunk's fixed record and unary segment.
@@ -240,7 +241,6 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
     ws->res_words = 0;
     ws->res_step_bits = step_bits;
     ws->res_k = k;
-    ws->sync_centre = 0;
   }
   for (uint64_t i = gid; i < nflags; i += (uint64_t)gridDim.x * blockDim.x) flags[i] = 0;
   for (uint64_t i = gid; i < nacc; i += (uint64_t)gridDim.x * blockDim.x) acc[i] = 0;
@@ -254,7 +254,7 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
 //  - the search variable is b, the binary32 bit pattern of the step;
 //  - a pass evaluates nc candidates centre + (2j-(nc-1)) 2^h (clamped to [2^-12, 2^12]); for
 //    each, the Rice k is the argmin (ties: smaller k) over kb..kb+3, kb = clamp(-exponent - 2, 0, 12);
-//  - the solve kernel interpolates linearly (IEEE double) between the two candidates that
+//  - the solve interpolates linearly (IEEE double) between the two candidates that
 //    bracket the target bit count (first candidate at or below it) or extrapolates from the end
 //    pair, rounds, clamps, and stores the answer as the next centre together with the k of the
 //    candidate nearest to it.  Pass A (8 candidates, h = 21: quarter octaves) starts at
@@ -331,13 +331,28 @@ __device__ void rate_solve(const int64_t* b, const double* R, const int* kc, int
   *k_out = kc[best];
 }
 
-// One rate pass's counters and candidates, for its solver.
+// One rate pass: its counters, candidates and workgroups.
 struct PassDesc {
-  const RateAcc* racc;
+  RateAcc* racc;
   int nc, half_log2, fixed_k;
   float target;
-  uint32_t N;
-  int final;  // this solve gives the call's operating point (it sets the point tag)
+  uint32_t N;     // sample tiles
+  uint32_t nblk;  // workgroups that add into the counters (workgroup b into set b mod kRcAccSlots)
+};
+
+// Arguments of the rate workgroups: the first workgroups of the encoder's launch when the call runs
+// rate control, or every workgroup of rate_kernel when hq_rate runs alone.
+struct RateArgs {
+  const void* x;
+  uint64_t T, seed;
+  uint32_t df;
+  Workspace* ws;
+  RatePub* pub;
+  PassDesc pa, pb;    // pass A (two passes only), and pass B or the single pass
+  int two_pass;
+  int64_t centre0;    // pass A's centre, or the fixed step's bits for the single pass
+  uint32_t nblk;      // rate workgroups: max(pa.nblk, pb.nblk)
+  uint32_t spin_budget;
 };
 
 struct SolveLds {
@@ -345,60 +360,162 @@ struct SolveLds {
   int64_t b[kRcCand];
   double R[kRcCand];
   int k[kRcCand];
-  int64_t xb;
-  int kres;
 };
 
-// Solve a rate pass around `centre` with the first lanes of a workgroup (every lane of the
-// workgroup calls it: it holds two barriers).  The counter sets are added in a fixed order; every
-// lane gets the result, and the workspace's step, k and centre are set to it.
-template <int LAT, int TL>
-__device__ void solve_pass(const PassDesc& pd, int64_t centre, Workspace* ws, SolveLds* L, int64_t* xb, int* k) {
-  const int tid = threadIdx.x;
-  if (tid < kRcCounters) {
-    uint64_t t = 0;
-#pragma unroll
-    for (int sl = 0; sl < kRcAccSlots; ++sl) t += pd.racc->cnt[sl][tid];
-    L->sumq[tid] = t;
-  }
-  __syncthreads();
-  if (tid < pd.nc) {
-    int64_t b;
-    double R;
-    int kk;
-    rate_candidate<LAT, TL>(L->sumq, centre, tid, pd.nc, pd.half_log2, pd.fixed_k, pd.N, &b, &R, &kk);
-    L->b[tid] = b;
-    L->R[tid] = R;
-    L->k[tid] = kk;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, TL, &L->xb, &L->kres);
-    ws->rc_centre = L->xb;
-    ws->step_bits = (uint32_t)L->xb;
-    ws->rice_k = L->kres;
-    ws->point_tag = pd.final ? kPointTag : 0u;
-  }
-  __syncthreads();
-  *xb = L->xb;
-  *k = L->kres;
-}
+// LDS of a rate workgroup.
+struct RateLds {
+  uint32_t red[kRcCounters];
+  SolveLds solve;
+  int64_t bcast;
+};
 
-// One wavefront's own solve of a rate pass (no barriers; the result is the same as solve_pass's:
-// the same counter sums and the same arithmetic), into L, which only this wavefront uses.
-template <int LAT, int TL>
-__device__ int64_t solve_pass_wave(const PassDesc& pd, int64_t centre, SolveLds* L) {
-  const int lane = threadIdx.x & 63;
-  if (lane < kRcCounters) {
-    uint64_t t = 0;
-#pragma unroll
-    for (int sl = 0; sl < kRcAccSlots; ++sl) t += __hip_atomic_load(&pd.racc->cnt[sl][lane], __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT);
-    L->sumq[lane] = t;
-  }
+// Orders one wavefront's LDS writes before its later reads (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Candidate j of a pass around `centre`, as a binary32 bit pattern.
+__device__ __forceinline__ int64_t candidate_bits(int64_t centre, int j, int nc, int half_log2) {
+  return nc == 1 ? centre
+                 : clamp_i64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2), kStepBitsMin,
+                             kStepBitsMax);
+}
+
+// One lane's octet of a sample tile: transformed values, dither and tile scale.
+struct Sample {
+  float y[8], u[8];
+  uint32_t sb;
+  bool valid;
+};
+
+// Sample tile i of a pass of N tiles (nothing past the sample): transform and dither of the lane's
+// octet.  Every lane of the wavefront calls it together.  True when the tile's energy is not finite.
+template <int LAT, bool DITHER, int DT, int TL>
+__device__ __forceinline__ bool sample_prepare(const RateArgs& A, uint32_t N, uint64_t i, int o, uint32_t sgn,
+                                               Sample& s) {
+  s.valid = i < N;
+  const uint64_t t = s.valid ? sample_tile(i, A.T, N) : 0;
+  bool finite;
+  s.sb = transform_octet<DT, TL>(A.x, t, s.valid, o, sgn, s.y, &finite);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s.u[k] = 0.0f;
+  if (DITHER) dither_octet<LAT>(A.seed, t, o, A.df, s.u);
+  return s.valid && !finite;
+}
+
+// Rice quotient sums of the lane's octet at candidate j of a pass around `centre`, over the
+// candidate's k window (q[w]; zeros for an invalid sample).  Each lane forms the multiplier of its
+// own tile (A2: and of the odd slots); j is the same in every lane.
+template <int LAT, bool DITHER, int TL>
+__device__ __forceinline__ void sample_eval(const Sample& s, int o, int64_t centre, const PassDesc& pd, int j,
+                                            uint32_t q[kRcKwin]) {
+  constexpr int LPT = Tiling<TL>::LPT;
+  const int64_t b = candidate_bits(centre, j, pd.nc, pd.half_log2);
+  const float step = __uint_as_float((uint32_t)b);
+  const uint32_t lane_neg = lane_sign_bit<LPT>(o);
+  const float m = tile_multiplier<false>(s.sb, step, lane_neg);
+  const float m1 = LAT == kLatA2 ? tile_multiplier<true>(s.sb, step, lane_neg) : m;
+  uint32_t sym[8], cos;
+  octet_symbols<LAT, DITHER>(s.y, m, m1, s.u, sym, &cos);
+  const int kb = pd.fixed_k >= 0 ? pd.fixed_k : kwin_base(b);
+#pragma unroll
+  for (int w = 0; w < kRcKwin; ++w) {
+    const int k = pd.fixed_k >= 0 ? pd.fixed_k : kb + w;
+    uint32_t t = 0;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) t += sym[sl] >> slot_width<LAT>(sl, k);
+    q[w] = s.valid ? t : 0u;
+  }
+}
+
+// Adds the workgroup's sums into counter set b mod kRcAccSlots of the pass: acc[jj][w] of
+// candidate j0 + jj (jj < nj; j0 and nj the same in a wavefront).  Every counter of the set
+// receives one contribution, zero or not, so that its count shows when all of the pass's
+// workgroups have added.  All lanes of the workgroup call it (two barriers).
+template <int NJ>
+__device__ void wg_add_counters(const uint32_t acc[NJ][kRcKwin], int j0, int nj, uint32_t* red, RateAcc* racc,
+                                uint32_t b) {
+  const int tid = threadIdx.x;
+  if (tid < kRcCounters) red[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+    for (int w = 0; w < kRcKwin; ++w)
+      if (jj < nj && acc[jj][w]) atomicAdd(&red[(j0 + jj) * kRcKwin + w], acc[jj][w]);
+  __syncthreads();
+  if (tid < kRcCounters)
+    __hip_atomic_fetch_add(&racc->cnt[b % kRcAccSlots][tid], (1ull << kCntShift) + red[tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Contributions that counter set s of a pass receives from its nblk workgroups.
+__device__ __forceinline__ uint32_t set_contribs(uint32_t s, uint32_t nblk) {
+  return s < nblk ? (nblk - 1u - s) / (uint32_t)kRcAccSlots + 1u : 0u;
+}
+
+// The pass's counters summed over its sets into sumq, as soon as every word holds all of its
+// contributions; false if that has not happened after `budget` polls.  One wavefront (all lanes).
+__device__ bool pass_sums_wave(const PassDesc& pd, uint32_t budget, uint64_t* sumq) {
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  for (uint32_t spins = 0;; ++spins) {
+    uint64_t sum = 0;
+    bool done = true;
+#pragma unroll
+    for (int m = 0; m < kRcAccSlots / 2; ++m) {
+      const int s = 2 * m + h;
+      const uint64_t w = __hip_atomic_load(&pd.racc->cnt[s][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      done = done && (uint32_t)(w >> kCntShift) == set_contribs((uint32_t)s, pd.nblk);
+      sum += w & ((1ull << kCntShift) - 1ull);
+    }
+    if (__ballot(!done) == 0) {
+      sum += __shfl_xor(sum, 32, 64);
+      if (lane < kRcCounters) sumq[lane] = sum;
+      wave_lds_sync();
+      return true;
+    }
+    if (spins >= budget) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Every sample tile of a pass evaluated by one wavefront at all of the pass's candidates, summed
+// into sumq: the same integer sums that the pass's workgroups add into its counters.  The fallback
+// of a wait that has exceeded its budget (written for size, not speed: it runs only then); all
+// lanes of the wavefront call it.  acc: kRcCounters words of LDS for this wavefront.
+template <int LAT, bool DITHER, int DT, int TL>
+__device__ void pass_sums_private(const RateArgs& A, const PassDesc& pd, int64_t centre, uint32_t* acc,
+                                  uint64_t* sumq) {
+  using TI = Tiling<TL>;
+  const int lane = threadIdx.x & 63, o = lane % TI::LPT, tw = lane / TI::LPT;
+  const uint32_t sgn = octet_sign_bits(A.seed, o);
+  if (lane < kRcCounters) acc[lane] = 0u;
+  wave_lds_sync();
+#pragma unroll 1
+  for (uint32_t i0 = 0; i0 < pd.N; i0 += (uint32_t)TI::TPW) {
+    Sample s;
+    sample_prepare<LAT, DITHER, DT, TL>(A, pd.N, (uint64_t)i0 + tw, o, sgn, s);
+#pragma unroll 1
+    for (int j = 0; j < pd.nc; ++j) {
+      uint32_t q[kRcKwin];
+      sample_eval<LAT, DITHER, TL>(s, o, centre, pd, j, q);
+#pragma unroll
+      for (int w = 0; w < kRcKwin; ++w)
+        if (q[w]) atomicAdd(&acc[j * kRcKwin + w], q[w]);
+    }
+  }
+  wave_lds_sync();
+  if (lane < kRcCounters) sumq[lane] = acc[lane];
+  wave_lds_sync();
+}
+
+// The candidates of a pass evaluated from its summed counters and solved by one wavefront (all
+// lanes call it): the next centre, or the final step bits, and the Rice k.  Wave-uniform results.
+template <int LAT, int TL>
+__device__ void solve_sums_wave(const PassDesc& pd, int64_t centre, SolveLds* L, int64_t* xb_out, int* k_out) {
+  const int lane = threadIdx.x & 63;
   if (lane < pd.nc) {
     int64_t b;
     double R;
@@ -408,168 +525,129 @@ __device__ int64_t solve_pass_wave(const PassDesc& pd, int64_t centre, SolveLds*
     L->R[lane] = R;
     L->k[lane] = kk;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_lds_sync();
   int64_t xb = 0;
-  int kres;
+  int kres = 0;
   if (lane == 0) rate_solve(L->b, L->R, L->k, pd.nc, pd.target, pd.N, TL, &xb, &kres);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)xb);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)xb >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
+  *xb_out = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xb);  // step bits: 32-bit, positive
+  *k_out = __builtin_amdgcn_readfirstlane(kres);
 }
 
-// The centre that workgroup 0 of this launch solves from the previous pass and publishes in `word`
-// (bit 63 set, the centre in the low 32 bits).  One lane per wavefront polls; after `budget` spin
-// rounds without it, the wavefront solves the previous pass itself (solve_pass_wave: the same
-// value), so the wait ends whatever order workgroups are started in.  Wave-uniform result.
-template <int LAT, int TL>
-__device__ int64_t wait_centre(const uint64_t* word, uint32_t budget, const PassDesc& prev, int64_t centre0,
-                               SolveLds* L) {
-  uint32_t got = 0, val = 0;
+// Solve of a pass by one wavefront from its counters, or, when they are not complete within the
+// budget, from its own evaluation of the whole sample (the same sums, hence the same result).
+template <int LAT, bool DITHER, int DT, int TL>
+__device__ void solve_pass_wave(const RateArgs& A, const PassDesc& pd, int64_t centre, uint32_t budget, RateLds* L,
+                                int64_t* xb, int* k) {
+  if (!pass_sums_wave(pd, budget, L->solve.sumq))
+    pass_sums_private<LAT, DITHER, DT, TL>(A, pd, centre, L->red, L->solve.sumq);
+  solve_sums_wave<LAT, TL>(pd, centre, &L->solve, xb, k);
+}
+
+// Polls a published word with lane 0 (bit 63 set once published): the word, or false after
+// `budget` polls.  Wave-uniform result.
+__device__ bool wait_pub(const uint64_t* word, uint32_t budget, uint64_t* val) {
+  uint32_t got = 0, lo = 0, hi = 0;
   if ((threadIdx.x & 63) == 0) {
     for (uint32_t spins = 0;; ++spins) {
       const uint64_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v >> 63) {
         got = 1;
-        val = (uint32_t)v;
+        lo = (uint32_t)v;
+        hi = (uint32_t)(v >> 32);
         break;
       }
       if (spins >= budget) break;
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  if (__builtin_amdgcn_readfirstlane(got)) return (int64_t)__builtin_amdgcn_readfirstlane(val);
-  return solve_pass_wave<LAT, TL>(prev, centre0, L);
+  got = __builtin_amdgcn_readfirstlane(got);
+  *val = ((uint64_t)__builtin_amdgcn_readfirstlane(hi) << 32) | __builtin_amdgcn_readfirstlane(lo);
+  return got != 0u;
 }
 
-// A wavefront takes TPW sample tiles and cpw of the pass's candidates; the cw = ceil(nc / cpw)
-// wavefronts that share a group of TPW tiles sit in the same workgroup, which therefore holds 4 / cw
-// tile groups (cw is 1, 2 or 4).  Splitting the candidates over wavefronts keeps each wavefront's
-// chain short and the pass latency low; every wavefront repeats its tiles' transform.
-// With solve_prev, workgroup 0 first solves the previous pass (prev, centre0) for this pass's
-// centre and publishes it in Workspace::sync_centre; the other workgroups transform their tiles
-// meanwhile and then wait for it (or, after spin_budget rounds, solve it themselves).
+// Publishes a word in every copy (lanes 0 .. kPubCopies-1 of the calling wavefront store one each).
+__device__ __forceinline__ void publish(uint64_t* words, uint64_t v) {
+  const int lane = threadIdx.x & 63;
+  if (lane < kPubCopies)
+    __hip_atomic_store(&words[lane * kPubStride], (1ull << 63) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Rate workgroup b (0 <= b < A.nblk).  Pass A: sample tiles b TPW .. b TPW + TPW - 1, two of its 8
+// candidates per wavefront (all four wavefronts take the same tiles).  Pass B (or the single
+// pass): sample tiles from 4 b TPW, TPW per wavefront, every candidate.  Workgroup 0 solves each
+// pass as soon as its counters are complete: pass A's solve, the centre of pass B, goes to every
+// rate workgroup through a published word (a workgroup that does not see it within its budget
+// solves pass A itself); pass B's solve is the call's operating point, which workgroup 0 stores in
+// the workspace and publishes to the chunk workgroups of the encoder.
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) void rate_kernel(const void* __restrict__ x, uint64_t T, uint32_t N,
-                                                      Workspace* ws, RateAcc* racc, uint64_t seed, uint32_t df,
-                                                      int nc, int half_log2, int fixed_k, float target, int cpw,
-                                                      int solve_prev, PassDesc prev, int64_t centre0,
-                                                      uint32_t spin_budget) {
-  constexpr int LPT = Tiling<TL>::LPT, TPW = Tiling<TL>::TPW;
-  __shared__ uint32_t s_red[1][kRcCand * kRcKwin];
-  __shared__ SolveLds s_solve;
-  __shared__ SolveLds s_fallback[kBlock / 64];  // one per wavefront, for wait_centre's own solve
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
-  int64_t centre_solved = 0;
-  const bool solver = solve_prev && blockIdx.x == 0;
-  if (solver) {
-    int kk;
-    solve_pass<LAT, TL>(prev, centre0, ws, &s_solve, &centre_solved, &kk);
-    if (tid == 0)
-      __hip_atomic_store(&ws->sync_centre, (1ull << 63) | (uint64_t)(uint32_t)centre_solved, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const int cw = (nc + cpw - 1) / cpw;
-  const int jlo = (wave % cw) * cpw, jhi = jlo + cpw;
-  const uint64_t i = ((uint64_t)blockIdx.x * (4 / cw) + wave / cw) * TPW + tw;
-  const bool valid = i < N;
-  const uint64_t t = valid ? sample_tile(i, T, N) : 0;
-  const uint32_t sgn = octet_sign_bits(seed, o);
-  float y[8];
-  bool finite;
-  const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
-  if (valid && !finite && o == 0 && jlo == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
-  float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (DITHER) dither_octet<LAT>(seed, t, o, df, u);
-  int64_t centre;
-  if (!solve_prev) {
-    centre = ws->rc_centre;  // stored by init_kernel
-  } else if (solver) {
-    centre = centre_solved;
-  } else {
-    centre = wait_centre<LAT, TL>(&ws->sync_centre, spin_budget, prev, centre0, &s_fallback[wave]);
-  }
-  // lane o computes the multiplier of candidate o mod 8 (A2: lanes 8..15 that of the odd slots, or,
-  // with 8 lanes per tile, every lane both); the group shares them by broadcast
-  const int jm = nc == 1 ? 0 : (o & 7);
-  const int64_t bm = nc == 1 ? centre
-                             : clamp_i64(centre + (int64_t)(2 * jm - (nc - 1)) * ((int64_t)1 << half_log2), kStepBitsMin,
-                                         kStepBitsMax);
-  const float stepm = __uint_as_float((uint32_t)bm);
-  const bool odd_lane = LAT == kLatA2 && LPT >= 16 && o >= 8;
-  const uint32_t m_mine = __float_as_uint(odd_lane ? tile_multiplier<true>(sb, stepm, 0u)
-                                                   : tile_multiplier<false>(sb, stepm, 0u));
-  const bool lane_neg = lane_sign_bit<LPT>(o) != 0u;
-  float mj[kRcCand], mo[kRcCand];
-  mj[0] = __uint_as_float(group_bcast<0, LPT>(m_mine)); mj[1] = __uint_as_float(group_bcast<1, LPT>(m_mine));
-  mj[2] = __uint_as_float(group_bcast<2, LPT>(m_mine)); mj[3] = __uint_as_float(group_bcast<3, LPT>(m_mine));
-  mj[4] = __uint_as_float(group_bcast<4, LPT>(m_mine)); mj[5] = __uint_as_float(group_bcast<5, LPT>(m_mine));
-  mj[6] = __uint_as_float(group_bcast<6, LPT>(m_mine)); mj[7] = __uint_as_float(group_bcast<7, LPT>(m_mine));
-  if constexpr (LAT == kLatA2 && LPT >= 16) {
-    mo[0] = __uint_as_float(group_bcast<8, LPT>(m_mine)); mo[1] = __uint_as_float(group_bcast<9, LPT>(m_mine));
-    mo[2] = __uint_as_float(group_bcast<10, LPT>(m_mine)); mo[3] = __uint_as_float(group_bcast<11, LPT>(m_mine));
-    mo[4] = __uint_as_float(group_bcast<12, LPT>(m_mine)); mo[5] = __uint_as_float(group_bcast<13, LPT>(m_mine));
-    mo[6] = __uint_as_float(group_bcast<14, LPT>(m_mine)); mo[7] = __uint_as_float(group_bcast<15, LPT>(m_mine));
-  } else if constexpr (LAT == kLatA2) {
-    const uint32_t m_odd = __float_as_uint(tile_multiplier<true>(sb, stepm, 0u));
-    mo[0] = __uint_as_float(group_bcast<0, LPT>(m_odd)); mo[1] = __uint_as_float(group_bcast<1, LPT>(m_odd));
-    mo[2] = __uint_as_float(group_bcast<2, LPT>(m_odd)); mo[3] = __uint_as_float(group_bcast<3, LPT>(m_odd));
-    mo[4] = __uint_as_float(group_bcast<4, LPT>(m_odd)); mo[5] = __uint_as_float(group_bcast<5, LPT>(m_odd));
-    mo[6] = __uint_as_float(group_bcast<6, LPT>(m_odd)); mo[7] = __uint_as_float(group_bcast<7, LPT>(m_odd));
-  } else {
+__device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
+  using TI = Tiling<TL>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
+  const uint32_t sgn = octet_sign_bits(A.seed, o);
+  const PassDesc& pb = A.pb;
+  const bool in_b = b < pb.nblk;
+  // pass B's sample first: its loads are in flight during pass A
+  Sample sb;
+  if (sample_prepare<LAT, DITHER, DT, TL>(A, pb.N, in_b ? ((uint64_t)b * 4 + wave) * TI::TPW + tw : pb.N, o, sgn,
+                                          sb) &&
+      o == 0)
+    atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
+  int64_t centre = A.centre0;
+  if (A.two_pass) {
+    const PassDesc& pa = A.pa;
+    if (b < pa.nblk) {  // uniform in the workgroup
+      Sample sa;
+      if (sample_prepare<LAT, DITHER, DT, TL>(A, pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa) && o == 0 &&
+          wave == 0)
+        atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
+      uint32_t acc[2][kRcKwin];
 #pragma unroll
-    for (int j = 0; j < kRcCand; ++j) mo[j] = mj[j];
-  }
-  uint32_t acc[kRcCand][kRcKwin];
-#pragma unroll
-  for (int j = 0; j < kRcCand; ++j)
-#pragma unroll
-    for (int w = 0; w < kRcKwin; ++w) acc[j][w] = 0;
-#pragma unroll
-  for (int j = 0; j < kRcCand; ++j) {
-    if (j < nc && j >= jlo && j < jhi) {  // uniform
-      const int64_t b = nc == 1 ? centre
-                                : clamp_i64(centre + (int64_t)(2 * j - (nc - 1)) * ((int64_t)1 << half_log2),
-                                            kStepBitsMin, kStepBitsMax);
-      const float m = lane_neg ? -mj[j] : mj[j];
-      const float m1 = lane_neg ? -mo[j] : mo[j];
-      uint32_t sym[8], cos;
-      octet_symbols<LAT, DITHER>(y, m, m1, u, sym, &cos);
-      const int kb = fixed_k >= 0 ? fixed_k : kwin_base(b);
-#pragma unroll
-      for (int w = 0; w < kRcKwin; ++w) {
-        const int k = fixed_k >= 0 ? fixed_k : kb + w;
-        uint32_t q = 0;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) q += sym[sl] >> slot_width<LAT>(sl, k);
-        acc[j][w] = valid ? q : 0u;
+      for (int jj = 0; jj < 2; ++jj) sample_eval<LAT, DITHER, TL>(sa, o, A.centre0, pa, 2 * wave + jj, acc[jj]);
+      wg_add_counters<2>(acc, 2 * wave, 2, L.red, pa.racc, b);
+    }
+    if (wave == 0) {
+      uint64_t v = 0;
+      int64_t c;
+      int k;
+      if (b != 0 && wait_pub(&A.pub->centre[(b % kPubCopies) * kPubStride], A.spin_budget, &v)) {
+        c = (int64_t)(uint32_t)v;
+      } else {  // the solver (workgroup 0), or a workgroup that has waited past its budget
+        solve_pass_wave<LAT, DITHER, DT, TL>(A, pa, A.centre0, A.spin_budget, &L, &c, &k);
+        if (b == 0) publish(A.pub->centre, (uint64_t)(uint32_t)c);
       }
+      if (lane == 0) L.bcast = c;
+    }
+    __syncthreads();
+    centre = L.bcast;
+  }
+  if (in_b) {  // uniform in the workgroup
+    uint32_t acc[kRcCandB][kRcKwin];
+#pragma unroll
+    for (int jj = 0; jj < kRcCandB; ++jj)
+      if (jj < pb.nc) sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, jj, acc[jj]);
+    wg_add_counters<kRcCandB>(acc, 0, pb.nc, L.red, pb.racc, b);
+  }
+  if (b == 0 && wave == 0) {
+    int64_t xb;
+    int k;
+    solve_pass_wave<LAT, DITHER, DT, TL>(A, pb, centre, A.spin_budget, &L, &xb, &k);
+    if (lane == 0) {
+      Workspace* ws = A.ws;
+      ws->rc_centre = xb;
+      ws->step_bits = (uint32_t)xb;
+      ws->rice_k = k;
+      ws->res_step_bits = (uint32_t)xb;
+      ws->res_k = k;
+      ws->point_tag = kPointTag;
     }
   }
-  // workgroup reduction through LDS atomics (no dependent shuffle chains)
-  if (tid < kRcCand * kRcKwin) s_red[0][tid] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kRcCand; ++j)
-#pragma unroll
-    for (int w = 0; w < kRcKwin; ++w)
-      if (j < nc && j >= jlo && j < jhi && acc[j][w]) atomicAdd(&s_red[0][j * kRcKwin + w], acc[j][w]);
-  __syncthreads();
-  // this workgroup's sums go into counter set blockIdx mod kRcAccSlots; rate_solve_kernel, the next
-  // launch on the stream, adds the sets up (the kernel boundary orders the atomics before its loads)
-  if (tid < kRcCounters && s_red[0][tid])
-    __hip_atomic_fetch_add(&racc->cnt[blockIdx.x % kRcAccSlots][tid], s_red[0][tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup: add up the counter sets of a rate pass, evaluate the candidates, solve.
-template <int LAT, int TL>
-__global__ __launch_bounds__(64) void rate_solve_kernel(Workspace* ws, PassDesc pd) {
-  __shared__ SolveLds s_solve;
-  int64_t xb;
-  int k;
-  solve_pass<LAT, TL>(pd, ws->rc_centre, ws, &s_solve, &xb, &k);
+// hq_rate alone: the rate workgroups in a launch of their own.
+template <int LAT, bool DITHER, int DT, int TL>
+__global__ __launch_bounds__(kBlock) void rate_kernel(RateArgs A) {
+  __shared__ RateLds L;
+  rate_workgroup<LAT, DITHER, DT, TL>(A, blockIdx.x, L);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1755,7 +1833,7 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode) {
   return hipGetLastError();
 }
 
-static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass, int final) {
+static PassDesc pass_desc(const EncodeArgs& a, int pass, int nc, int half_log2, uint32_t N, uint32_t nblk) {
   PassDesc d;
   d.racc = rate_acc(a.ws, pass);
   d.nc = nc;
@@ -1763,37 +1841,34 @@ static PassDesc pass_desc(const EncodeArgs& a, int nc, int half_log2, uint32_t N
   d.fixed_k = a.rice_k;
   d.target = a.target;
   d.N = N;
-  d.final = final;
+  d.nblk = nblk;
   return d;
 }
 
-hipError_t launch_rate_pass(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass, int nc0,
-                            int half_log2_0, uint32_t N0, int64_t centre0) {
-  // pass A (8 candidates, a small sample): two candidates per wavefront, so that the pass is not
-  // one long chain per wavefront; otherwise every wavefront takes all candidates of its tiles
-  const int cpw = nc == kRcCand ? 2 : nc;
-  const int cw = (nc + cpw - 1) / cpw;  // 1, 2 or 4 wavefronts per group of a wavefront's tiles
-  if (cw != 1 && cw != 2 && cw != 4) return hipErrorInvalidValue;  // nc is 1, 2, 4 or 8
-  const uint32_t tpw = 64u / ((uint32_t)a.tile / 8u);  // tiles per wavefront
-  const uint32_t tiles_per_block = tpw * (uint32_t)(4 / cw);
-  const uint32_t blocks = (N + tiles_per_block - 1) / tiles_per_block;
-  if (blocks == 0) return hipSuccess;
-  const int solve_prev = pass > 0 ? 1 : 0;
-  const PassDesc prev = solve_prev ? pass_desc(a, nc0, half_log2_0, N0, pass - 1, 0) : PassDesc{};
-#define HQ_RATE(L, D, T, TL)                                                                           \
-  hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, N, a.ws, \
-                     rate_acc(a.ws, pass), a.seed, (uint32_t)a.dither, nc, half_log2, a.rice_k, a.target, cpw,      \
-                     solve_prev, prev, centre0, a.spin_budget)
-  HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_RATE);
-#undef HQ_RATE
-  return hipGetLastError();
+static RateArgs rate_args(const EncodeArgs& a, const RatePlan& rp) {
+  RateArgs r;
+  r.x = a.x;
+  r.T = a.tiles;
+  r.seed = a.seed;
+  r.df = (uint32_t)a.dither;
+  r.ws = a.ws;
+  r.pub = rate_pub(a.ws);
+  r.two_pass = rp.two_pass;
+  r.pa = pass_desc(a, 0, kRcCand, 21, rp.two_pass ? rp.NA : 0u, rp.two_pass ? rp.blkA : 0u);
+  r.pb = rp.two_pass ? pass_desc(a, 1, kRcCandB, 18, rp.NB, rp.blkB) : pass_desc(a, 1, 1, 0, rp.NB, rp.blkB);
+  r.centre0 = rp.centre0;
+  r.nblk = r.pa.nblk > r.pb.nblk ? r.pa.nblk : r.pb.nblk;
+  r.spin_budget = a.spin_budget;
+  return r;
 }
 
-hipError_t launch_rate_solve(const EncodeArgs& a, int nc, int half_log2, uint32_t N, int pass) {
-  const PassDesc pd = pass_desc(a, nc, half_log2, N, pass, 1);
-#define HQ_SOLVE(L, D, T, TL) hipLaunchKernelGGL((rate_solve_kernel<L, TL>), dim3(1), dim3(64), 0, a.stream, a.ws, pd)
-  HQ_DISPATCH(a.lattice, false, 0, a.tile, HQ_SOLVE);
-#undef HQ_SOLVE
+hipError_t launch_rate(const EncodeArgs& a, const RatePlan& rp) {
+  if (!rp.needed) return hipSuccess;
+  const RateArgs r = rate_args(a, rp);
+#define HQ_RATE(L, D, T, TL) \
+  hipLaunchKernelGGL((rate_kernel<L, D, T, TL>), dim3(r.nblk), dim3(kBlock), 0, a.stream, r)
+  HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_RATE);
+#undef HQ_RATE
   return hipGetLastError();
 }
 
