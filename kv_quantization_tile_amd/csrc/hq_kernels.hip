@@ -586,20 +586,17 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
   const uint32_t sgn = octet_sign_bits(A.seed, o);
   const PassDesc& pb = A.pb;
   const bool in_b = b < pb.nblk;
-  // pass B's sample first: its loads are in flight during pass A
-  Sample sb;
-  if (sample_prepare<LAT, DITHER, DT, TL>(A, pb.N, in_b ? ((uint64_t)b * 4 + wave) * TI::TPW + tw : pb.N, o, sgn,
-                                          sb) &&
-      o == 0)
-    atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
+  // both passes' samples first, so that their loads are in flight together
+  Sample sb, sa;
+  const bool in_a = A.two_pass && b < A.pa.nblk;  // uniform in the workgroup
+  const bool nf_b = sample_prepare<LAT, DITHER, DT, TL>(
+      A, pb.N, in_b ? ((uint64_t)b * 4 + wave) * TI::TPW + tw : pb.N, o, sgn, sb);
+  const bool nf_a = in_a && sample_prepare<LAT, DITHER, DT, TL>(A, A.pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa);
+  if (o == 0 && (nf_b || (nf_a && wave == 0))) atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
   int64_t centre = A.centre0;
   if (A.two_pass) {
     const PassDesc& pa = A.pa;
-    if (b < pa.nblk) {  // uniform in the workgroup
-      Sample sa;
-      if (sample_prepare<LAT, DITHER, DT, TL>(A, pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa) && o == 0 &&
-          wave == 0)
-        atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
+    if (in_a) {
       uint32_t acc[2][kRcKwin];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) sample_eval<LAT, DITHER, TL>(sa, o, A.centre0, pa, 2 * wave + jj, acc[jj]);
@@ -619,13 +616,16 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
     }
     __syncthreads();
     centre = L.bcast;
-  }
-  if (in_b) {  // uniform in the workgroup
-    uint32_t acc[kRcCandB][kRcKwin];
+    if (in_b) {  // uniform in the workgroup: pass B's four candidates, independent of one another
+      uint32_t acc[kRcCandB][kRcKwin];
 #pragma unroll
-    for (int jj = 0; jj < kRcCandB; ++jj)
-      if (jj < pb.nc) sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, jj, acc[jj]);
-    wg_add_counters<kRcCandB>(acc, 0, pb.nc, L.red, pb.racc, b);
+      for (int jj = 0; jj < kRcCandB; ++jj) sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, jj, acc[jj]);
+      wg_add_counters<kRcCandB>(acc, 0, kRcCandB, L.red, pb.racc, b);
+    }
+  } else if (in_b) {  // the single pass: one candidate
+    uint32_t acc[1][kRcKwin];
+    sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, 0, acc[0]);
+    wg_add_counters<1>(acc, 0, 1, L.red, pb.racc, b);
   }
   if (b == 0 && wave == 0) {
     int64_t xb;
@@ -644,8 +644,10 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
 }
 
 // hq_rate alone: the rate workgroups in a launch of their own.
+// Two workgroups per CU are all it runs (512 workgroups for tiles of 128), so the compiler may
+// spend registers on overlapping the candidates' independent evaluations.
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) void rate_kernel(RateArgs A) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) void rate_kernel(RateArgs A) {
   __shared__ RateLds L;
   rate_workgroup<LAT, DITHER, DT, TL>(A, blockIdx.x, L);
 }
