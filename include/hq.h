@@ -18,7 +18,9 @@
  *    device); `params`, `info`, `out_bytes` are HOST pointers.  `stream` arguments of type
  *    hq_stream_t are hipStream_t values (0 = the null stream).
  *  - The caller owns every buffer.  The library allocates no device memory and keeps no state
- *    between calls apart from immutable constants; one workspace serves one call in flight.
+ *    between calls apart from immutable constants and a counter that numbers calls (a workspace
+ *    reports the errors recorded under the number of its last call, so nothing has to be cleared
+ *    before a call); one workspace serves one call in flight.
  *  - Tensors are flat arrays of n values, n a multiple of the tile length TL (64, 128 or 256; 128
  *    by default); tile t is values [TL t, TL t + TL).
  *  - Every call returns HQ_OK (0) or a negative hq_status code; no exception crosses the ABI.

@@ -6,7 +6,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 
 #include "../../include/hq.h"
 #include "hq_internal.h"
@@ -75,6 +78,20 @@ int status_from_flags(uint32_t f) {
 
 size_t workspace_bytes_for(uint64_t n) { return kWsHeader + kWsRate + align256h(8ull * (chunks_of(n) + 1)); }
 
+// Numbers of calls (see Workspace::err): consecutive from a random 64-bit start, so that a
+// workspace's earlier contents never carry the number of a new call.
+std::atomic<uint64_t> g_next_call{0};
+std::once_flag g_call_once;
+uint64_t next_call() {
+  std::call_once(g_call_once, [] {
+    std::random_device rd;
+    const uint64_t r = ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^
+                       (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    g_next_call.store(r | 1u);
+  });
+  return g_next_call.fetch_add(1);
+}
+
 uint32_t spin_budget() {
   const char* e = getenv("HQ_SPIN_BUDGET");
   if (!e || !*e) return kSpinBudget;
@@ -102,6 +119,7 @@ EncodeArgs make_args(const void* x, int dtype, uint64_t n, const hq_params* p, v
   a.ws = static_cast<Workspace*>(ws);
   a.stream = static_cast<hipStream_t>(s);
   a.spin_budget = spin_budget();
+  a.call = next_call();
   return a;
 }
 
@@ -156,7 +174,7 @@ int read_results(void* ws, hipStream_t s, Results* r) {
   Workspace h;
   if (hipMemcpyAsync(&h, ws, sizeof(Workspace), hipMemcpyDeviceToHost, s) != hipSuccess) return HQ_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return HQ_ERR_HIP;
-  r->status = h.status;
+  r->status = error_flags(h);
   r->step_bits = h.res_step_bits;
   r->k = h.res_k;
   r->total_bytes = h.res_total_bytes;
@@ -334,7 +352,7 @@ int hq_rate(const void* x, int32_t dtype, uint64_t n, const hq_params* params, h
   if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
       hipStreamSynchronize(a.stream) != hipSuccess)
     return HQ_ERR_HIP;
-  if (h.status) return status_from_flags(h.status);
+  if (error_flags(h)) return status_from_flags(error_flags(h));
   if (info) {
     memset(info, 0, sizeof(*info));
     float st;
@@ -391,7 +409,7 @@ int hq_decode(const void* stream_data, uint64_t stream_bytes, void* out, int32_t
   if (((uintptr_t)stream_data & 15u) || ((uintptr_t)out & 15u) || ((uintptr_t)workspace & 255u))
     return HQ_ERR_INVALID_ARG;
   if (launch_decode(static_cast<const uint8_t*>(stream_data), stream_bytes, out, out_dtype, n,
-                    static_cast<Workspace*>(workspace), static_cast<hipStream_t>(stream)) != hipSuccess)
+                    static_cast<Workspace*>(workspace), next_call(), static_cast<hipStream_t>(stream)) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }
@@ -418,20 +436,19 @@ int hq_gemv(const void* stream_data, uint64_t stream_bytes, uint64_t rows, uint6
   float* xt = reinterpret_cast<float*>(w + kWsHeader);
   float* tp = reinterpret_cast<float*>(w + kWsHeader + gemv_xt_bytes(cols));
   if (launch_gemv(static_cast<const uint8_t*>(stream_data), stream_bytes, rows, cols, x, x_dtype, y,
-                  static_cast<Workspace*>(workspace), xt, tp, static_cast<hipStream_t>(stream)) != hipSuccess)
+                  static_cast<Workspace*>(workspace), xt, tp, next_call(), static_cast<hipStream_t>(stream)) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }
 
 int hq_status(void* workspace, hq_stream_t stream) {
   if (!workspace) return HQ_ERR_INVALID_ARG;
-  uint32_t f = 0;
+  Workspace h;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(&f, reinterpret_cast<char*>(workspace) + offsetof(Workspace, status), 4,
-                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+  if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return HQ_ERR_HIP;
-  return status_from_flags(f);
+  return status_from_flags(error_flags(h));
 }
 
 int hq_codes(const void* x, int32_t dtype, uint64_t n, const hq_params* params, int32_t* codes, uint16_t* scales,

@@ -6,7 +6,7 @@
 
 namespace hq {
 
-// Device-side error flags recorded in Workspace::status.  kErrNoPoint: an encode at the operating
+// Device-side error flags recorded in Workspace::err.  kErrNoPoint: an encode at the operating
 // point left in the workspace (step == -1) found none there.
 enum { kErrNonfinite = 1u, kErrCapacity = 2u, kErrCorrupt = 4u, kErrTimeout = 8u, kErrRange = 16u,
        kErrNoPoint = 32u };
@@ -27,8 +27,7 @@ constexpr int kRcKwin = 4;
 // Device workspace.  The fixed part is 4 KiB; the encoder's look-back flags (one 64-bit word per
 // chunk, plus one) follow it.  Every field is (re)initialised by the first kernel of a call.
 struct alignas(256) Workspace {
-  uint32_t pad2[2];
-  uint32_t status;       // error flags (kErr*)
+  uint32_t pad2[3];
   uint32_t step_bits;    // operating point chosen so far (binary32 bits of the step)
   int32_t rice_k;
   uint32_t pad0;
@@ -56,6 +55,12 @@ struct alignas(256) Workspace {
   uint64_t dec_words;
   // kPointTag while step_bits / rice_k hold a complete operating point
   uint32_t point_tag;
+  // Errors: err[b] holds the number of the last call that recorded error flag 1 << b, and `call`
+  // the number of the call that last used the workspace (its kernels write it).  The flags of
+  // that call are the bits b with err[b] == call, so no kernel has to clear anything first.  The
+  // library numbers calls from a random 64-bit start.
+  uint64_t call;
+  uint64_t err[8];
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
 constexpr size_t kWsHeader = 4096;
@@ -118,6 +123,7 @@ struct EncodeArgs {
   Workspace* ws;
   hipStream_t stream;
   uint32_t spin_budget;
+  uint64_t call;       // number of this call (see Workspace::err)
 };
 
 // Modes of the call's first kernel (see init_kernel): the operating point is provisional (rate
@@ -141,9 +147,17 @@ hipError_t launch_rate(const EncodeArgs& a, const RatePlan& rp);
 // The encoder, at the operating point the workspace holds.
 hipError_t launch_encode(const EncodeArgs& a);
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
-                         Workspace* ws, hipStream_t stream);
+                         Workspace* ws, uint64_t call, hipStream_t stream);
 hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales);
 hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
-                       float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream);
+                       float* y, Workspace* ws, float* xt, float* tp, uint64_t call, hipStream_t stream);
+
+// The error flags that the workspace's last call recorded (host copy of the workspace header).
+inline uint32_t error_flags(const Workspace& h) {
+  uint32_t f = 0;
+  for (int b = 0; b < 8; ++b)
+    if (h.err[b] == h.call) f |= 1u << b;
+  return f;
+}
 
 }  // namespace hq

@@ -118,6 +118,14 @@ __device__ __forceinline__ int64_t clamp_i64(int64_t v, int64_t lo, int64_t hi) 
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Records error flags of call `call` in the workspace (see Workspace::err): every writer of a flag
+// stores the same value, so plain relaxed stores suffice and nothing needs clearing first.
+__device__ __forceinline__ void record_error(Workspace* ws, uint64_t call, uint32_t flags) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+    if ((flags >> b) & 1u) __hip_atomic_store(&ws->err[b], call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Lane layout of a tile length TL: LPT lanes per tile, TPW tiles per wavefront, TPR tiles per
 // workgroup round, CT tiles per chunk (four rounds, kChunkValues values).
 template <int TL>
@@ -208,14 +216,15 @@ __device__ __forceinline__ void octet_symbols(const float* y, float m, float m1,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Resets a call's workspace: status, results, the look-back flags and the rate counters.
+// Resets a call's workspace: results, the look-back flags and the rate counters, and numbers the
+// workspace with the call (its errors are then those recorded under that number).
 // mode kInitProvisional / kInitFinal: the operating point becomes (step_bits, k), and the point tag
 // says whether it is complete (kInitFinal) or awaits rate passes (their last solve sets the tag).
 // mode kInitKeep (an encode with step == -1): the operating point already in the workspace is
 // kept; without a valid tag, or with a step or k out of range, the call records kErrNoPoint and
 // the encoder runs at a harmless point (step 1, k 0) so that every access stays in bounds.
 __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uint32_t* acc, uint32_t nacc,
-                            int64_t centre, uint32_t step_bits, int32_t k, int mode) {
+                            int64_t centre, uint32_t step_bits, int32_t k, int mode, uint64_t call) {
   const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid == 0) {
     uint32_t status = 0;
@@ -232,7 +241,8 @@ __global__ void init_kernel(Workspace* ws, uint64_t* flags, uint64_t nflags, uin
       ws->point_tag = mode == kInitFinal ? kPointTag : 0u;
       ws->rc_centre = centre;
     }
-    ws->status = status;
+    ws->call = call;
+    if (status) record_error(ws, call, status);
     ws->step_bits = step_bits;
     ws->rice_k = k;
     ws->res_total_bytes = 0;
@@ -353,6 +363,7 @@ struct RateArgs {
   int64_t centre0;    // pass A's centre, or the fixed step's bits for the single pass
   uint32_t nblk;      // rate workgroups: max(pa.nblk, pb.nblk)
   uint32_t spin_budget;
+  uint64_t call;
 };
 
 struct SolveLds {
@@ -592,7 +603,7 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
   const bool nf_b = sample_prepare<LAT, DITHER, DT, TL>(
       A, pb.N, in_b ? ((uint64_t)b * 4 + wave) * TI::TPW + tw : pb.N, o, sgn, sb);
   const bool nf_a = in_a && sample_prepare<LAT, DITHER, DT, TL>(A, A.pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa);
-  if (o == 0 && (nf_b || (nf_a && wave == 0))) atomicOr(&A.ws->status, (uint32_t)kErrNonfinite);
+  if (o == 0 && (nf_b || (nf_a && wave == 0))) record_error(A.ws, A.call, kErrNonfinite);
   int64_t centre = A.centre0;
   if (A.two_pass) {
     const PassDesc& pa = A.pa;
@@ -820,6 +831,7 @@ struct EncParams {
   Workspace* ws;
   uint64_t* flags;
   uint32_t spin_budget;
+  uint64_t call;
 };
 
 // The encoder's LDS: the chunk's fixed record, the unary staging window, per-round wavefront totals,
@@ -878,7 +890,7 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
       write_header(P.out, P.cap, LAT, P.dflags, k, step_bits, P.seed, P.n, P.T, 0, F, fixed_off, unary_off, 0, 0,
                    0, total, TL, __builtin_ctz(TI::CT));
       if (P.cap >= kHeaderBytes + 4) reinterpret_cast<uint32_t*>(P.out)[kHeaderBytes / 4] = 0;
-      if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+      if (total > P.cap) record_error(ws, P.call, kErrCapacity);
       ws->res_total_bytes = total;
       ws->res_payload_bits = 0;
       ws->res_unary_bits = 0;
@@ -926,7 +938,7 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
     const float Sr = rr == 0 ? S[0] : rr == 1 ? S[1] : rr == 2 ? S[2] : S[3];
     const bool fin = isfinite(Sr);
     const uint64_t t = (uint64_t)c * TI::CT + (uint32_t)TI::TPR * rr + (uint32_t)TI::TPW * wave + tw;
-    if (!fin && t < P.T && o < 4) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+    if (!fin && t < P.T && o < 4) record_error(ws, P.call, kErrNonfinite);
     sb_mine = tile_scale_bits<TL>(fin ? Sr : 0.0f);
     m_mine = (LAT == kLatA2 && (o & 4)) ? tile_multiplier<true>(sb_mine, step, 0u)
                                         : tile_multiplier<false>(sb_mine, step, 0u);
@@ -1090,15 +1102,15 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
       uint4* dst = reinterpret_cast<uint4*>(P.out + fbase);
       for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) dst[i] = s_fixed4[i];
     } else if (tid == 0) {
-      atomicOr(&ws->status, (uint32_t)kErrCapacity);
+      record_error(ws, P.call, kErrCapacity);
     }
   }
   if (tid == 0) {
-    if (prefix + W > 0xFFFFFFFFull) atomicOr(&ws->status, (uint32_t)kErrRange);  // u32 chunk index
+    if (prefix + W > 0xFFFFFFFFull) record_error(ws, P.call, kErrRange);  // u32 chunk index
     if (kHeaderBytes + 4ull * c + 4 <= P.cap)
       reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[c] = (uint32_t)prefix;
     else
-      atomicOr(&ws->status, (uint32_t)kErrCapacity);
+      record_error(ws, P.call, kErrCapacity);
   }
 
   const uint64_t ubase = unary_off + 8ull * prefix;
@@ -1140,7 +1152,7 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
       for (uint32_t i = tid; i < nw; i += kBlock) dst[i] = s_unary[i];
     }
   }
-  if (!fits && tid == 0) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+  if (!fits && tid == 0) record_error(ws, P.call, kErrCapacity);
 
   if (c == P.chunks - 1 && tid == 0) {
     const uint64_t words = prefix + W;
@@ -1151,7 +1163,7 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
                  words, ubits, payload, total, TL, __builtin_ctz(TI::CT));
     if (kHeaderBytes + 4ull * P.chunks + 4 <= P.cap)
       reinterpret_cast<uint32_t*>(P.out + kHeaderBytes)[P.chunks] = (uint32_t)words;
-    if (total > P.cap) atomicOr(&ws->status, (uint32_t)kErrCapacity);
+    if (total > P.cap) record_error(ws, P.call, kErrCapacity);
     ws->res_total_bytes = total;
     ws->res_payload_bits = payload;
     ws->res_unary_bits = ubits;
@@ -1175,7 +1187,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DITHER ?
 template <int LAT, bool DITHER, int DT, int TL>
 __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ x, uint64_t T, uint64_t seed,
                                                        uint32_t df, uint32_t step_bits, int32_t* __restrict__ codes,
-                                                       uint16_t* __restrict__ scales, Workspace* ws) {
+                                                       uint16_t* __restrict__ scales, Workspace* ws, uint64_t call) {
   using TI = Tiling<TL>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
   const uint64_t t = (uint64_t)blockIdx.x * TI::TPR + wave * TI::TPW + tw;
@@ -1184,7 +1196,7 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
   float y[8];
   bool finite;
   const uint32_t sb = transform_octet<DT, TL>(x, t, valid, o, sgn, y, &finite);
-  if (valid && !finite && o == 0) atomicOr(&ws->status, (uint32_t)kErrNonfinite);
+  if (valid && !finite && o == 0) record_error(ws, call, kErrNonfinite);
   float u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (DITHER) dither_octet<LAT>(seed, t, o, df, u);
   int32_t code[8];
@@ -1200,86 +1212,102 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(const void* __restrict__ 
 // ---------------------------------------------------------------------------------------------
 // Decoder.
 // The stream header's validity and the fields the decoder needs.
-struct HeaderCheck {
-  uint32_t ok, tile;
-  uint64_t seed;
+// Fields of a stream header that the decoder needs.
+struct DecInfo {
+  uint32_t tile, lattice, dither, F, chunks, step_bits;
+  int k;
+  uint64_t seed, tiles, fixed_off, unary_off, words;
 };
 
-// Header validation by one workgroup (every lane calls it: it holds two barriers).  cols: the row
-// length of a matrix product (a whole number of the stream's tiles), 0 for a plain decode.  With
-// `publish`, lane 0 records the result in the workspace (status, and the decoder's fields when the
-// stream is valid); every lane receives the result in *res (LDS).
-__device__ void check_header(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, uint64_t cols,
-                             Workspace* ws, bool publish, HeaderCheck* res) {
-  __shared__ uint32_t s_h[32];
-  __shared__ uint32_t s_idx[2];
-  const int tid = threadIdx.x;
-  const bool have = in_bytes >= (uint64_t)kHeaderBytes;
-  if (tid < 32) s_h[tid] = have ? reinterpret_cast<const uint32_t*>(in)[tid] : 0u;
-  __syncthreads();
-  const uint32_t* h = s_h;
+// Validates the stream header of `in` (in_bytes bytes) for n values and, for a matrix product, a row
+// length cols of whole tiles (0 for a plain decode), with the first and last chunk index entries,
+// and fills *d.  Scalar loads: every lane computes the same.  False for a corrupt stream.
+__device__ __forceinline__ bool read_header(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n,
+                                            uint64_t cols, DecInfo* d) {
+  // a chunk is kChunkValues values at every tile length: the chunk count, and with it the first and
+  // last index entries, follow from n, so their loads go out with the header's
+  const uint32_t chunks = (uint32_t)((n + kChunkValues - 1) / kChunkValues);
+  if (in_bytes < (uint64_t)kHeaderBytes + 4ull * ((uint64_t)chunks + 1)) return false;
+  const uint32_t* __restrict__ h = reinterpret_cast<const uint32_t*>(in);
+  const uint32_t* __restrict__ idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
+  const uint32_t i_first = idx[0], i_last = idx[chunks];
   const uint64_t hn = ((uint64_t)h[7] << 32) | h[6];
   const uint32_t htile = h[2] & 0xFFFFu;
   const bool tile_ok = htile == 64u || htile == 128u || htile == 256u;
   const uint32_t tile = tile_ok ? htile : 128u;
   const uint32_t ct = (uint32_t)kChunkValues / tile;  // tiles per chunk
   const uint64_t T = n / tile;
-  const uint32_t chunks = (uint32_t)((T + ct - 1) / ct);
   const int lattice = (int)((h[1] >> 16) & 0xFF), flags = (int)(h[1] >> 24), k = (int)((h[2] >> 16) & 0xFF);
   const bool flags_ok = flags == 0 || (flags <= 7 && (flags & 1));  // dither flags
-  bool ok = have && tile_ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags_ok &&
-            k <= 15 && (h[2] >> 24) == (uint32_t)__builtin_ctz(ct) && h[3] >= kStepBitsMin &&
-            h[3] <= kStepBitsMax && hn == n && (n % tile) == 0 && (cols % tile) == 0;
-  uint32_t F = 0;
-  if (ok) {
-    const int kh = k > 0 ? k - 1 : 0;
-    const int rem = lattice == kLatE8 ? 7 * k + kh
-                    : lattice == kLatD4 ? 6 * k + 2 * kh
-                    : lattice == kLatA2 ? 4 * k + 4 * kh
-                                        : 8 * k;
-    const uint32_t oct = tile / 8u;
-    F = 16u + (lattice == kLatE8 ? oct : lattice == kLatA2 ? 4u * oct : 0u) + oct * (uint32_t)rem;
-  }
+  if (!(tile_ok && h[0] == kMagic && (h[1] & 0xFFFFu) == kVersion && lattice <= kLatA2 && flags_ok && k <= 15 &&
+        (h[2] >> 24) == (uint32_t)__builtin_ctz(ct) && h[3] >= kStepBitsMin && h[3] <= kStepBitsMax && hn == n &&
+        (n % tile) == 0 && (cols % tile) == 0))
+    return false;
+  const int kh = k > 0 ? k - 1 : 0;
+  const int rem = lattice == kLatE8 ? 7 * k + kh
+                  : lattice == kLatD4 ? 6 * k + 2 * kh
+                  : lattice == kLatA2 ? 4 * k + 4 * kh
+                                      : 8 * k;
+  const uint32_t oct = tile / 8u;
+  const uint32_t F = 16u + (lattice == kLatE8 ? oct : lattice == kLatA2 ? 4u * oct : 0u) + oct * (uint32_t)rem;
   const uint64_t fixed_off = align256(kHeaderBytes + 4ull * (chunks + 1));
   const uint64_t unary_off = align256(fixed_off + (uint64_t)chunks * ct * F / 8ull);
   const uint64_t words = ((uint64_t)h[17] << 32) | h[16];
   const uint64_t total = ((uint64_t)h[23] << 32) | h[22];
-  ok = ok && (((uint64_t)h[9] << 32) | h[8]) == T && h[10] == chunks && h[11] == F &&
-       (((uint64_t)h[13] << 32) | h[12]) == fixed_off && (((uint64_t)h[15] << 32) | h[14]) == unary_off &&
-       total <= in_bytes && words <= (1ull << 32) && unary_off + 8ull * words == total;
-  if (ok && tid < 2) s_idx[tid] = reinterpret_cast<const uint32_t*>(in + kHeaderBytes)[tid == 0 ? 0 : chunks];
-  __syncthreads();
-  if (tid == 0) {
-    ok = ok && s_idx[0] == 0u && (uint64_t)s_idx[1] == words;
-    res->ok = ok ? 1u : 0u;
-    res->tile = tile;
-    res->seed = ((uint64_t)h[5] << 32) | h[4];
-    if (publish) {
-      ws->dec_valid = 0;
-      ws->status = ok ? 0u : (uint32_t)kErrCorrupt;
-      if (ok) {
-        ws->dec_tile = tile;
-        ws->dec_lattice = (uint32_t)lattice;
-        ws->dec_dither = (uint32_t)flags;
-        ws->dec_k = k;
-        ws->dec_step_bits = h[3];
-        ws->dec_F = F;
-        ws->dec_chunks = chunks;
-        ws->dec_seed = res->seed;
-        ws->dec_tiles = T;
-        ws->dec_fixed_off = fixed_off;
-        ws->dec_unary_off = unary_off;
-        ws->dec_words = words;
-        ws->dec_valid = 1;
-      }
-    }
-  }
-  __syncthreads();
+  if (!((((uint64_t)h[9] << 32) | h[8]) == T && h[10] == chunks && h[11] == F &&
+        (((uint64_t)h[13] << 32) | h[12]) == fixed_off && (((uint64_t)h[15] << 32) | h[14]) == unary_off &&
+        total <= in_bytes && words <= (1ull << 32) && unary_off + 8ull * words == total))
+    return false;
+  if (!(i_first == 0u && (uint64_t)i_last == words)) return false;
+  d->tile = tile;
+  d->lattice = (uint32_t)lattice;
+  d->dither = (uint32_t)flags;
+  d->k = k;
+  d->step_bits = h[3];
+  d->F = F;
+  d->chunks = chunks;
+  d->seed = ((uint64_t)h[5] << 32) | h[4];
+  d->tiles = T;
+  d->fixed_off = fixed_off;
+  d->unary_off = unary_off;
+  d->words = words;
+  return true;
 }
 
-__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws) {
-  __shared__ HeaderCheck s_res;
-  check_header(in, in_bytes, n, 0, ws, true, &s_res);
+// The header check of a matrix product, whose later kernels read the header's fields from the
+// workspace: read_header, and lane 0 of the calling workgroup numbers the workspace with the call,
+// publishes the fields (or the error) there.
+__device__ bool check_header(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, uint64_t cols,
+                             Workspace* ws, bool publish, uint64_t call, DecInfo* d) {
+  const bool ok = read_header(in, in_bytes, n, cols, d);
+  if (publish && threadIdx.x == 0) {
+    ws->call = call;
+    ws->dec_valid = 0;
+    if (!ok) record_error(ws, call, kErrCorrupt);
+    if (ok) {
+      ws->dec_tile = d->tile;
+      ws->dec_lattice = d->lattice;
+      ws->dec_dither = d->dither;
+      ws->dec_k = d->k;
+      ws->dec_step_bits = d->step_bits;
+      ws->dec_F = d->F;
+      ws->dec_chunks = d->chunks;
+      ws->dec_seed = d->seed;
+      ws->dec_tiles = d->tiles;
+      ws->dec_fixed_off = d->fixed_off;
+      ws->dec_unary_off = d->unary_off;
+      ws->dec_words = d->words;
+      ws->dec_valid = 1;
+    }
+  }
+  return ok;
+}
+
+// The header check alone (a matrix product of an empty matrix).
+__global__ void decode_check_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, Workspace* ws,
+                                    uint64_t call) {
+  DecInfo d;
+  check_header(in, in_bytes, n, 0, ws, true, call, &d);
 }
 
 constexpr int kMaxSymsPerChunk = kChunkValues;
@@ -1341,7 +1369,8 @@ constexpr uint32_t kPos16Words = 2048;       // 65536 bits
 constexpr uint32_t kPosHalf = kMaxSymsPerChunk / 2;
 template <int MODE>
 __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t nsym,
-                                                uint32_t* s_pos, uint32_t* s_boundary, Workspace* ws) {
+                                                uint32_t* s_pos, uint32_t* s_boundary, Workspace* ws,
+                                                uint64_t call) {
   uint32_t* s_wsum = s_pos;  // the four wavefront totals, read before any position is written
   uint16_t* t16 = reinterpret_cast<uint16_t*>(s_pos);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1368,7 +1397,7 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
   const uint32_t total = (t0 + t1) + (t2 + t3);
   __syncthreads();  // every lane has the totals before the table is overwritten
   if (total != nsym) {  // uniform: the whole workgroup leaves
-    if (tid == 0 && MODE != 2) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+    if (tid == 0 && MODE != 2) record_error(ws, call, kErrCorrupt);
     return false;
   }
   uint32_t g = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + incl - cnt;
@@ -1413,7 +1442,7 @@ __device__ __forceinline__ bool unary_positions(const uint32_t* __restrict__ seg
 
 template <int LAT, int DT_OUT, bool GEMV, int TL, int KC = -1>
 __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in, void* __restrict__ out,
-                                                  Workspace* ws, uint32_t c, uint32_t tiles_c,
+                                                  Workspace* ws, uint64_t call, uint32_t c, uint32_t tiles_c,
                                                   const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t* s_pos,
                                                   uint32_t* s_boundary, GemvArgs g) {
   using TI = Tiling<TL>;
@@ -1424,16 +1453,18 @@ __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % LPT, tw = lane / LPT;
   // KC >= 0: the stream's Rice parameter as a compile-time constant (the header check has
   // verified that the record length matches it)
-  const int k = KC >= 0 ? KC : ws->dec_k;
-  const uint32_t F = KC >= 0 ? tile_fixed_bits<LAT, TL>(KC) : ws->dec_F;
-  const uint32_t df = ws->dec_dither;  // dither flags of the stream
+  // the stream's fields, read from its (validated, read-only) header where they are needed
+  const uint32_t* __restrict__ hw = reinterpret_cast<const uint32_t*>(in);
+  const int k = KC >= 0 ? KC : (int)((hw[2] >> 16) & 0xFFu);
+  const uint32_t F = KC >= 0 ? tile_fixed_bits<LAT, TL>(KC) : hw[11];
+  const uint32_t df = hw[1] >> 24;  // dither flags of the stream
   const bool dither = df != 0u;
-  const uint64_t seed = ws->dec_seed;
-  const float step = __uint_as_float(ws->dec_step_bits);
+  const uint64_t seed = ((uint64_t)hw[5] << 32) | hw[4];
+  const float step = __uint_as_float(hw[3]);
   const int RW = octet_rem_bits<LAT>(k);
   const uint32_t hdr = (uint32_t)tile_hdr_bits<LAT, TL>();
   const uint32_t* __restrict__ fw =
-      reinterpret_cast<const uint32_t*>(in + ws->dec_fixed_off + (uint64_t)c * ((uint64_t)TI::CT * F / 8ull));
+      reinterpret_cast<const uint32_t*>(in + (((uint64_t)hw[13] << 32) | hw[12]) + (uint64_t)c * ((uint64_t)TI::CT * F / 8ull));
   // output factor per coordinate: +-1/TL with the sign of D and of the lane's butterfly sign; the
   // fused multiply-add with +0 below is exact and turns an exact zero into +0
   const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit<LPT>(o) ? 0xFFu : 0u);
@@ -1649,61 +1680,88 @@ __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in
   // the first round's record words are in flight while the positions are found
   issue(0);
   const uint32_t nsym = tiles_c * (uint32_t)TL;
-  if (!(wide ? unary_positions<1>(seg, nW32, nsym, s_pos, s_boundary, ws)
-              : unary_positions<0>(seg, nW32, nsym, s_pos, s_boundary, ws)))
+  if (!(wide ? unary_positions<1>(seg, nW32, nsym, s_pos, s_boundary, ws, call)
+              : unary_positions<0>(seg, nW32, nsym, s_pos, s_boundary, ws, call)))
     return;
   do_round(0);
   do_round(1);
   if (wide) {
     __syncthreads();  // every read of the first half is done before the table is rewritten
-    if (!unary_positions<2>(seg, nW32, nsym, s_pos, s_boundary, ws)) return;
+    if (!unary_positions<2>(seg, nW32, nsym, s_pos, s_boundary, ws, call)) return;
   }
   do_round(2);
   do_round(3);
-  if (bad) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+  if (bad) record_error(ws, call, kErrCorrupt);
 }
 
-// One workgroup per chunk: the chunk's index entries are checked, then decode_chunk of the stream's
-// lattice and tile length finds the terminator positions (unary_positions) and decodes the tiles.
+// One workgroup per chunk.  A plain decode validates the stream header in every workgroup (scalar
+// loads of 128 bytes; workgroup 0 numbers the workspace with the call), a matrix product takes the
+// fields its rotation kernel checked and published.  Then the chunk's index entries are checked,
+// and decode_chunk of the stream's lattice and tile length finds the terminator positions
+// (unary_positions) and decodes the tiles.
 template <int DT_OUT, bool GEMV>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_kernel(
-    const uint8_t* __restrict__ in, void* __restrict__ out, Workspace* ws, GemvArgs gv) {
+    const uint8_t* __restrict__ in, uint64_t in_bytes, uint64_t n, void* __restrict__ out, Workspace* ws,
+    GemvArgs gv, uint64_t call) {
   // 16 KiB of terminator positions (8192 16-bit or 4096 32-bit entries) and the boundary word: the
   // register budget of six waves per SIMD, not LDS, sets the occupancy
   __shared__ uint4 s_pos4[kMaxSymsPerChunk / 8];
   __shared__ uint32_t s_boundary;
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
-  if (!ws->dec_valid) return;
   const int tid = threadIdx.x;
   const uint32_t c = blockIdx.x;
-  const uint32_t chunks = ws->dec_chunks;
+  // a chunk holds kChunkValues values at every tile length, so n gives the chunk count: while the
+  // header is in flight the chunk's index entries can be requested too (when the stream is long
+  // enough to hold the index at all)
+  const uint32_t chunks_n = (uint32_t)((n + kChunkValues - 1) / kChunkValues);
+  const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
+  const bool idx_in = in_bytes >= (uint64_t)kHeaderBytes + 4ull * ((uint64_t)chunks_n + 1) && c < chunks_n;
+  const uint32_t w0 = idx_in ? idx[c] : 0u, w1 = idx_in ? idx[c + 1] : 0u;
+  if (GEMV) {
+    if (!ws->dec_valid) return;
+  } else {
+    DecInfo d;
+    const bool ok = read_header(in, in_bytes, n, 0, &d);
+    if (tid == 0) {
+      if (c == 0) __hip_atomic_store(&ws->call, call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!ok) record_error(ws, call, kErrCorrupt);
+    }
+    if (!ok) return;
+  }
+  // the stream's fields, read again from its validated header (read-only, so the compiler may
+  // reload them instead of keeping them in registers)
+  const uint32_t* __restrict__ hw = reinterpret_cast<const uint32_t*>(in);
+  const uint32_t chunks = hw[10];
   if (c >= chunks) return;
-  const uint64_t T = ws->dec_tiles;
-  const uint32_t tile = ws->dec_tile;
+  const uint64_t T = ((uint64_t)hw[9] << 32) | hw[8];
+  const uint32_t tile = hw[2] & 0xFFFFu;
+  const uint32_t lattice = (hw[1] >> 16) & 0xFFu;
+  const int hk = (int)((hw[2] >> 16) & 0xFFu);
+  const uint64_t words = ((uint64_t)hw[17] << 32) | hw[16];
+  const uint64_t unary_off = ((uint64_t)hw[15] << 32) | hw[14];
   const uint32_t ct = (uint32_t)kChunkValues / tile;
   const uint32_t tiles_c = (uint32_t)min((uint64_t)ct, T - (uint64_t)c * ct);
-  const uint32_t* idx = reinterpret_cast<const uint32_t*>(in + kHeaderBytes);
-  const uint32_t w0 = idx[c], w1 = idx[c + 1];
-  if (w1 < w0 || (uint64_t)w1 > ws->dec_words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
-    if (tid == 0) atomicOr(&ws->status, (uint32_t)kErrCorrupt);
+  if (w1 < w0 || (uint64_t)w1 > words || (uint64_t)(w1 - w0) * 64ull > 0xFFFFFFFFull) {
+    if (tid == 0) record_error(ws, call, kErrCorrupt);
     return;
   }
-  const uint32_t* __restrict__ seg = reinterpret_cast<const uint32_t*>(in + ws->dec_unary_off + 8ull * w0);
+  const uint32_t* __restrict__ seg = reinterpret_cast<const uint32_t*>(in + unary_off + 8ull * w0);
   const uint32_t nW32 = 2u * (w1 - w0);
   // uniform dispatch on the stream's lattice and tile length
-#define HQ_DEC_LAT(TLV)                                                                                      \
-  switch (ws->dec_lattice) {                                                                                 \
-    case kLatE8: decode_chunk_body<kLatE8, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
-    case kLatA2: decode_chunk_body<kLatA2, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
-    case kLatD4: decode_chunk_body<kLatD4, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break; \
-    default: decode_chunk_body<kLatZ, DT_OUT, GEMV, TLV>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;      \
+#define HQ_DEC_ARGS in, out, ws, call, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv
+#define HQ_DEC_LAT(TLV)                                                                  \
+  switch (lattice) {                                                                     \
+    case kLatE8: decode_chunk_body<kLatE8, DT_OUT, GEMV, TLV>(HQ_DEC_ARGS); break;       \
+    case kLatA2: decode_chunk_body<kLatA2, DT_OUT, GEMV, TLV>(HQ_DEC_ARGS); break;       \
+    case kLatD4: decode_chunk_body<kLatD4, DT_OUT, GEMV, TLV>(HQ_DEC_ARGS); break;       \
+    default: decode_chunk_body<kLatZ, DT_OUT, GEMV, TLV>(HQ_DEC_ARGS); break;            \
   }
-  if (tile == 128u && ws->dec_lattice == kLatE8 && ws->dec_k <= 3) {
-    switch (ws->dec_k) {
-      case 0: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 0>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
-      case 1: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 1>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
-      case 2: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 2>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
-      default: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 3>(in, out, ws, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv); break;
+  if (tile == 128u && lattice == kLatE8 && hk <= 3) {
+    switch (hk) {
+      case 0: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 0>(HQ_DEC_ARGS); break;
+      case 1: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 1>(HQ_DEC_ARGS); break;
+      case 2: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 2>(HQ_DEC_ARGS); break;
+      default: decode_chunk_body<kLatE8, DT_OUT, GEMV, 128, 3>(HQ_DEC_ARGS); break;
     }
   } else if (tile == 64u) {
     HQ_DEC_LAT(64)
@@ -1713,6 +1771,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6, 8))) 
     HQ_DEC_LAT(128)
   }
 #undef HQ_DEC_LAT
+#undef HQ_DEC_ARGS
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1758,17 +1817,15 @@ __device__ __forceinline__ void gemv_rotate_tiles(const void* __restrict__ x, ui
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gemv_rotate_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
                                                              uint64_t n, const void* __restrict__ x, uint64_t cols,
-                                                             Workspace* ws, float* __restrict__ xt) {
-  __shared__ HeaderCheck s_res;
-  check_header(in, in_bytes, n, cols, ws, blockIdx.x == 0, &s_res);
-  if (!s_res.ok) return;
-  const uint32_t tile = s_res.tile;
-  if (tile == 64u)
-    gemv_rotate_tiles<DT, 64>(x, cols, s_res.seed, xt);
-  else if (tile == 256u)
-    gemv_rotate_tiles<DT, 256>(x, cols, s_res.seed, xt);
+                                                             Workspace* ws, float* __restrict__ xt, uint64_t call) {
+  DecInfo d;
+  if (!check_header(in, in_bytes, n, cols, ws, blockIdx.x == 0, call, &d)) return;
+  if (d.tile == 64u)
+    gemv_rotate_tiles<DT, 64>(x, cols, d.seed, xt);
+  else if (d.tile == 256u)
+    gemv_rotate_tiles<DT, 256>(x, cols, d.seed, xt);
   else
-    gemv_rotate_tiles<DT, 128>(x, cols, s_res.seed, xt);
+    gemv_rotate_tiles<DT, 128>(x, cols, d.seed, xt);
 }
 
 // y_r = sum over the row's column tiles of the tile partials, in column order (one lane per row).
@@ -1831,7 +1888,7 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode) {
     k = a.rice_k >= 0 ? a.rice_k : kwin_base(centre) + 1;
   }
   hipLaunchKernelGGL(init_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.ws, lookback_flags(a.ws),
-                     nflags, reinterpret_cast<uint32_t*>(rate_acc(a.ws, 0)), nacc, centre, step_bits, k, mode);
+                     nflags, reinterpret_cast<uint32_t*>(rate_acc(a.ws, 0)), nacc, centre, step_bits, k, mode, a.call);
   return hipGetLastError();
 }
 
@@ -1861,6 +1918,7 @@ static RateArgs rate_args(const EncodeArgs& a, const RatePlan& rp) {
   r.centre0 = rp.centre0;
   r.nblk = r.pa.nblk > r.pb.nblk ? r.pa.nblk : r.pb.nblk;
   r.spin_budget = a.spin_budget;
+  r.call = a.call;
   return r;
 }
 
@@ -1887,6 +1945,7 @@ hipError_t launch_encode(const EncodeArgs& a) {
   P.ws = a.ws;
   P.flags = lookback_flags(a.ws);
   P.spin_budget = a.spin_budget;
+  P.call = a.call;
   const uint32_t blocks = a.chunks ? a.chunks : 1u;
 #define HQ_ENC(L, D, T, TL) \
   hipLaunchKernelGGL((encode_kernel<L, D, T, TL>), dim3(blocks), dim3(kBlock), 0, a.stream, P)
@@ -1901,48 +1960,50 @@ hipError_t launch_codes(const EncodeArgs& a, int32_t* codes, uint16_t* scales) {
   if (blocks == 0) return hipSuccess;
 #define HQ_CODES(L, D, T, TL)                                                                          \
   hipLaunchKernelGGL((codes_kernel<L, D, T, TL>), dim3((uint32_t)blocks), dim3(kBlock), 0, a.stream, a.x, a.tiles, \
-                     a.seed, (uint32_t)a.dither, a.fixed_step_bits, codes, scales, a.ws)
+                     a.seed, (uint32_t)a.dither, a.fixed_step_bits, codes, scales, a.ws, a.call)
   HQ_DISPATCH(a.lattice, a.dither, a.dtype, a.tile, HQ_CODES);
 #undef HQ_CODES
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const uint8_t* in, uint64_t in_bytes, void* out, int out_dtype, uint64_t n,
-                         Workspace* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                         Workspace* ws, uint64_t call, hipStream_t stream) {
   // a chunk holds kChunkValues values at every tile length (the header check rejects an n that
-  // is not a whole number of the stream's tiles)
+  // is not a whole number of the stream's tiles); an empty tensor still gets the header check
   const uint64_t chunks = (n + kChunkValues - 1) / kChunkValues;
-  if (chunks == 0) return hipSuccess;
+  const uint32_t blocks = chunks ? (uint32_t)chunks : 1u;
   const GemvArgs none{nullptr, 128u, nullptr};
   if (out_dtype == 1)
-    hipLaunchKernelGGL((decode_kernel<1, false>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws, none);
+    hipLaunchKernelGGL((decode_kernel<1, false>), dim3(blocks), dim3(kBlock), 0, stream, in, in_bytes, n, out, ws,
+                       none, call);
   else
-    hipLaunchKernelGGL((decode_kernel<0, false>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, out, ws, none);
+    hipLaunchKernelGGL((decode_kernel<0, false>), dim3(blocks), dim3(kBlock), 0, stream, in, in_bytes, n, out, ws,
+                       none, call);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint8_t* in, uint64_t in_bytes, uint64_t rows, uint64_t cols, const void* x, int x_dtype,
-                       float* y, Workspace* ws, float* xt, float* tp, hipStream_t stream) {
+                       float* y, Workspace* ws, float* xt, float* tp, uint64_t call, hipStream_t stream) {
   const uint64_t n = rows * cols;
   if (n == 0) {  // nothing to multiply (x may then be null): check the stream only
-    hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws);
+    hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(64), 0, stream, in, in_bytes, n, ws, call);
     return hipGetLastError();
   }
   // the rotation kernel also checks the header (its workgroup 0 publishes the check)
   const uint32_t rblocks = (uint32_t)((cols + 2047) / 2048);
   if (x_dtype == 1)
-    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt);
+    hipLaunchKernelGGL(gemv_rotate_kernel<1>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt,
+                       call);
   else
-    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt);
+    hipLaunchKernelGGL(gemv_rotate_kernel<0>, dim3(rblocks), dim3(kBlock), 0, stream, in, in_bytes, n, x, cols, ws, xt,
+                       call);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunks = (n + kChunkValues - 1) / kChunkValues;
   if (chunks == 0) return hipSuccess;
   const GemvArgs g{xt, cols, tp};
-  hipLaunchKernelGGL((decode_kernel<1, true>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, nullptr, ws, g);
+  hipLaunchKernelGGL((decode_kernel<1, true>), dim3((uint32_t)chunks), dim3(kBlock), 0, stream, in, in_bytes, n,
+                     nullptr, ws, g, call);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemv_rows_kernel, dim3((uint32_t)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, tp,
