@@ -971,6 +971,9 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
     const uint64_t t = (uint64_t)c * TI::CT + tc;
     const bool valid = t < P.T;
     if (__ballot(!isfinite(S[r]))) {  // uniform test: the common case skips the block entirely
+      // (the empty asm keeps the branch: without it the compiler runs the block with an empty
+      // execution mask, eight instructions per round)
+      __asm__ volatile("");
       if (!isfinite(S[r])) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[r][i] = 0.0f;
