@@ -1450,7 +1450,7 @@ template <int LAT, int DT_OUT, bool GEMV, int TL, int KC = -1>
 __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in, void* __restrict__ out,
                                                   Workspace* ws, uint64_t call, uint32_t c, uint32_t tiles_c,
                                                   const uint32_t* __restrict__ seg, uint32_t nW32, uint32_t* s_pos,
-                                                  uint32_t* s_boundary, GemvArgs g) {
+                                                  uint32_t* s_boundary, float4* s_fac, GemvArgs g) {
   using TI = Tiling<TL>;
   constexpr int LPT = TI::LPT;
   constexpr float kInvTile = 1.0f / (float)TL;  // exact power of two
@@ -1473,10 +1473,21 @@ __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in
       reinterpret_cast<const uint32_t*>(in + (((uint64_t)hw[13] << 32) | hw[12]) + (uint64_t)c * ((uint64_t)TI::CT * F / 8ull));
   // output factor per coordinate: +-1/TL with the sign of D and of the lane's butterfly sign; the
   // fused multiply-add with +0 below is exact and turns an exact zero into +0
-  const uint32_t sgn = octet_sign_bits(seed, o) ^ (lane_sign_bit<LPT>(o) ? 0xFFu : 0u);
-  float cmul[8];
+  // These factors and the cross-lane butterflies' +-1 depend only on the octet index o: a table of
+  // them per o (lanes 0 .. LPT-1 fill it; the barriers of unary_positions publish it) is read
+  // again in every round, which costs three LDS reads instead of about 40 vector instructions of
+  // re-deriving them from o (the registers to keep them would cost a wave per SIMD).
+  if (tid < LPT) {
+    const uint32_t sgn = octet_sign_bits(seed, tid) ^ (lane_sign_bit<LPT>(tid) ? 0xFFu : 0u);
+    float f[12];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cmul[i] = ((sgn >> i) & 1u) ? -kInvTile : kInvTile;
+    for (int i = 0; i < 8; ++i) f[i] = ((sgn >> i) & 1u) ? -kInvTile : kInvTile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[8 + j] = (tid & (1 << j)) ? -1.0f : 1.0f;
+    s_fac[3 * tid] = make_float4(f[0], f[1], f[2], f[3]);
+    s_fac[3 * tid + 1] = make_float4(f[4], f[5], f[6], f[7]);
+    s_fac[3 * tid + 2] = make_float4(f[8], f[9], f[10], f[11]);
+  }
   bool bad = false;
   // record words of a round: the tile header (scale, then E8 coset bits), the word with the octet's
   // coset bits when they are not in that window (A2's four; E8 at 32 lanes per tile), and the
@@ -1661,8 +1672,14 @@ __device__ __forceinline__ void decode_chunk_body(const uint8_t* __restrict__ in
       return;
     }
     fwht_lane(yv);
-    fwht_cross<LPT>(yv, o);
+    // the table's address is made opaque per round so that its entries are read here, not kept
+    uint32_t fo = 3u * (uint32_t)o;
+    __asm__ volatile("" : "+v"(fo));
+    const float4 c0 = s_fac[fo], c1 = s_fac[fo + 1], sg4 = s_fac[fo + 2];
+    const float sg[5] = {sg4.x, sg4.y, sg4.z, sg4.w, (o & 16) ? -1.0f : 1.0f};
+    fwht_cross_s<LPT>(yv, sg);
     if (valid) {
+      const float cmul[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       float xo[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) xo[i] = __builtin_fmaf(yv[i], cmul[i], 0.0f);
@@ -1715,6 +1732,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7, 8))) 
   // weight's stream)
   __shared__ uint4 s_pos4[kMaxSymsPerChunk / 8];
   __shared__ uint32_t s_boundary;
+  __shared__ float4 s_fac[3 * 32];  // per octet index: 8 output factors, 4 butterfly signs
   uint32_t* s_pos = reinterpret_cast<uint32_t*>(s_pos4);
   const int tid = threadIdx.x;
   const uint32_t c = blockIdx.x;
@@ -1756,7 +1774,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7, 8))) 
   const uint32_t* __restrict__ seg = reinterpret_cast<const uint32_t*>(in + unary_off + 8ull * w0);
   const uint32_t nW32 = 2u * (w1 - w0);
   // uniform dispatch on the stream's lattice and tile length
-#define HQ_DEC_ARGS in, out, ws, call, c, tiles_c, seg, nW32, s_pos, &s_boundary, gv
+#define HQ_DEC_ARGS in, out, ws, call, c, tiles_c, seg, nW32, s_pos, &s_boundary, s_fac, gv
 #define HQ_DEC_LAT(TLV)                                                                  \
   switch (lattice) {                                                                     \
     case kLatE8: decode_chunk_body<kLatE8, DT_OUT, GEMV, TLV>(HQ_DEC_ARGS); break;       \
