@@ -76,14 +76,16 @@ constexpr int kCntShift = 40;
 struct RateAcc {
   uint64_t cnt[kRcAccSlots][kRcCounters];
 };
-// Word in which rate workgroup 0 publishes pass A's solve, the centre of pass B, to the other rate
-// workgroups of the launch (bit 63 set = published, the centre in the low 32 bits).  kPubCopies
-// copies, kPubStride words (256 bytes) apart, so that the waiting workgroups spread their polls
-// over several addresses.
+// Word in which rate workgroup 0 publishes pass A's solve, the centre of pass B, to pass B's
+// workgroups (bit 63 set = published, the centre in the low 32 bits): kPubCopies copies,
+// kPubStride words (256 bytes) apart, so that the waiting workgroups spread their polls over
+// several addresses; and the count of pass B's workgroups that have added their sums, whose last
+// solves pass B.
 constexpr int kPubCopies = 16;
 constexpr int kPubStride = 32;
 struct RatePub {
   uint64_t centre[kPubCopies * kPubStride];
+  uint64_t done_b[kPubStride];  // pass B's workgroups that have added their sums (word 0)
 };
 constexpr size_t kWsRate = 2 * sizeof(RateAcc) + sizeof(RatePub);  // pass A, pass B, published centre
 static_assert(kWsRate % 256 == 0, "rate counters keep the flags 256-byte aligned");
@@ -134,7 +136,7 @@ hipError_t launch_init(const EncodeArgs& a, int64_t centre, int mode);
 // Rate control of one call (see rate_workgroup in hq_kernels.hip): two passes (pass A: 8
 // candidates around centre0 on NA sample tiles; pass B: 4 candidates around pass A's solve on NB
 // tiles), or, for a fixed step with automatic k, one pass of the single candidate centre0 on NB
-// tiles.  blkA / blkB workgroups run the passes (the first max(blkA, blkB) workgroups of a launch).
+// tiles.  blkA workgroups run pass A and the next blkB pass B (blkA + blkB workgroups in all).
 struct RatePlan {
   int needed;
   int two_pass;

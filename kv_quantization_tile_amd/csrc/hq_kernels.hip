@@ -362,7 +362,7 @@ struct RateArgs {
   PassDesc pa, pb;    // pass A (two passes only), and pass B or the single pass
   int two_pass;
   int64_t centre0;    // pass A's centre, or the fixed step's bits for the single pass
-  uint32_t nblk;      // rate workgroups: max(pa.nblk, pb.nblk)
+  uint32_t nblk;      // rate workgroups: pa.nblk (pass A: workgroups 0 ..) + pb.nblk (pass B: the next)
   uint32_t spin_budget;
   uint64_t call;
 };
@@ -447,8 +447,8 @@ __device__ __forceinline__ void sample_eval(const Sample& s, int o, int64_t cent
 // receives one contribution, zero or not, so that its count shows when all of the pass's
 // workgroups have added.  All lanes of the workgroup call it (two barriers).
 template <int NJ>
-__device__ void wg_add_counters(const uint32_t acc[NJ][kRcKwin], int j0, int nj, uint32_t* red, RateAcc* racc,
-                                uint32_t b) {
+__device__ uint64_t wg_add_counters(const uint32_t acc[NJ][kRcKwin], int j0, int nj, uint32_t* red, RateAcc* racc,
+                                    uint32_t b) {
   const int tid = threadIdx.x;
   if (tid < kRcCounters) red[tid] = 0u;
   __syncthreads();
@@ -458,9 +458,14 @@ __device__ void wg_add_counters(const uint32_t acc[NJ][kRcKwin], int j0, int nj,
     for (int w = 0; w < kRcKwin; ++w)
       if (jj < nj && acc[jj][w]) atomicAdd(&red[(j0 + jj) * kRcKwin + w], acc[jj][w]);
   __syncthreads();
-  if (tid < kRcCounters)
-    __hip_atomic_fetch_add(&racc->cnt[b % kRcAccSlots][tid], (1ull << kCntShift) + red[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t old = 0;
+  if (tid < kRcCounters) {
+    old = __hip_atomic_fetch_add(&racc->cnt[b % kRcAccSlots][tid], (1ull << kCntShift) + red[tid], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    // the returned value is waited for: the add has been performed before anything that follows
+    __asm__ volatile("" ::"v"(old) : "memory");
+  }
+  return old;  // lane 0: the set's first word before this workgroup's add
 }
 
 // Contributions that counter set s of a pass receives from its nblk workgroups.
@@ -584,65 +589,89 @@ __device__ __forceinline__ void publish(uint64_t* words, uint64_t v) {
     __hip_atomic_store(&words[lane * kPubStride], (1ull << 63) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Rate workgroup b (0 <= b < A.nblk).  Pass A: sample tiles b TPW .. b TPW + TPW - 1, two of its 8
-// candidates per wavefront (all four wavefronts take the same tiles).  Pass B (or the single
-// pass): sample tiles from 4 b TPW, TPW per wavefront, every candidate.  Workgroup 0 solves each
-// pass as soon as its counters are complete: pass A's solve, the centre of pass B, goes to every
-// rate workgroup through a published word (a workgroup that does not see it within its budget
-// solves pass A itself); pass B's solve is the call's operating point, which workgroup 0 stores in
-// the workspace and publishes to the chunk workgroups of the encoder.
+// Rate workgroup b (0 <= b < A.nblk).  Workgroups 0 .. pa.nblk-1 run pass A: sample tiles
+// b TPW .. b TPW + TPW - 1, two of its 8 candidates per wavefront (the four wavefronts take the
+// same tiles); none of them waits, except workgroup 0, which then solves pass A as soon as its
+// counters are complete and publishes the result, pass B's centre.  The next pb.nblk workgroups
+// run pass B (or the single pass): sample tiles from 4 j TPW (j = b - pa.nblk), TPW per
+// wavefront, every candidate, at the published centre (a workgroup that does not see it within
+// its budget solves pass A itself); the last of them to add its sums solves pass B, stores the
+// operating point in the workspace (the encoder, the next launch, reads it there) and leaves.
+// Only pass B's workgroups wait, for pass A's, which come before them in the grid: no wait
+// depends on how many workgroups the GPU holds at once.
 template <int LAT, bool DITHER, int DT, int TL>
 __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
   using TI = Tiling<TL>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, o = lane % TI::LPT, tw = lane / TI::LPT;
   const uint32_t sgn = octet_sign_bits(A.seed, o);
+  // waits for another workgroup's result: far beyond any wait in normal operation (the fallback
+  // computes the awaited value itself, at the cost of evaluating a whole sample in one wavefront)
+  const uint32_t budget = A.spin_budget > 0xFFFFFFFFu / 256u ? 0xFFFFFFFFu : A.spin_budget * 256u;
+  if (b < A.pa.nblk) {  // pass A (uniform in the workgroup)
+    const PassDesc& pa = A.pa;
+    Sample sa;
+    if (sample_prepare<LAT, DITHER, DT, TL>(A, pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa) && o == 0 &&
+        wave == 0)
+      record_error(A.ws, A.call, kErrNonfinite);
+    uint32_t acc[2][kRcKwin];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) sample_eval<LAT, DITHER, TL>(sa, o, A.centre0, pa, 2 * wave + jj, acc[jj]);
+    wg_add_counters<2>(acc, 2 * wave, 2, L.red, pa.racc, b);
+    if (b == 0 && wave == 0) {
+      int64_t c;
+      int k;
+      solve_pass_wave<LAT, DITHER, DT, TL>(A, pa, A.centre0, budget, &L, &c, &k);
+      publish(A.pub->centre, (uint64_t)(uint32_t)c);
+    }
+    return;
+  }
   const PassDesc& pb = A.pb;
-  const bool in_b = b < pb.nblk;
-  // both passes' samples first, so that their loads are in flight together
-  Sample sb, sa;
-  const bool in_a = A.two_pass && b < A.pa.nblk;  // uniform in the workgroup
-  const bool nf_b = sample_prepare<LAT, DITHER, DT, TL>(
-      A, pb.N, in_b ? ((uint64_t)b * 4 + wave) * TI::TPW + tw : pb.N, o, sgn, sb);
-  const bool nf_a = in_a && sample_prepare<LAT, DITHER, DT, TL>(A, A.pa.N, (uint64_t)b * TI::TPW + tw, o, sgn, sa);
-  if (o == 0 && (nf_b || (nf_a && wave == 0))) record_error(A.ws, A.call, kErrNonfinite);
+  const uint32_t j = b - A.pa.nblk;  // pass B workgroup
+  uint64_t old0 = 0;
+  Sample sb;
+  if (sample_prepare<LAT, DITHER, DT, TL>(A, pb.N, ((uint64_t)j * 4 + wave) * TI::TPW + tw, o, sgn, sb) &&
+      o == 0)
+    record_error(A.ws, A.call, kErrNonfinite);
   int64_t centre = A.centre0;
   if (A.two_pass) {
-    const PassDesc& pa = A.pa;
-    if (in_a) {
-      uint32_t acc[2][kRcKwin];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) sample_eval<LAT, DITHER, TL>(sa, o, A.centre0, pa, 2 * wave + jj, acc[jj]);
-      wg_add_counters<2>(acc, 2 * wave, 2, L.red, pa.racc, b);
-    }
     if (wave == 0) {
       uint64_t v = 0;
       int64_t c;
       int k;
-      if (b != 0 && wait_pub(&A.pub->centre[(b % kPubCopies) * kPubStride], A.spin_budget, &v)) {
+      if (wait_pub(&A.pub->centre[(j % kPubCopies) * kPubStride], budget, &v)) {
         c = (int64_t)(uint32_t)v;
-      } else {  // the solver (workgroup 0), or a workgroup that has waited past its budget
-        solve_pass_wave<LAT, DITHER, DT, TL>(A, pa, A.centre0, A.spin_budget, &L, &c, &k);
-        if (b == 0) publish(A.pub->centre, (uint64_t)(uint32_t)c);
+      } else {  // not published within the budget: pass A solved here
+        solve_pass_wave<LAT, DITHER, DT, TL>(A, A.pa, A.centre0, budget, &L, &c, &k);
       }
       if (lane == 0) L.bcast = c;
     }
     __syncthreads();
     centre = L.bcast;
-    if (in_b) {  // uniform in the workgroup: pass B's four candidates, independent of one another
-      uint32_t acc[kRcCandB][kRcKwin];
+    uint32_t acc[kRcCandB][kRcKwin];  // pass B's four candidates, independent of one another
 #pragma unroll
-      for (int jj = 0; jj < kRcCandB; ++jj) sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, jj, acc[jj]);
-      wg_add_counters<kRcCandB>(acc, 0, kRcCandB, L.red, pb.racc, b);
-    }
-  } else if (in_b) {  // the single pass: one candidate
+    for (int jj = 0; jj < kRcCandB; ++jj) sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, jj, acc[jj]);
+    old0 = wg_add_counters<kRcCandB>(acc, 0, kRcCandB, L.red, pb.racc, j);
+  } else {  // the single pass: one candidate
     uint32_t acc[1][kRcKwin];
     sample_eval<LAT, DITHER, TL>(sb, o, centre, pb, 0, acc[0]);
-    wg_add_counters<1>(acc, 0, 1, L.red, pb.racc, b);
+    old0 = wg_add_counters<1>(acc, 0, 1, L.red, pb.racc, j);
   }
-  if (b == 0 && wave == 0) {
+  // the workgroup that completes the first word of its counter set (the word counts its own
+  // contributions) counts the set in; the one that counts the last set in solves pass B (16
+  // workgroups meet at that count rather than all of them: contended atomics on one word queue)
+  if (tid == 0) {
+    const uint32_t s = j % kRcAccSlots;
+    const uint32_t nsets = pb.nblk < (uint32_t)kRcAccSlots ? pb.nblk : (uint32_t)kRcAccSlots;
+    bool last = false;
+    if ((uint32_t)(old0 >> kCntShift) + 1u == set_contribs(s, pb.nblk))
+      last = __hip_atomic_fetch_add(&A.pub->done_b[0], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == nsets;
+    L.bcast = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (L.bcast && wave == 0) {
     int64_t xb;
     int k;
-    solve_pass_wave<LAT, DITHER, DT, TL>(A, pb, centre, A.spin_budget, &L, &xb, &k);
+    solve_pass_wave<LAT, DITHER, DT, TL>(A, pb, centre, budget, &L, &xb, &k);
     if (lane == 0) {
       Workspace* ws = A.ws;
       ws->rc_centre = xb;
@@ -655,11 +684,8 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
   }
 }
 
-// hq_rate alone: the rate workgroups in a launch of their own.
-// Two workgroups per CU are all it runs (512 workgroups for tiles of 128), so the compiler may
-// spend registers on overlapping the candidates' independent evaluations.
 template <int LAT, bool DITHER, int DT, int TL>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) void rate_kernel(RateArgs A) {
+__global__ __launch_bounds__(kBlock) void rate_kernel(RateArgs A) {
   __shared__ RateLds L;
   rate_workgroup<LAT, DITHER, DT, TL>(A, blockIdx.x, L);
 }
@@ -1942,7 +1968,7 @@ static RateArgs rate_args(const EncodeArgs& a, const RatePlan& rp) {
   r.pa = pass_desc(a, 0, kRcCand, 21, rp.two_pass ? rp.NA : 0u, rp.two_pass ? rp.blkA : 0u);
   r.pb = rp.two_pass ? pass_desc(a, 1, kRcCandB, 18, rp.NB, rp.blkB) : pass_desc(a, 1, 1, 0, rp.NB, rp.blkB);
   r.centre0 = rp.centre0;
-  r.nblk = r.pa.nblk > r.pb.nblk ? r.pa.nblk : r.pb.nblk;
+  r.nblk = r.pa.nblk + r.pb.nblk;
   r.spin_budget = a.spin_budget;
   r.call = a.call;
   return r;

@@ -42,7 +42,7 @@ def test_sizes_match_oracle_layout(orc):
     out = ctypes.c_uint64(0)
     assert L.hq_stream_fixed_bytes(256, 2, 4, 32, ctypes.byref(out)) == hq.HQ_ERR_UNSUPPORTED
     assert L.hq_stream_fixed_bytes(64, 2, 4, 128, ctypes.byref(out)) == hq.HQ_ERR_INVALID_ARG  # n % tile
-    rate = 2 * 16 * 32 * 8 + 16 * 256  # two rate passes (16 sets of 32 64-bit counters), 16 copies of the published centre
+    rate = 2 * 16 * 32 * 8 + 16 * 256 + 256  # two rate passes (16 sets of 32 64-bit counters), 16 copies of the published centre, the done count
     assert hq.hq_workspace_size(0) == 4096 + rate + 256
     assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + rate + ((8 * 101 + 255) // 256) * 256
 
