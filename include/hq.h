@@ -192,7 +192,7 @@ int hq_encode(const void *x, int32_t dtype, uint64_t n, const hq_params *params,
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): hq_encode without a workspace argument.  The workspace
- * is a static device array of the library, 1,065,216 bytes on each GPU the library runs on, held
+ * is a static device array of the library, 1,065,472 bytes on each GPU the library runs on, held
  * until the process ends; it serves n up to 2^30 values (HQ_ERR_SCRATCH above that).  The call
  * allocates nothing.  Arguments, results and errors are those of hq_encode with the same params
  * (the same kernels, the same stream bytes); step == -1 takes the operating point of the previous

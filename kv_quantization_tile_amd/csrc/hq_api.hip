@@ -239,8 +239,8 @@ uint64_t encode_bound_at(uint64_t n, int lattice, uint32_t tile, double step, in
 
 // ---- the allocation-free encode: its workspace is a static device array ------------------------
 // Largest n of hq_encode_noalloc, and the array sized for it: the workspace of an encode of that
-// many values (4 KiB of state, 12 KiB of rate counters and published words, one 8-byte offset flag
-// per 8192-value chunk plus one): 1,065,216 bytes per GPU, held until the process ends.
+// many values (4 KiB of state, 12.25 KiB of rate counters and published words, one 8-byte offset flag
+// per 8192-value chunk plus one): 1,065,472 bytes per GPU, held until the process ends.
 constexpr uint64_t kNoAllocMaxValues = 1ull << 30;
 constexpr size_t kScratchBytes =
     kWsHeader + kWsRate + ((8ull * ((kNoAllocMaxValues + 8191) / 8192 + 1) + 255) & ~(uint64_t)255);

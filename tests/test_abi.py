@@ -45,6 +45,8 @@ def test_sizes_match_oracle_layout(orc):
     rate = 2 * 16 * 32 * 8 + 16 * 256 + 256  # two rate passes (16 sets of 32 64-bit counters), 16 copies of the published centre, the done count
     assert hq.hq_workspace_size(0) == 4096 + rate + 256
     assert hq.hq_workspace_size(128 * 64 * 100) == 4096 + rate + ((8 * 101 + 255) // 256) * 256
+    # the allocation-free encode's static array is the workspace of its largest call (2^30 values)
+    assert hq.hq_workspace_size(1 << 30) == 1_065_472
 
 
 def _encode_rc(params, n=128, ws_bytes=1 << 20, x=1 << 20, out=1 << 20, ws=1 << 21):
