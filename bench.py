@@ -96,13 +96,24 @@ def measured_copy_gbs(torch, reps: int = 20) -> float:
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: the model name, and its family, model and stepping
+    numbers (some hosts report only a generic model name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "cpu MHz") and k not in fields:
+                    fields[k] = v
+            elif fields:
+                break  # the first processor's block is enough
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    mhz = f", {float(fields['cpu MHz']):.0f} MHz" if "cpu MHz" in fields else ""
+    return f"{fields.get('model name', 'unknown')} ({ids}{mhz})"
 
 
 def workload(cfg: str, bps, dither_flags: int = 1):
