@@ -1120,21 +1120,20 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
     };
     const uint64_t ex = lookback_wave(P.flags, c, agg, P.spin_budget, agg_of);
     if (lane == 0) s_prefix = ex;
+  } else {
+    // the chunk's fixed record (its place does not depend on the prefix), by the other
+    // wavefronts while wavefront 0 looks back
+    const uint64_t fbase = fixed_off + (uint64_t)c * chunk_bytes;
+    if (fbase + chunk_bytes <= P.cap) {
+      uint4* dst = reinterpret_cast<uint4*>(P.out + fbase);
+      for (uint32_t i = tid - 64u; i < fixed_words / 4; i += kBlock - 64u) dst[i] = s_fixed4[i];
+    } else if (tid == 64) {
+      record_error(ws, P.call, kErrCapacity);
+    }
   }
   __syncthreads();
   const uint64_t prefix = s_prefix & kWordsMask;
   const uint64_t prefix_pad = s_prefix >> kPadShift;
-
-  // fixed record of the chunk
-  {
-    const uint64_t fbase = fixed_off + (uint64_t)c * chunk_bytes;
-    if (fbase + chunk_bytes <= P.cap) {
-      uint4* dst = reinterpret_cast<uint4*>(P.out + fbase);
-      for (uint32_t i = tid; i < fixed_words / 4; i += kBlock) dst[i] = s_fixed4[i];
-    } else if (tid == 0) {
-      record_error(ws, P.call, kErrCapacity);
-    }
-  }
   if (tid == 0) {
     if (prefix + W > 0xFFFFFFFFull) record_error(ws, P.call, kErrRange);  // u32 chunk index
     if (kHeaderBytes + 4ull * c + 4 <= P.cap)
