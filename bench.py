@@ -51,7 +51,7 @@ def parse():
                     help="model / kv_all: streams the resident tensors are issued on, round-robin")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv", action="store_true",
-                    help="default run: skip the second workload (one KV call) timed beside the weight")
+                    help="default run: skip the KV calls (E8 + dither at 2 and 3 bits per value) timed beside the weight")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 256 MiB (known traffic), for scaling "
@@ -921,13 +921,15 @@ def main():
     import kv_quantization_tile_amd as hq
 
     # the headline workload (the weight by default), and, in the default run, one KV call beside it
+    # at 2 and at 3 bits per value
     x_host, cfg, seed = workload(args.config, args.bps, args.dither_flags)
     K = args.steps
     r = measure(hq, torch, x_host, cfg, seed, K, args.warmup)
-    second = None
+    seconds = []
     if args.config == "weight" and args.bps is None and not args.no_kv:
-        xk, cfgk, seedk = workload("kv", None, 1)
-        second = (xk, cfgk, seedk, measure(hq, torch, xk, cfgk, seedk, K, args.warmup))
+        for key, bps in (("kv", None), ("kv_3bps", 3.0)):
+            xk, cfgk, seedk = workload("kv", bps, 1)
+            seconds.append((key, xk, cfgk, seedk, measure(hq, torch, xk, cfgk, seedk, K, args.warmup)))
 
     result = {
         "metric": METRIC,
@@ -949,12 +951,11 @@ def main():
     copy_gbs = measured_copy_gbs(torch)
     result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
     result["roofline"]["frac_of_measured_copy"] = round(r["roofline"]["achieved"] / copy_gbs, 4)
-    if second is not None:
-        xk, cfgk, seedk, rk = second
-        result["extra"]["kv"] = {"workload": rk["config"]["workload"], "value_gbs": round(rk["value"], 2),
-                                 "ms_per_step": round(rk["ms_per_step"], 5), "config": rk["config"],
-                                 "roofline": {**rk["roofline"], "measured_copy_gbs": round(copy_gbs, 1)},
-                                 **rk["extra"]}
+    for key, xk, cfgk, seedk, rk in seconds:
+        result["extra"][key] = {"workload": rk["config"]["workload"], "value_gbs": round(rk["value"], 2),
+                                "ms_per_step": round(rk["ms_per_step"], 5), "config": rk["config"],
+                                "roofline": {**rk["roofline"], "measured_copy_gbs": round(copy_gbs, 1)},
+                                **rk["extra"]}
 
     if not args.no_cpu_baseline or not args.no_parity:
         import oracle
@@ -966,12 +967,11 @@ def main():
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline_all_cores(oracle, x_host, r["config"], seed, times,
                                                             host_threads())
-        if second is not None:
-            xk, cfgk, seedk, rk = second
+        for key, xk, cfgk, seedk, rk in seconds:
             repk, tk = parity_report(hq, torch, oracle, xk, rk["config"], seedk, rk["_dev"])
             if not args.no_parity:
-                result["extra"]["kv"]["parity"] = repk
-            result["extra"]["kv"]["cpu_oracle_one_thread_gbs"] = round(
+                result["extra"][key]["parity"] = repk
+            result["extra"][key]["cpu_oracle_one_thread_gbs"] = round(
                 2 * xk.size / (tk["encode_s"] + tk["decode_s"]) / 1e9, 4)
     print(json.dumps(result), flush=True)
 
