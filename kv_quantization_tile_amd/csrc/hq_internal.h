@@ -143,8 +143,8 @@ struct RatePlan {
   int64_t centre0;
   uint32_t NA, NB, blkA, blkB;
 };
-// Rate control: one launch of the rate workgroups, whose workgroup 0 leaves the operating point in
-// the workspace (nothing when rp.needed is 0).
+// Rate control: one launch of the rate workgroups, whose pass-B solver leaves the operating point
+// in the workspace (nothing when rp.needed is 0).
 hipError_t launch_rate(const EncodeArgs& a, const RatePlan& rp);
 // The encoder, at the operating point the workspace holds.
 hipError_t launch_encode(const EncodeArgs& a);

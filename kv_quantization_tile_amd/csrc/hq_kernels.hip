@@ -6,14 +6,19 @@
 //
 // Kernels of one encode call, all on the caller's stream, with no host round trip in between:
 //   init_kernel     clears the workspace flags and counters and seeds the rate search;
-//   rate_kernel     the rate search in one launch: its workgroups evaluate candidate steps on
-//                   samples of tiles into per-pass counters, and its workgroup 0 solves pass A
-//                   (8 candidates, quarter octaves) for pass B's centre, publishes it to the
-//                   others, and solves pass B (4 candidates, 1/16 octave) for the operating point;
-//   encode_kernel   one workgroup per 64-tile chunk: load, sign, FWHT, scale, lattice, strip, Rice
-//                   lengths, workgroup scan, decoupled look-back over chunks for the unary offsets,
-//                   and coalesced stores of the chunk's fixed record and unary segment.
-// Decode: decode_check (header validation, 1 lane) then decode_kernel (one workgroup per chunk).
+//   rate_kernel     the rate search in one launch: its first workgroups evaluate pass A's 8
+//                   candidate steps (quarter octaves) on samples of tiles into counters, and
+//                   workgroup 0 solves pass A for pass B's centre and publishes it; the workgroups
+//                   after them evaluate pass B's 4 candidates (1/16 octave) around that centre, and
+//                   the one that completes the last counter set solves pass B for the operating
+//                   point;
+//   encode_kernel   one workgroup per 8192-value chunk: load, sign, FWHT, scale, lattice, strip,
+//                   Rice lengths, workgroup scan, decoupled look-back over chunks for the unary
+//                   offsets, and coalesced stores of the chunk's fixed record and unary segment.
+// Decode: decode_kernel, one workgroup per chunk, each checking the stream header itself.  The
+// fused product: gemv_rotate_kernel (the activation, and the header check), decode_kernel with the
+// product in place of the inverse transform, gemv_rows_kernel; decode_check_kernel checks the
+// header of an empty product's stream.
 #include "hq_device.h"
 #include "hq_internal.h"
 
