@@ -208,6 +208,7 @@ def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=N
     torch.cuda.synchronize()
     st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
+    fallbacks = hq.hq_fallbacks(ws)  # the last timed encode: waits that ran out of their budget
     r = {"encode_ms": float(np.mean([a.elapsed_time(b) for a, b, _ in ev])),
          "decode_ms": float(np.mean([b.elapsed_time(c) for _, b, c in ev])),
          "step_ms": step_ms}
@@ -788,7 +789,8 @@ def measure(hq, torch, x_host, cfg, seed, K, W):
                   "step_alg_bytes": alg_step,
                   "step_hbm_gbs": round(alg_step / (step_ms * 1e-3) / 1e9, 1),
                   "step_hbm_frac": round(alg_step / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "host_wall_ms_per_step": round(wall / K * 1e3, 5)},
+                  "host_wall_ms_per_step": round(wall / K * 1e3, 5),
+                  "fallbacks_last_timed_encode": fallbacks},
         "_dev": dict(x=x, out=out, y=y, total_bytes=total_bytes, step=float(info["step"]), k=int(info["rice_k"])),
     }
     return r

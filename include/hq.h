@@ -221,6 +221,18 @@ int hq_decode(const void *stream_data, uint64_t stream_bytes, void *out, int32_t
  * the device-side outcome of the calls above (no step of the method of its own). */
 int hq_status(void *workspace, hq_stream_t stream);
 
+/* Diagnostic of the last call that used `workspace` (waits for `stream`): which of its bounded
+ * cross-workgroup waits ran out of their spin budget and computed the awaited value themselves.
+ * No passage of the pages defines these waits: they are this codec's way of running rate targeting
+ * (component 3 of "Methodology: the HyperQuant pipeline") and the stream's chunk offsets in single
+ * launches.  A fallback gives the same result as the normal path, only later (microseconds to
+ * milliseconds), so the flags concern speed, never correctness.  *flags receives bit 0: a
+ * look-back computed a predecessor chunk's offset contribution from its input; bit 1: a rate
+ * workgroup solved pass A itself instead of waiting for its published centre; bit 2: a rate
+ * solver evaluated a pass's whole sample itself.  Errors: HQ_ERR_INVALID_ARG (null pointer),
+ * HQ_ERR_HIP. */
+int hq_fallbacks(const void *workspace, hq_stream_t stream, uint32_t *flags);
+
 /* Workspace bytes for hq_gemv on a [rows][cols] matrix (host only; enough for any tile length).
  * Holds the rotated activation and the per-tile partial products of the fused product below. */
 int hq_gemv_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);

@@ -5,7 +5,7 @@ declared in ``include/hq.h``.  PyTorch provides device memory and the stream.  T
 fallback: if the library is missing the calls raise.
 
 Entry points mirror the C ABI: ``hq_encode``, ``hq_decode``, ``hq_rate``, ``hq_codes``,
-``hq_status``, ``hq_workspace_size``, ``hq_stream_fixed_bytes``, ``hq_encode_bound``,
+``hq_status``, ``hq_fallbacks``, ``hq_workspace_size``, ``hq_stream_fixed_bytes``, ``hq_encode_bound``,
 ``hq_version``, ``hq_strerror``.
 """
 from __future__ import annotations
@@ -23,7 +23,8 @@ HQ_F32, HQ_BF16 = 0, 1
 LATTICES = {"z": HQ_Z, "d4": HQ_D4, "e8": HQ_E8, "a2": HQ_A2}
 
 EXPORTS = ("hq_version", "hq_strerror", "hq_workspace_size", "hq_stream_fixed_bytes", "hq_encode_bound", "hq_rate",
-           "hq_encode", "hq_encode_noalloc", "hq_decode", "hq_status", "hq_codes", "hq_gemv_workspace_size", "hq_gemv",
+           "hq_encode", "hq_encode_noalloc", "hq_decode", "hq_status", "hq_fallbacks", "hq_codes",
+           "hq_gemv_workspace_size", "hq_gemv",
            "hq_haar_matrix", "hq_rotate", "hq_srft_encode", "hq_srft_decode")
 
 
@@ -70,6 +71,7 @@ def lib():
         L.hq_encode_noalloc.argtypes = [P, i32, u64, P, P, u64, P, P, P]
         L.hq_decode.argtypes = [P, u64, P, i32, u64, P, sz, P]
         L.hq_status.argtypes = [P, P]
+        L.hq_fallbacks.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
         L.hq_codes.argtypes = [P, i32, u64, P, P, P, P, sz, P]
         L.hq_gemv_workspace_size.argtypes = [u64, u64, ctypes.POINTER(sz)]
         L.hq_gemv.argtypes = [P, u64, u64, u64, P, i32, P, P, sz, P]
@@ -374,6 +376,19 @@ def hq_codes(x, step: float, lattice="e8", seed=0, dither=False, ws=None, stream
 
 def hq_status(ws, stream=None) -> int:
     return int(lib().hq_status(ctypes.c_void_p(ws.data_ptr()), _stream_handle(stream)))
+
+
+# bits of hq_fallbacks
+FALLBACK_LOOKBACK, FALLBACK_CENTRE, FALLBACK_PRIVATE = 1, 2, 4
+
+
+def hq_fallbacks(ws, stream=None) -> int:
+    """Which bounded waits of the workspace's last call took their (slower, same-result) fallback:
+    bit 0 a look-back aggregate, bit 1 pass A's centre, bit 2 a pass's private evaluation."""
+    f = ctypes.c_uint32(0)
+    _check(lib().hq_fallbacks(ctypes.c_void_p(ws.data_ptr()), _stream_handle(stream), ctypes.byref(f)),
+           "hq_fallbacks")
+    return int(f.value)
 
 
 def header_fields(stream_bytes_host) -> dict:

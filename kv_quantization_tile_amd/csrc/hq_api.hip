@@ -451,6 +451,17 @@ int hq_status(void* workspace, hq_stream_t stream) {
   return status_from_flags(error_flags(h));
 }
 
+int hq_fallbacks(const void* workspace, hq_stream_t stream, uint32_t* flags) {
+  if (!workspace || !flags) return HQ_ERR_INVALID_ARG;
+  Workspace h;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&h, workspace, sizeof(Workspace), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return HQ_ERR_HIP;
+  *flags = fallback_flags(h);
+  return HQ_OK;
+}
+
 int hq_codes(const void* x, int32_t dtype, uint64_t n, const hq_params* params, int32_t* codes, uint16_t* scales,
              void* workspace, size_t workspace_bytes, hq_stream_t stream) {
   if (!params || !(params->step > 0.0f)) return HQ_ERR_INVALID_ARG;

@@ -61,8 +61,21 @@ struct alignas(256) Workspace {
   // library numbers calls from a random 64-bit start.
   uint64_t call;
   uint64_t err[8];
+  // Fallbacks, numbered the same way: slow[i] holds the number of the last call in which a bounded
+  // wait of kind i ran out of its spin budget and its wavefront computed the awaited value itself
+  // (the same result, later): kSlowLookback a look-back predecessor's aggregate, kSlowCentre pass
+  // A's solve in a pass-B workgroup, kSlowPrivate a pass's sums evaluated by its solver alone.
+  uint64_t slow[4];
 };
 static_assert(sizeof(Workspace) <= 4096, "workspace header");
+enum { kSlowLookback = 0, kSlowCentre = 1, kSlowPrivate = 2 };
+// The fallbacks the workspace's last call took (bit i: slow[i] holds that call's number).
+inline uint32_t fallback_flags(const Workspace& h) {
+  uint32_t f = 0;
+  for (int i = 0; i < 3; ++i)
+    if (h.slow[i] == h.call) f |= 1u << i;
+  return f;
+}
 constexpr size_t kWsHeader = 4096;
 // Counters of the two rate passes.  A workgroup of a pass adds its sums into one of kRcAccSlots
 // counter sets (workgroup index mod kRcAccSlots, so that few workgroups share an address).  Each

@@ -132,6 +132,11 @@ __device__ __forceinline__ void record_error(Workspace* ws, uint64_t call, uint3
     if ((flags >> b) & 1u) __hip_atomic_store(&ws->err[b], call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Marks that `call` took fallback `kind` (a wait that ran out of its budget; see Workspace::slow).
+__device__ __forceinline__ void record_fallback(Workspace* ws, uint64_t call, int kind) {
+  __hip_atomic_store(&ws->slow[kind], call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Lane layout of a tile length TL: LPT lanes per tile, TPW tiles per wavefront, TPR tiles per
 // workgroup round, CT tiles per chunk (four rounds, kChunkValues values).
 template <int TL>
@@ -513,6 +518,7 @@ __device__ void pass_sums_private(const RateArgs& A, const PassDesc& pd, int64_t
   using TI = Tiling<TL>;
   const int lane = threadIdx.x & 63, o = lane % TI::LPT, tw = lane / TI::LPT;
   const uint32_t sgn = octet_sign_bits(A.seed, o);
+  if (lane == 0) record_fallback(A.ws, A.call, kSlowPrivate);
   if (lane < kRcCounters) acc[lane] = 0u;
   wave_lds_sync();
 #pragma unroll 1
@@ -646,6 +652,7 @@ __device__ void rate_workgroup(const RateArgs& A, uint32_t b, RateLds& L) {
       if (wait_pub(&A.pub->centre[(j % kPubCopies) * kPubStride], budget, &v)) {
         c = (int64_t)(uint32_t)v;
       } else {  // not published within the budget: pass A solved here
+        if (lane == 0) record_fallback(A.ws, A.call, kSlowCentre);
         solve_pass_wave<LAT, DITHER, DT, TL>(A, A.pa, A.centre0, budget, &L, &c, &k);
       }
       if (lane == 0) L.bcast = c;
@@ -1121,6 +1128,7 @@ __device__ __forceinline__ void encode_chunk(const EncParams& P, EncLds& lds) {
     const uint64_t agg = W | ((64ull * W - B) << kPadShift);
     // the look-back's fallback: a predecessor's aggregate computed by this wavefront
     auto agg_of = [&](uint32_t p) -> uint64_t {
+      if (lane == 0) record_fallback(ws, P.call, kSlowLookback);
       return chunk_aggregate<LAT, DITHER, DT, TL>(P.x, P.T, P.seed, P.dflags, p, k, step_bits, sgn, lane_neg);
     };
     const uint64_t ex = lookback_wave(P.flags, c, agg, P.spin_budget, agg_of);

@@ -483,13 +483,22 @@ def test_wait_fallbacks_give_the_same_streams(orc, monkeypatch, case):
         x, lat, tb, seed, dither, tile = synth.weight(rows=700), "d4", 3.0, 1, True, 64
     else:
         x, lat, tb, seed, dither, tile = synth.weight(rows=700), "a2", 3.0, 1, False, 256
-    s_gpu, info = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile)
+    ws = hq.workspace(x.size)
+    s_gpu, info = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile, ws=ws)
+    fb = hq.hq_fallbacks(ws)
     s_orc, info_orc = orc.encode(x, LAT[lat], tb, seed=seed, dither=dither, tile=tile)
     assert info["step"] == info_orc["step"] and info["rice_k"] == info_orc["k"]
     assert_same_stream(host_bytes(s_gpu), s_orc, case)
+    # the fallbacks did run: every pass-B workgroup starts before workgroup 0 can have published
+    # pass A's solve, so with no budget each solves pass A itself; and among the weight's 7168
+    # chunks some look-back finds a predecessor not yet published
+    assert fb & hq.FALLBACK_CENTRE, fb
+    if case == "weight_full":
+        assert fb & hq.FALLBACK_LOOKBACK, fb
     monkeypatch.delenv("HQ_SPIN_BUDGET")
-    s_again, _ = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile)
+    s_again, _ = hq.hq_encode(dev(x), lat, tb, seed=seed, dither=dither, tile=tile, ws=ws)
     assert torch.equal(s_again, s_gpu)
+    assert hq.hq_fallbacks(ws) == 0  # with the normal budget no wait runs out
 
 
 def test_deterministic_repeat():

@@ -3,7 +3,8 @@
 right in any case but costs milliseconds.  These tests guard the normal path: a call with rate
 control must not reach a fallback when the launch needs more workgroups than the GPU holds at once
 (tiles of 256 values: 2048 rate workgroups) or when other streams' kernels hold the CUs.  A call
-takes about 0.1-0.2 ms normally and several milliseconds on a fallback; the bound is 5 ms."""
+takes about 0.1-0.2 ms normally and several milliseconds on a fallback; the bound is 5 ms, and
+hq_fallbacks must report none for the workspace's last call."""
 import numpy as np
 import pytest
 
@@ -49,6 +50,7 @@ def test_rate_control_takes_its_normal_path(tile):
     times, ws = timed_encodes(x, tile)
     torch.cuda.synchronize()
     assert hq.hq_status(ws) == hq.HQ_OK
+    assert hq.hq_fallbacks(ws) == 0  # the last call: no wait ran out of its budget
     ms = [a.elapsed_time(b) for a, b in times[1:]]
     assert max(ms) < BOUND_MS, ms
 
@@ -80,5 +82,6 @@ def test_rate_control_beside_other_streams():
     torch.cuda.synchronize()
     for out, y, ws, wsd in bufs:
         assert hq.hq_status(ws) == hq.HQ_OK and hq.hq_status(wsd) == hq.HQ_OK
+        assert hq.hq_fallbacks(ws) == 0
     ms = [a.elapsed_time(b) for a, b in marks]
     assert max(ms) < BOUND_MS, ms
