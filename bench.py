@@ -208,7 +208,6 @@ def time_call(hq, torch, x, lat, tb, seed, dither, steps, warmup, out=None, ws=N
     torch.cuda.synchronize()
     st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
-    fallbacks = hq.hq_fallbacks(ws)  # the last timed encode: waits that ran out of their budget
     r = {"encode_ms": float(np.mean([a.elapsed_time(b) for a, b, _ in ev])),
          "decode_ms": float(np.mean([b.elapsed_time(c) for _, b, c in ev])),
          "step_ms": step_ms}
@@ -719,6 +718,7 @@ def measure(hq, torch, x_host, cfg, seed, K, W):
     step_ms = t_start.elapsed_time(t_end) / K
     st, st2 = hq.hq_status(ws), hq.hq_status(ws_dec)
     assert st == 0 and st2 == 0, (st, st2)
+    fallbacks = hq.hq_fallbacks(ws)  # the last timed encode: waits that ran out of their budget
     g_step = out[:128].clone()
 
     # breakdown (separate loops): encode with rate control, decode; rate control, the encode kernel
